@@ -1,0 +1,228 @@
+"""Benchmark of the KATA causal linear-attention forward on one MI355X.
+
+Default workload (the headline metric): the exact O(T) chunked-state forward,
+B=1, H=16, T=131072, p=32 (n=528), dv=64, bf16 inputs, fp32 accumulation, C=64,
+associative inter-segment scan; seeded N(0,1) synthetic inputs (seed 2).
+One step = one kata_chunked_fwd call = every kernel of the forward (segment summaries,
+scan, chunk pass). Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--chunk 64|128] [--scan associative|sequential]
+                    [--workload long|quadratic|decode] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "kernelized_linear_attention_normalize_amd", "csrc")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources; a traffic figure is only reported for the exact sources
+    its counters were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str):
+    """HBM bytes per launch from a committed counter summary (profiles/<name>), or None
+    when absent or taken on different sources."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash() or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def chunked_flops_per_head_token(n: int, p: int, dv: int, C: int) -> int:
+    # state readout + state build: 2 n (dv+1) each; causal intra-chunk pairs: (C+1)/2 per
+    # token, 2p (score) + 2(dv+1) (weighted [V | 1]) each
+    return 4 * n * (dv + 1) + (C + 1) * (p + dv + 1)
+
+
+def cpu_baseline_long(q, k, v, H, budget_s=15.0):
+    """The float64 oracle (definition form, per query row) on uniformly sampled rows of
+    head 0 of the same workload; tokens/s = rows/s / H (a token needs all H heads)."""
+    from oracle import kata_oracle as ko
+    T = q.shape[-2]
+    rng = np.random.default_rng(5)
+    rows_done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = sorted(rng.integers(0, T, 16).tolist())
+        ko.naive_rows(q[0, 0], k[0, 0], v[0, 0], rows)
+        rows_done += len(rows)
+    el = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": rows_done / el / H, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle.naive_rows (float64) on {rows_done} uniformly sampled query rows of "
+                      f"head 0 of the T={T} workload in {el:.1f} s; tokens/s = rows/s / {H} heads; "
+                      f"BLAS threads = {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--scan", default="associative", choices=["associative", "sequential"])
+    ap.add_argument("--workload", default="long", choices=["long", "quadratic", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kernelized_linear_attention_normalize_amd as kata
+    from kata_inputs import DECODE, WORKLOADS, draw_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.workload == "long":
+        w = WORKLOADS["long"]
+        B, H, T, p, dv, C = w.B, w.H, w.T, w.p, w.dv, args.chunk
+        q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd = to(q), to(k), to(v)
+        out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+        need = kata.chunked_workspace_bytes(B, H, T, p, dv, C, kata._scan_code(args.scan))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        step = lambda: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws)
+        n = p * (p + 1) // 2
+        flops = chunked_flops_per_head_token(n, p, dv, C) * B * H * T
+        units = B * T
+        metric = "chunked KATA fwd tokens/s at T=131072 (1 GPU) + % bf16 MFMA peak"
+        config = {"workload": f"long: chunked forward B={B} H={H} T={T} p={p} (n={n}) dv={dv} "
+                              f"C={C} scan={args.scan}", "global_batch": B, "seq_len": T,
+                  "heads": H, "p": p, "dv": dv, "chunk": C, "scan": args.scan,
+                  "parallelism": "single-gpu"}
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        traffic_file = f"chunked_long_C{C}_{args.scan}_traffic.txt"
+    elif args.workload == "quadratic":
+        w = WORKLOADS["quadratic"]
+        B, H, T, p, dv = w.B, w.H, w.T, w.p, w.dv
+        q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd = to(q), to(k), to(v)
+        out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+        step = lambda: kata.quadratic_fwd(qd, kd, vd, out=out)
+        pairs = B * H * T * (T + 1) // 2
+        flops = (2 * p + 2 * (dv + 1)) * pairs
+        units = B * T
+        metric = "flash-style KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
+        config = {"workload": f"quadratic: flash-style forward B={B} H={H} T={T} p={p} dv={dv}",
+                  "global_batch": B, "seq_len": T, "heads": H, "p": p, "dv": dv,
+                  "parallelism": "single-gpu"}
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        traffic_file = "quadratic_traffic.txt"
+    else:
+        from oracle import kata_oracle as ko  # state prefill of the decode workload (input data)
+        from kata_inputs import draw_decode_history, draw_decode_steps
+        N, H, p, dv = DECODE["N"], DECODE["H"], DECODE["p"], DECODE["dv"]
+        n = p * (p + 1) // 2
+        kh, vh = draw_decode_history(DECODE["hist_seed"], N, H, DECODE["hist"], p, dv)
+        S0 = np.empty((N, H, n, dv), np.float32)
+        Z0 = np.empty((N, H, n), np.float32)
+        for i in range(N):
+            s, z = ko.prefill_state(kh[i], vh[i])
+            S0[i], Z0[i] = s, z
+        del kh, vh
+        qs, ks, vs = draw_decode_steps(DECODE["step_seed"], DECODE["steps"], N, H, p, dv)
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd = to(qs), to(ks), to(vs)
+        S = torch.from_numpy(S0).to(dev)
+        Z = torch.from_numpy(Z0).to(dev)
+        out = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+        nsteps = DECODE["steps"]
+        ctr = {"i": 0}
+
+        def step():
+            i = ctr["i"] % nsteps
+            ctr["i"] += 1
+            return kata.decode_step(qd[i], kd[i], vd[i], S, Z, out=out)
+        flops = None
+        units = N
+        bytes_alg = N * H * (2 * n * dv * 4 + 2 * n * 4 + (2 * p + 2 * dv) * 2)
+        metric = "recurrent decode step tokens/s (128 seqs x 16 heads) + % HBM bandwidth"
+        config = {"workload": f"decode: {N} sequences x H={H}, p={p} (n={n}) dv={dv}, fp32 state "
+                              f"from a {DECODE['hist']}-token history, bf16 tokens",
+                  "global_batch": N, "heads": H, "p": p, "dv": dv, "parallelism": "single-gpu"}
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        traffic_file = "decode_traffic.txt"
+
+    torch.cuda.synchronize(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_total = e0.elapsed_time(e1)
+    ms = ms_total / args.steps
+    value = units / (ms * 1e-3)
+
+    if flops is not None:
+        achieved = flops / (ms * 1e-3) / 1e12
+        alg_per_launch = flops
+    else:
+        achieved = bytes_alg / (ms * 1e-3) / 1e9
+        alg_per_launch = bytes_alg
+    traffic = read_traffic(traffic_file)
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "algorithmic_per_launch": alg_per_launch,
+            "launch": "one API call (all kernels of one step)"}
+
+    # spot parity on a few rows (outside the timed region)
+    parity = None
+    if args.workload in ("long", "quadratic"):
+        from oracle import kata_oracle as ko
+        res = out.float().cpu().numpy()
+        rows = [0, 1, 63, 64, T // 2, T - 1]
+        parity = max(ko.row_rel_err(res[0, h, rows], ko.naive_rows(q[0, h], k[0, h], v[0, h], rows))
+                     for h in (0, H - 1))
+
+    cpu = None
+    if args.workload == "long" and not args.no_cpu_baseline:
+        cpu = cpu_baseline_long(q, k, v, H)
+
+    rec = {"metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1))", "config": config, "roofline": roof,
+           "cpu_baseline": cpu, "parity_row_rel_err": parity, "source_hash": source_hash()}
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

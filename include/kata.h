@@ -1,0 +1,145 @@
+/*
+ * kata.h - C ABI of the MI355X (gfx950) KATA causal linear-attention library.
+ *
+ * The method: "Kernelized Linear Attention: Breaking the Capacity Wall with Symmetric
+ * Cones" (Ghriss & Chakraborty, arXiv 2607.17419). Each query and key is projected onto
+ * the unit sphere and lifted to the rank-one PSD feature psi(u) = u u^T (arXiv HTML page,
+ * rank-one lift display after Eq. (8)); the feature is stored in n = p(p+1)/2 packed
+ * coordinates (Eq. (8)); the output is the normalized causal readout
+ *     o_t = psi(q_t)^T S_t / psi(q_t)^T Z_t,  S_t = sum_{s<=t} psi(k_s) v_s^T,
+ *     Z_t = sum_{s<=t} psi(k_s)
+ * (normalized-readout paragraph; feature-value state display). Equivalently
+ *     o_t = sum_{s<=t} (q_hat_t . k_hat_s)^2 v_s / sum_{s<=t} (q_hat_t . k_hat_s)^2.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory, allocated and owned by the caller, contiguous
+ *     row-major, 16-byte aligned. The library never allocates, never frees, never
+ *     synchronises and keeps no mutable global state; calls only enqueue work on
+ *     `stream` and return. Results are valid once the stream has executed the work.
+ *   - Arguments are validated on the host before any HIP call. A call with a zero-sized
+ *     problem (rows, B, H, T or N equal to 0) does nothing and returns KATA_OK; its
+ *     pointers may then be NULL.
+ *   - Packed feature order: row-major upper triangle including the diagonal,
+ *     idx(i,j) = i*p - i*(i-1)/2 + (j-i) for 0 <= i <= j < p; off-diagonal entries carry
+ *     a factor sqrt(2) so that <psi(a), psi(b)> = (a_hat . b_hat)^2 and ||psi(a)|| = 1.
+ *   - A zero input vector lifts to zero (no epsilon); a zero denominator gives a zero
+ *     output row (no epsilon). Causality is inclusive (s <= t). NaN/Inf propagate.
+ *   - dtype: KATA_DTYPE_F32 (float) or KATA_DTYPE_BF16 (bfloat16, stored as uint16).
+ *     bf16 inputs are computed with bf16 MFMA operands and fp32 accumulation; fp32 inputs
+ *     are computed in fp32 throughout.
+ *   - Errors are reported only through the returned status; KATA_ERR_HIP means the
+ *     kernel launch failed (hipGetLastError) and the outputs are unspecified.
+ */
+#ifndef KATA_H
+#define KATA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* kata_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum { KATA_DTYPE_F32 = 0, KATA_DTYPE_BF16 = 1 } kata_dtype_t;
+
+typedef enum {
+  /* The inter-chunk prefix is one sequential pass over all chunks: one workgroup per
+   * (b,h) carries the state through every chunk (depth N_C; the pages' sequential
+   * chunk traversal, chunked-forward paragraph). Needs no workspace. */
+  KATA_SCAN_SEQUENTIAL = 0,
+  /* Chunks are grouped into segments; per-segment state summaries are combined by a
+   * log-depth (Hillis-Steele) associative scan, then every segment runs its chunks from
+   * its exclusive prefix (chunked-forward paragraph: the prefix over chunks is an
+   * associative vector-space cumulative sum). Needs the workspace. */
+  KATA_SCAN_ASSOCIATIVE = 1
+} kata_scan_t;
+
+typedef enum {
+  KATA_OK = 0,
+  KATA_ERR_NULL = 1,        /* a required pointer is NULL */
+  KATA_ERR_SHAPE = 2,       /* a size is negative, zero where it must be positive, or too large */
+  KATA_ERR_DTYPE = 3,       /* a dtype argument is not a kata_dtype_t value */
+  KATA_ERR_UNSUPPORTED = 4, /* valid but not implemented (p, dv, C combination) */
+  KATA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  KATA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+  KATA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than kata_chunked_workspace_bytes */
+  KATA_ERR_HIP = 8,         /* a HIP launch failed */
+  KATA_ERR_SCAN = 9         /* scan is not a kata_scan_t value */
+} kata_status_t;
+
+/* n = p(p+1)/2 (Eq. (8)); -1 if p < 1. */
+int64_t kata_packed_dim(int p);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kata_status_string(kata_status_t s);
+
+/*
+ * kata_lift - packed rank-one lift of each row (rank-one lift display after Eq. (8)).
+ *   u   : [rows, p] in u_dt.           psi : [rows, n] in psi_dt, n = p(p+1)/2.
+ *   psi[r, idx(i,j)] = c_ij * u_hat[r,i] * u_hat[r,j], c_ii = 1, c_ij = sqrt(2) (i<j),
+ *   u_hat = u / ||u|| computed in fp32 (zero row -> zero lift).
+ *   Supported: 1 <= p <= 128. psi must not overlap u (KATA_ERR_ALIAS).
+ */
+kata_status_t kata_lift(const void* u, kata_dtype_t u_dt, int64_t rows, int p,
+                        void* psi, kata_dtype_t psi_dt, kata_stream_t stream);
+
+/*
+ * Workspace bytes kata_chunked_fwd needs for these arguments (0 if none). Depends only
+ * on its arguments, not on the device. Returns 0 for arguments kata_chunked_fwd would
+ * reject.
+ */
+size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C,
+                                    kata_scan_t scan, kata_dtype_t in_dt);
+
+/*
+ * kata_chunked_fwd - exact O(T) chunked-state forward (chunked-forward paragraph).
+ *   q, k : [B, H, T, p] in in_dt.   v : [B, H, T, dv] in in_dt.   o : [B, H, T, dv] in o_dt.
+ *   Per chunk of C tokens: the intra-chunk causal block (q_hat . k_hat)^2 over s <= t in
+ *   the chunk, plus the readout psi(q_t)^T [S | Z] of the state accumulated over all
+ *   earlier chunks; then the chunk's psi(K)^T [V | 1] is added to the state.
+ *   T need not be a multiple of C (the tail chunk is zero-padded; zero keys add nothing).
+ *   workspace: device buffer of at least kata_chunked_workspace_bytes(...) bytes,
+ *   owned by the caller; its contents on entry are ignored and on exit unspecified.
+ *   It may be NULL when that size is 0.
+ *   Supported: p in {16, 32}; dv in {16, 32, 64}; C in {32, 64, 128}.
+ *   o must not overlap q, k, v or the workspace.
+ */
+kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                               int C, kata_scan_t scan, void* workspace,
+                               size_t workspace_bytes, kata_stream_t stream);
+
+/*
+ * kata_quadratic_fwd - flash-attention-style forward without a state (abstract: the
+ * flash-attention-style operating point). For each query block the kernel walks the key
+ * blocks s <= t, accumulating sum_s (q_hat . k_hat_s)^2 [v_s | 1] on chip, and divides
+ * once at the end. Weights lie in [0, 1], so no running maximum or rescaling is needed.
+ *   q, k : [B, H, T, p] in in_dt.   v, o : [B, H, T, dv] (o in o_dt).
+ *   Supported: p in {16, 32, 64}; dv in {16, 32, 64}. o must not overlap q, k, v.
+ */
+kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                 void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                 kata_stream_t stream);
+
+/*
+ * kata_decode_step - one recurrent inference step per sequence and head (abstract:
+ * constant-time recurrent inference; feature-value state display): update, then read out
+ *     S += psi(k) v^T,  Z += psi(k),  o = psi(q)^T S / psi(q)^T Z.
+ *   q, k : [N, H, p] in in_dt.   v : [N, H, dv] in in_dt.   o : [N, H, dv] in o_dt.
+ *   S : [N, H, n, dv] float32 and Z : [N, H, n] float32, packed order above; both are
+ *   read and updated IN PLACE (they are the complete recurrent state: saving them is a
+ *   checkpoint, resuming from them continues bit for bit).
+ *   Supported: 1 <= p <= 64; 1 <= dv <= 64 with dv % 4 == 0.
+ *   o, S and Z must not overlap each other or q, k, v.
+ */
+kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               float* S, float* Z, void* o, kata_dtype_t o_dt, int N, int H,
+                               int p, int dv, kata_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATA_H */

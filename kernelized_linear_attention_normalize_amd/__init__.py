@@ -1,0 +1,187 @@
+"""Python binding of libkata.so, the MI355X (gfx950) KATA causal linear-attention library.
+
+Thin ctypes layer: it checks tensor placement, dtype and contiguity, allocates outputs
+and workspaces with torch on the tensors' device, and passes raw device pointers and the
+current HIP stream to the C ABI declared in include/kata.h. Every step of the computation
+runs in the library's HIP kernels; there is no CPU path. If the library is missing the
+calls raise.
+
+The method: "Kernelized Linear Attention: Breaking the Capacity Wall with Symmetric
+Cones" (arXiv 2607.17419): o_t = psi(q_t)^T S_t / psi(q_t)^T Z_t with the rank-one lift
+psi(u) = u_hat u_hat^T packed into n = p(p+1)/2 coordinates.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["KataError", "library_path", "load", "packed_dim", "lift", "chunked_workspace_bytes",
+           "chunked_fwd", "quadratic_fwd", "decode_step", "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkata.so")
+_lib = None
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+SCAN_SEQUENTIAL, SCAN_ASSOCIATIVE = 0, 1
+_STATUS = {0: "KATA_OK", 1: "KATA_ERR_NULL", 2: "KATA_ERR_SHAPE", 3: "KATA_ERR_DTYPE",
+           4: "KATA_ERR_UNSUPPORTED", 5: "KATA_ERR_ALIGN", 6: "KATA_ERR_ALIAS",
+           7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN"}
+
+
+class KataError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkata.so (raises if it has not been built) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.kata_packed_dim.argtypes, lib.kata_packed_dim.restype = [I], I64
+    lib.kata_status_string.argtypes, lib.kata_status_string.restype = [I], ctypes.c_char_p
+    lib.kata_lift.argtypes, lib.kata_lift.restype = [P, I, I64, I, P, I, P], I
+    lib.kata_chunked_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.kata_chunked_workspace_bytes.restype = SZ
+    lib.kata_chunked_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, P]
+    lib.kata_chunked_fwd.restype = I
+    lib.kata_quadratic_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, P]
+    lib.kata_quadratic_fwd.restype = I
+    lib.kata_decode_step.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P]
+    lib.kata_decode_step.restype = I
+    _lib = lib
+    return lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("KATA tensors must be on a GPU device (no CPU path)")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("KATA tensors must be contiguous")
+    return dev
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KataError(status, where)
+
+
+def packed_dim(p: int) -> int:
+    return int(load().kata_packed_dim(p))
+
+
+def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """[..., p] -> [..., p(p+1)/2]: packed psi(u_hat) (rank-one lift, after Eq. (8))."""
+    lib = load()
+    dev = _dev(u)
+    p = u.shape[-1]
+    rows = u.numel() // p if p else 0
+    out = torch.empty(u.shape[:-1] + (packed_dim(p),), dtype=out_dtype or u.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_lift(u.data_ptr(), _dt(u), rows, p, out.data_ptr(), _dt(out),
+                             _stream(dev)), "kata_lift")
+    return out
+
+
+def chunked_workspace_bytes(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16):
+    return int(load().kata_chunked_workspace_bytes(B, H, T, p, dv, C, int(scan),
+                                                   DTYPE_BF16 if in_dtype == torch.bfloat16 else DTYPE_F32))
+
+
+def _scan_code(scan) -> int:
+    if isinstance(scan, str):
+        return {"sequential": SCAN_SEQUENTIAL, "associative": SCAN_ASSOCIATIVE}[scan]
+    return int(scan)
+
+
+def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,
+                workspace=None):
+    """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv]."""
+    lib = load()
+    dev = _dev(q, k, v)
+    B, H, T, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k and v")
+    sc = _scan_code(scan)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
+    _dev(out, q)
+    need = int(lib.kata_chunked_workspace_bytes(B, H, T, p, dv, C, sc, _dt(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        _check(lib.kata_chunked_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                    out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc, ws_ptr,
+                                    ws_bytes, _stream(dev)), "kata_chunked_fwd")
+    return out
+
+
+def quadratic_fwd(q, k, v, out_dtype=None, out=None):
+    """Flash-style quadratic forward (no state). q, k: [B,H,T,p]; v: [B,H,T,dv]."""
+    lib = load()
+    dev = _dev(q, k, v)
+    B, H, T, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k and v")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
+    _dev(out, q)
+    with torch.cuda.device(dev):
+        _check(lib.kata_quadratic_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                      out.data_ptr(), _dt(out), B, H, T, p, dv, _stream(dev)),
+               "kata_quadratic_fwd")
+    return out
+
+
+def decode_step(q, k, v, S, Z, out_dtype=None, out=None):
+    """One recurrent step: S += psi(k) v^T, Z += psi(k), o = psi(q)^T S / psi(q)^T Z.
+    q, k: [N,H,p]; v: [N,H,dv]; S: [N,H,n,dv] fp32 and Z: [N,H,n] fp32 updated in place."""
+    lib = load()
+    dev = _dev(q, k, v, S, Z)
+    N, H, p = q.shape
+    dv = v.shape[-1]
+    n = packed_dim(p)
+    if S.dtype != torch.float32 or Z.dtype != torch.float32:
+        raise TypeError("S and Z must be float32")
+    if tuple(S.shape) != (N, H, n, dv) or tuple(Z.shape) != (N, H, n):
+        raise ValueError("state shape mismatch")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=out_dtype or v.dtype, device=dev)
+    _dev(out, q)
+    with torch.cuda.device(dev):
+        _check(lib.kata_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                    S.data_ptr(), Z.data_ptr(), out.data_ptr(), _dt(out), N, H, p,
+                                    dv, _stream(dev)), "kata_decode_step")
+    return out

@@ -1,0 +1,234 @@
+// C ABI of the KATA library: argument validation (host only, before any HIP call),
+// dtype/shape dispatch, workspace sizing and kernel launches on the caller's stream.
+// The entry points are declared, with their contracts, in include/kata.h.
+#include "kata.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "kata_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = INT32_MAX;
+
+bool valid_dt(kata_dtype_t d) { return d == KATA_DTYPE_F32 || d == KATA_DTYPE_BF16; }
+size_t dt_size(kata_dtype_t d) { return d == KATA_DTYPE_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool in_set(int x, std::initializer_list<int> s) {
+  for (int y : s)
+    if (x == y) return true;
+  return false;
+}
+
+// element count a*b*c*d without signed overflow, or -1
+int64_t mul4(int64_t a, int64_t b, int64_t c, int64_t d) {
+  const int64_t lim = INT64_MAX / 8;
+  int64_t r = 1;
+  for (int64_t x : {a, b, c, d}) {
+    if (x != 0 && r > lim / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+kata_status_t hip_status(hipError_t e) { return e == hipSuccess ? KATA_OK : KATA_ERR_HIP; }
+
+}  // namespace
+
+namespace kata {
+
+SegPlan seg_plan(int B, int H, int T, int C, int scan) {
+  SegPlan s;
+  s.nchunks = (T + C - 1) / C;
+  if (scan == KATA_SCAN_SEQUENTIAL || s.nchunks <= 1) {
+    s.nseg = 1;
+    s.cps = s.nchunks;
+    return s;
+  }
+  // aim for about one workgroup per compute unit of a 256-CU part; at most 64 segments
+  const int64_t BH = (int64_t)B * H;
+  int64_t want = (256 + BH - 1) / BH;
+  if (want > 64) want = 64;
+  if (want > s.nchunks) want = s.nchunks;
+  if (want < 1) want = 1;
+  s.cps = (int)((s.nchunks + want - 1) / want);
+  s.nseg = (s.nchunks + s.cps - 1) / s.cps;
+  return s;
+}
+
+}  // namespace kata
+
+extern "C" {
+
+int64_t kata_packed_dim(int p) { return p < 1 ? -1 : (int64_t)p * (p + 1) / 2; }
+
+const char* kata_status_string(kata_status_t s) {
+  switch (s) {
+    case KATA_OK: return "KATA_OK";
+    case KATA_ERR_NULL: return "KATA_ERR_NULL: a required pointer is NULL";
+    case KATA_ERR_SHAPE: return "KATA_ERR_SHAPE: invalid or too large size";
+    case KATA_ERR_DTYPE: return "KATA_ERR_DTYPE: invalid dtype";
+    case KATA_ERR_UNSUPPORTED: return "KATA_ERR_UNSUPPORTED: unsupported p / dv / C combination";
+    case KATA_ERR_ALIGN: return "KATA_ERR_ALIGN: pointer not 16-byte aligned";
+    case KATA_ERR_ALIAS: return "KATA_ERR_ALIAS: output overlaps another buffer";
+    case KATA_ERR_WORKSPACE: return "KATA_ERR_WORKSPACE: workspace missing or too small";
+    case KATA_ERR_HIP: return "KATA_ERR_HIP: kernel launch failed";
+    case KATA_ERR_SCAN: return "KATA_ERR_SCAN: invalid scan mode";
+  }
+  return "KATA_ERR_UNKNOWN";
+}
+
+kata_status_t kata_lift(const void* u, kata_dtype_t u_dt, int64_t rows, int p, void* psi,
+                        kata_dtype_t psi_dt, kata_stream_t stream) {
+  if (!valid_dt(u_dt) || !valid_dt(psi_dt)) return KATA_ERR_DTYPE;
+  if (rows < 0 || p < 1) return KATA_ERR_SHAPE;
+  if (p > 128) return KATA_ERR_UNSUPPORTED;
+  if (rows == 0) return KATA_OK;
+  const int64_t n = kata_packed_dim(p);
+  if (mul4(rows, n, 1, 1) < 0 || (rows + 15) / 16 > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!u || !psi) return KATA_ERR_NULL;
+  if (!aligned16(u) || !aligned16(psi)) return KATA_ERR_ALIGN;
+  if (overlap(u, rows * p * dt_size(u_dt), psi, rows * n * dt_size(psi_dt))) return KATA_ERR_ALIAS;
+  return hip_status(kata::launch_lift(u, u_dt == KATA_DTYPE_BF16, rows, p, psi,
+                                      psi_dt == KATA_DTYPE_BF16, (hipStream_t)stream));
+}
+
+// shared checks of the [B,H,T,*] forward entry points; returns KATA_OK to continue,
+// or a status to return (zero_size set when the call is a no-op)
+static kata_status_t check_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               const void* o, kata_dtype_t o_dt, int B, int H, int T, int p,
+                               int dv, bool& zero_size) {
+  zero_size = false;
+  if (!valid_dt(in_dt) || !valid_dt(o_dt)) return KATA_ERR_DTYPE;
+  if (B < 0 || H < 0 || T < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
+  if ((int64_t)B * H * T == 0) {
+    zero_size = true;
+    return KATA_OK;
+  }
+  if (mul4(B, H, T, p > dv ? p : dv) < 0) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !o) return KATA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KATA_ERR_ALIGN;
+  return KATA_OK;
+}
+
+static kata_status_t check_fwd_alias(const void* q, const void* k, const void* v,
+                                     kata_dtype_t in_dt, const void* o, kata_dtype_t o_dt, int B,
+                                     int H, int T, int p, int dv) {
+  const size_t rows = (size_t)B * H * T;
+  const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
+  const size_t ob = rows * dv * dt_size(o_dt);
+  if (overlap(o, ob, q, qb) || overlap(o, ob, k, qb) || overlap(o, ob, v, vb)) return KATA_ERR_ALIAS;
+  return KATA_OK;
+}
+
+size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan,
+                                    kata_dtype_t in_dt) {
+  if (!valid_dt(in_dt) || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
+  if (B <= 0 || H <= 0 || T <= 0 || p < 1 || dv < 1 || C < 1) return 0;
+  if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128})) return 0;
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  if (plan.nseg <= 1) return 0;
+  const int64_t sf = in_dt == KATA_DTYPE_BF16 ? kata::mfma_state_floats(p, dv) : kata::f32_state_floats(p, dv);
+  return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
+}
+
+kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                               int C, kata_scan_t scan, void* workspace, size_t workspace_bytes,
+                               kata_stream_t stream) {
+  if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
+  if (C < 1) return KATA_ERR_SHAPE;
+  bool zero = false;
+  kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
+  if (s != KATA_OK || zero) return s;
+  if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128}))
+    return KATA_ERR_UNSUPPORTED;
+  if (in_dt == KATA_DTYPE_F32 && kata::f32_chunked_lds_bytes(p, dv, C) > 160 * 1024)
+    return KATA_ERR_UNSUPPORTED;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
+  const size_t need = kata_chunked_workspace_bytes(B, H, T, p, dv, C, scan, in_dt);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KATA_ERR_ALIGN;
+    const size_t ob = (size_t)B * H * T * dv * dt_size(o_dt);
+    if (overlap(o, ob, workspace, need)) return KATA_ERR_ALIAS;
+  }
+  float* ws = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  const bool ob16 = o_dt == KATA_DTYPE_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  if (in_dt == KATA_DTYPE_BF16)
+    return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k),
+                                                static_cast<const uint16_t*>(v), o, ob16, B, H, T,
+                                                p, dv, C, plan, ws, st));
+  return hip_status(kata::launch_chunked_f32(static_cast<const float*>(q),
+                                             static_cast<const float*>(k),
+                                             static_cast<const float*>(v), o, ob16, B, H, T, p, dv,
+                                             C, plan, ws, st));
+}
+
+kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                 void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                 kata_stream_t stream) {
+  bool zero = false;
+  kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
+  if (s != KATA_OK || zero) return s;
+  if (!in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) return KATA_ERR_UNSUPPORTED;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
+  if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
+  const bool ob16 = o_dt == KATA_DTYPE_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  if (in_dt == KATA_DTYPE_BF16)
+    return hip_status(kata::launch_quadratic_bf16(static_cast<const uint16_t*>(q),
+                                                  static_cast<const uint16_t*>(k),
+                                                  static_cast<const uint16_t*>(v), o, ob16, B, H,
+                                                  T, p, dv, st));
+  return hip_status(kata::launch_quadratic_f32(static_cast<const float*>(q),
+                                               static_cast<const float*>(k),
+                                               static_cast<const float*>(v), o, ob16, B, H, T, p,
+                                               dv, st));
+}
+
+kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               float* S, float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
+                               int dv, kata_stream_t stream) {
+  if (!valid_dt(in_dt) || !valid_dt(o_dt)) return KATA_ERR_DTYPE;
+  if (N < 0 || H < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
+  if (p > 64 || dv > 64 || dv % 4 != 0) return KATA_ERR_UNSUPPORTED;
+  const int64_t NH = (int64_t)N * H;
+  if (NH == 0) return KATA_OK;
+  if (NH > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !S || !Z || !o) return KATA_ERR_NULL;
+  for (const void* ptr : {q, k, v, (const void*)S, (const void*)Z, (const void*)o})
+    if (!aligned16(ptr)) return KATA_ERR_ALIGN;
+  const int64_t n = kata_packed_dim(p);
+  const size_t qb = NH * p * dt_size(in_dt), vb = NH * dv * dt_size(in_dt);
+  const size_t ob = NH * dv * dt_size(o_dt), Sb = NH * n * dv * 4, Zb = NH * n * 4;
+  const void* outs[3] = {o, S, Z};
+  const size_t outb[3] = {ob, Sb, Zb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], outb[i], q, qb) || overlap(outs[i], outb[i], k, qb) ||
+        overlap(outs[i], outb[i], v, vb))
+      return KATA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
+  }
+  return hip_status(kata::launch_decode(q, k, v, in_dt == KATA_DTYPE_BF16, S, Z, o,
+                                        o_dt == KATA_DTYPE_BF16, N, H, p, dv,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,13 @@
+// Instantiations of the bf16 chunked forward for p = 16, dv = 64 (see kata_chunked.h).
+#include "kata_chunked.h"
+
+namespace kata {
+namespace chk {
+template hipError_t launch_pdc<16, 64, 32>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
+                                         int, int, const SegPlan&, float*, hipStream_t);
+template hipError_t launch_pdc<16, 64, 64>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
+                                         int, int, const SegPlan&, float*, hipStream_t);
+template hipError_t launch_pdc<16, 64, 128>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
+                                          int, int, const SegPlan&, float*, hipStream_t);
+}  // namespace chk
+}  // namespace kata

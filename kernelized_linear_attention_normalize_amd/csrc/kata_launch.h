@@ -1,0 +1,40 @@
+// Internal host-side launchers (one per kernel family). Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kata {
+
+// segment plan of the chunked forward (shared by the workspace query and the launch)
+struct SegPlan {
+  int nchunks;       // ceil(T / C)
+  int nseg;          // number of segments per (b,h)
+  int cps;           // chunks per segment (last segment may have fewer)
+};
+SegPlan seg_plan(int B, int H, int T, int C, int scan);
+
+// floats of one segment summary in the bf16 MFMA kernel's tile layout
+int64_t mfma_state_floats(int p, int dv);
+// floats of one segment summary in the fp32 kernel's layout (S then Z, packed order)
+int64_t f32_state_floats(int p, int dv);
+// dynamic LDS bytes of the fp32 chunked kernel (0 if it cannot run)
+size_t f32_chunked_lds_bytes(int p, int dv, int C);
+
+hipError_t launch_lift(const void* u, bool u_bf16, int64_t rows, int p, void* psi, bool psi_bf16,
+                       hipStream_t st);
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf16, float* S,
+                         float* Z, void* o, bool o_bf16, int N, int H, int p, int dv,
+                         hipStream_t st);
+hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
+                              int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
+                              float* ws, hipStream_t st);
+hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
+                                bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
+hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                               bool o_bf16, int B, int H, int T, int p, int dv, int C,
+                               const SegPlan& plan, float* ws, hipStream_t st);
+hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
+
+}  // namespace kata

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry
+point declared in include/kata.h, and validates arguments before any HIP call.
+
+Only validation paths are exercised: every call below returns an error (or is a zero-size
+no-op) before the library touches the device; the fake pointers are never dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kernelized_linear_attention_normalize_amd as kata
+from kernelized_linear_attention_normalize_amd import build_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, BF16 = 0, 1
+SEQ, ASSOC = 0, 1
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN = range(10)
+A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kata.library_path()):
+        build_lib.build()
+    return kata.load()
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "kata.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kata_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"kata_lift", "kata_chunked_fwd", "kata_quadratic_fwd", "kata_decode_step",
+                          "kata_packed_dim", "kata_status_string", "kata_chunked_workspace_bytes"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_packed_dim_and_status_strings(lib):
+    assert lib.kata_packed_dim(32) == 528 and lib.kata_packed_dim(64) == 2080
+    assert lib.kata_packed_dim(0) == -1
+    for s in range(10):
+        assert lib.kata_status_string(s).startswith(b"KATA_")
+
+
+def _chunked(lib, q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=1, H=1, T=128,
+             p=32, dv=64, C=64, scan=SEQ, ws=None, wsb=0):
+    return lib.kata_chunked_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, ws, wsb, None)
+
+
+def test_chunked_validation(lib):
+    assert _chunked(lib, in_dt=7) == E_DTYPE
+    assert _chunked(lib, o_dt=-1) == E_DTYPE
+    assert _chunked(lib, scan=5) == E_SCAN
+    assert _chunked(lib, T=-1) == E_SHAPE
+    assert _chunked(lib, C=0) == E_SHAPE
+    assert _chunked(lib, p=0) == E_SHAPE
+    assert _chunked(lib, T=0, q=None, k=None, v=None, o=None) == OK       # zero-size no-op
+    assert _chunked(lib, B=0) == OK
+    assert _chunked(lib, q=None) == E_NULL
+    assert _chunked(lib, o=None) == E_NULL
+    assert _chunked(lib, k=A + 4) == E_ALIGN
+    assert _chunked(lib, p=24) == E_UNSUP
+    assert _chunked(lib, p=64) == E_UNSUP
+    assert _chunked(lib, dv=48) == E_UNSUP
+    assert _chunked(lib, C=16) == E_UNSUP
+    assert _chunked(lib, o=A + 4096) == E_ALIAS                          # o overlaps k
+    # associative mode needs the workspace
+    need = lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16)
+    assert need > 0
+    kw = dict(B=1, H=16, T=131072, scan=ASSOC, o=A + (1 << 34))
+    assert _chunked(lib, **kw) == E_WS
+    assert _chunked(lib, ws=A + (1 << 36), wsb=need - 1, **kw) == E_WS
+    assert _chunked(lib, ws=A + (1 << 36) + 8, wsb=need, **kw) == E_ALIGN
+    assert _chunked(lib, ws=A + (1 << 34), wsb=need, **kw) == E_ALIAS    # workspace overlaps o
+    # fp32 path: state must fit in LDS
+    assert _chunked(lib, in_dt=F32, p=32, dv=64, C=128) == E_UNSUP
+
+
+def test_workspace_bytes(lib):
+    # sequential mode and single-segment problems need none
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, SEQ, BF16) == 0
+    assert lib.kata_chunked_workspace_bytes(1, 1, 64, 32, 64, 64, ASSOC, BF16) == 0
+    assert lib.kata_chunked_workspace_bytes(1, 1, 64, 33, 64, 64, ASSOC, BF16) == 0   # unsupported
+    # long config: 16 heads x 16 segments, 15 summaries each of (33 tiles x 4 + 4) x 256 floats
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16) == 16 * 15 * (33 * 4 * 256 + 4 * 256) * 4
+    # fp32 layout: n*dv + n floats per summary
+    w = lib.kata_chunked_workspace_bytes(1, 1, 256, 16, 16, 32, ASSOC, F32)
+    assert w == 7 * (136 * 16 + 136) * 4
+
+
+def test_quadratic_and_lift_and_decode_validation(lib):
+    q = lambda **kw: lib.kata_quadratic_fwd(kw.get("q", A), A + 4096, A + 8192, kw.get("dt", BF16),
+                                            kw.get("o", A + (1 << 30)), BF16, 1, 1, kw.get("T", 64),
+                                            kw.get("p", 64), kw.get("dv", 64), None)
+    assert q(dt=3) == E_DTYPE and q(T=-2) == E_SHAPE and q(T=0) == OK
+    assert q(p=48) == E_UNSUP and q(q=None) == E_NULL and q(o=A + 8192) == E_ALIAS
+    assert lib.kata_lift(A, F32, 10, 129, A + (1 << 30), F32, None) == E_UNSUP
+    assert lib.kata_lift(A, F32, -1, 8, A + (1 << 30), F32, None) == E_SHAPE
+    assert lib.kata_lift(A, F32, 0, 8, None, F32, None) == OK
+    assert lib.kata_lift(A, F32, 10, 8, A + 64, F32, None) == E_ALIAS
+    assert lib.kata_lift(A, 2, 10, 8, A + (1 << 30), F32, None) == E_DTYPE
+    d = lambda **kw: lib.kata_decode_step(A, A + 4096, A + 8192, BF16, kw.get("S", A + (1 << 30)),
+                                          kw.get("Z", A + (1 << 31)), kw.get("o", A + (1 << 32)), BF16,
+                                          kw.get("N", 4), 2, kw.get("p", 32), kw.get("dv", 64), None)
+    assert d(N=0) == OK and d(p=65) == E_UNSUP and d(dv=62) == E_UNSUP
+    assert d(S=None) == E_NULL and d(Z=A + (1 << 30) + 16) == E_ALIAS
+    assert d(o=A + 4096) == E_ALIAS and d(S=A + (1 << 30) + 4) == E_ALIGN

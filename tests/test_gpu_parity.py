@@ -1,0 +1,226 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bar: max over output rows of ||o_gpu - o_ref||_inf / ||o_ref||_inf <= 1e-4 for fp32 inputs
+and <= 2e-2 for bf16 inputs; the packed index map of kata_lift must match exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import kernelized_linear_attention_normalize_amd as kata
+from kata_inputs import WORKLOADS, draw_qkv, round_bf16
+from oracle import kata_oracle as ko
+from tests.gpu_util import TOL, row_rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(tag, seed, B, H, T, p, dv, dt):
+    print(f"[case] {tag} seed={seed} B={B} H={H} T={T} p={p} dv={dv} dtype={dt}", flush=True)
+    return draw_qkv(seed, B, H, T, p, dv, dt)
+
+
+# ------------------------------------------------------------------ lift
+@pytest.mark.parametrize("p", [1, 3, 16, 32, 64, 128])
+def test_lift_index_map_exact(p):
+    ii, jj = ko.packed_pairs(p)
+    n = ko.packed_dim(p)
+    rows = []
+    for i in range(p):
+        e = np.zeros(p, np.float32); e[i] = 2.0
+        rows.append(e)
+    for (i, j) in [(0, p - 1), (p // 2, p - 1), (0, p // 3)]:
+        if i != j:
+            e = np.zeros(p, np.float32); e[i] = e[j] = 1.0
+            rows.append(e)
+    u = np.stack(rows)
+    psi = to_np(kata.lift(to_dev(u, "f32")))
+    assert psi.shape == (len(rows), n)
+    for r in range(p):  # e_i -> a single 1 at the position of (i, i)
+        nz = np.flatnonzero(psi[r])
+        assert len(nz) == 1 and (ii[nz[0]], jj[nz[0]]) == (r, r) and psi[r, nz[0]] == 1.0
+    for r in range(p, len(rows)):
+        i, j = np.flatnonzero(u[r])[[0, -1]]
+        nz = set((int(ii[x]), int(jj[x])) for x in np.flatnonzero(psi[r]))
+        assert nz == {(i, i), (j, j), (i, j)}
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_lift_values(in_dt, out_dt):
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal((1000, 32)).astype(np.float32)
+    u[5] = 0.0
+    if in_dt == "bf16":
+        u = round_bf16(u)
+    out = kata.lift(to_dev(u, in_dt), out_dtype=torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    got = to_np(out)
+    ref = ko.lift(u)
+    tol = 1e-6 if out_dt == "f32" else 2 ** -8
+    assert np.all(got[5] == 0.0)
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) < tol * 4
+    assert np.allclose(np.linalg.norm(got[np.arange(1000) != 5], axis=-1), 1.0, atol=tol * 8)
+
+
+# ------------------------------------------------------------------ tiny (fp32)
+@pytest.mark.parametrize("scan", ["sequential", "associative"])
+def test_tiny_chunked(scan):
+    w = WORKLOADS["tiny"]
+    q, k, v = _case("tiny-chunked", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    ref = ko.naive(q, k, v)
+    got = to_np(kata.chunked_fwd(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), C=32, scan=scan))
+    assert row_rel_err(got, ref) <= TOL["f32"]
+
+
+def test_tiny_quadratic():
+    w = WORKLOADS["tiny"]
+    q, k, v = _case("tiny-quadratic", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    ref = ko.naive(q, k, v)
+    got = to_np(kata.quadratic_fwd(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")))
+    assert row_rel_err(got, ref) <= TOL["f32"]
+
+
+def test_tiny_recurrent_decode():
+    w = WORKLOADS["tiny"]
+    q, k, v = _case("tiny-recurrent", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    ref = ko.naive(q, k, v)
+    n = ko.packed_dim(w.p)
+    S = torch.zeros((w.B, w.H, n, w.dv), dtype=torch.float32, device="cuda:0")
+    Z = torch.zeros((w.B, w.H, n), dtype=torch.float32, device="cuda:0")
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = []
+    for t in range(w.T):
+        outs.append(kata.decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                     vd[:, :, t].contiguous(), S, Z))
+    got = to_np(torch.stack(outs, dim=2))
+    assert row_rel_err(got, ref) <= TOL["f32"]
+    S_ref, Z_ref = ko.prefill_state(k, v)
+    assert np.allclose(to_np(S), S_ref, rtol=1e-4, atol=1e-4)
+    assert np.allclose(to_np(Z), Z_ref, rtol=1e-4, atol=1e-4)
+
+
+# ------------------------------------------------------------------ bf16 chunked: shapes, tails, modes
+@pytest.mark.parametrize("p,dv,C,T", [(32, 64, 64, 700), (32, 64, 128, 1000), (32, 64, 32, 300),
+                                      (16, 16, 32, 257), (16, 64, 64, 640), (32, 32, 128, 129),
+                                      (32, 16, 64, 65), (16, 32, 128, 390)])
+def test_chunked_bf16_shapes(p, dv, C, T):
+    q, k, v = _case("chunked-bf16", 11, 2, 3, T, p, dv, "bf16")
+    q[0, 1, 7] = 0.0          # a zero query row
+    k[1, 0, :3] = 0.0         # zero keys at the start of a sequence
+    ref = ko.naive(q, k, v)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    for scan in ("sequential", "associative"):
+        got = to_np(kata.chunked_fwd(qd, kd, vd, C=C, scan=scan))
+        err = row_rel_err(got, ref)
+        print(f"  scan={scan} rel_err={err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+    got32 = to_np(kata.chunked_fwd(qd, kd, vd, C=C, scan="associative", out_dtype=torch.float32))
+    assert row_rel_err(got32, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [1, 5, 31, 64])
+def test_chunked_short_sequences(T):
+    q, k, v = _case("chunked-short", 12, 1, 2, T, 32, 64, "bf16")
+    ref = ko.naive(q, k, v)
+    got = to_np(kata.chunked_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), C=64))
+    assert row_rel_err(got, ref) <= TOL["bf16"]
+
+
+def test_chunked_empty_is_noop():
+    q = torch.zeros((1, 2, 0, 32), dtype=torch.bfloat16, device="cuda:0")
+    v = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    assert kata.chunked_fwd(q, q, v, C=64).shape == (1, 2, 0, 64)
+    assert kata.quadratic_fwd(q, q, v).shape == (1, 2, 0, 64)
+
+
+def test_chunked_deterministic():
+    q, k, v = _case("determinism", 13, 1, 4, 3000, 32, 64, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    a = kata.chunked_fwd(qd, kd, vd, C=64)
+    b = kata.chunked_fwd(qd, kd, vd, C=64)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ mid config
+def test_mid_chunked_quadratic_oracle():
+    w = WORKLOADS["mid"]
+    q, k, v = _case("mid", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    heads = [(0, 0), (3, 7), (7, 15)]
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    ch = to_np(kata.chunked_fwd(qd, kd, vd, C=64, scan="associative"))
+    chs = to_np(kata.chunked_fwd(qd, kd, vd, C=64, scan="sequential"))
+    qu = to_np(kata.quadratic_fwd(qd, kd, vd))
+    for (b, h) in heads:
+        ref = ko.naive(q[b, h], k[b, h], v[b, h])
+        for name, got in (("chunked", ch), ("chunked-seq", chs), ("quadratic", qu)):
+            err = row_rel_err(got[b, h], ref)
+            print(f"  head=({b},{h}) {name} rel_err={err:.3e}", flush=True)
+            assert err <= TOL["bf16"]
+    # the two forms agree everywhere (both are within tolerance of the same oracle)
+    assert row_rel_err(ch, qu) <= 2 * TOL["bf16"]
+
+
+# ------------------------------------------------------------------ long config (sampled rows)
+@pytest.mark.parametrize("C", [64, 128])
+def test_long_chunked_sampled(C):
+    w = WORKLOADS["long"]
+    q, k, v = _case("long", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    got = kata.chunked_fwd(qd, kd, vd, C=C, scan="associative")
+    rng = np.random.default_rng(99)
+    rows = sorted(set([0, 1, 2, 7, 63, 64, 65, C - 1, C, 8191, 8192, w.T - 1]
+                      + list(rng.integers(0, w.T, 40))))
+    for h in (0, 9, 15):
+        ref = ko.naive_rows(q[0, h], k[0, h], v[0, h], rows)
+        g = to_np(got[0, h, rows])
+        err = row_rel_err(g, ref)
+        print(f"  C={C} head={h} rel_err={err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+    if C == 64:
+        seq = kata.chunked_fwd(qd, kd, vd, C=C, scan="sequential")
+        assert row_rel_err(to_np(seq), to_np(got)) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ quadratic config
+def test_quadratic_config_sampled():
+    w = WORKLOADS["quadratic"]
+    q, k, v = _case("quadratic", w.seed, w.B, w.H, w.T, w.p, w.dv, w.dtype)
+    got = kata.quadratic_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"))
+    rng = np.random.default_rng(98)
+    rows = sorted(set([0, 1, 5, 127, 128, 4095, w.T - 1] + list(rng.integers(0, w.T, 30))))
+    for (b, h) in ((0, 0), (1, 8), (1, 15)):
+        ref = ko.naive_rows(q[b, h], k[b, h], v[b, h], rows)
+        err = row_rel_err(to_np(got[b, h, rows]), ref)
+        print(f"  head=({b},{h}) rel_err={err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("p,dv,T", [(16, 16, 200), (32, 32, 333), (64, 16, 130), (16, 64, 1)])
+def test_quadratic_shapes(p, dv, T):
+    q, k, v = _case("quadratic-shapes", 14, 2, 2, T, p, dv, "bf16")
+    q[1, 1, 3 % T] = 0.0
+    ref = ko.naive(q, k, v)
+    got = to_np(kata.quadratic_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")))
+    assert row_rel_err(got, ref) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ decode (small)
+def test_decode_small_from_prefill():
+    rng = np.random.default_rng(15)
+    N, H, p, dv, Th, steps = 3, 2, 32, 64, 200, 20
+    kh = rng.standard_normal((N, H, Th, p)).astype(np.float32)
+    vh = rng.standard_normal((N, H, Th, dv)).astype(np.float32)
+    S0, Z0 = ko.prefill_state(kh, vh)
+    S0, Z0 = np.ascontiguousarray(S0, np.float32), np.ascontiguousarray(Z0, np.float32)
+    qs = round_bf16(rng.standard_normal((steps, N, H, p)).astype(np.float32))
+    ks = round_bf16(rng.standard_normal((steps, N, H, p)).astype(np.float32))
+    vs = round_bf16(rng.standard_normal((steps, N, H, dv)).astype(np.float32))
+    ref, S_ref, Z_ref = ko.decode_steps(S0, Z0, qs, ks, vs)
+    S = torch.from_numpy(S0).cuda(); Z = torch.from_numpy(Z0).cuda()
+    qd, kd, vd = to_dev(qs, "bf16"), to_dev(ks, "bf16"), to_dev(vs, "bf16")
+    outs = [kata.decode_step(qd[s], kd[s], vd[s], S, Z) for s in range(steps)]
+    got = to_np(torch.stack(outs))
+    assert row_rel_err(got, ref) <= TOL["bf16"]
+    assert np.allclose(to_np(S), S_ref, rtol=1e-4, atol=1e-3)
+    assert np.allclose(to_np(Z), Z_ref, rtol=1e-4, atol=1e-3)
