@@ -16,24 +16,30 @@
 //     In tile tau, row m (0..15) holds a pair (i, j) in which one index is m (or 16+m)
 //     and the other is m rotated by a tile constant inside its 16-lane row. Hence a
 //     lane that holds the natural components k_hat[t][m], k_hat[t][16+m] builds its
-//     A-operand row with ONE v_mul_f32 whose second operand is a DPP row rotation:
-//     the lift costs one multiply per feature and never touches LDS or HBM.
+//     A-operand row of psi(K)^T with ONE v_mul_f32 whose first operand is a DPP row
+//     rotation: the lift costs one multiply per feature and never touches LDS or HBM.
 //     p = 32 gives 33 tiles = 528 features exactly; p = 16 gives 9 tiles (136 + 8 pad).
 //   * The state S (fp32) lives in MFMA accumulators, split by feature tiles over the 4
-//     waves. The accumulator layout of a 16x16 tile (rows 4g..4g+3 in lane group g) is
-//     used directly as the B operand of the readout psi(Q) S (k-slots permuted the same
-//     way on the A side), so S needs no LDS round trip: one cvt_pk_bf16 per 2 entries.
+//     waves (each wave builds its own tiles). After each chunk's build, every wave
+//     writes its tiles once to LDS as bf16 in the B-operand order of the readout (the
+//     16x16 accumulator rows 4g..4g+3 become the k-slots of lane group g; the A side
+//     permutes its k-slots the same way).
+//   * Readout: each wave owns 16 tokens of the chunk and computes psi(q)^T S over ALL
+//     features from the shared bf16 state, so its output needs no cross-wave reduction.
+//     Its psi(q) A operand comes from a per-lane-group rotated copy of q_hat (raw
+//     products q_i q_j): one multiply per feature.
 //   * Off-diagonal coordinates carry sqrt(2) in psi; their product c_ij^2 = 2 is folded
-//     into the state build (the key side is scaled by 2), so the readout side uses raw
-//     products q_i q_j.
+//     into the state build (a 2 k_hat copy is staged in LDS), so the readout side uses
+//     raw products.
 //   * The denominator psi(q)^T Z = q_hat^T M q_hat with the Gram matrix
 //     M = sum_s k_hat_s k_hat_s^T (p x p): M is updated and applied with split-bf16
 //     MFMAs (hi*hi + hi*lo + lo*hi), so the normaliser is fp32-accurate.
 //   * Intra-chunk block: S^T = K_hat Q_hat^T (keys as M), W = (S^T)^2 masked, rounded to
 //     bf16, O += W V. Global chunk 0, where denominators are sums of few weights, uses
 //     split-bf16 scores.
-//   * Each wave's readout covers its own features for every token of the chunk; the 4
-//     partial outputs are summed through LDS, divided by the denominator and stored.
+//   * Per chunk: readout phase | barrier | build phase (which also stages the next
+//     chunk's row data) | barrier. Global loads for the next chunk are in flight during
+//     the readout phase.
 //   * SEQUENTIAL: one workgroup per (b,h) walks all chunks. ASSOCIATIVE: a summary pass
 //     writes each segment's [S | M] (fp32, in this tile layout), an in-place scan forms
 //     exclusive prefixes, and every segment runs its chunks from its prefix.
@@ -49,7 +55,6 @@ hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st)
 
 namespace chk {
 
-constexpr int NW = 4;
 enum : int { K_DIAG = 0, K_WITHIN = 1, K_WITHIN8 = 2, K_CROSS = 3 };
 
 template <int P> constexpr int ntiles() { return P == 32 ? 33 : 9; }
@@ -66,17 +71,13 @@ template <int P> constexpr int tile_delta(int t) {
   if (P == 16) return t == 0 ? 0 : (t < 8 ? t : 8);
   return t < 2 ? 0 : (t < 16 ? (t - 2) % 7 + 1 : (t == 16 ? 8 : t - 17));
 }
-// contiguous tile ranges per wave: p=32 -> 9,8,8,8; p=16 -> 3,2,2,2
-template <int P> constexpr int wave_t0(int w) { return P == 32 ? (w == 0 ? 0 : 1 + 8 * w) : (w == 0 ? 0 : 1 + 2 * w); }
-template <int P> constexpr int wave_nt(int w) { return P == 32 ? (w == 0 ? 9 : 8) : (w == 0 ? 3 : 2); }
-
 // lane m of each 16-lane row receives x from lane (m + D) & 15 (DPP row_ror by 16 - D)
 template <int D>
 __device__ __forceinline__ float rot(float x) {
   if constexpr ((D & 15) == 0) return x;
   else
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                  0x120 + (16 - (D & 15)), 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                               0x120 + (16 - (D & 15)), 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -87,36 +88,20 @@ __device__ __forceinline__ bf16x8_t zero_bf8() {
   return __builtin_bit_cast(bf16x8_t, u16x8_t{0, 0, 0, 0, 0, 0, 0, 0});
 }
 
-// A operand of the state build for tile TAU: row m = this lane's feature, 8 tokens.
-// N[h][j] = k_hat[token j][16h + m]; N2 = 2 N (folds c_ij^2 = 2 of off-diagonal entries).
-template <int P, int TAU>
-__device__ __forceinline__ bf16x8_t build_frag(const float (&N)[P / 16][8], const float (&N2)[P / 16][8],
-                                               bool mlow) {
-  constexpr int kind = tile_kind<P>(TAU), h = tile_half<P>(TAU), d = tile_delta<P>(TAU);
-  bf16x8_t r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float x;
-    if constexpr (kind == K_DIAG) {
-      x = N[h][j] * N[h][j];
-    } else if constexpr (kind == K_WITHIN) {
-      x = N2[h][j] * rot<d>(N[h][j]);
-    } else if constexpr (kind == K_WITHIN8) {
-      if constexpr (P == 32) {
-        const float a = mlow ? N2[0][j] : N2[1][j];
-        const float b = mlow ? N[1][j] : N[0][j];
-        x = a * rot<8>(b);
-      } else {
-        const float a = mlow ? N2[0][j] : 0.f;
-        x = a * rot<8>(N[0][j]);
-      }
-    } else {
-      x = N2[0][j] * rot<d>(N[P / 16 - 1][j]);
-    }
-    r[j] = (__bf16)x;
-  }
-  return r;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+__device__ __forceinline__ bf16x8_t pack8(const float (&x)[8]) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])});
+}
+// low / high bf16 of a packed pair as fp32
+__device__ __forceinline__ float lo_f32(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
 // readout-side feature of row 4g + JJ of tile TAU for this lane's token, from
 // Y[x] = q_hat[(x & ~15) | ((x + 4g) & 15)] (raw product; c^2 sits in the state)
@@ -142,62 +127,142 @@ __device__ __forceinline__ float ro_feat(const float (&Y)[P], bool glow) {
 
 template <int P, int T1, int T2, bool HAS2>
 __device__ __forceinline__ bf16x8_t readout_frag(const float (&Y)[P], bool glow) {
-  bf16x8_t r;
-  r[0] = (__bf16)ro_feat<P, T1, 0>(Y, glow);
-  r[1] = (__bf16)ro_feat<P, T1, 1>(Y, glow);
-  r[2] = (__bf16)ro_feat<P, T1, 2>(Y, glow);
-  r[3] = (__bf16)ro_feat<P, T1, 3>(Y, glow);
+  float x[8];
+  x[0] = ro_feat<P, T1, 0>(Y, glow);
+  x[1] = ro_feat<P, T1, 1>(Y, glow);
+  x[2] = ro_feat<P, T1, 2>(Y, glow);
+  x[3] = ro_feat<P, T1, 3>(Y, glow);
   if constexpr (HAS2) {
-    r[4] = (__bf16)ro_feat<P, T2, 0>(Y, glow);
-    r[5] = (__bf16)ro_feat<P, T2, 1>(Y, glow);
-    r[6] = (__bf16)ro_feat<P, T2, 2>(Y, glow);
-    r[7] = (__bf16)ro_feat<P, T2, 3>(Y, glow);
+    x[4] = ro_feat<P, T2, 0>(Y, glow);
+    x[5] = ro_feat<P, T2, 1>(Y, glow);
+    x[6] = ro_feat<P, T2, 2>(Y, glow);
+    x[7] = ro_feat<P, T2, 3>(Y, glow);
   } else {
-    r[4] = r[5] = r[6] = r[7] = (__bf16)0.f;
+    x[4] = x[5] = x[6] = x[7] = 0.f;
   }
-  return r;
+  return pack8(x);
 }
 
 // split x (8 fp32) into bf16 hi and lo = bf16(x - hi)
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = pk2(x[2 * j], x[2 * j + 1]);
+    l[j] = pk2(x[2 * j] - lo_f32(h[j]), x[2 * j + 1] - hi_f32(h[j]));
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+// ---- work split over the 8 waves of a workgroup
+constexpr int NW = 8;
+// state-build tiles per wave, aligned to readout pairs (2 tiles) so every wave writes whole
+// 16-byte state fragments: p=32 -> 4 tiles each, wave 7 also the odd tile 32 (33 tiles);
+// p=16 -> waves 0..3 two tiles, wave 4 tile 8, waves 5..7 none (9 tiles)
+template <int P> constexpr int wave_t0(int w) { return P == 32 ? 4 * w : (w < 5 ? 2 * w : 9); }
+template <int P> constexpr int wave_nt(int w) { return P == 32 ? (w == 7 ? 5 : 4) : (w < 4 ? 2 : (w == 4 ? 1 : 0)); }
+// register array extent (at least 1; a wave without tiles keeps one unused)
+template <int P> constexpr int wave_na(int w) { return wave_nt<P>(w) > 0 ? wave_nt<P>(w) : 1; }
+// Gram-matrix tile owned by wave w (-1: none; p=32 has 4 tiles, on waves 3..6, p=16 one)
+template <int P> constexpr int m_tile(int w) { return P == 32 ? (w >= 3 && w < 7 ? w - 3 : -1) : (w == 5 ? 0 : -1); }
+
+// A operand of the state build for tile TAU: row m = this lane's feature, 8 tokens.
+// N[h][j] = k_hat[token j][16h + m]; N2 = 2 N carries c_ij^2 = 2 of off-diagonal
+// coordinates and is always the DPP-rotated operand (the compiler then folds the row
+// rotation into the multiply).
+template <int P, int TAU>
+__device__ __forceinline__ bf16x8_t build_frag(const float (&N)[P / 16][8], const float (&N2)[P / 16][8],
+                                               bool mlow) {
+  constexpr int kind = tile_kind<P>(TAU), h = tile_half<P>(TAU), d = tile_delta<P>(TAU);
+  float x[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
+    if constexpr (kind == K_DIAG) {
+      x[j] = N[h][j] * N[h][j];
+    } else if constexpr (kind == K_WITHIN) {
+      x[j] = N[h][j] * rot<d>(N2[h][j]);
+    } else if constexpr (kind == K_WITHIN8) {
+      if constexpr (P == 32) {
+        const float a = mlow ? N[0][j] : N[1][j];
+        const float b = mlow ? N2[1][j] : N2[0][j];
+        x[j] = a * rot<8>(b);
+      } else {
+        const float a = mlow ? N[0][j] : 0.f;
+        x[j] = a * rot<8>(N2[0][j]);
+      }
+    } else {
+      x[j] = N[0][j] * rot<d>(N2[P / 16 - 1][j]);
+    }
   }
+  return pack8(x);
 }
+
+// physical LDS row of V^T column d: the low 2 bits are XOR-swizzled by (d / 8) & 3 so the
+// transposed writes of 4 column groups land in distinct banks
+__device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 3); }
 
 template <int P, int DV, int C>
 struct Cfg {
-  static constexpr int NT = DV / 16;          // output column tiles
-  static constexpr int NH = P / 16;           // 16-component halves
-  static constexpr int NMT = C / 16;          // token tiles per chunk
-  static constexpr int GMT = NMT < 4 ? NMT : 4;  // token tiles per readout group
-  static constexpr int NG = NMT / GMT;        // readout groups per chunk
-  static constexpr int KSTEP = C / 32;        // 32-token k-steps of the build
-  static constexpr int QP = P + 4;            // fp32 pitch of q_hat / k_hat rows
-  static constexpr int KTP = C + 4;           // fp32 pitch of k_hat^T rows
-  static constexpr int VTP = C + 8;           // bf16 pitch of V^T rows
-  static constexpr int MP = P + 8;            // bf16 pitch of the Gram matrix rows
-  static constexpr int PP = DV + 4;           // fp32 pitch of the partial outputs
-  static constexpr int NTL = ntiles<P>();
-  static constexpr int64_t STATE_FLOATS = (int64_t)NTL * NT * 256 + NH * NH * 256;
-  // LDS layout (bytes)
-  static constexpr int OFF_QH = 0;
+  static constexpr int NT = DV / 16;            // output column tiles
+  static constexpr int NH = P / 16;             // 16-component halves
+  static constexpr int NMT = C / 16;            // token tiles per chunk
+  static constexpr int FS = NW / NMT;           // waves sharing one token tile's readout
+  static constexpr int KSTEP = C / 32;          // 32-token k-steps of the build
+  static constexpr int NTL = ntiles<P>();       // 16-feature tiles
+  static constexpr int NPAIR = (NTL + 1) / 2;   // 32-feature readout k-steps
+  // LDS pitches: 16-byte reads by lanes (row ln, group lg) at ln * pitch + 4 lg floats are
+  // conflict-free when the pitch is 8 * odd floats modulo 128 (measured on gfx950)
+  static constexpr int QP = P + 8;              // fp32 pitch of q_hat / k_hat rows
+  // k_hat^T: component row r at r * KTP + 8 (r / KQ) (skew per staging quarter), token
+  // planes HP apart; with KTP = 16 (mod 32) both its transposed 4-byte writes and the
+  // build's 16-byte reads are conflict-free
+  static constexpr int HP = C / 2;
+  static constexpr int KTP = 16 + 32 * ((C + 8 + 31) / 32);
+  static constexpr int VTP = 80 + 128 * ((C - 80 + 127) / 128);  // bf16 pitch of V^T rows
+  static constexpr int MP = C == 128 ? P : P + 8;  // bf16 pitch of the Gram matrix rows (unpadded where LDS is short)
+  static constexpr int SB_BYTES = NPAIR * NT * 64 * 16;            // bf16 state, B-fragment order
+  static constexpr int PART_BYTES = NMT * (FS - 1) * NT * 64 * 16;  // partial outputs (fp32 acc layout)
+  static constexpr int lds_for(bool dual) {
+    return SB_BYTES + 2 * C * QP * 4 + (dual ? 2 : 1) * DV * VTP * 2 + P * KTP * 4 + 2 * P * MP * 2 + PART_BYTES;
+  }
+  // separate V^T copies for the intra block and the build let the next chunk's rows be
+  // staged while the build runs (2 barriers per chunk instead of 3)
+  static constexpr bool DUALV = lds_for(true) <= 160 * 1024;
+  static constexpr int OFF_SB = 0;
+  static constexpr int OFF_QH = OFF_SB + SB_BYTES;
   static constexpr int OFF_KH = OFF_QH + C * QP * 4;
-  static constexpr int OFF_KT = OFF_KH + C * QP * 4;
-  static constexpr int OFF_VT = OFF_KT + P * KTP * 4;
-  static constexpr int OFF_M = OFF_VT + DV * VTP * 2;           // [2 buf][hi,lo][P][MP] bf16
-  static constexpr int OFF_DEN = OFF_M + 2 * 2 * P * MP * 2;
-  static constexpr int OFF_PP = OFF_DEN + C * 4;
-  static constexpr int LDS = OFF_PP + NW * GMT * 16 * PP * 4;
+  static constexpr int OFF_VT = OFF_KH + C * QP * 4;                 // V^T read by the intra block
+  static constexpr int OFF_VB = OFF_VT + (DUALV ? DV * VTP * 2 : 0);  // V^T read by the build
+  static constexpr int OFF_KT = OFF_VB + DV * VTP * 2;
+  static constexpr int OFF_M = OFF_KT + P * KTP * 4;                // bf16 [hi,lo][P][MP]
+  static constexpr int OFF_PART = OFF_M + 2 * P * MP * 2;
+  static constexpr int LDS = OFF_PART + PART_BYTES;
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  // global-load work per thread
-  static constexpr int ROWS_PT = (C + 63) / 64;                // q/k rows per thread
-  static constexpr int KQ = P / 4;                             // components per thread
-  static constexpr int VPIECES = (C / 2) * (DV / 8);           // (key pair, 8 columns) pieces
-  static constexpr int VPT = (VPIECES + 255) / 256;
+  // summary pass: build operands only, double-buffered
+  static constexpr int SUM_BUF = DV * VTP * 2 + P * KTP * 4;
+  static constexpr int SUM_LDS = 2 * SUM_BUF;
+  static constexpr int64_t STATE_FLOATS = (int64_t)NTL * NT * 256 + NH * NH * 256;
+  // staging work per thread: 4 threads per q/k row (KQ components), one (key pair,
+  // 8 columns) V piece
+  static constexpr int KQ = P / 4;
+  static constexpr int QK_PIECES = 2 * 4 * C;                  // q and k row pieces
+  static_assert(VTP >= C && KTP >= 24 + 2 * HP, "pitches");
+  static constexpr int QKI = (QK_PIECES + 511) / 512;
+  static constexpr int VPIECES = (C / 2) * (DV / 8);
+  static constexpr int VI = (VPIECES + 511) / 512;
+  // V piece pc -> (key pair vp, column group vd): each 32-lane half loads 8 key pairs x 4
+  // column groups (64 contiguous bytes per row) whose transposed LDS writes hit 32
+  // distinct banks (key-pair positions distinct mod 8, rows swizzled by vd & 3)
+  __device__ static __forceinline__ void vpiece(int pc, int& vp, int& vd) {
+    constexpr int NVD = DV / 8, VL = NVD < 4 ? NVD : 4, VH = NVD / VL;
+    const int qd = pc / (8 * VL), r = pc % (8 * VL);
+    const int vl = r / VL, sg = qd / VH;
+    vd = r % VL + VL * (qd % VH);
+    vp = 16 * (sg >> 1) + 4 * (sg & 1) + (vl & 3) + 8 * (vl >> 2);
+  }
+  // readout pair ranges: split fs covers pairs [pr(fs), pr(fs+1))
+  static constexpr int pr(int fs) { return fs >= FS ? NPAIR : (fs * (NPAIR + 1)) / FS; }
 };
 
 struct Args {
@@ -210,455 +275,539 @@ struct Args {
   int o_f32;  // output dtype: 1 = fp32, 0 = bf16
 };
 
-// store CPL consecutive outputs of one row
-template <int CPL>
-__device__ __forceinline__ void store_row(const Args& a, int64_t off, const float (&s)[CPL], float inv) {
-  if (a.o_f32) {
-    float* ob = static_cast<float*>(a.o) + off;
-#pragma unroll
-    for (int e = 0; e < CPL; e += 4)
-      *reinterpret_cast<f32x4_t*>(ob + e) = f32x4_t{s[e] * inv, s[e + 1] * inv, s[e + 2] * inv, s[e + 3] * inv};
-  } else {
-    uint16_t* ob = static_cast<uint16_t*>(a.o) + off;
-#pragma unroll
-    for (int e = 0; e < CPL; e += 4)
-      *reinterpret_cast<u16x4_t*>(ob + e) = u16x4_t{f32_to_bf16_bits(s[e] * inv), f32_to_bf16_bits(s[e + 1] * inv),
-                                                    f32_to_bf16_bits(s[e + 2] * inv), f32_to_bf16_bits(s[e + 3] * inv)};
-  }
+// fast reciprocal square root / reciprocal (about 1 ulp; results feed bf16 MFMA operands)
+__device__ __forceinline__ float inv_norm_fast(float ss) { return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f; }
+
+// raw buffer resource over [base, base + bytes): loads past the end return 0 and stores
+// past the end are dropped by the hardware range check, so ragged tails need no branches
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-// ---- chunk staging: global bf16 -> registers (prefetch) -> normalised LDS (stage)
+// ---- chunk staging: global bf16 -> registers (load) -> normalised LDS layouts
 template <int P, int DV, int C, bool WITH_Q>
 struct Stager {
   using CF = Cfg<P, DV, C>;
-  uint16_t qr[CF::ROWS_PT][CF::KQ];
-  uint16_t kr[CF::ROWS_PT][CF::KQ];
-  u16x8_t vr[CF::VPT][2];
+  typedef uint16_t row_t __attribute__((ext_vector_type(P / 4)));
+  row_t qk[CF::QKI];          // piece i: q (first 4C pieces) or k row piece
+  u16x8_t vr[CF::VI][2];
+  const uint16_t *qb, *kb, *vb;
+  int T;
 
-  __device__ __forceinline__ void load_row(uint16_t (&dst)[CF::KQ], const uint16_t* src) {
-    if constexpr (CF::KQ == 8) *reinterpret_cast<u16x8_t*>(&dst[0]) = *reinterpret_cast<const u16x8_t*>(src);
-    else *reinterpret_cast<u16x4_t*>(&dst[0]) = *reinterpret_cast<const u16x4_t*>(src);
+  __device__ __forceinline__ void init(const Args& a, int64_t bh) {
+    qb = a.q + bh * a.T * P;
+    kb = a.k + bh * a.T * P;
+    vb = a.v + bh * a.T * DV;
+    T = a.T;
   }
 
-  __device__ __forceinline__ void prefetch(const Args& a, int64_t bh, int t0) {
+  __device__ __forceinline__ row_t load_piece(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (P == 32)
+      return __builtin_bit_cast(row_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    else
+      return __builtin_bit_cast(row_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  }
+
+  // the chunk's rows t0.. as buffers: rows past T read as zero
+  __device__ __forceinline__ void load(int t0) {
     const int tid = threadIdx.x;
-    const int kq = tid & 3;
+    const uint32_t left = (uint32_t)(T - t0);
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)t0 * P, left * P * 2);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * P, left * P * 2);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vb + (int64_t)t0 * DV, left * DV * 2);
 #pragma unroll
-    for (int i = 0; i < CF::ROWS_PT; ++i) {
-      const int row = (tid >> 2) + 64 * i;
-      const int t = t0 + row;
-#pragma unroll
-      for (int e = 0; e < CF::KQ; ++e) qr[i][e] = kr[i][e] = 0;
-      if (row < C && t < a.T) {
-        const int64_t off = (bh * a.T + t) * P + kq * CF::KQ;
-        if (WITH_Q) load_row(qr[i], a.q + off);
-        load_row(kr[i], a.k + off);
-      }
+    for (int i = 0; i < CF::QKI; ++i) {
+      const int pc = tid + 512 * i;
+      // q or k is uniform across a wave (4C is a multiple of 64)
+      const int isq = __builtin_amdgcn_readfirstlane(pc < 4 * C ? 1 : 0);
+      const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
+      const uint32_t voff = (uint32_t)(row * P + kq * CF::KQ) * 2;
+      if (pc < CF::QK_PIECES && (WITH_Q || !isq)) qk[i] = load_piece(isq ? rq : rk, voff, 0);
     }
 #pragma unroll
-    for (int i = 0; i < CF::VPT; ++i) {
-      const int pc = tid + 256 * i;
-      vr[i][0] = vr[i][1] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < CF::VI; ++i) {
+      const int pc = tid + 512 * i;
       if (pc < CF::VPIECES) {
-        const int vp = pc / (DV / 8), vd = pc % (DV / 8);
-        const int t = t0 + 2 * vp;
-        const uint16_t* src = a.v + (bh * a.T + t) * DV + 8 * vd;
-        if (t < a.T) vr[i][0] = *reinterpret_cast<const u16x8_t*>(src);
-        if (t + 1 < a.T) vr[i][1] = *reinterpret_cast<const u16x8_t*>(src + DV);
+        int vp, vd;
+        CF::vpiece(pc, vp, vd);
+        const uint32_t voff = (uint32_t)(2 * vp * DV + 8 * vd) * 2;
+        vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+        vr[i][1] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + DV * 2, 0, 0));
       }
     }
   }
 
-  __device__ __forceinline__ void stage(char* lds) {
-    const int tid = threadIdx.x;
-    const int kq = tid & 3;
-    float* qh = reinterpret_cast<float*>(lds + CF::OFF_QH);
-    float* kh = reinterpret_cast<float*>(lds + CF::OFF_KH);
-    float* kt = reinterpret_cast<float*>(lds + CF::OFF_KT);
-    uint32_t* vt = reinterpret_cast<uint32_t*>(lds + CF::OFF_VT);
+  // normalised row piece (4 consecutive lanes share a row; the norm is combined over them)
+  __device__ __forceinline__ void normalise(const row_t& src, float (&x)[CF::KQ]) {
+    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < CF::ROWS_PT; ++i) {
-      const int row = (tid >> 2) + 64 * i;
-#pragma unroll
-      for (int isq = 0; isq < (WITH_Q ? 2 : 1); ++isq) {
-        const uint16_t(&src)[CF::KQ] = (WITH_Q && isq == 0) ? qr[i] : kr[i];
-        float x[CF::KQ];
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < CF::KQ; ++e) {
-          x[e] = bf16_bits_to_f32(src[e]);
-          ss += x[e] * x[e];
-        }
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        const float inv = inv_norm(ss);
-        if (row < C) {
-          float* dst = ((WITH_Q && isq == 0) ? qh : kh) + row * CF::QP + kq * CF::KQ;
-#pragma unroll
-          for (int e = 0; e < CF::KQ; ++e) {
-            x[e] *= inv;
-            dst[e] = x[e];
-          }
-          if (!(WITH_Q && isq == 0)) {
-#pragma unroll
-            for (int e = 0; e < CF::KQ; ++e) kt[(kq * CF::KQ + e) * CF::KTP + row] = x[e];
-          }
-        }
-      }
+    for (int e = 0; e < CF::KQ; ++e) {
+      x[e] = bf16_bits_to_f32(src[e]);
+      ss += x[e] * x[e];
     }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    const float inv = inv_norm_fast(ss);
 #pragma unroll
-    for (int i = 0; i < CF::VPT; ++i) {
-      const int pc = tid + 256 * i;
+    for (int e = 0; e < CF::KQ; ++e) x[e] *= inv;
+  }
+
+  // V^T (bf16 [DV][VTP]); key 32a + 16s + 4g + j is stored at 32a + 8g + 4s + j, so lane
+  // group g reads its 8 k-slots (keys 32a + 4g + j, 32a + 16 + 4g + j: the row order of the
+  // score fragments and of the k_hat^T planes) with one 16-byte read
+  __device__ __forceinline__ void write_vt(char* vt_bytes) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CF::VI; ++i) {
+      const int pc = tid + 512 * i;
       if (pc < CF::VPIECES) {
-        const int vp = pc / (DV / 8), vd = pc % (DV / 8);
+        int vp, vd;
+        CF::vpiece(pc, vp, vd);
+        const int k = 2 * vp;
+        const int pos = (k & ~31) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3);
+        // column 8 vd + e lives in row 8 vd + (e ^ (vd & 3)) (see vt_row)
+        char* base = vt_bytes + ((8 * vd) * CF::VTP + pos) * 2;
+        char* rb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rb[j] = base + (j ^ (vd & 3)) * CF::VTP * 2;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          vt[((8 * vd + e) * CF::VTP + 2 * vp) >> 1] = (uint32_t)vr[i][0][e] | ((uint32_t)vr[i][1][e] << 16);
+          *reinterpret_cast<uint32_t*>(rb[e & 3] + (e & 4) * CF::VTP * 2) =
+              (uint32_t)vr[i][0][e] | ((uint32_t)vr[i][1][e] << 16);
       }
     }
+  }
+
+  // row-major q_hat, k_hat (fp32) and V^T for the readout / intra block
+  __device__ __forceinline__ void stage_rows(char* lds, int off_vt) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CF::QKI; ++i) {
+      const int pc = tid + 512 * i;
+      if (CF::QK_PIECES % 512 != 0 && pc >= CF::QK_PIECES) continue;  // whole waves
+      const bool isq = pc < 4 * C;
+      if (!WITH_Q && isq) continue;
+      const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
+      float x[CF::KQ];
+      normalise(qk[i], x);
+      float* dst = reinterpret_cast<float*>(lds + (isq ? CF::OFF_QH : CF::OFF_KH)) + row * CF::QP + kq * CF::KQ;
+#pragma unroll
+      for (int e = 0; e < CF::KQ; e += 4)
+        *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{x[e], x[e + 1], x[e + 2], x[e + 3]};
+    }
+    write_vt(lds + off_vt);
+  }
+
+  // k_hat^T (fp32) and V^T for the state build (at byte offsets off_kt, off_vb)
+  __device__ __forceinline__ void stage_build(char* lds, int off_kt, int off_vb) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CF::QKI; ++i) {
+      const int pc = tid + 512 * i;
+      if (CF::QK_PIECES % 512 != 0 && pc >= CF::QK_PIECES) continue;
+      if (pc < 4 * C) continue;  // q pieces
+      const int row = (pc - 4 * C) >> 2, kq = pc & 3;
+      float x[CF::KQ];
+      normalise(qk[i], x);
+      // component row r starts at r * KTP + 8 (r / KQ); token t sits in plane (t / 16) & 1
+      // at (t / 32) * 16 + t % 16 of it
+      float* kt = reinterpret_cast<float*>(lds + off_kt) + (kq * CF::KQ) * CF::KTP + 8 * kq +
+                  ((row >> 4) & 1) * CF::HP + (row >> 5) * 16 + (row & 15);
+#pragma unroll
+      for (int e = 0; e < CF::KQ; ++e) kt[e * CF::KTP] = x[e];
+    }
+    write_vt(lds + off_vb);
   }
 };
 
-// ---- per-wave body; W (wave index) is a template parameter so every tile index is a
-// compile-time constant and the lift indexes registers directly.
-template <int P, int DV, int C, bool FWD, int W>
-__device__ __forceinline__ void run_wave(const Args& a, char* lds) {
+// ---- state build over this wave's tiles for one chunk
+template <int P, int DV, int C, int W>
+__device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16], f32x4_t& Mt,
+                                            const float* khT, const uint16_t* vb_lds) {
   using CF = Cfg<P, DV, C>;
   constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W);
-  constexpr int NPAIR = (NTW + 1) / 2;
-  constexpr bool OWN_M = W < NH * NH;
-  constexpr int MRT = W / NH, MCT = W % NH;  // Gram tile owned (when OWN_M)
+  constexpr int MT = m_tile<P>(W), MRT = MT / NH, MCT = MT % NH;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
-  const bool mlow = ln < 8, glow = lg < 2;
+  const bool mlow = ln < 8;
+#pragma unroll
+  for (int ks = 0; ks < CF::KSTEP; ++ks) {
+    float N[NH][8], N2[NH][8];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      // k-slot (lg, j) is token 32ks + 16 (j / 4) + 4lg + j % 4: plane 0, then plane 1
+      const float* src = khT + (16 * h + ln) * CF::KTP + 8 * ((16 * h + ln) / CF::KQ) + 16 * ks + 4 * lg;
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + CF::HP);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        N[h][e] = x0[e];
+        N[h][4 + e] = x1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) N2[h][e] = N[h][e] + N[h][e];
+    }
+    bf16x8_t vbf[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+      vbf[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(vb_lds + vt_row(16 * dt + ln) * CF::VTP + 32 * ks + 8 * lg));
+    [&]<int... TI>(std::integer_sequence<int, TI...>) {
+      (([&] {
+         const bf16x8_t af = build_frag<P, T0 + TI>(N, N2, mlow);
+#pragma unroll
+         for (int dt = 0; dt < NT; ++dt) S[TI][dt] = mfma(af, vbf[dt], S[TI][dt]);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, NTW>{});
+    if constexpr (MT >= 0) {  // Gram tile M[16 MRT.., 16 MCT..] += K^T K over these 32 tokens
+      Mt = mfma(pack8(N[MRT]), pack8(N[MCT]), Mt);
+    }
+  }
+}
 
-  float* qh = reinterpret_cast<float*>(lds + CF::OFF_QH);
-  float* kh = reinterpret_cast<float*>(lds + CF::OFF_KH);
-  float* khT = reinterpret_cast<float*>(lds + CF::OFF_KT);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds + CF::OFF_VT);
+// ---- forward of one segment; W (wave index) is a template parameter so every tile and
+// pair index is a compile-time constant and the lift indexes registers directly.
+template <int P, int DV, int C, int W>
+__device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
+  using CF = Cfg<P, DV, C>;
+  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W);
+  constexpr int MT = m_tile<P>(W), MRT = MT / NH, MCT = MT % NH;
+  constexpr int TT = W % CF::NMT, FSI = W / CF::NMT;   // token tile, feature split
+  constexpr bool OWNER = FSI == CF::FS - 1;            // intra block, denominator, output
+  constexpr int PB = CF::pr(FSI), PE = CF::pr(FSI + 1);
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+  const bool glow = lg < 2;
+
+  const float* qh = reinterpret_cast<const float*>(lds + CF::OFF_QH);
+  const float* kh = reinterpret_cast<const float*>(lds + CF::OFF_KH);
+  const float* khT = reinterpret_cast<const float*>(lds + CF::OFF_KT);
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(lds + CF::OFF_VT);
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(lds + CF::OFF_VB);
   uint16_t* mlds = reinterpret_cast<uint16_t*>(lds + CF::OFF_M);
-  float* den = reinterpret_cast<float*>(lds + CF::OFF_DEN);
-  float* pp = reinterpret_cast<float*>(lds + CF::OFF_PP);
+  char* sb = lds + CF::OFF_SB;
+  char* part = lds + CF::OFF_PART;
 
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
   const int nchunks = (a.T + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
+  const int osz = a.o_f32 ? 4 : 2;
+  char* obase = static_cast<char*>(a.o) + bh * a.T * DV * osz;
 
-  // ---- initial state
-  f32x4_t S[NTW][NT];
+  // ---- initial state (exclusive prefix of this segment, or zero)
+  f32x4_t S[wave_na<P>(W)][NT];
   f32x4_t Mt = zero4();
-  const bool from_ws = FWD && seg > 0;
-  {
-    const float* src = from_ws ? a.ws + (bh * (a.nseg - 1) + (seg - 1)) * CF::STATE_FLOATS : nullptr;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) S[i][dt] = zero4();
+  if (seg > 0) {
+    const float* src = a.ws + (bh * (a.nseg - 1) + (seg - 1)) * CF::STATE_FLOATS;
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
-        S[i][dt] = from_ws ? *reinterpret_cast<const f32x4_t*>(src + (((T0 + i) * NT + dt) * 64 + lane) * 4) : zero4();
-    if constexpr (OWN_M)
-      if (from_ws) Mt = *reinterpret_cast<const f32x4_t*>(src + (int64_t)CF::NTL * NT * 256 + (W * 64 + lane) * 4);
+        S[i][dt] = *reinterpret_cast<const f32x4_t*>(src + (((T0 + i) * NT + dt) * 64 + lane) * 4);
+    if constexpr (MT >= 0)
+      Mt = *reinterpret_cast<const f32x4_t*>(src + (int64_t)CF::NTL * NT * 256 + (MT * 64 + lane) * 4);
   }
-  auto write_m = [&](int buf) {  // Gram tile -> LDS as bf16 hi / lo
-    if constexpr (OWN_M) {
-      uint16_t* mh = mlds + (buf * 2 + 0) * P * CF::MP;
-      uint16_t* ml = mlds + (buf * 2 + 1) * P * CF::MP;
+  auto write_m = [&]() {  // Gram tile -> LDS as bf16 hi / lo
+    if constexpr (MT >= 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * MRT + 4 * lg + r, col = 16 * MCT + ln;
         const uint16_t h = f32_to_bf16_bits(Mt[r]);
-        mh[row * CF::MP + col] = h;
-        ml[row * CF::MP + col] = f32_to_bf16_bits(Mt[r] - bf16_bits_to_f32(h));
+        mlds[row * CF::MP + col] = h;
+        mlds[P * CF::MP + row * CF::MP + col] = f32_to_bf16_bits(Mt[r] - bf16_bits_to_f32(h));
       }
     }
   };
-  bf16x8_t Sb[NPAIR][NT];
-  auto convert_state = [&]() {
+  auto write_state = [&]() {  // tiles 2i, 2i+1 of this wave form readout pair (T0 + 2i) / 2
 #pragma unroll
-    for (int pi = 0; pi < NPAIR; ++pi)
+    for (int i = 0; i < NTW; i += 2) {
+      const int pair = (T0 + i) >> 1;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
-        bf16x8_t b;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = (__bf16)S[2 * pi][dt][r];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) b[4 + r] = (2 * pi + 1 < NTW) ? (__bf16)S[2 * pi + 1 < NTW ? 2 * pi + 1 : 0][dt][r] : (__bf16)0.f;
-        Sb[pi][dt] = b;
+        u32x4_t u;
+        u[0] = pk2(S[i][dt][0], S[i][dt][1]);
+        u[1] = pk2(S[i][dt][2], S[i][dt][3]);
+        if (i + 1 < NTW) {
+          u[2] = pk2(S[i + 1 < NTW ? i + 1 : i][dt][0], S[i + 1 < NTW ? i + 1 : i][dt][1]);
+          u[3] = pk2(S[i + 1 < NTW ? i + 1 : i][dt][2], S[i + 1 < NTW ? i + 1 : i][dt][3]);
+        } else {
+          u[2] = u[3] = 0;  // the odd last tile has no partner
+        }
+        *reinterpret_cast<u32x4_t*>(sb + ((pair * NT + dt) * 64 + lane) * 16) = u;
       }
+    }
   };
-  if constexpr (FWD) convert_state();
-  write_m(c0 & 1);
 
-  Stager<P, DV, C, FWD> stg;
-  stg.prefetch(a, bh, c0 * C);
-  stg.stage(lds);
+  Stager<P, DV, C, true> stg;
+  stg.init(a, bh);
+  stg.load(c0 * C);
+  stg.stage_rows(lds, CF::OFF_VT);
+  stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
+  write_state();
+  write_m();
+  if (CF::DUALV && c0 + 1 < c1) stg.load((c0 + 1) * C);
   __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
-    const int cur = c & 1;
-    if (c + 1 < c1) stg.prefetch(a, bh, t0 + C);
-
-    if constexpr (FWD) {
-      const bool split = c == 0;
-      // ---- intra-chunk block and denominator for the token tiles this wave owns
-      f32x4_t Oi[(CF::NMT + 3) / 4][NT];
-#pragma unroll
-      for (int oi = 0; oi < (CF::NMT + 3) / 4; ++oi) {
-        const int mt = W + 4 * oi;
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) Oi[oi][dt] = zero4();
-        if (mt >= CF::NMT) continue;
-        // query operand (B of S^T and of X^T): q_hat[16mt + ln][8lg..8lg+7]
-        bf16x8_t qbh = zero_bf8(), qbl = zero_bf8();
-        if (P == 32 || lg < 2) {
-          const float* src = qh + (16 * mt + ln) * CF::QP + 8 * lg;
-          const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
-          const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-          const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          split8(xs, qbh, qbl);
-        }
-        // den_inter partial: X^T = M Q_hat^T (rows: components), then q_hat . X
-        float dpart = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < NH; ++rt) {
-          bf16x8_t mh = zero_bf8(), ml = zero_bf8();
-          if (P == 32 || lg < 2) {
-            const uint16_t* mrow = mlds + (cur * 2) * P * CF::MP + (16 * rt + ln) * CF::MP + 8 * lg;
-            mh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(mrow));
-            ml = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(mrow + P * CF::MP));
-          }
-          f32x4_t X = zero4();
-          X = mfma(mh, qbh, X);
-          X = mfma(ml, qbh, X);
-          X = mfma(mh, qbl, X);
-          const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + (16 * mt + ln) * CF::QP + 16 * rt + 4 * lg);
-          dpart += X[0] * qv[0] + X[1] * qv[1] + X[2] * qv[2] + X[3] * qv[3];
-        }
-        // S^T = K_hat Q_hat^T over key tiles kt <= mt; W = (S^T)^2; O += W V
-#pragma unroll
-        for (int kp = 0; kp < (CF::NMT + 1) / 2; ++kp) {
-          if (2 * kp > mt) continue;
-          float wv[8];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int kt = 2 * kp + half;
-            f32x4_t St = zero4();
-            if (kt <= mt) {
-              bf16x8_t kbh = zero_bf8(), kbl = zero_bf8();
-              if (P == 32 || lg < 2) {
-                const float* src = kh + (16 * kt + ln) * CF::QP + 8 * lg;
-                const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
-                const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-                const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                split8(xs, kbh, kbl);
-              }
-              St = mfma(kbh, qbh, St);
-              if (split) {
-                St = mfma(kbl, qbh, St);
-                St = mfma(kbh, qbl, St);
-              }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float w = St[r] * St[r];
-              if (kt == mt && 4 * lg + r > ln) w = 0.f;  // causal: key <= query
-              if (kt > mt) w = 0.f;
-              const __bf16 wb = (__bf16)w;
-              wv[4 * half + r] = (float)wb;
-              dpart += (float)wb;
-            }
-          }
-          bf16x8_t wa;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) wa[j] = (__bf16)wv[j];
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) {
-            const uint16_t* row = vt + (16 * dt + ln) * CF::VTP + 32 * kp + 4 * lg;
-            const u16x4_t x0 = *reinterpret_cast<const u16x4_t*>(row);
-            const u16x4_t x1 = *reinterpret_cast<const u16x4_t*>(row + 16);
-            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, u16x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
-            Oi[oi][dt] = mfma(wa, vb, Oi[oi][dt]);
-          }
-        }
-        dpart += __shfl_xor(dpart, 16, 64);
-        dpart += __shfl_xor(dpart, 32, 64);
-        if (lg == 0) den[16 * mt + ln] = dpart;
-      }
-
-      // ---- readout psi(Q) S over this wave's features, per token group
-#pragma unroll
-      for (int g = 0; g < CF::NG; ++g) {
-#pragma unroll
-        for (int ml = 0; ml < CF::GMT; ++ml) {
-          const int mt = g * CF::GMT + ml;
-          f32x4_t acc[NT];
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) acc[dt] = (mt % 4 == W) ? Oi[mt / 4][dt] : zero4();
-          float Y[P];
-          {
-            const float* src = qh + (16 * mt + ln) * CF::QP;
-#pragma unroll
-            for (int h = 0; h < NH; ++h)
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 16 * h + ((4 * u + 4 * lg) & 15));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Y[16 * h + 4 * u + e] = x[e];
-              }
-          }
-          [&]<int... PI>(std::integer_sequence<int, PI...>) {
-            (([&] {
-               constexpr int t1 = T0 + 2 * PI, t2 = T0 + 2 * PI + 1;
-               constexpr bool has2 = 2 * PI + 1 < NTW;
-               const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
-#pragma unroll
-               for (int dt = 0; dt < NT; ++dt) acc[dt] = mfma(af, Sb[PI][dt], acc[dt]);
-             }()),
-             ...);
-          }(std::make_integer_sequence<int, NPAIR>{});
-          float* dst = pp + (W * CF::GMT + ml) * 16 * CF::PP;
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(4 * lg + r) * CF::PP + 16 * dt + ln] = acc[dt][r];
-        }
-        if (g + 1 < CF::NG) {
-          __syncthreads();
-          if (W < CF::GMT) {
-            // reduce (same code as after the build, for an earlier token group)
-            const int mt = g * CF::GMT + W;
-            constexpr int CPL = DV / 4;
-            const int row = lane >> 2, col0 = (lane & 3) * CPL;
-            const int t = t0 + 16 * mt + row;
-            float s[CPL];
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) s[e] = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-              const float* src = pp + ((w2 * CF::GMT + W) * 16 + row) * CF::PP + col0;
-#pragma unroll
-              for (int e = 0; e < CPL; e += 4) {
-                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + e);
-                s[e] += x[0]; s[e + 1] += x[1]; s[e + 2] += x[2]; s[e + 3] += x[3];
-              }
-            }
-            const float dn = den[16 * mt + row];
-            const float inv = dn > 0.f ? 1.0f / dn : 0.f;
-            if (t < a.T) store_row<CPL>(a, (bh * a.T + t) * DV + col0, s, inv);
-          }
-          __syncthreads();
-        }
+    if constexpr (CF::DUALV) {
+      if (c > c0) {  // build operands of this chunk (its rows were staged during the last build)
+        stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
+        if (c + 1 < c1) stg.load(t0 + C);
       }
     }
-
-    // ---- state build: S += psi(K_c)^T V_c over this wave's tiles; Gram tile update
+    // ================= readout phase =================
+    const int qrow = 16 * TT + ln;
+    f32x4_t O[NT];
 #pragma unroll
-    for (int ks = 0; ks < CF::KSTEP; ++ks) {
-      float N[NH][8], N2[NH][8];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const float* src = khT + (16 * h + ln) * CF::KTP + 32 * ks + 8 * lg;
+    for (int dt = 0; dt < NT; ++dt) O[dt] = zero4();
+    float dpart = 0.f;
+    if constexpr (OWNER) {
+      // query operand (B of S^T and of X^T): q_hat[qrow][8lg..8lg+7] as bf16 hi / lo
+      // component k-slots of lane group lg: 4lg..4lg+3 and 16+4lg..16+4lg+3 (16-byte steps)
+      bf16x8_t qbh, qbl;
+      {
+        const float* src = qh + qrow * CF::QP + 4 * lg;
         const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          N[h][e] = x0[e];
-          N[h][4 + e] = x1[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) N2[h][e] = 2.f * N[h][e];
+        const f32x4_t x1 = P == 32 ? *reinterpret_cast<const f32x4_t*>(src + 16) : zero4();
+        const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        split8(xs, qbh, qbl);
       }
-      bf16x8_t vb[NT];
+      // denominator, inter-chunk part: X^T = M Q_hat^T (rows: components), then q_hat . X
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-        vb[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(vt + (16 * dt + ln) * CF::VTP + 32 * ks + 8 * lg));
-      [&]<int... TI>(std::integer_sequence<int, TI...>) {
+      for (int rt = 0; rt < NH; ++rt) {
+        const uint16_t* mrow = mlds + (16 * rt + ln) * CF::MP + 4 * lg;
+        const u32x2_t h0 = *reinterpret_cast<const u32x2_t*>(mrow);
+        const u32x2_t l0 = *reinterpret_cast<const u32x2_t*>(mrow + P * CF::MP);
+        const u32x2_t h1 = P == 32 ? *reinterpret_cast<const u32x2_t*>(mrow + 16) : u32x2_t{0, 0};
+        const u32x2_t l1 = P == 32 ? *reinterpret_cast<const u32x2_t*>(mrow + P * CF::MP + 16) : u32x2_t{0, 0};
+        const bf16x8_t mh = __builtin_bit_cast(bf16x8_t, u32x4_t{h0[0], h0[1], h1[0], h1[1]});
+        const bf16x8_t ml = __builtin_bit_cast(bf16x8_t, u32x4_t{l0[0], l0[1], l1[0], l1[1]});
+        f32x4_t X = zero4();
+        X = mfma(mh, qbh, X);
+        X = mfma(ml, qbh, X);
+        X = mfma(mh, qbl, X);
+        const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + qrow * CF::QP + 16 * rt + 4 * lg);
+        dpart += X[0] * qv[0] + X[1] * qv[1] + X[2] * qv[2] + X[3] * qv[3];
+      }
+      // intra block: S^T = K_hat Q_hat^T over key tiles kt <= TT; W = (S^T)^2; O += W V.
+      // Global chunk 0 (denominators of few weights) uses split-bf16 scores.
+      const bool split = c == 0;
+#pragma unroll
+      for (int kp = 0; kp <= TT / 2; ++kp) {
+        float wv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kt = 2 * kp + half;
+          f32x4_t St = zero4();
+          if (kt <= TT) {
+            bf16x8_t kbh, kbl;
+            const float* src = kh + (16 * kt + ln) * CF::QP + 4 * lg;
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
+            const f32x4_t x1 = P == 32 ? *reinterpret_cast<const f32x4_t*>(src + 16) : zero4();
+            float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            if (split) {
+              split8(xs, kbh, kbl);
+              St = mfma(kbh, qbh, St);
+              St = mfma(kbl, qbh, St);
+              St = mfma(kbh, qbl, St);
+            } else {
+              St = mfma(pack8(xs), qbh, St);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float w = St[r] * St[r];
+            if (kt == TT && 4 * lg + r > ln) w = 0.f;  // causal: key <= query on the diagonal tile
+            wv[4 * half + r] = w;
+            dpart += w;
+          }
+        }
+        const bf16x8_t wa = pack8(wv);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          // keys 32kp + 4lg + j and 32kp + 16 + 4lg + j, stored adjacent (permuted V^T)
+          const bf16x8_t vbf = *reinterpret_cast<const bf16x8_t*>(vt + vt_row(16 * dt + ln) * CF::VTP + 32 * kp + 8 * lg);
+          O[dt] = mfma(wa, vbf, O[dt]);
+        }
+      }
+      dpart += __shfl_xor(dpart, 16, 64);
+      dpart += __shfl_xor(dpart, 32, 64);  // denominator of query qrow, in every lane group
+    }
+    // readout psi(Q) S over pairs [PB, PE): Y[x] = q_hat[qrow][(x & ~15) | ((x + 4 lg) & 15)]
+    {
+      float Y[P];
+      const float* src = qh + qrow * CF::QP;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 16 * h + ((4 * u + 4 * lg) & 15));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Y[16 * h + 4 * u + e] = x[e];
+        }
+      [&]<int... PI>(std::integer_sequence<int, PI...>) {
         (([&] {
-           const bf16x8_t af = build_frag<P, T0 + TI>(N, N2, mlow);
+           constexpr int t1 = 2 * (PB + PI), t2 = t1 + 1;
+           constexpr bool has2 = t2 < CF::NTL;
+           const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
 #pragma unroll
-           for (int dt = 0; dt < NT; ++dt) S[TI][dt] = mfma(af, vb[dt], S[TI][dt]);
+           for (int dt = 0; dt < NT; ++dt) {
+             const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(sb + (((PB + PI) * NT + dt) * 64 + lane) * 16);
+             O[dt] = mfma(af, bfr, O[dt]);
+           }
          }()),
          ...);
-      }(std::make_integer_sequence<int, NTW>{});
-      if constexpr (OWN_M) {
-        bf16x8_t ah, al, bh_, bl;
-        split8(N[MRT], ah, al);
-        split8(N[MCT], bh_, bl);
-        Mt = mfma(ah, bh_, Mt);
-        Mt = mfma(al, bh_, Mt);
-        Mt = mfma(ah, bl, Mt);
-      }
+      }(std::make_integer_sequence<int, PE - PB>{});
     }
-    write_m(cur ^ 1);
-    if constexpr (FWD) convert_state();
-    __syncthreads();
-
-    if constexpr (FWD) {
-      // ---- combine the 4 partial outputs of the last token group, normalise, store
-      if (W < CF::GMT) {
-        const int mt = (CF::NG - 1) * CF::GMT + W;
-        constexpr int CPL = DV / 4;
-        const int row = lane >> 2, col0 = (lane & 3) * CPL;
-        const int t = t0 + 16 * mt + row;
-        float s[CPL];
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) s[e] = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-          const float* src = pp + ((w2 * CF::GMT + W) * 16 + row) * CF::PP + col0;
-#pragma unroll
-          for (int e = 0; e < CPL; e += 4) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + e);
-            s[e] += x[0]; s[e + 1] += x[1]; s[e + 2] += x[2]; s[e + 3] += x[3];
-          }
-        }
-        const float dn = den[16 * mt + row];
-        const float inv = dn > 0.f ? 1.0f / dn : 0.f;
-        if (t < a.T) store_row<CPL>(a, (bh * a.T + t) * DV + col0, s, inv);
-      }
-    }
-    if (c + 1 < c1) stg.stage(lds);
-    __syncthreads();
-  }
-
-  if constexpr (!FWD) {  // segment summary -> workspace slot seg
-    float* dst = a.ws + (bh * (a.nseg - 1) + seg) * CF::STATE_FLOATS;
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    if constexpr (!OWNER) {
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
-        *reinterpret_cast<f32x4_t*>(dst + (((T0 + i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
-    if constexpr (OWN_M)
-      *reinterpret_cast<f32x4_t*>(dst + (int64_t)CF::NTL * NT * 256 + (W * 64 + lane) * 4) = Mt;
+        *reinterpret_cast<f32x4_t*>(part + (((TT * (CF::FS - 1) + FSI) * NT + dt) * 64 + lane) * 16) = O[dt];
+    }
+    __syncthreads();
+    // ================= build phase =================
+    if constexpr (OWNER) {  // combine the partial outputs, normalise and store
+#pragma unroll
+      for (int f = 0; f < CF::FS - 1; ++f)
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+          O[dt] += *reinterpret_cast<const f32x4_t*>(part + (((TT * (CF::FS - 1) + f) * NT + dt) * 64 + lane) * 16);
+      float inv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float dn = __shfl(dpart, 4 * lg + r, 64);
+        inv[r] = dn > 0.f ? __builtin_amdgcn_rcpf(dn) : 0.f;
+      }
+      // output rows t0 + 16 TT + 4 lg + r, column 16 dt + ln (stores past T are dropped)
+      const uint32_t voff = (uint32_t)((16 * TT + 4 * lg) * DV + ln);
+      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)t0 * DV * osz, (uint32_t)(a.T - t0) * DV * osz);
+      if (a.o_f32) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[dt][r] * inv[r]), ro, (voff + r * DV + 16 * dt) * 4, 0, 0);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const uint32_t pr = pk2(O[dt][r] * inv[r], O[dt][r + 1] * inv[r + 1]);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pr, ro, (voff + r * DV + 16 * dt) * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pr >> 16), ro, (voff + (r + 1) * DV + 16 * dt) * 2, 0, 0);
+          }
+      }
+    }
+    build_chunk<P, DV, C, W>(S, Mt, khT, vb);
+    write_state();
+    write_m();
+    if constexpr (CF::DUALV) {
+      if (c + 1 < c1) stg.stage_rows(lds, CF::OFF_VT);  // rows of the next chunk (readout buffers are free)
+      __syncthreads();
+    } else {
+      __syncthreads();
+      if (c + 1 < c1) {
+        stg.load(t0 + C);
+        stg.stage_rows(lds, CF::OFF_VT);
+        stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
+      }
+      __syncthreads();
+    }
   }
 }
 
+// ---- summary of one segment: [S | M] after its chunks, written to workspace slot seg
+template <int P, int DV, int C, int W>
+__device__ __forceinline__ void run_sum(const Args& a, char* lds) {
+  using CF = Cfg<P, DV, C>;
+  constexpr int NT = CF::NT, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W), MT = m_tile<P>(W);
+  constexpr int OKT = 0, OVB = P * CF::KTP * 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = blockIdx.x / a.nblk_per_bh;
+  const int seg = blockIdx.x % a.nblk_per_bh;
+  const int nchunks = (a.T + C - 1) / C;
+  const int c0 = seg * a.cps;
+  const int c1 = min(nchunks, c0 + a.cps);
+
+  f32x4_t S[wave_na<P>(W)][NT];
+  f32x4_t Mt = zero4();
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) S[i][dt] = zero4();
+
+  Stager<P, DV, C, false> stg;
+  stg.init(a, bh);
+  stg.load(c0 * C);
+  stg.stage_build(lds, OKT, OVB);
+  if (c0 + 1 < c1) stg.load((c0 + 1) * C);
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    char* base = lds + buf * CF::SUM_BUF;
+    build_chunk<P, DV, C, W>(S, Mt, reinterpret_cast<const float*>(base + OKT),
+                             reinterpret_cast<const uint16_t*>(base + OVB));
+    if (c + 1 < c1) {
+      stg.stage_build(lds + (buf ^ 1) * CF::SUM_BUF, OKT, OVB);
+      if (c + 2 < c1) stg.load((c + 2) * C);
+    }
+    __syncthreads();
+  }
+  float* dst = a.ws + (bh * (a.nseg - 1) + seg) * CF::STATE_FLOATS;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+      *reinterpret_cast<f32x4_t*>(dst + (((T0 + i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
+  if constexpr (MT >= 0)
+    *reinterpret_cast<f32x4_t*>(dst + (int64_t)CF::NTL * NT * 256 + (MT * 64 + lane) * 4) = Mt;
+}
+
+template <int P, int DV, int C, bool FWD, int W>
+__device__ __forceinline__ void run_wave(const Args& a, char* lds) {
+  if constexpr (FWD) run_fwd<P, DV, C, W>(a, lds);
+  else run_sum<P, DV, C, W>(a, lds);
+}
+
 template <int P, int DV, int C, bool FWD>
-__global__ __launch_bounds__(256, 1) void chunked_bf16_kernel(Args a) {
-  __shared__ __align__(16) char lds[Cfg<P, DV, C>::LDS];
+__global__ __launch_bounds__(512, 1) void chunked_bf16_kernel(Args a) {
+  extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
     case 0: run_wave<P, DV, C, FWD, 0>(a, lds); break;
     case 1: run_wave<P, DV, C, FWD, 1>(a, lds); break;
     case 2: run_wave<P, DV, C, FWD, 2>(a, lds); break;
-    default: run_wave<P, DV, C, FWD, 3>(a, lds); break;
+    case 3: run_wave<P, DV, C, FWD, 3>(a, lds); break;
+    case 4: run_wave<P, DV, C, FWD, 4>(a, lds); break;
+    case 5: run_wave<P, DV, C, FWD, 5>(a, lds); break;
+    case 6: run_wave<P, DV, C, FWD, 6>(a, lds); break;
+    default: run_wave<P, DV, C, FWD, 7>(a, lds); break;
   }
 }
 
 template <int P, int DV, int C>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                       int B, int H, int T, const SegPlan& plan, float* ws, hipStream_t st) {
+  using CF = Cfg<P, DV, C>;
   const int BH = B * H;
   Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1};
   hipError_t e;
   if (plan.nseg > 1) {
+    auto ks = chunked_bf16_kernel<P, DV, C, false>;
+    if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS)) != hipSuccess) return e;
     a.nblk_per_bh = plan.nseg - 1;
-    chunked_bf16_kernel<P, DV, C, false><<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), 0, st>>>(a);
+    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(512), CF::SUM_LDS, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(ws, BH, plan.nseg - 1, Cfg<P, DV, C>::STATE_FLOATS, st)) != hipSuccess) return e;
+    if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;
   }
+  auto kf = chunked_bf16_kernel<P, DV, C, true>;
+  if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;
-  chunked_bf16_kernel<P, DV, C, true><<<dim3((unsigned)(BH * plan.nseg)), dim3(256), 0, st>>>(a);
+  kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), CF::LDS, st>>>(a);
   return hipGetLastError();
 }
 
