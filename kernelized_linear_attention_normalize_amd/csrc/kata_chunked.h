@@ -158,14 +158,17 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8
 // ---- work split over the 8 waves of a workgroup
 constexpr int NW = 8;
 // state-build tiles per wave, aligned to readout pairs (2 tiles) so every wave writes whole
-// 16-byte state fragments: p=32 -> 4 tiles each, wave 7 also the odd tile 32 (33 tiles);
-// p=16 -> waves 0..3 two tiles, wave 4 tile 8, waves 5..7 none (9 tiles)
-template <int P> constexpr int wave_t0(int w) { return P == 32 ? 4 * w : (w < 5 ? 2 * w : 9); }
-template <int P> constexpr int wave_nt(int w) { return P == 32 ? (w == 7 ? 5 : 4) : (w < 4 ? 2 : (w == 4 ? 1 : 0)); }
+// 16-byte state fragments. p=32: wave 0 has tiles 0..3 and the odd tile 32, wave w > 0 has
+// 4w..4w+3; p=16: waves 0..3 have 2w, 2w+1, wave 4 tile 8, waves 5..7 none. Low waves get
+// the extra build work: the high waves of a token tile carry its intra block.
+template <int P> constexpr int wave_nt(int w) { return P == 32 ? (w == 0 ? 5 : 4) : (w < 4 ? 2 : (w == 4 ? 1 : 0)); }
+template <int P> constexpr int wave_tile(int w, int i) {
+  return P == 32 ? (w == 0 ? (i < 4 ? i : 32) : 4 * w + i) : (w < 4 ? 2 * w + i : 8);
+}
 // register array extent (at least 1; a wave without tiles keeps one unused)
 template <int P> constexpr int wave_na(int w) { return wave_nt<P>(w) > 0 ? wave_nt<P>(w) : 1; }
-// Gram-matrix tile owned by wave w (-1: none; p=32 has 4 tiles, on waves 3..6, p=16 one)
-template <int P> constexpr int m_tile(int w) { return P == 32 ? (w >= 3 && w < 7 ? w - 3 : -1) : (w == 5 ? 0 : -1); }
+// Gram-matrix tile owned by wave w (-1: none; p=32 has 4 tiles, on waves 1..4, p=16 one)
+template <int P> constexpr int m_tile(int w) { return P == 32 ? (w >= 1 && w <= 4 ? w - 1 : -1) : (w == 5 ? 0 : -1); }
 
 // A operand of the state build for tile TAU: row m = this lane's feature, 8 tokens.
 // N[h][j] = k_hat[token j][16h + m]; N2 = 2 N carries c_ij^2 = 2 of off-diagonal
@@ -223,21 +226,16 @@ struct Cfg {
   static constexpr int MP = C == 128 ? P : P + 8;  // bf16 pitch of the Gram matrix rows (unpadded where LDS is short)
   static constexpr int SB_BYTES = NPAIR * NT * 64 * 16;            // bf16 state, B-fragment order
   static constexpr int PART_BYTES = NMT * (FS - 1) * NT * 64 * 16;  // partial outputs (fp32 acc layout)
-  static constexpr int lds_for(bool dual) {
-    return SB_BYTES + 2 * C * QP * 4 + (dual ? 2 : 1) * DV * VTP * 2 + P * KTP * 4 + 2 * P * MP * 2 + PART_BYTES;
-  }
-  // separate V^T copies for the intra block and the build let the next chunk's rows be
-  // staged while the build runs (2 barriers per chunk instead of 3)
-  static constexpr bool DUALV = lds_for(true) <= 160 * 1024;
+  static constexpr int PD_BYTES = FS > 1 ? NMT * 64 * 4 : 0;        // denominators handed to the other splits
   static constexpr int OFF_SB = 0;
   static constexpr int OFF_QH = OFF_SB + SB_BYTES;
   static constexpr int OFF_KH = OFF_QH + C * QP * 4;
-  static constexpr int OFF_VT = OFF_KH + C * QP * 4;                 // V^T read by the intra block
-  static constexpr int OFF_VB = OFF_VT + (DUALV ? DV * VTP * 2 : 0);  // V^T read by the build
-  static constexpr int OFF_KT = OFF_VB + DV * VTP * 2;
+  static constexpr int OFF_VT = OFF_KH + C * QP * 4;  // V^T, read by the intra block and the build
+  static constexpr int OFF_KT = OFF_VT + DV * VTP * 2;
   static constexpr int OFF_M = OFF_KT + P * KTP * 4;                // bf16 [hi,lo][P][MP]
   static constexpr int OFF_PART = OFF_M + 2 * P * MP * 2;
-  static constexpr int LDS = OFF_PART + PART_BYTES;
+  static constexpr int OFF_PD = OFF_PART + PART_BYTES;
+  static constexpr int LDS = OFF_PD + PD_BYTES;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   // summary pass: build operands only, double-buffered
   static constexpr int SUM_BUF = DV * VTP * 2 + P * KTP * 4;
@@ -261,8 +259,24 @@ struct Cfg {
     vd = r % VL + VL * (qd % VH);
     vp = 16 * (sg >> 1) + 4 * (sg & 1) + (vl & 3) + 8 * (vl >> 2);
   }
-  // readout pair ranges: split fs covers pairs [pr(fs), pr(fs+1))
-  static constexpr int pr(int fs) { return fs >= FS ? NPAIR : (fs * (NPAIR + 1)) / FS; }
+  // readout pair ranges of token tile tt: split fs covers pairs [pr(fs, tt), pr(fs + 1, tt)).
+  // The last split also runs the intra block and the denominator (more work for larger tt),
+  // so it takes fewer pairs; the others share the rest evenly.
+  static constexpr int owner_pairs(int tt) {
+    const int even = NPAIR / FS, less = 2 + tt / 2;
+    return FS == 1 ? NPAIR : (even - less >= 1 ? even - less : 1);
+  }
+  static constexpr int pr(int fs, int tt) {
+    return fs >= FS ? NPAIR : (FS == 1 ? 0 : (fs * (NPAIR - owner_pairs(tt))) / (FS - 1));
+  }
+  // the FS splits of a token tile share its output: split out_owner(dt) normalises and
+  // stores output column tile dt, after adding the other splits' partial sums
+  static constexpr int out_owner(int dt) { return NT >= FS ? dt * FS / NT : dt; }
+  static constexpr bool owns_any(int f) { return NT >= FS || f < NT; }
+  // LDS slot of split f's partial sum of column tile dt of token tile tt (f != out_owner(dt))
+  static constexpr int part_slot(int tt, int dt, int f) {
+    return (tt * NT + dt) * (FS - 1) + (f < out_owner(dt) ? f : f - 1);
+  }
 };
 
 struct Args {
@@ -290,6 +304,7 @@ struct Stager {
   using CF = Cfg<P, DV, C>;
   typedef uint16_t row_t __attribute__((ext_vector_type(P / 4)));
   row_t qk[CF::QKI];          // piece i: q (first 4C pieces) or k row piece
+  float kx[CF::QKI][CF::KQ];  // normalised k pieces of the rows staged last (forward only)
   u16x8_t vr[CF::VI][2];
   const uint16_t *qb, *kb, *vb;
   int T;
@@ -379,7 +394,7 @@ struct Stager {
   }
 
   // row-major q_hat, k_hat (fp32) and V^T for the readout / intra block
-  __device__ __forceinline__ void stage_rows(char* lds, int off_vt) {
+  __device__ __forceinline__ void stage_rows(char* lds) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < CF::QKI; ++i) {
@@ -388,18 +403,19 @@ struct Stager {
       const bool isq = pc < 4 * C;
       if (!WITH_Q && isq) continue;
       const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
-      float x[CF::KQ];
+      float(&x)[CF::KQ] = kx[i];  // kept for stage_kt of the same chunk
       normalise(qk[i], x);
       float* dst = reinterpret_cast<float*>(lds + (isq ? CF::OFF_QH : CF::OFF_KH)) + row * CF::QP + kq * CF::KQ;
 #pragma unroll
       for (int e = 0; e < CF::KQ; e += 4)
         *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{x[e], x[e + 1], x[e + 2], x[e + 3]};
     }
-    write_vt(lds + off_vt);
   }
 
-  // k_hat^T (fp32) and V^T for the state build (at byte offsets off_kt, off_vb)
-  __device__ __forceinline__ void stage_build(char* lds, int off_kt, int off_vb) {
+  // k_hat^T (fp32) for the state build at byte offset off_kt; ROWS_STAGED: stage_rows already
+  // normalised this chunk's k pieces
+  template <bool ROWS_STAGED>
+  __device__ __forceinline__ void stage_kt(char* lds, int off_kt) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < CF::QKI; ++i) {
@@ -408,7 +424,12 @@ struct Stager {
       if (pc < 4 * C) continue;  // q pieces
       const int row = (pc - 4 * C) >> 2, kq = pc & 3;
       float x[CF::KQ];
-      normalise(qk[i], x);
+      if constexpr (ROWS_STAGED) {
+#pragma unroll
+        for (int e = 0; e < CF::KQ; ++e) x[e] = kx[i][e];
+      } else {
+        normalise(qk[i], x);
+      }
       // component row r starts at r * KTP + 8 (r / KQ); token t sits in plane (t / 16) & 1
       // at (t / 32) * 16 + t % 16 of it
       float* kt = reinterpret_cast<float*>(lds + off_kt) + (kq * CF::KQ) * CF::KTP + 8 * kq +
@@ -416,7 +437,6 @@ struct Stager {
 #pragma unroll
       for (int e = 0; e < CF::KQ; ++e) kt[e * CF::KTP] = x[e];
     }
-    write_vt(lds + off_vb);
   }
 };
 
@@ -425,7 +445,7 @@ template <int P, int DV, int C, int W>
 __device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16], f32x4_t& Mt,
                                             const float* khT, const uint16_t* vb_lds) {
   using CF = Cfg<P, DV, C>;
-  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W);
+  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W);
   constexpr int MT = m_tile<P>(W), MRT = MT / NH, MCT = MT % NH;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const bool mlow = ln < 8;
@@ -452,7 +472,7 @@ __device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16]
       vbf[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(vb_lds + vt_row(16 * dt + ln) * CF::VTP + 32 * ks + 8 * lg));
     [&]<int... TI>(std::integer_sequence<int, TI...>) {
       (([&] {
-         const bf16x8_t af = build_frag<P, T0 + TI>(N, N2, mlow);
+         const bf16x8_t af = build_frag<P, wave_tile<P>(W, TI)>(N, N2, mlow);
 #pragma unroll
          for (int dt = 0; dt < NT; ++dt) S[TI][dt] = mfma(af, vbf[dt], S[TI][dt]);
        }()),
@@ -469,11 +489,11 @@ __device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16]
 template <int P, int DV, int C, int W>
 __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   using CF = Cfg<P, DV, C>;
-  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W);
+  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W);
   constexpr int MT = m_tile<P>(W), MRT = MT / NH, MCT = MT % NH;
   constexpr int TT = W % CF::NMT, FSI = W / CF::NMT;   // token tile, feature split
   constexpr bool OWNER = FSI == CF::FS - 1;            // intra block, denominator, output
-  constexpr int PB = CF::pr(FSI), PE = CF::pr(FSI + 1);
+  constexpr int PB = CF::pr(FSI, TT), PE = CF::pr(FSI + 1, TT);
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const bool glow = lg < 2;
 
@@ -481,10 +501,10 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   const float* kh = reinterpret_cast<const float*>(lds + CF::OFF_KH);
   const float* khT = reinterpret_cast<const float*>(lds + CF::OFF_KT);
   const uint16_t* vt = reinterpret_cast<const uint16_t*>(lds + CF::OFF_VT);
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(lds + CF::OFF_VB);
   uint16_t* mlds = reinterpret_cast<uint16_t*>(lds + CF::OFF_M);
   char* sb = lds + CF::OFF_SB;
   char* part = lds + CF::OFF_PART;
+  float* pd = reinterpret_cast<float*>(lds + CF::OFF_PD);
 
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
@@ -507,7 +527,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
-        S[i][dt] = *reinterpret_cast<const f32x4_t*>(src + (((T0 + i) * NT + dt) * 64 + lane) * 4);
+        S[i][dt] = *reinterpret_cast<const f32x4_t*>(src + ((wave_tile<P>(W, i) * NT + dt) * 64 + lane) * 4);
     if constexpr (MT >= 0)
       Mt = *reinterpret_cast<const f32x4_t*>(src + (int64_t)CF::NTL * NT * 256 + (MT * 64 + lane) * 4);
   }
@@ -522,10 +542,10 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
       }
     }
   };
-  auto write_state = [&]() {  // tiles 2i, 2i+1 of this wave form readout pair (T0 + 2i) / 2
+  auto write_state = [&]() {  // tiles 2i, 2i+1 of this wave form readout pair wave_tile(2i) / 2
 #pragma unroll
     for (int i = 0; i < NTW; i += 2) {
-      const int pair = (T0 + i) >> 1;
+      const int pair = wave_tile<P>(W, i) >> 1;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
         u32x4_t u;
@@ -545,22 +565,20 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   Stager<P, DV, C, true> stg;
   stg.init(a, bh);
   stg.load(c0 * C);
-  stg.stage_rows(lds, CF::OFF_VT);
-  stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
+  stg.stage_rows(lds);
+  stg.template stage_kt<true>(lds, CF::OFF_KT);
+  stg.write_vt(lds + CF::OFF_VT);
   write_state();
   write_m();
-  if (CF::DUALV && c0 + 1 < c1) stg.load((c0 + 1) * C);
   __syncthreads();
 
+  // Per chunk c, two phases: (1) readout of chunk c from the state before it (LDS) and the
+  // build of chunk c into the registers; (2) output, staging of chunk c + 1, and the state
+  // after chunk c into LDS. Both readout and build read only the state before chunk c.
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
-    if constexpr (CF::DUALV) {
-      if (c > c0) {  // build operands of this chunk (its rows were staged during the last build)
-        stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
-        if (c + 1 < c1) stg.load(t0 + C);
-      }
-    }
-    // ================= readout phase =================
+    if (c + 1 < c1) stg.load(t0 + C);  // rows of the next chunk, staged in phase 2
+    // ================= phase 1: readout =================
     const int qrow = 16 * TT + ln;
     f32x4_t O[NT];
 #pragma unroll
@@ -632,7 +650,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
         for (int dt = 0; dt < NT; ++dt) {
           // keys 32kp + 4lg + j and 32kp + 16 + 4lg + j, stored adjacent (permuted V^T)
           const bf16x8_t vbf = *reinterpret_cast<const bf16x8_t*>(vt + vt_row(16 * dt + ln) * CF::VTP + 32 * kp + 8 * lg);
-          O[dt] = mfma(wa, vbf, O[dt]);
+          O[dt] = mfma(vbf, wa, O[dt]);  // O^T += V^T W^T
         }
       }
       dpart += __shfl_xor(dpart, 16, 64);
@@ -658,66 +676,52 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 #pragma unroll
            for (int dt = 0; dt < NT; ++dt) {
              const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(sb + (((PB + PI) * NT + dt) * 64 + lane) * 16);
-             O[dt] = mfma(af, bfr, O[dt]);
+             O[dt] = mfma(bfr, af, O[dt]);  // O^T += S^T psi(Q)^T
            }
          }()),
          ...);
       }(std::make_integer_sequence<int, PE - PB>{});
     }
-    if constexpr (!OWNER) {
+    // ================= phase 1: build =================
+    build_chunk<P, DV, C, W>(S, Mt, khT, vt);
+    // O holds O^T: lane (ln, lg) has columns 16 dt + 4 lg + r of query 16 TT + ln
+    if constexpr (CF::FS > 1) {
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
-        *reinterpret_cast<f32x4_t*>(part + (((TT * (CF::FS - 1) + FSI) * NT + dt) * 64 + lane) * 16) = O[dt];
+        if (CF::out_owner(dt) != FSI)
+          *reinterpret_cast<f32x4_t*>(part + (CF::part_slot(TT, dt, FSI) * 64 + lane) * 16) = O[dt];
+      if constexpr (OWNER) pd[TT * 64 + lane] = dpart;
     }
     __syncthreads();
-    // ================= build phase =================
-    if constexpr (OWNER) {  // combine the partial outputs, normalise and store
-#pragma unroll
-      for (int f = 0; f < CF::FS - 1; ++f)
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-          O[dt] += *reinterpret_cast<const f32x4_t*>(part + (((TT * (CF::FS - 1) + f) * NT + dt) * 64 + lane) * 16);
-      float inv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float dn = __shfl(dpart, 4 * lg + r, 64);
-        inv[r] = dn > 0.f ? __builtin_amdgcn_rcpf(dn) : 0.f;
-      }
-      // output rows t0 + 16 TT + 4 lg + r, column 16 dt + ln (stores past T are dropped)
-      const uint32_t voff = (uint32_t)((16 * TT + 4 * lg) * DV + ln);
+    // ================= phase 2 =================
+    if constexpr (CF::owns_any(FSI)) {  // add the other splits' sums, normalise, store
+      float den = dpart;
+      if constexpr (!OWNER) den = pd[TT * 64 + lane];
+      const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
       const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)t0 * DV * osz, (uint32_t)(a.T - t0) * DV * osz);
-      if (a.o_f32) {
+      const uint32_t ob = (uint32_t)((16 * TT + ln) * DV + 4 * lg);  // rows past T are dropped
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+      for (int dt = 0; dt < NT; ++dt) {
+        if (CF::out_owner(dt) != FSI) continue;
+        f32x4_t o = O[dt];
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[dt][r] * inv[r]), ro, (voff + r * DV + 16 * dt) * 4, 0, 0);
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const uint32_t pr = pk2(O[dt][r] * inv[r], O[dt][r + 1] * inv[r + 1]);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pr, ro, (voff + r * DV + 16 * dt) * 2, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pr >> 16), ro, (voff + (r + 1) * DV + 16 * dt) * 2, 0, 0);
-          }
+        for (int f = 0; f < CF::FS; ++f)
+          if (f != FSI) o += *reinterpret_cast<const f32x4_t*>(part + (CF::part_slot(TT, dt, f) * 64 + lane) * 16);
+        o *= inv;
+        if (a.o_f32)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, (ob + 16 * dt) * 4, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pk2(o[0], o[1]), pk2(o[2], o[3])}, ro, (ob + 16 * dt) * 2, 0, 0);
       }
     }
-    build_chunk<P, DV, C, W>(S, Mt, khT, vb);
-    write_state();
+    if (c + 1 < c1) {
+      stg.stage_rows(lds);
+      stg.template stage_kt<true>(lds, CF::OFF_KT);
+      stg.write_vt(lds + CF::OFF_VT);
+    }
+    write_state();  // last: waits for the build's MFMAs
     write_m();
-    if constexpr (CF::DUALV) {
-      if (c + 1 < c1) stg.stage_rows(lds, CF::OFF_VT);  // rows of the next chunk (readout buffers are free)
-      __syncthreads();
-    } else {
-      __syncthreads();
-      if (c + 1 < c1) {
-        stg.load(t0 + C);
-        stg.stage_rows(lds, CF::OFF_VT);
-        stg.stage_build(lds, CF::OFF_KT, CF::OFF_VB);
-      }
-      __syncthreads();
-    }
+    __syncthreads();
   }
 }
 
@@ -725,7 +729,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 template <int P, int DV, int C, int W>
 __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   using CF = Cfg<P, DV, C>;
-  constexpr int NT = CF::NT, NTW = wave_nt<P>(W), T0 = wave_t0<P>(W), MT = m_tile<P>(W);
+  constexpr int NT = CF::NT, NTW = wave_nt<P>(W), MT = m_tile<P>(W);
   constexpr int OKT = 0, OVB = P * CF::KTP * 4;
   const int lane = threadIdx.x & 63;
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
@@ -744,7 +748,8 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   Stager<P, DV, C, false> stg;
   stg.init(a, bh);
   stg.load(c0 * C);
-  stg.stage_build(lds, OKT, OVB);
+  stg.template stage_kt<false>(lds, OKT);
+  stg.write_vt(lds + OVB);
   if (c0 + 1 < c1) stg.load((c0 + 1) * C);
   __syncthreads();
   for (int c = c0; c < c1; ++c) {
@@ -753,7 +758,8 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
     build_chunk<P, DV, C, W>(S, Mt, reinterpret_cast<const float*>(base + OKT),
                              reinterpret_cast<const uint16_t*>(base + OVB));
     if (c + 1 < c1) {
-      stg.stage_build(lds + (buf ^ 1) * CF::SUM_BUF, OKT, OVB);
+      stg.template stage_kt<false>(lds + (buf ^ 1) * CF::SUM_BUF, OKT);
+      stg.write_vt(lds + (buf ^ 1) * CF::SUM_BUF + OVB);
       if (c + 2 < c1) stg.load((c + 2) * C);
     }
     __syncthreads();
@@ -763,7 +769,7 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt)
-      *reinterpret_cast<f32x4_t*>(dst + (((T0 + i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
+      *reinterpret_cast<f32x4_t*>(dst + ((wave_tile<P>(W, i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
   if constexpr (MT >= 0)
     *reinterpret_cast<f32x4_t*>(dst + (int64_t)CF::NTL * NT * 256 + (MT * 64 + lane) * 4) = Mt;
 }
