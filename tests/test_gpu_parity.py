@@ -119,6 +119,20 @@ def test_chunked_bf16_shapes(p, dv, C, T):
     assert row_rel_err(got32, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("H,dt,p,dv", [(1, "bf16", 32, 64), (10, "bf16", 32, 64), (1, "f32", 16, 32),
+                                       (10, "f32", 16, 32)])
+def test_chunked_many_segments(H, dt, p, dv):
+    """Few heads over many chunks: 63 (H=1) and 25 (H=10) segment summaries per head go
+    through the inter-segment scan (its 64- and 32-lane segment layouts)."""
+    q, k, v = _case("chunked-segments", 14, 1, H, 4096, p, dv, dt)
+    ref = ko.naive(q, k, v)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    got = to_np(kata.chunked_fwd(qd, kd, vd, C=32, scan="associative", out_dtype=torch.float32))
+    err = row_rel_err(got, ref)
+    print(f"  rel_err={err:.3e}", flush=True)
+    assert err <= TOL[dt]
+
+
 @pytest.mark.parametrize("T", [1, 5, 31, 64])
 def test_chunked_short_sequences(T):
     q, k, v = _case("chunked-short", 12, 1, 2, T, 32, 64, "bf16")
