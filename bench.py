@@ -3,11 +3,16 @@
 Default workload (the headline metric): the exact O(T) chunked-state forward,
 B=1, H=16, T=131072, p=32 (n=528), dv=64, bf16 inputs, fp32 accumulation, C=64,
 associative inter-segment scan; seeded N(0,1) synthetic inputs (seed 2).
-One step = one kata_chunked_fwd call = every kernel of the forward (segment summaries,
-scan, chunk pass). Prints ONE JSON line.
+One step = the whole forward: its three passes (segment summaries, scan, segments),
+issued as kata_chunked_fwd_passes calls on one stream with HIP events between them, so
+the dominant kernel (the segment pass, which performs all of the method's flops) is timed
+on its own. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--chunk 64|128] [--scan associative|sequential]
-                    [--workload long|quadratic|decode] [--no-cpu-baseline]
+                    [--workload long|quadratic|decode|copy] [--no-cpu-baseline]
+
+--workload copy times a plain device-to-device copy of 1 GiB (torch's copy kernel); it is
+the reference for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels.
 """
 from __future__ import annotations
 
@@ -88,7 +93,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--scan", default="associative", choices=["associative", "sequential"])
-    ap.add_argument("--workload", default="long", choices=["long", "quadratic", "decode"])
+    ap.add_argument("--workload", default="long", choices=["long", "quadratic", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,7 +118,11 @@ def main():
         out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
         need = kata.chunked_workspace_bytes(B, H, T, p, dv, C, kata._scan_code(args.scan))
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        step = lambda: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws)
+        passes = (kata.PASS_SUMMARIES, kata.PASS_SCAN, kata.PASS_SEGMENTS)
+        step = [lambda m=m: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws,
+                                             passes=m) for m in passes]
+        dominant = 2  # the segment pass
+        kernel_name = f"chunked_bf16_kernel<{p}, {dv}, {C}, true>"
         n = p * (p + 1) // 2
         flops = chunked_flops_per_head_token(n, p, dv, C) * B * H * T
         units = B * T
@@ -131,7 +140,9 @@ def main():
         to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
         qd, kd, vd = to(q), to(k), to(v)
         out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
-        step = lambda: kata.quadratic_fwd(qd, kd, vd, out=out)
+        step = [lambda: kata.quadratic_fwd(qd, kd, vd, out=out)]
+        dominant = 0
+        kernel_name = "quadratic_bf16_kernel"
         pairs = B * H * T * (T + 1) // 2
         flops = (2 * p + 2 * (dv + 1)) * pairs
         units = B * T
@@ -141,6 +152,20 @@ def main():
                   "parallelism": "single-gpu"}
         bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
         traffic_file = "quadratic_traffic.txt"
+    elif args.workload == "copy":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        step = [lambda: dst.copy_(src)]
+        dominant = 0
+        kernel_name = "copy (torch elementwise)"
+        flops = None
+        units = nbytes
+        bytes_alg = 2 * nbytes
+        metric = "device copy bytes/s (counter calibration)"
+        config = {"workload": f"copy: {nbytes} bytes bf16 device to device", "parallelism": "single-gpu"}
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        traffic_file = "copy_traffic.txt"
     else:
         from oracle import kata_oracle as ko  # state prefill of the decode workload (input data)
         from kata_inputs import draw_decode_history, draw_decode_steps
@@ -162,10 +187,13 @@ def main():
         nsteps = DECODE["steps"]
         ctr = {"i": 0}
 
-        def step():
+        def decode():
             i = ctr["i"] % nsteps
             ctr["i"] += 1
             return kata.decode_step(qd[i], kd[i], vd[i], S, Z, out=out)
+        step = [decode]
+        dominant = 0
+        kernel_name = "decode_kernel"
         flops = None
         units = N
         bytes_alg = N * H * (2 * n * dv * 4 + 2 * n * 4 + (2 * p + 2 * dv) * 2)
@@ -176,32 +204,45 @@ def main():
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         traffic_file = "decode_traffic.txt"
 
+    # every launch of a step is bracketed by HIP events on the stream it runs on
     torch.cuda.synchronize(dev)
     for _ in range(args.warmup):
-        step()
+        for call in step:
+            call()
     torch.cuda.synchronize(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step) + 1)] for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, call in enumerate(step):
+            call()
+            ev[i][j + 1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms_total = e0.elapsed_time(e1)
     ms = ms_total / args.steps
     value = units / (ms * 1e-3)
+    launch_ms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
+                 for j in range(len(step))]
+    ms_dom = launch_ms[dominant]
 
+    # roofline of the dominant kernel: algorithmic work of one launch / its mean duration
     if flops is not None:
-        achieved = flops / (ms * 1e-3) / 1e12
+        achieved = flops / (ms_dom * 1e-3) / 1e12
         alg_per_launch = flops
+        step_frac = flops / (ms * 1e-3) / 1e12 / peak
     else:
-        achieved = bytes_alg / (ms * 1e-3) / 1e9
+        achieved = bytes_alg / (ms_dom * 1e-3) / 1e9
         alg_per_launch = bytes_alg
+        step_frac = bytes_alg / (ms * 1e-3) / 1e9 / peak
     traffic = read_traffic(traffic_file)
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "algorithmic_per_launch": alg_per_launch,
-            "launch": "one API call (all kernels of one step)"}
+            "kernel": kernel_name, "kernel_ms": round(ms_dom, 5),
+            "algorithmic_per_launch": alg_per_launch, "step_frac": round(step_frac, 4),
+            "launch_ms": [round(x, 5) for x in launch_ms]}
 
     # spot parity on a few rows (outside the timed region)
     parity = None
@@ -216,7 +257,8 @@ def main():
     if args.workload == "long" and not args.no_cpu_baseline:
         cpu = cpu_baseline_long(q, k, v, H)
 
-    rec = {"metric": metric, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+    rec = {"metric": metric, "value": round(value, 1),
+           "unit": "bytes/s" if args.workload == "copy" else "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1))", "config": config, "roofline": roof,

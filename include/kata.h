@@ -66,8 +66,17 @@ typedef enum {
   KATA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
   KATA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than kata_chunked_workspace_bytes */
   KATA_ERR_HIP = 8,         /* a HIP launch failed */
-  KATA_ERR_SCAN = 9         /* scan is not a kata_scan_t value */
+  KATA_ERR_SCAN = 9,        /* scan is not a kata_scan_t value */
+  KATA_ERR_PASS = 10        /* passes is not a non-empty combination of kata_pass_t bits */
 } kata_status_t;
+
+/* The three passes of the chunked forward (bit mask). */
+typedef enum {
+  KATA_PASS_SUMMARIES = 1, /* per-segment state summaries into the workspace */
+  KATA_PASS_SCAN = 2,      /* in-place associative scan of the summaries over the segments */
+  KATA_PASS_SEGMENTS = 4,  /* every segment's chunks from its prefix: writes o */
+  KATA_PASS_ALL = 7
+} kata_pass_t;
 
 /* n = p(p+1)/2 (Eq. (8)); -1 if p < 1. */
 int64_t kata_packed_dim(int p);
@@ -110,6 +119,25 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata
                                void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
                                int C, kata_scan_t scan, void* workspace,
                                size_t workspace_bytes, kata_stream_t stream);
+
+/*
+ * kata_chunked_fwd_passes - kata_chunked_fwd split into its passes (chunked-forward
+ * paragraph: chunk summaries, the associative prefix over them, then every chunk from
+ * its prefix). passes is a mask of kata_pass_t bits; the enabled passes run in the order
+ * SUMMARIES, SCAN, SEGMENTS. Calls with masks 1, 2 and 4, issued in that order on one
+ * stream with the same arguments and workspace, enqueue exactly the kernels of one
+ * kata_chunked_fwd call and give the same o, bit for bit; mask 7 is kata_chunked_fwd.
+ * The workspace carries the summaries between the calls and must not be touched in
+ * between. With one segment (KATA_SCAN_SEQUENTIAL, or a single chunk) SUMMARIES and SCAN
+ * enqueue nothing. Uses: timing the passes separately, and placing work between them
+ * (for instance combining summaries of sequence shards held elsewhere). Arguments,
+ * validation and errors as kata_chunked_fwd, plus KATA_ERR_PASS for a bad mask.
+ */
+kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
+                                      int T, int p, int dv, int C, kata_scan_t scan,
+                                      void* workspace, size_t workspace_bytes, int passes,
+                                      kata_stream_t stream);
 
 /*
  * kata_quadratic_fwd - flash-attention-style forward without a state (abstract: the

@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = ["KataError", "library_path", "load", "packed_dim", "lift", "chunked_workspace_bytes",
-           "chunked_fwd", "quadratic_fwd", "decode_step", "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE"]
+           "chunked_fwd", "quadratic_fwd", "decode_step", "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE",
+           "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS", "PASS_ALL"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -26,9 +27,10 @@ _lib = None
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 SCAN_SEQUENTIAL, SCAN_ASSOCIATIVE = 0, 1
+PASS_SUMMARIES, PASS_SCAN, PASS_SEGMENTS, PASS_ALL = 1, 2, 4, 7
 _STATUS = {0: "KATA_OK", 1: "KATA_ERR_NULL", 2: "KATA_ERR_SHAPE", 3: "KATA_ERR_DTYPE",
            4: "KATA_ERR_UNSUPPORTED", 5: "KATA_ERR_ALIGN", 6: "KATA_ERR_ALIAS",
-           7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN"}
+           7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN", 10: "KATA_ERR_PASS"}
 
 
 class KataError(RuntimeError):
@@ -57,6 +59,8 @@ def load():
     lib.kata_chunked_workspace_bytes.restype = SZ
     lib.kata_chunked_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.kata_chunked_fwd.restype = I
+    lib.kata_chunked_fwd_passes.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, I, P]
+    lib.kata_chunked_fwd_passes.restype = I
     lib.kata_quadratic_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd.restype = I
     lib.kata_decode_step.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P]
@@ -123,8 +127,10 @@ def _scan_code(scan) -> int:
 
 
 def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,
-                workspace=None):
-    """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv]."""
+                workspace=None, passes: int = PASS_ALL):
+    """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv].
+    passes: subset of the passes to enqueue (PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS);
+    running them in separate calls needs the same out and workspace each time."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -141,9 +147,15 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(dev):
-        _check(lib.kata_chunked_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
-                                    out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc, ws_ptr,
-                                    ws_bytes, _stream(dev)), "kata_chunked_fwd")
+        if passes == PASS_ALL:
+            _check(lib.kata_chunked_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                        out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc, ws_ptr,
+                                        ws_bytes, _stream(dev)), "kata_chunked_fwd")
+        else:
+            _check(lib.kata_chunked_fwd_passes(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                               out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc,
+                                               ws_ptr, ws_bytes, int(passes), _stream(dev)),
+                   "kata_chunked_fwd_passes")
     return out
 
 

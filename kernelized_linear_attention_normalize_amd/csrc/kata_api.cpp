@@ -85,6 +85,7 @@ const char* kata_status_string(kata_status_t s) {
     case KATA_ERR_WORKSPACE: return "KATA_ERR_WORKSPACE: workspace missing or too small";
     case KATA_ERR_HIP: return "KATA_ERR_HIP: kernel launch failed";
     case KATA_ERR_SCAN: return "KATA_ERR_SCAN: invalid scan mode";
+    case KATA_ERR_PASS: return "KATA_ERR_PASS: invalid pass mask";
   }
   return "KATA_ERR_UNKNOWN";
 }
@@ -143,11 +144,13 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
   return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
 }
 
-kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
-                               void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
-                               int C, kata_scan_t scan, void* workspace, size_t workspace_bytes,
-                               kata_stream_t stream) {
+kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
+                                      int T, int p, int dv, int C, kata_scan_t scan,
+                                      void* workspace, size_t workspace_bytes, int passes,
+                                      kata_stream_t stream) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
+  if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
   bool zero = false;
   kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
@@ -173,11 +176,19 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), o, ob16, B, H, T,
-                                                p, dv, C, plan, ws, st));
+                                                p, dv, C, plan, ws, passes, st));
   return hip_status(kata::launch_chunked_f32(static_cast<const float*>(q),
                                              static_cast<const float*>(k),
                                              static_cast<const float*>(v), o, ob16, B, H, T, p, dv,
-                                             C, plan, ws, st));
+                                             C, plan, ws, passes, st));
+}
+
+kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                               int C, kata_scan_t scan, void* workspace, size_t workspace_bytes,
+                               kata_stream_t stream) {
+  return kata_chunked_fwd_passes(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, workspace,
+                                 workspace_bytes, KATA_PASS_ALL, stream);
 }
 
 kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,

@@ -797,19 +797,21 @@ __global__ __launch_bounds__(512, 1) void chunked_bf16_kernel(Args a) {
 
 template <int P, int DV, int C>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
-                      int B, int H, int T, const SegPlan& plan, float* ws, hipStream_t st) {
+                      int B, int H, int T, const SegPlan& plan, float* ws, int passes, hipStream_t st) {
   using CF = Cfg<P, DV, C>;
   const int BH = B * H;
   Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1};
   hipError_t e;
-  if (plan.nseg > 1) {
+  if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     auto ks = chunked_bf16_kernel<P, DV, C, false>;
     if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS)) != hipSuccess) return e;
     a.nblk_per_bh = plan.nseg - 1;
     ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(512), CF::SUM_LDS, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;
   }
+  if (plan.nseg > 1 && (passes & PASS_SCAN))
+    if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;
+  if (!(passes & PASS_SEGMENTS)) return hipSuccess;
   auto kf = chunked_bf16_kernel<P, DV, C, true>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;

@@ -146,18 +146,22 @@ hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st)
 
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, hipStream_t st) {
+                              float* ws, int passes, hipStream_t st) {
   const int BH = B * H;
   const size_t lds = f32_chunked_lds_bytes(p, dv, C);
-  if (plan.nseg > 1) {
+  if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     auto kfn = chunked_f32_kernel<false, 1>;
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
         q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(ws, BH, plan.nseg - 1, f32_state_floats(p, dv), st)) != hipSuccess) return e;
   }
+  if (plan.nseg > 1 && (passes & PASS_SCAN)) {
+    hipError_t e = launch_scan(ws, BH, plan.nseg - 1, f32_state_floats(p, dv), st);
+    if (e != hipSuccess) return e;
+  }
+  if (!(passes & PASS_SEGMENTS)) return hipSuccess;
   auto kfn = o_bf16 ? chunked_f32_kernel<true, 0> : chunked_f32_kernel<false, 0>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -14,6 +14,9 @@ struct SegPlan {
 };
 SegPlan seg_plan(int B, int H, int T, int C, int scan);
 
+// passes of the chunked forward (the values of kata_pass_t)
+enum : int { PASS_SUMMARIES = 1, PASS_SCAN = 2, PASS_SEGMENTS = 4 };
+
 // floats of one segment summary in the bf16 MFMA kernel's tile layout
 int64_t mfma_state_floats(int p, int dv);
 // floats of one segment summary in the fp32 kernel's layout (S then Z, packed order)
@@ -28,12 +31,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf
                          hipStream_t st);
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, hipStream_t st);
+                              float* ws, int passes, hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
-                               const SegPlan& plan, float* ws, hipStream_t st);
+                               const SegPlan& plan, float* ws, int passes, hipStream_t st);
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 

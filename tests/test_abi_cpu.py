@@ -18,7 +18,7 @@ from kernelized_linear_attention_normalize_amd import build_lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 F32, BF16 = 0, 1
 SEQ, ASSOC = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN = range(10)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN, E_PASS = range(11)
 A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never dereferenced)
 
 
@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 def test_packed_dim_and_status_strings(lib):
     assert lib.kata_packed_dim(32) == 528 and lib.kata_packed_dim(64) == 2080
     assert lib.kata_packed_dim(0) == -1
-    for s in range(10):
+    for s in range(11):
         assert lib.kata_status_string(s).startswith(b"KATA_")
 
 
@@ -82,6 +82,23 @@ def test_chunked_validation(lib):
     assert _chunked(lib, ws=A + (1 << 34), wsb=need, **kw) == E_ALIAS    # workspace overlaps o
     # fp32 path: state must fit in LDS
     assert _chunked(lib, in_dt=F32, p=32, dv=64, C=128) == E_UNSUP
+
+
+def test_chunked_passes_validation(lib):
+    def passes(mask, **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=1, H=1, T=128,
+                 p=32, dv=64, C=64, scan=SEQ, ws=None, wsb=0)
+        a.update(kw)
+        return lib.kata_chunked_fwd_passes(a["q"], a["k"], a["v"], a["in_dt"], a["o"], a["o_dt"], a["B"],
+                                           a["H"], a["T"], a["p"], a["dv"], a["C"], a["scan"], a["ws"],
+                                           a["wsb"], mask, None)
+    for bad in (0, 8, -1, 15):
+        assert passes(bad) == E_PASS
+    assert passes(7, scan=5) == E_SCAN           # shared validation, checked in the same order
+    assert passes(4, in_dt=9) == E_DTYPE
+    assert passes(1, q=None) == E_NULL
+    kw = dict(B=1, H=16, T=131072, scan=ASSOC, o=A + (1 << 34))
+    assert passes(2, **kw) == E_WS                # every pass needs the workspace of its plan
 
 
 def test_workspace_bytes(lib):

@@ -148,6 +148,22 @@ def test_chunked_empty_is_noop():
     assert kata.quadratic_fwd(q, q, v).shape == (1, 2, 0, 64)
 
 
+@pytest.mark.parametrize("dt,scan", [("bf16", "associative"), ("bf16", "sequential"), ("f32", "associative")])
+def test_chunked_passes_match_one_call(dt, scan):
+    """The three passes issued as separate calls reproduce one kata_chunked_fwd call bit for bit."""
+    p, dv = (32, 64) if dt == "bf16" else (16, 32)
+    q, k, v = _case("chunked-passes", 15, 1, 3, 2500, p, dv, dt)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    one = kata.chunked_fwd(qd, kd, vd, C=64, scan=scan)
+    need = kata.chunked_workspace_bytes(1, 3, 2500, p, dv, 64, kata._scan_code(scan),
+                                        torch.bfloat16 if dt == "bf16" else torch.float32)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(one)
+    for mask in (kata.PASS_SUMMARIES, kata.PASS_SCAN, kata.PASS_SEGMENTS):
+        kata.chunked_fwd(qd, kd, vd, C=64, scan=scan, out=out, workspace=ws, passes=mask)
+    assert torch.equal(out, one)
+
+
 def test_chunked_deterministic():
     q, k, v = _case("determinism", 13, 1, 4, 3000, 32, 64, "bf16")
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
