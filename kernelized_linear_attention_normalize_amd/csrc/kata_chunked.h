@@ -11,7 +11,7 @@
 //   * the remark on the fused rank-two forward: the per-token psi tensor is never
 //     written to HBM.
 //
-// Design (one workgroup = 4 waves per (b,h,segment); the state never leaves the chip):
+// Design (one workgroup = 8 waves per (b,h,segment); the state never leaves the chip):
 //   * The n = p(p+1)/2 packed features are ordered internally as tiles of 16 features.
 //     In tile tau, row m (0..15) holds a pair (i, j) in which one index is m (or 16+m)
 //     and the other is m rotated by a tile constant inside its 16-lane row. Hence a
@@ -19,30 +19,32 @@
 //     A-operand row of psi(K)^T with ONE v_mul_f32 whose first operand is a DPP row
 //     rotation: the lift costs one multiply per feature and never touches LDS or HBM.
 //     p = 32 gives 33 tiles = 528 features exactly; p = 16 gives 9 tiles (136 + 8 pad).
-//   * The state S (fp32) lives in MFMA accumulators, split by feature tiles over the 4
-//     waves (each wave builds its own tiles). After each chunk's build, every wave
-//     writes its tiles once to LDS as bf16 in the B-operand order of the readout (the
-//     16x16 accumulator rows 4g..4g+3 become the k-slots of lane group g; the A side
-//     permutes its k-slots the same way).
-//   * Readout: each wave owns 16 tokens of the chunk and computes psi(q)^T S over ALL
-//     features from the shared bf16 state, so its output needs no cross-wave reduction.
-//     Its psi(q) A operand comes from a per-lane-group rotated copy of q_hat (raw
-//     products q_i q_j): one multiply per feature.
+//   * The state S (fp32) lives in MFMA accumulators, split by feature tiles over the 8
+//     waves in whole readout pairs (two tiles = one 32-feature k-step). After each
+//     chunk's build every wave writes its pairs once to LDS as bf16 B fragments
+//     (accumulator rows 4g..4g+3 of the two tiles become the k-slots of lane group g;
+//     the readout side permutes its k-slots the same way).
+//   * Readout: wave w serves token tile w mod (C/16) over a range of the feature pairs;
+//     the splits of a token tile exchange partial sums through LDS. Operands are swapped
+//     (O^T = S^T psi(Q)^T): each lane ends with 4 consecutive output columns of one query.
+//     psi(q) comes from a per-lane-group rotated copy of q_hat (raw products q_i q_j).
 //   * Off-diagonal coordinates carry sqrt(2) in psi; their product c_ij^2 = 2 is folded
-//     into the state build (a 2 k_hat copy is staged in LDS), so the readout side uses
-//     raw products.
+//     into the state build (the DPP source is 2 k_hat), so the readout uses raw products.
 //   * The denominator psi(q)^T Z = q_hat^T M q_hat with the Gram matrix
 //     M = sum_s k_hat_s k_hat_s^T (p x p): M is updated and applied with split-bf16
 //     MFMAs (hi*hi + hi*lo + lo*hi), so the normaliser is fp32-accurate.
 //   * Intra-chunk block: S^T = K_hat Q_hat^T (keys as M), W = (S^T)^2 masked, rounded to
-//     bf16, O += W V. Global chunk 0, where denominators are sums of few weights, uses
-//     split-bf16 scores.
-//   * Per chunk: readout phase | barrier | build phase (which also stages the next
-//     chunk's row data) | barrier. Global loads for the next chunk are in flight during
-//     the readout phase.
+//     bf16, O^T += V^T W^T. Global chunk 0, where denominators are sums of few weights,
+//     uses split-bf16 scores.
+//   * Per chunk: phase 1 = readout from the state before the chunk + the chunk's build
+//     into the registers (both read only the state before it) | barrier | phase 2 =
+//     output, staging of the next chunk, state back to LDS | barrier.
+//   * LDS layouts follow measured gfx950 bank behaviour: 4-byte writes go in 32-lane
+//     passes over 32 banks; 16-byte reads by lanes (row, group) at row * pitch + 4 group
+//     floats are conflict-free for pitch = 8 * odd (mod 128 floats).
 //   * SEQUENTIAL: one workgroup per (b,h) walks all chunks. ASSOCIATIVE: a summary pass
 //     writes each segment's [S | M] (fp32, in this tile layout), an in-place scan forms
-//     exclusive prefixes, and every segment runs its chunks from its prefix.
+//     the prefixes, and every segment runs its chunks from its prefix.
 #pragma once
 #include <utility>
 
