@@ -29,7 +29,9 @@
 //     (O^T = S^T psi(Q)^T): each lane ends with 4 consecutive output columns of one query.
 //     psi(q) comes from a per-lane-group rotated copy of q_hat (raw products q_i q_j).
 //   * Off-diagonal coordinates carry sqrt(2) in psi; their product c_ij^2 = 2 is folded
-//     into the state build (the DPP source is 2 k_hat), so the readout uses raw products.
+//     into the state build: k_hat^T is staged as sqrt(2) k_hat, so an off-diagonal product
+//     is 2 k_i k_j, a diagonal one is halved, and the Gram tile (2 M) is halved when
+//     applied. The readout uses raw products q_i q_j.
 //   * The denominator psi(q)^T Z = q_hat^T M q_hat with the Gram matrix
 //     M = sum_s k_hat_s k_hat_s^T (p x p): M is updated and applied with split-bf16
 //     MFMAs (hi*hi + hi*lo + lo*hi), so the normaliser is fp32-accurate.
@@ -172,32 +174,50 @@ template <int P> constexpr int wave_na(int w) { return wave_nt<P>(w) > 0 ? wave_
 // Gram-matrix tile owned by wave w (-1: none; p=32 has 4 tiles, on waves 1..4, p=16 one)
 template <int P> constexpr int m_tile(int w) { return P == 32 ? (w >= 1 && w <= 4 ? w - 1 : -1) : (w == 5 ? 0 : -1); }
 
+// Build-work maps: state tiles, Gram tile and (pass 1 only) one column tile of the odd
+// state tile 32 per wave. Map8: the forward's 8 waves, as above.
+struct Map8 {
+  template <int P> static constexpr int nt(int w) { return wave_nt<P>(w); }
+  template <int P> static constexpr int tile(int w, int i) { return wave_tile<P>(w, i); }
+  template <int P> static constexpr int mtile(int w) { return m_tile<P>(w); }
+  template <int P> static constexpr int xdt(int, int) { return -1; }
+};
+// Map16: pass 1 (segment summaries) on 16 waves, 4 per SIMD. p=32: wave w builds tiles
+// 2w, 2w+1; tile 32 is split by output column tile over waves 0..NT-1; Gram tiles on waves
+// 4..7. p=16: wave w < 9 builds tile w; the Gram tile is on wave 9.
+struct Map16 {
+  template <int P> static constexpr int nt(int w) { return P == 32 ? 2 : (w < 9 ? 1 : 0); }
+  template <int P> static constexpr int tile(int w, int i) { return P == 32 ? 2 * w + i : (w < 9 ? w : 0); }
+  template <int P> static constexpr int mtile(int w) { return P == 32 ? (w >= 4 && w < 8 ? w - 4 : -1) : (w == 9 ? 0 : -1); }
+  template <int P> static constexpr int xdt(int w, int nt) { return P == 32 && w < nt ? w : -1; }
+};
+template <class MAP, int P> constexpr int map_na(int w) { return MAP::template nt<P>(w) > 0 ? MAP::template nt<P>(w) : 1; }
+
 // A operand of the state build for tile TAU: row m = this lane's feature, 8 tokens.
-// N[h][j] = k_hat[token j][16h + m]; N2 = 2 N carries c_ij^2 = 2 of off-diagonal
-// coordinates and is always the DPP-rotated operand (the compiler then folds the row
-// rotation into the multiply).
+// N[h][j] = sqrt(2) k_hat[token j][16h + m] (staged that way): an off-diagonal product
+// N_i N_j = 2 k_i k_j already carries c_ij^2 = 2, a diagonal one is halved. Both operands
+// come straight from LDS, so the compiler folds the DPP row rotation into the multiply.
 template <int P, int TAU>
-__device__ __forceinline__ bf16x8_t build_frag(const float (&N)[P / 16][8], const float (&N2)[P / 16][8],
-                                               bool mlow) {
+__device__ __forceinline__ bf16x8_t build_frag(const float (&N)[P / 16][8], bool mlow) {
   constexpr int kind = tile_kind<P>(TAU), h = tile_half<P>(TAU), d = tile_delta<P>(TAU);
   float x[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if constexpr (kind == K_DIAG) {
-      x[j] = N[h][j] * N[h][j];
+      x[j] = (N[h][j] * N[h][j]) * 0.5f;
     } else if constexpr (kind == K_WITHIN) {
-      x[j] = N[h][j] * rot<d>(N2[h][j]);
+      x[j] = N[h][j] * rot<d>(N[h][j]);
     } else if constexpr (kind == K_WITHIN8) {
       if constexpr (P == 32) {
         const float a = mlow ? N[0][j] : N[1][j];
-        const float b = mlow ? N2[1][j] : N2[0][j];
+        const float b = mlow ? N[1][j] : N[0][j];
         x[j] = a * rot<8>(b);
       } else {
         const float a = mlow ? N[0][j] : 0.f;
-        x[j] = a * rot<8>(N2[0][j]);
+        x[j] = a * rot<8>(N[0][j]);
       }
     } else {
-      x[j] = N[0][j] * rot<d>(N2[P / 16 - 1][j]);
+      x[j] = N[0][j] * rot<d>(N[P / 16 - 1][j]);
     }
   }
   return pack8(x);
@@ -265,7 +285,7 @@ struct Cfg {
   // The last split also runs the intra block and the denominator (more work for larger tt),
   // so it takes fewer pairs; the others share the rest evenly.
   static constexpr int owner_pairs(int tt) {
-    const int even = NPAIR / FS, less = 2 + tt / 2;
+    const int even = NPAIR / FS, less = 3 + tt / 2;
     return FS == 1 ? NPAIR : (even - less >= 1 ? even - less : 1);
   }
   static constexpr int pr(int fs, int tt) {
@@ -305,9 +325,26 @@ template <int P, int DV, int C, bool WITH_Q>
 struct Stager {
   using CF = Cfg<P, DV, C>;
   typedef uint16_t row_t __attribute__((ext_vector_type(P / 4)));
-  row_t qk[CF::QKI];          // piece i: q (first 4C pieces) or k row piece
-  float kx[CF::QKI][CF::KQ];  // normalised k pieces of the rows staged last (forward only)
-  u16x8_t vr[CF::VI][2];
+  // WITH_Q (forward, 512 threads): q then k row pieces on tid + 512 i, V pieces on
+  // tid + 512 i. Otherwise (pass 1, 1024 threads): k pieces on threads 0..4C-1 and V pieces
+  // on the threads after them, one of either per thread.
+  static constexpr int NQK = WITH_Q ? CF::QKI : 1, NV = WITH_Q ? CF::VI : 1;
+  static_assert(WITH_Q || 4 * C + CF::VPIECES <= 1024, "pass-1 staging layout");
+  row_t qk[NQK];          // piece i: q (first 4C pieces) or k row piece
+  float kx[NQK][CF::KQ];  // normalised k pieces of the rows staged last (forward only)
+  u16x8_t vr[NV][2];
+  // q/k piece index of slot i (k pieces are numbered from 4C), -1 for none
+  __device__ static __forceinline__ int qk_piece(int i) {
+    const int tid = threadIdx.x;
+    if constexpr (WITH_Q) return tid + 512 * i;
+    return tid < 4 * C ? 4 * C + tid : -1;
+  }
+  // V piece index of slot i (may be out of [0, VPIECES))
+  __device__ static __forceinline__ int v_piece(int i) {
+    const int tid = threadIdx.x;
+    if constexpr (WITH_Q) return tid + 512 * i;
+    return tid - 4 * C;
+  }
   const uint16_t *qb, *kb, *vb;
   int T;
 
@@ -333,8 +370,9 @@ struct Stager {
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * P, left * P * 2);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vb + (int64_t)t0 * DV, left * DV * 2);
 #pragma unroll
-    for (int i = 0; i < CF::QKI; ++i) {
-      const int pc = tid + 512 * i;
+    for (int i = 0; i < NQK; ++i) {
+      const int pc = qk_piece(i);
+      if (pc < 0) continue;  // whole waves
       // q or k is uniform across a wave (4C is a multiple of 64)
       const int isq = __builtin_amdgcn_readfirstlane(pc < 4 * C ? 1 : 0);
       const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
@@ -342,9 +380,9 @@ struct Stager {
       if (pc < CF::QK_PIECES && (WITH_Q || !isq)) qk[i] = load_piece(isq ? rq : rk, voff, 0);
     }
 #pragma unroll
-    for (int i = 0; i < CF::VI; ++i) {
-      const int pc = tid + 512 * i;
-      if (pc < CF::VPIECES) {
+    for (int i = 0; i < NV; ++i) {
+      const int pc = v_piece(i);
+      if (pc >= 0 && pc < CF::VPIECES) {
         int vp, vd;
         CF::vpiece(pc, vp, vd);
         const uint32_t voff = (uint32_t)(2 * vp * DV + 8 * vd) * 2;
@@ -355,7 +393,7 @@ struct Stager {
   }
 
   // normalised row piece (4 consecutive lanes share a row; the norm is combined over them)
-  __device__ __forceinline__ void normalise(const row_t& src, float (&x)[CF::KQ]) {
+  __device__ __forceinline__ void normalise(const row_t& src, float (&x)[CF::KQ], float scale = 1.f) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < CF::KQ; ++e) {
@@ -364,7 +402,7 @@ struct Stager {
     }
     ss += __shfl_xor(ss, 1, 64);
     ss += __shfl_xor(ss, 2, 64);
-    const float inv = inv_norm_fast(ss);
+    const float inv = inv_norm_fast(ss) * scale;
 #pragma unroll
     for (int e = 0; e < CF::KQ; ++e) x[e] *= inv;
   }
@@ -373,11 +411,10 @@ struct Stager {
   // group g reads its 8 k-slots (keys 32a + 4g + j, 32a + 16 + 4g + j: the row order of the
   // score fragments and of the k_hat^T planes) with one 16-byte read
   __device__ __forceinline__ void write_vt(char* vt_bytes) {
-    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < CF::VI; ++i) {
-      const int pc = tid + 512 * i;
-      if (pc < CF::VPIECES) {
+    for (int i = 0; i < NV; ++i) {
+      const int pc = v_piece(i);
+      if (pc >= 0 && pc < CF::VPIECES) {
         int vp, vd;
         CF::vpiece(pc, vp, vd);
         const int k = 2 * vp;
@@ -397,10 +434,10 @@ struct Stager {
 
   // row-major q_hat, k_hat (fp32) and V^T for the readout / intra block
   __device__ __forceinline__ void stage_rows(char* lds) {
-    const int tid = threadIdx.x;
+    static_assert(WITH_Q, "forward staging");
 #pragma unroll
-    for (int i = 0; i < CF::QKI; ++i) {
-      const int pc = tid + 512 * i;
+    for (int i = 0; i < NQK; ++i) {
+      const int pc = qk_piece(i);
       if (CF::QK_PIECES % 512 != 0 && pc >= CF::QK_PIECES) continue;  // whole waves
       const bool isq = pc < 4 * C;
       if (!WITH_Q && isq) continue;
@@ -418,19 +455,18 @@ struct Stager {
   // normalised this chunk's k pieces
   template <bool ROWS_STAGED>
   __device__ __forceinline__ void stage_kt(char* lds, int off_kt) {
-    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < CF::QKI; ++i) {
-      const int pc = tid + 512 * i;
-      if (CF::QK_PIECES % 512 != 0 && pc >= CF::QK_PIECES) continue;
+    for (int i = 0; i < NQK; ++i) {
+      const int pc = qk_piece(i);
+      if (pc < 0 || (CF::QK_PIECES % 512 != 0 && pc >= CF::QK_PIECES)) continue;
       if (pc < 4 * C) continue;  // q pieces
       const int row = (pc - 4 * C) >> 2, kq = pc & 3;
-      float x[CF::KQ];
+      float x[CF::KQ];  // sqrt(2) k_hat (see build_frag)
       if constexpr (ROWS_STAGED) {
 #pragma unroll
-        for (int e = 0; e < CF::KQ; ++e) x[e] = kx[i][e];
+        for (int e = 0; e < CF::KQ; ++e) x[e] = kx[i][e] * 1.41421356237309515f;
       } else {
-        normalise(qk[i], x);
+        normalise(qk[i], x, 1.41421356237309515f);
       }
       // component row r starts at r * KTP + 8 (r / KQ); token t sits in plane (t / 16) & 1
       // at (t / 32) * 16 + t % 16 of it
@@ -443,17 +479,18 @@ struct Stager {
 };
 
 // ---- state build over this wave's tiles for one chunk
-template <int P, int DV, int C, int W>
-__device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16], f32x4_t& Mt,
-                                            const float* khT, const uint16_t* vb_lds) {
+template <int P, int DV, int C, class MAP, int W>
+__device__ __forceinline__ void build_chunk(f32x4_t (&S)[(map_na<MAP, P>(W))][DV / 16], f32x4_t& Sx,
+                                            f32x4_t& Mt, const float* khT, const uint16_t* vb_lds) {
   using CF = Cfg<P, DV, C>;
-  constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W);
-  constexpr int MT = m_tile<P>(W), MRT = MT / NH, MCT = MT % NH;
+  constexpr int NT = CF::NT, NH = CF::NH, NTW = MAP::template nt<P>(W);
+  constexpr int MT = MAP::template mtile<P>(W), MRT = MT / NH, MCT = MT % NH;
+  constexpr int XDT = MAP::template xdt<P>(W, NT);
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const bool mlow = ln < 8;
 #pragma unroll
   for (int ks = 0; ks < CF::KSTEP; ++ks) {
-    float N[NH][8], N2[NH][8];
+    float N[NH][8];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       // k-slot (lg, j) is token 32ks + 16 (j / 4) + 4lg + j % 4: plane 0, then plane 1
@@ -465,8 +502,6 @@ __device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16]
         N[h][e] = x0[e];
         N[h][4 + e] = x1[e];
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) N2[h][e] = N[h][e] + N[h][e];
     }
     bf16x8_t vbf[NT];
 #pragma unroll
@@ -474,13 +509,14 @@ __device__ __forceinline__ void build_chunk(f32x4_t (&S)[wave_na<P>(W)][DV / 16]
       vbf[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(vb_lds + vt_row(16 * dt + ln) * CF::VTP + 32 * ks + 8 * lg));
     [&]<int... TI>(std::integer_sequence<int, TI...>) {
       (([&] {
-         const bf16x8_t af = build_frag<P, wave_tile<P>(W, TI)>(N, N2, mlow);
+         const bf16x8_t af = build_frag<P, MAP::template tile<P>(W, TI)>(N, mlow);
 #pragma unroll
          for (int dt = 0; dt < NT; ++dt) S[TI][dt] = mfma(af, vbf[dt], S[TI][dt]);
        }()),
        ...);
     }(std::make_integer_sequence<int, NTW>{});
-    if constexpr (MT >= 0) {  // Gram tile M[16 MRT.., 16 MCT..] += K^T K over these 32 tokens
+    if constexpr (XDT >= 0) Sx = mfma(build_frag<P, ntiles<P>() - 1>(N, mlow), vbf[XDT], Sx);
+    if constexpr (MT >= 0) {  // Gram tile of 2 M = sum 2 k k^T over these 32 tokens (halved when applied)
       Mt = mfma(pack8(N[MRT]), pack8(N[MCT]), Mt);
     }
   }
@@ -538,9 +574,10 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * MRT + 4 * lg + r, col = 16 * MCT + ln;
-        const uint16_t h = f32_to_bf16_bits(Mt[r]);
+        const float m = 0.5f * Mt[r];  // the tile holds 2 M (built from sqrt(2) k_hat)
+        const uint16_t h = f32_to_bf16_bits(m);
         mlds[row * CF::MP + col] = h;
-        mlds[P * CF::MP + row * CF::MP + col] = f32_to_bf16_bits(Mt[r] - bf16_bits_to_f32(h));
+        mlds[P * CF::MP + row * CF::MP + col] = f32_to_bf16_bits(m - bf16_bits_to_f32(h));
       }
     }
   };
@@ -615,8 +652,9 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
         dpart += X[0] * qv[0] + X[1] * qv[1] + X[2] * qv[2] + X[3] * qv[3];
       }
       // intra block: S^T = K_hat Q_hat^T over key tiles kt <= TT; W = (S^T)^2; O += W V.
-      // Global chunk 0 (denominators of few weights) uses split-bf16 scores.
-      const bool split = c == 0;
+      // Global chunk 0 (denominators of few weights) uses split-bf16 scores; the two
+      // variants are separate code so the common one carries no split work.
+      auto intra = [&]<bool SPLIT>() {
 #pragma unroll
       for (int kp = 0; kp <= TT / 2; ++kp) {
         float wv[8];
@@ -630,7 +668,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
             const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
             const f32x4_t x1 = P == 32 ? *reinterpret_cast<const f32x4_t*>(src + 16) : zero4();
             float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            if (split) {
+            if constexpr (SPLIT) {
               split8(xs, kbh, kbl);
               St = mfma(kbh, qbh, St);
               St = mfma(kbl, qbh, St);
@@ -655,6 +693,11 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
           O[dt] = mfma(vbf, wa, O[dt]);  // O^T += V^T W^T
         }
       }
+      };
+      if (c == 0)
+        intra.template operator()<true>();
+      else
+        intra.template operator()<false>();
       dpart += __shfl_xor(dpart, 16, 64);
       dpart += __shfl_xor(dpart, 32, 64);  // denominator of query qrow, in every lane group
     }
@@ -670,22 +713,28 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) Y[16 * h + 4 * u + e] = x[e];
         }
+      // state fragments of the next pair are read while this pair's features are built
+      bf16x8_t fr[2][NT];
+      auto load_pair = [&](int pair, bf16x8_t(&dst)[NT]) {
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+          dst[dt] = *reinterpret_cast<const bf16x8_t*>(sb + ((pair * NT + dt) * 64 + lane) * 16);
+      };
+      if constexpr (PE > PB) load_pair(PB, fr[0]);
       [&]<int... PI>(std::integer_sequence<int, PI...>) {
         (([&] {
            constexpr int t1 = 2 * (PB + PI), t2 = t1 + 1;
            constexpr bool has2 = t2 < CF::NTL;
+           if constexpr (PB + PI + 1 < PE) load_pair(PB + PI + 1, fr[(PI + 1) & 1]);
            const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
 #pragma unroll
-           for (int dt = 0; dt < NT; ++dt) {
-             const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(sb + (((PB + PI) * NT + dt) * 64 + lane) * 16);
-             O[dt] = mfma(bfr, af, O[dt]);  // O^T += S^T psi(Q)^T
-           }
+           for (int dt = 0; dt < NT; ++dt) O[dt] = mfma(fr[PI & 1][dt], af, O[dt]);  // O^T += S^T psi(Q)^T
          }()),
          ...);
       }(std::make_integer_sequence<int, PE - PB>{});
     }
     // ================= phase 1: build =================
-    build_chunk<P, DV, C, W>(S, Mt, khT, vt);
+    build_chunk<P, DV, C, Map8, W>(S, Mt, Mt, khT, vt);  // no odd-tile slice in the forward
     // O holds O^T: lane (ln, lg) has columns 16 dt + 4 lg + r of query 16 TT + ln
     if constexpr (CF::FS > 1) {
 #pragma unroll
@@ -727,11 +776,12 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   }
 }
 
-// ---- summary of one segment: [S | M] after its chunks, written to workspace slot seg
+// ---- pass 1: summary [S | M] of one segment after its chunks, to workspace slot seg
 template <int P, int DV, int C, int W>
-__device__ __forceinline__ void run_sum(const Args& a, char* lds) {
+__device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
   using CF = Cfg<P, DV, C>;
-  constexpr int NT = CF::NT, NTW = wave_nt<P>(W), MT = m_tile<P>(W);
+  constexpr int NT = CF::NT, NTW = Map16::nt<P>(W), MT = Map16::mtile<P>(W);
+  constexpr int XDT = Map16::xdt<P>(W, NT);
   constexpr int OKT = 0, OVB = P * CF::KTP * 4;
   const int lane = threadIdx.x & 63;
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
@@ -740,8 +790,8 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
 
-  f32x4_t S[wave_na<P>(W)][NT];
-  f32x4_t Mt = zero4();
+  f32x4_t S[(map_na<Map16, P>(W))][NT];
+  f32x4_t Sx = zero4(), Mt = zero4();
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
@@ -754,11 +804,11 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   stg.write_vt(lds + OVB);
   if (c0 + 1 < c1) stg.load((c0 + 1) * C);
   __syncthreads();
-  for (int c = c0; c < c1; ++c) {
+  for (int c = c0; c < c1; ++c) {  // k_hat^T / V^T double-buffered: one barrier per chunk
     const int buf = (c - c0) & 1;
     char* base = lds + buf * CF::SUM_BUF;
-    build_chunk<P, DV, C, W>(S, Mt, reinterpret_cast<const float*>(base + OKT),
-                             reinterpret_cast<const uint16_t*>(base + OVB));
+    build_chunk<P, DV, C, Map16, W>(S, Sx, Mt, reinterpret_cast<const float*>(base + OKT),
+                                    reinterpret_cast<const uint16_t*>(base + OVB));
     if (c + 1 < c1) {
       stg.template stage_kt<false>(lds + (buf ^ 1) * CF::SUM_BUF, OKT);
       stg.write_vt(lds + (buf ^ 1) * CF::SUM_BUF + OVB);
@@ -771,29 +821,50 @@ __device__ __forceinline__ void run_sum(const Args& a, char* lds) {
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt)
-      *reinterpret_cast<f32x4_t*>(dst + ((wave_tile<P>(W, i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
+      *reinterpret_cast<f32x4_t*>(dst + ((Map16::tile<P>(W, i) * NT + dt) * 64 + lane) * 4) = S[i][dt];
+  if constexpr (XDT >= 0)
+    *reinterpret_cast<f32x4_t*>(dst + (((ntiles<P>() - 1) * NT + XDT) * 64 + lane) * 4) = Sx;
   if constexpr (MT >= 0)
     *reinterpret_cast<f32x4_t*>(dst + (int64_t)CF::NTL * NT * 256 + (MT * 64 + lane) * 4) = Mt;
 }
 
-template <int P, int DV, int C, bool FWD, int W>
-__device__ __forceinline__ void run_wave(const Args& a, char* lds) {
-  if constexpr (FWD) run_fwd<P, DV, C, W>(a, lds);
-  else run_sum<P, DV, C, W>(a, lds);
-}
-
-template <int P, int DV, int C, bool FWD>
+// forward of the segments (8 waves)
+template <int P, int DV, int C>
 __global__ __launch_bounds__(512, 1) void chunked_bf16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
-    case 0: run_wave<P, DV, C, FWD, 0>(a, lds); break;
-    case 1: run_wave<P, DV, C, FWD, 1>(a, lds); break;
-    case 2: run_wave<P, DV, C, FWD, 2>(a, lds); break;
-    case 3: run_wave<P, DV, C, FWD, 3>(a, lds); break;
-    case 4: run_wave<P, DV, C, FWD, 4>(a, lds); break;
-    case 5: run_wave<P, DV, C, FWD, 5>(a, lds); break;
-    case 6: run_wave<P, DV, C, FWD, 6>(a, lds); break;
-    default: run_wave<P, DV, C, FWD, 7>(a, lds); break;
+    case 0: run_fwd<P, DV, C, 0>(a, lds); break;
+    case 1: run_fwd<P, DV, C, 1>(a, lds); break;
+    case 2: run_fwd<P, DV, C, 2>(a, lds); break;
+    case 3: run_fwd<P, DV, C, 3>(a, lds); break;
+    case 4: run_fwd<P, DV, C, 4>(a, lds); break;
+    case 5: run_fwd<P, DV, C, 5>(a, lds); break;
+    case 6: run_fwd<P, DV, C, 6>(a, lds); break;
+    default: run_fwd<P, DV, C, 7>(a, lds); break;
+  }
+}
+
+// segment summaries (16 waves)
+template <int P, int DV, int C>
+__global__ __launch_bounds__(1024, 1) void summary_bf16_kernel(Args a) {
+  extern __shared__ __align__(16) char lds[];
+  switch (threadIdx.x >> 6) {
+    case 0: run_sum16<P, DV, C, 0>(a, lds); break;
+    case 1: run_sum16<P, DV, C, 1>(a, lds); break;
+    case 2: run_sum16<P, DV, C, 2>(a, lds); break;
+    case 3: run_sum16<P, DV, C, 3>(a, lds); break;
+    case 4: run_sum16<P, DV, C, 4>(a, lds); break;
+    case 5: run_sum16<P, DV, C, 5>(a, lds); break;
+    case 6: run_sum16<P, DV, C, 6>(a, lds); break;
+    case 7: run_sum16<P, DV, C, 7>(a, lds); break;
+    case 8: run_sum16<P, DV, C, 8>(a, lds); break;
+    case 9: run_sum16<P, DV, C, 9>(a, lds); break;
+    case 10: run_sum16<P, DV, C, 10>(a, lds); break;
+    case 11: run_sum16<P, DV, C, 11>(a, lds); break;
+    case 12: run_sum16<P, DV, C, 12>(a, lds); break;
+    case 13: run_sum16<P, DV, C, 13>(a, lds); break;
+    case 14: run_sum16<P, DV, C, 14>(a, lds); break;
+    default: run_sum16<P, DV, C, 15>(a, lds); break;
   }
 }
 
@@ -805,16 +876,16 @@ hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, v
   Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
-    auto ks = chunked_bf16_kernel<P, DV, C, false>;
+    auto ks = summary_bf16_kernel<P, DV, C>;
     if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS)) != hipSuccess) return e;
     a.nblk_per_bh = plan.nseg - 1;
-    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(512), CF::SUM_LDS, st>>>(a);
+    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(1024), CF::SUM_LDS, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN))
     if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;
   if (!(passes & PASS_SEGMENTS)) return hipSuccess;
-  auto kf = chunked_bf16_kernel<P, DV, C, true>;
+  auto kf = chunked_bf16_kernel<P, DV, C>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), CF::LDS, st>>>(a);
