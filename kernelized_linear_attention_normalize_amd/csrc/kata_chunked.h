@@ -92,14 +92,6 @@ __device__ __forceinline__ bf16x8_t zero_bf8() {
   return __builtin_bit_cast(bf16x8_t, u16x8_t{0, 0, 0, 0, 0, 0, 0, 0});
 }
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 __device__ __forceinline__ bf16x8_t pack8(const float (&x)[8]) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])});
 }
@@ -223,9 +215,6 @@ __device__ __forceinline__ bf16x8_t build_frag(const float (&N)[P / 16][8], bool
   return pack8(x);
 }
 
-// physical LDS row of V^T column d: the low 2 bits are XOR-swizzled by (d / 8) & 3 so the
-// transposed writes of 4 column groups land in distinct banks
-__device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 3); }
 
 template <int P, int DV, int C>
 struct Cfg {
@@ -271,16 +260,7 @@ struct Cfg {
   static constexpr int QKI = (QK_PIECES + 511) / 512;
   static constexpr int VPIECES = (C / 2) * (DV / 8);
   static constexpr int VI = (VPIECES + 511) / 512;
-  // V piece pc -> (key pair vp, column group vd): each 32-lane half loads 8 key pairs x 4
-  // column groups (64 contiguous bytes per row) whose transposed LDS writes hit 32
-  // distinct banks (key-pair positions distinct mod 8, rows swizzled by vd & 3)
-  __device__ static __forceinline__ void vpiece(int pc, int& vp, int& vd) {
-    constexpr int NVD = DV / 8, VL = NVD < 4 ? NVD : 4, VH = NVD / VL;
-    const int qd = pc / (8 * VL), r = pc % (8 * VL);
-    const int vl = r / VL, sg = qd / VH;
-    vd = r % VL + VL * (qd % VH);
-    vp = 16 * (sg >> 1) + 4 * (sg & 1) + (vl & 3) + 8 * (vl >> 2);
-  }
+  __device__ static __forceinline__ void vpiece(int pc, int& vp, int& vd) { vt_piece<DV>(pc, vp, vd); }
   // readout pair ranges of token tile tt: split fs covers pairs [pr(fs, tt), pr(fs + 1, tt)).
   // The last split also runs the intra block and the denominator (more work for larger tt),
   // so it takes fewer pairs; the others share the rest evenly.
@@ -311,14 +291,7 @@ struct Args {
   int o_f32;  // output dtype: 1 = fp32, 0 = bf16
 };
 
-// fast reciprocal square root / reciprocal (about 1 ulp; results feed bf16 MFMA operands)
-__device__ __forceinline__ float inv_norm_fast(float ss) { return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f; }
 
-// raw buffer resource over [base, base + bytes): loads past the end return 0 and stores
-// past the end are dropped by the hardware range check, so ragged tails need no branches
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
 
 // ---- chunk staging: global bf16 -> registers (load) -> normalised LDS layouts
 template <int P, int DV, int C, bool WITH_Q>
@@ -417,8 +390,7 @@ struct Stager {
       if (pc >= 0 && pc < CF::VPIECES) {
         int vp, vd;
         CF::vpiece(pc, vp, vd);
-        const int k = 2 * vp;
-        const int pos = (k & ~31) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3);
+        const int pos = vt_pos(2 * vp);
         // column 8 vd + e lives in row 8 vd + (e ^ (vd & 3)) (see vt_row)
         char* base = vt_bytes + ((8 * vd) * CF::VTP + pos) * 2;
         char* rb[4];

@@ -7,6 +7,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 namespace kata {
 
@@ -34,6 +38,41 @@ __device__ __forceinline__ void store_from_f32(void* base, int64_t i, float x) {
 
 // 1/||u|| for a row with squared norm ss; 0 for a zero row (the lift of 0 is 0).
 __device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? 1.0f / sqrtf(ss) : 0.f; }
+// fast reciprocal square root (about 1 ulp; results feed bf16 MFMA operands)
+__device__ __forceinline__ float inv_norm_fast(float ss) { return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f; }
+
+// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// raw buffer resource over [base, base + bytes): loads past the end return 0 and stores
+// past the end are dropped by the hardware range check, so ragged tails need no branches
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// ---- V^T staging shared by the MFMA kernels. Keys come in pairs (2 rows of V, 8 columns
+// per piece); V^T is bf16 [DV][pitch] in LDS.
+// Key position: key 32a + 16s + 4g + j is stored at 32a + 8g + 4s + j, so MFMA lane group g
+// reads its 8 k-slots (keys 32a + 4g + j and 32a + 16 + 4g + j: the row order of 16x16
+// score accumulators) with one 16-byte read.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~31) + 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3); }
+// Physical LDS row of V^T column d: the low 2 bits are XOR-swizzled by (d / 8) & 3 so the
+// transposed writes of 4 column groups land in distinct banks.
+__device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 3); }
+// Piece pc -> (key pair vp, column group vd): each 32-lane half loads 8 key pairs x 4
+// column groups (64 contiguous bytes per row) whose transposed 4-byte LDS writes hit 32
+// distinct banks (key-pair positions distinct mod 8, rows swizzled by vd & 3) when the
+// pitch in floats is 8 modulo 32. Needs a multiple of 16 key pairs.
+template <int DV>
+__device__ __forceinline__ void vt_piece(int pc, int& vp, int& vd) {
+  constexpr int NVD = DV / 8, VL = NVD < 4 ? NVD : 4, VH = NVD / VL;
+  const int qd = pc / (8 * VL), r = pc % (8 * VL);
+  const int vl = r / VL, sg = qd / VH;
+  vd = r % VL + VL * (qd % VH);
+  vp = 16 * (sg >> 1) + 4 * (sg & 1) + (vl & 3) + 8 * (vl >> 2);
+}
 
 // Packed coordinate f of the row-major upper triangle (incl. diagonal) -> (i, j).
 // start(i) = i*p - i*(i-1)/2 is the packed index of (i, i).

@@ -6,27 +6,29 @@
 // Eq. (8)); the normalized readout with explicit denominator (normalized-readout
 // paragraph); inclusive causality of the state S_t (feature-value state display).
 //
-// Per workgroup: 128 queries of one (b,h), 4 waves x 32 queries. Key blocks of 64 are
-// normalised once per workgroup into LDS (bf16 K_hat, K_hat transposed-free; V stored
-// transposed so the W.V operand is two 8-byte reads), double-buffered with the next
-// block's global loads issued before the current block's MFMAs.
-//   S^T = K_hat Q_hat^T   (16x16x32 bf16 MFMA, keys as M so the accumulator is already
-//                          the A operand layout of the next product)
-//   W   = (S^T)^2, causal mask on the diagonal blocks, rounded to bf16
-//   [O | den] += W [V | 1] (the ones column gives the denominator from the same weights)
-// Weights lie in [0, 1] and the denominator is a plain sum, so unlike softmax there is no
-// running maximum and no rescaling. For the first 128 queries, where a denominator is a
-// sum of only a few weights, the scores use a split-bf16 product (hi*hi + lo*hi + hi*lo).
+// Per workgroup: 256 queries of one (b,h), 4 waves x 64 queries; key blocks of 64,
+// double-buffered in LDS with one barrier per block (the next block's global loads are in
+// flight during the current block's MFMAs).
+//   * Scores from the raw bf16 inputs: a bf16 x bf16 product is exact in fp32, so the MFMA
+//     dot product q . k is exact up to fp32 accumulation; s = (q . k) / ||k|| is formed in
+//     fp32 with a per-key reciprocal norm staged next to the raw K rows. The query's 1/||q||^2
+//     scales the numerator and the denominator of every output row alike, so it is left
+//     out. Hence no normalised or split copies of q or k are needed.
+//   * S^T = K Q^T (16x16x32 bf16 MFMA, keys as M: the accumulator rows are the k-slots of
+//     the next product), W = (S^T / ||k||)^2 masked on the diagonal blocks, rounded to bf16.
+//   * O^T += V^T W^T and den += 1^T W^T (operands swapped, so a lane ends with 4 consecutive
+//     output columns of one query, stored with one 8-byte write, and its own denominator).
+// Weights lie in [0, ||q||^2] and the denominator is a plain sum, so unlike softmax there is
+// no running maximum and no rescaling.
 #include "kata_device.h"
 #include "kata_launch.h"
 
 namespace kata {
 
 namespace quad {
-constexpr int BM = 128, BN = 64, QW = 32, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
+constexpr int BM = 256, BN = 64, QW = 64, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
+constexpr int VTP = 80;  // bf16 pitch of V^T rows (160 bytes: conflict-free 16-byte reads)
 }
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -39,116 +41,84 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
                                                                 void* __restrict__ o, int T,
                                                                 int nqb) {
   using namespace quad;
-  constexpr int KS = (P + 31) / 32;    // 32-wide k-steps over the components
-  constexpr int KPITCH = P + 8;        // bf16 row pitch of K_hat in LDS
-  constexpr int VPITCH = BN + 8;       // bf16 row pitch of V^T in LDS
-  constexpr int NT = DV / 16;          // 16-wide output column tiles
-  constexpr int KQ = P / 4;            // components per staging thread (4 threads per key row)
-  constexpr int KBUF = BN * KPITCH, VBUF = DV * VPITCH;
-  __shared__ __align__(16) uint16_t sKh[2][KBUF];
-  __shared__ __align__(16) uint16_t sKl[2][KBUF];
-  __shared__ __align__(16) uint16_t sVt[2][VBUF];
+  constexpr int KS = (P + 31) / 32;                        // 32-wide k-steps over components
+  constexpr int KP = P == 64 ? 80 : (P == 32 ? 48 : 16);   // bf16 pitch of K rows (8 * odd floats)
+  constexpr int NT = DV / 16;                              // 16-wide output column tiles
+  constexpr int KPC = P / 8;                               // 16-byte pieces per key row
+  constexpr int KPIECES = BN * KPC;
+  constexpr int KI = (KPIECES + 255) / 256;
+  constexpr int VPIECES = (BN / 2) * (DV / 8);
+  static_assert(VPIECES <= 256 && KPIECES % 64 == 0, "staging layout");
+  __shared__ __align__(16) uint16_t sK[2][BN * KP];
+  __shared__ __align__(16) float sInvK[2][BN];
+  __shared__ __align__(16) uint16_t sVt[2][DV * VTP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int64_t bh = blockIdx.x / nqb;
   const int qb0 = (nqb - 1 - (int)(blockIdx.x % nqb)) * BM;  // longest rows first
   const int qw0 = qb0 + wave * QW;
-  const bool split = qb0 == 0;
-  const uint16_t* qbase = q + bh * (int64_t)T * P;
-  const uint16_t* kbase = k + bh * (int64_t)T * P;
-  const uint16_t* vbase = v + bh * (int64_t)T * DV;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + bh * (int64_t)T * P, (uint32_t)T * P * 2);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + bh * (int64_t)T * P, (uint32_t)T * P * 2);
+  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
 
-  // ---- this lane's query fragments (B operand of S^T): query 16*qt + ln, comps 32*ks + 8*lg..+7
-  bf16x8_t qh[NQT][KS], ql[NQT][KS];
+  // ---- raw query fragments (B operand of S^T): query qw0 + 16 qt + ln, comps 32 ks + 8 lg..
+  bf16x8_t qf[NQT][KS];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const int t = qw0 + 16 * qt + ln;
-    float x[KS][8];
-    float ss = 0.f;
+  for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int c0 = 32 * ks + 8 * lg;
-      u16x8_t raw = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (t < T && c0 < P) raw = *reinterpret_cast<const u16x8_t*>(qbase + (int64_t)t * P + c0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[ks][j] = bf16_bits_to_f32(raw[j]);
-        ss += x[ks][j] * x[ks][j];
-      }
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (P >= 32 || lg < 2)  // rows past T read as zero
+        raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)((qw0 + 16 * qt + ln) * P + 32 * ks + 8 * lg) * 2, 0, 0);
+      qf[qt][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = inv_norm(ss);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u16x8_t h, l;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float y = x[ks][j] * inv;
-        h[j] = f32_to_bf16_bits(y);
-        l[j] = f32_to_bf16_bits(y - bf16_bits_to_f32(h[j]));
-      }
-      qh[qt][ks] = as_bf16x8(h);
-      ql[qt][ks] = as_bf16x8(l);
-    }
-  }
 
-  // ---- key-block staging: 4 threads per key row normalise and write bf16 hi/lo;
-  //      V is written transposed, one (key pair, 8 columns) piece per thread.
-  const int krow = tid >> 2, kq = tid & 3;
-  constexpr int VPIECES = (BN / 2) * (DV / 8);
-  const int vpair = tid / (DV / 8), vdg = tid % (DV / 8);
-  uint16_t kreg[KQ];
-  u16x8_t vreg0, vreg1;
+  // ---- key-block staging: raw K rows (16-byte pieces) + 1/||k|| per key; V^T with the
+  //      shared permuted / swizzled layout, one (key pair, 8 columns) piece per thread
+  u32x4_t kreg[KI];
+  u32x4_t vreg[2];
+  int vp = 0, vd = 0;
+  if (tid < VPIECES) vt_piece<DV>(tid, vp, vd);
   auto prefetch = [&](int kb0) {
-    const int key = kb0 + krow;
 #pragma unroll
-    for (int i = 0; i < KQ; ++i) kreg[i] = 0;
-    if (key < T) {
-      const uint16_t* src = kbase + (int64_t)key * P + kq * KQ;
-      if constexpr (KQ == 16) {
-        *reinterpret_cast<u16x8_t*>(&kreg[0]) = *reinterpret_cast<const u16x8_t*>(src);
-        *reinterpret_cast<u16x8_t*>(&kreg[8]) = *reinterpret_cast<const u16x8_t*>(src + 8);
-      } else if constexpr (KQ == 8) {
-        *reinterpret_cast<u16x8_t*>(&kreg[0]) = *reinterpret_cast<const u16x8_t*>(src);
-      } else {
-        *reinterpret_cast<u16x4_t*>(&kreg[0]) = *reinterpret_cast<const u16x4_t*>(src);
-      }
+    for (int i = 0; i < KI; ++i) {
+      const int pc = tid + 256 * i;
+      if (pc < KPIECES)
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((kb0 + pc / KPC) * P + 8 * (pc % KPC)) * 2, 0, 0);
     }
-    vreg0 = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    vreg1 = vreg0;
     if (tid < VPIECES) {
-      const int key0 = kb0 + 2 * vpair;
-      if (key0 < T) vreg0 = *reinterpret_cast<const u16x8_t*>(vbase + (int64_t)key0 * DV + 8 * vdg);
-      if (key0 + 1 < T) vreg1 = *reinterpret_cast<const u16x8_t*>(vbase + (int64_t)(key0 + 1) * DV + 8 * vdg);
+      const uint32_t off = (uint32_t)((kb0 + 2 * vp) * DV + 8 * vd) * 2;
+      vreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      vreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + DV * 2, 0, 0);
     }
   };
   auto stage = [&](int buf) {
-    float x[KQ];
-    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < KQ; ++i) {
-      x[i] = bf16_bits_to_f32(kreg[i]);
-      ss += x[i] * x[i];
-    }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    const float inv = inv_norm(ss);
-    uint16_t* dh = &sKh[buf][krow * KPITCH + kq * KQ];
-    uint16_t* dl = &sKl[buf][krow * KPITCH + kq * KQ];
+    for (int i = 0; i < KI; ++i) {
+      const int pc = tid + 256 * i;
+      if (pc < KPIECES) {  // whole waves
+        const int row = pc / KPC, col = pc % KPC;
+        *reinterpret_cast<u32x4_t*>(&sK[buf][row * KP + 8 * col]) = kreg[i];
+        float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < KQ; ++i) {
-      const float y = x[i] * inv;
-      const uint16_t h = f32_to_bf16_bits(y);
-      dh[i] = h;
-      dl[i] = f32_to_bf16_bits(y - bf16_bits_to_f32(h));
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_bits_to_f32(kreg[i][e] & 0xffffu), hi = __uint_as_float(kreg[i][e] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+#pragma unroll
+        for (int m = 1; m < KPC; m <<= 1) ss += __shfl_xor(ss, m, 64);  // the row's pieces are adjacent lanes
+        if (col == 0) sInvK[buf][row] = inv_norm_fast(ss);
+      }
     }
     if (tid < VPIECES) {
-      uint32_t* vt = reinterpret_cast<uint32_t*>(&sVt[buf][0]);
+      char* base = reinterpret_cast<char*>(&sVt[buf][0]) + ((8 * vd) * VTP + vt_pos(2 * vp)) * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vt[((8 * vdg + i) * VPITCH + 2 * vpair) >> 1] = (uint32_t)vreg0[i] | ((uint32_t)vreg1[i] << 16);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = (vreg[0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t b = (vreg[1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(base + ((e & 4) + ((e & 3) ^ (vd & 3))) * VTP * 2) = a | (b << 16);
+      }
     }
   };
 
@@ -159,10 +129,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  u16x8_t ones_u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ones_u[j] = 0x3F80;  // bf16 1.0
-  const bf16x8_t ones = as_bf16x8(ones_u);
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   const int kend = min(T, qb0 + BM);
   const int nkb = (kend + BN - 1) / BN;
@@ -175,82 +142,67 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
     if (kb + 1 < nkb) prefetch(kb0 + BN);
     if (kb0 <= qw0 + QW - 1 && qw0 < T) {
       const bool diag = kb0 + BN - 1 > qw0;  // some (key > query) pairs in this block
-      // S^T tiles: keys 16*kt + row, queries 16*qt + col
-      f32x4_t St[NKT][NQT];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) St[kt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u16x8_t ah = {0, 0, 0, 0, 0, 0, 0, 0}, al = ah;
-          if (P >= 32 || lg < 2) {
-            ah = *reinterpret_cast<const u16x8_t*>(&sKh[buf][(16 * kt + ln) * KPITCH + 32 * ks + 8 * lg]);
-            if (split) al = *reinterpret_cast<const u16x8_t*>(&sKl[buf][(16 * kt + ln) * KPITCH + 32 * ks + 8 * lg]);
-          }
-#pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) {
-            St[kt][qt] = mfma16(as_bf16x8(ah), qh[qt][ks], St[kt][qt]);
-            if (split) {
-              St[kt][qt] = mfma16(as_bf16x8(al), qh[qt][ks], St[kt][qt]);
-              St[kt][qt] = mfma16(as_bf16x8(ah), ql[qt][ks], St[kt][qt]);
-            }
-          }
-        }
-      }
-      // W = S^2 (masked on the diagonal), packed as the A operand of W.[V|1]
 #pragma unroll
       for (int kp = 0; kp < NKP; ++kp) {
-        // V^T operand for this key pair: keys 32kp + 4lg + j and 32kp + 16 + 4lg + j
+        // S^T tiles of key pair kp: keys 32 kp + 16 h + 4 lg + r (rows), queries 16 qt + ln
+        f32x4_t St[2][NQT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kt = 2 * kp + h;
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) St[h][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t a = {0u, 0u, 0u, 0u};
+            if (P >= 32 || lg < 2) a = *reinterpret_cast<const u32x4_t*>(&sK[buf][(16 * kt + ln) * KP + 32 * ks + 8 * lg]);
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) St[h][qt] = mfma16(__builtin_bit_cast(bf16x8_t, a), qf[qt][ks], St[h][qt]);
+          }
+        }
+        const f32x4_t ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
+        const f32x4_t ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
+        // V^T operand: keys 32kp + 4lg + j and 32kp + 16 + 4lg + j, one 16-byte read
         bf16x8_t vb[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const uint16_t* row = &sVt[buf][(16 * nt + ln) * VPITCH + 32 * kp + 4 * lg];
-          const u16x4_t a = *reinterpret_cast<const u16x4_t*>(row);
-          const u16x4_t b = *reinterpret_cast<const u16x4_t*>(row + 16);
-          vb[nt] = as_bf16x8(u16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
-        }
+        for (int nt = 0; nt < NT; ++nt)
+          vb[nt] = *reinterpret_cast<const bf16x8_t*>(&sVt[buf][vt_row(16 * nt + ln) * VTP + 32 * kp + 8 * lg]);
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
           const int query = qw0 + 16 * qt + ln;
-          u16x8_t w;
+          float w[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int kt = 2 * kp + (j >> 2), r = j & 3;
-            const float s = St[kt][qt][r];
-            float ww = s * s;
-            if (diag) {
-              const int key = kb0 + 16 * kt + 4 * lg + r;
-              ww = key <= query ? ww : 0.f;
-            }
-            w[j] = f32_to_bf16_bits(ww);
+            const int h = j >> 2, r = j & 3;
+            const float s = St[h][qt][r] * (h ? ik1[r] : ik0[r]);
+            w[j] = s * s;
+            if (diag && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[j] = 0.f;
           }
-          const bf16x8_t wa = as_bf16x8(w);
+          const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])});
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) O[qt][nt] = mfma16(wa, vb[nt], O[qt][nt]);
-          D[qt] = mfma16(wa, ones, D[qt]);
+          for (int nt = 0; nt < NT; ++nt) O[qt][nt] = mfma16(vb[nt], wa, O[qt][nt]);  // O^T += V^T W^T
+          D[qt] = mfma16(ones, wa, D[qt]);
         }
       }
     }
-    if (kb + 1 < nkb) {
-      __syncthreads();  // every wave is done with buffer buf^1 (used two blocks ago)
-      stage(buf ^ 1);
-      __syncthreads();
-    }
+    if (kb + 1 < nkb) stage(buf ^ 1);  // buffer of block kb - 1: every wave is past it
+    __syncthreads();
   }
 
-  // ---- epilogue: o[query, d] = O / den; lane holds queries 16qt + 4lg + r, column 16nt + ln
+  // ---- epilogue: lane holds columns 16 nt + 4 lg + r of query qw0 + 16 qt + ln
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
+    const int query = qw0 + 16 * qt + ln;
+    if (query >= T) continue;
+    const float den = D[qt][0];
+    const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int query = qw0 + 16 * qt + 4 * lg + r;
-      if (query >= T) continue;
-      const float den = D[qt][r];
-      const float inv = den > 0.f ? 1.0f / den : 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        store_from_f32<OUT_BF16>(o, (bh * T + query) * (int64_t)DV + 16 * nt + ln, O[qt][nt][r] * inv);
+    for (int nt = 0; nt < NT; ++nt) {
+      const f32x4_t x = O[qt][nt] * inv;
+      const int64_t idx = (bh * T + query) * (int64_t)DV + 16 * nt + 4 * lg;
+      if constexpr (OUT_BF16)
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + idx) = u32x2_t{pk2(x[0], x[1]), pk2(x[2], x[3])};
+      else
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + idx) = x;
     }
   }
 }
