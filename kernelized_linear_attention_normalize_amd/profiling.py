@@ -2,6 +2,9 @@
 
     python -m kernelized_linear_attention_normalize_amd.profiling kernels \\
         --stats <dir>/<prefix>_kernel_stats.csv --cmd "<the profiled command>" --out profiles/<name>.txt
+    python -m kernelized_linear_attention_normalize_amd.profiling mfma \\
+        --pmc <csv with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, GRBM_GUI_ACTIVE> --kernel <substring> \\
+        --cmd "<command>" --out profiles/<name>_mfma.txt
     python -m kernelized_linear_attention_normalize_amd.profiling traffic \\
         --kernel <substring> --fetch <csv> --write <csv> --copy-fetch <csv> --copy-write <csv> \\
         --copy-bytes <bytes> --cmd "<commands>" --out profiles/<name>_traffic.txt
@@ -101,6 +104,30 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+# MI355X: 256 CUs x 4 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE is reported summed over the XCDs
+SIMDS, XCDS = 1024, 8
+
+
+def cmd_mfma(a):
+    busy, n = counter_per_dispatch(a.pmc, "SQ_VALU_MFMA_BUSY_CYCLES", a.kernel)
+    insts, _ = counter_per_dispatch(a.pmc, "SQ_INSTS_MFMA", a.kernel)
+    gui, _ = counter_per_dispatch(a.pmc, "GRBM_GUI_ACTIVE", a.kernel)
+    cycles = gui / XCDS
+    frac = busy / (cycles * SIMDS)
+    lines = [f"# MFMA pipe occupancy of '{a.kernel}' from rocprofv3 PMC counters",
+             f"# command: {a.cmd}",
+             f"# busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs);",
+             f"# it counts every executed MFMA (padding and recompute included), unlike the",
+             f"# algorithmic fraction bench.py reports.",
+             f"mfma_insts_per_dispatch: {insts:.0f}   (mean over {n} dispatches)",
+             f"mfma_busy_cycles_per_dispatch: {busy:.0f}",
+             f"gpu_active_cycles_per_xcd: {cycles:.0f}",
+             f"mfma_busy_fraction: {frac:.4f}",
+             f"source_hash: {source_hash()}"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -111,6 +138,11 @@ def main():
     k.add_argument("--top", type=int, default=8)
     k.add_argument("--bench-log", default="")
     k.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--fetch", required=True)
@@ -122,7 +154,7 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     a = ap.parse_args()
-    cmd_kernels(a) if a.what == "kernels" else cmd_traffic(a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
 
 
 if __name__ == "__main__":
