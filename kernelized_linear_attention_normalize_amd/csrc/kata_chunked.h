@@ -27,17 +27,20 @@
 //   * Readout: wave w serves token tile w mod (C/16) over a range of the feature pairs;
 //     the splits of a token tile exchange partial sums through LDS. Operands are swapped
 //     (O^T = S^T psi(Q)^T): each lane ends with 4 consecutive output columns of one query.
-//     psi(q) comes from a per-lane-group rotated copy of q_hat (raw products q_i q_j).
+//     psi(q) comes from a per-lane-group rotated copy of q (raw products q_i q_j).
+//   * Queries are used as given, not normalised: psi(q) = ||q||^2 psi(q_hat) scales the
+//     numerator and the denominator of o_t alike. The raw bf16 q is exact as an MFMA
+//     operand, so the denominator and the intra scores need no split query.
 //   * Off-diagonal coordinates carry sqrt(2) in psi; their product c_ij^2 = 2 is folded
 //     into the state build: k_hat^T is staged as sqrt(2) k_hat, so an off-diagonal product
 //     is 2 k_i k_j, a diagonal one is halved, and the Gram tile (2 M) is halved when
 //     applied. The readout uses raw products q_i q_j.
-//   * The denominator psi(q)^T Z = q_hat^T M q_hat with the Gram matrix
-//     M = sum_s k_hat_s k_hat_s^T (p x p): M is updated and applied with split-bf16
-//     MFMAs (hi*hi + hi*lo + lo*hi), so the normaliser is fp32-accurate.
-//   * Intra-chunk block: S^T = K_hat Q_hat^T (keys as M), W = (S^T)^2 masked, rounded to
+//   * The denominator psi(q)^T Z = q^T M q with the Gram matrix M = sum_s k_hat_s k_hat_s^T
+//     (p x p), applied as bf16 hi + lo of M against the exact q (2 MFMAs per tile), so the
+//     normaliser is fp32-accurate.
+//   * Intra-chunk block: S^T = K_hat Q^T (keys as M), W = (S^T)^2 masked, rounded to
 //     bf16, O^T += V^T W^T. Global chunk 0, where denominators are sums of few weights,
-//     uses split-bf16 scores.
+//     uses split-bf16 keys.
 //   * Per chunk: phase 1 = readout from the state before the chunk + the chunk's build
 //     into the registers (both read only the state before it) | barrier | phase 2 =
 //     output, staging of the next chunk, state back to LDS | barrier.
@@ -414,8 +417,13 @@ struct Stager {
       const bool isq = pc < 4 * C;
       if (!WITH_Q && isq) continue;
       const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
-      float(&x)[CF::KQ] = kx[i];  // kept for stage_kt of the same chunk
-      normalise(qk[i], x);
+      float(&x)[CF::KQ] = kx[i];  // k: kept for stage_kt of the same chunk
+      if (isq) {  // queries are used unnormalised: the scale of q cancels in the output
+#pragma unroll
+        for (int e = 0; e < CF::KQ; ++e) x[e] = bf16_bits_to_f32(qk[i][e]);
+      } else {
+        normalise(qk[i], x);
+      }
       float* dst = reinterpret_cast<float*>(lds + (isq ? CF::OFF_QH : CF::OFF_KH)) + row * CF::QP + kq * CF::KQ;
 #pragma unroll
       for (int e = 0; e < CF::KQ; e += 4)
@@ -596,17 +604,18 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
     for (int dt = 0; dt < NT; ++dt) O[dt] = zero4();
     float dpart = 0.f;
     if constexpr (OWNER) {
-      // query operand (B of S^T and of X^T): q_hat[qrow][8lg..8lg+7] as bf16 hi / lo
-      // component k-slots of lane group lg: 4lg..4lg+3 and 16+4lg..16+4lg+3 (16-byte steps)
-      bf16x8_t qbh, qbl;
+      // query operand (B of S^T and of X^T): the raw query row is exact in bf16.
+      // Component k-slots of lane group lg: 4lg..4lg+3 and 16+4lg..16+4lg+3 (16-byte steps)
+      bf16x8_t qbh;
       {
         const float* src = qh + qrow * CF::QP + 4 * lg;
         const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
         const f32x4_t x1 = P == 32 ? *reinterpret_cast<const f32x4_t*>(src + 16) : zero4();
         const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        split8(xs, qbh, qbl);
+        qbh = pack8(xs);
       }
-      // denominator, inter-chunk part: X^T = M Q_hat^T (rows: components), then q_hat . X
+      // denominator, inter-chunk part: X^T = M Q^T (rows: components; M as bf16 hi + lo),
+      // then q . X
 #pragma unroll
       for (int rt = 0; rt < NH; ++rt) {
         const uint16_t* mrow = mlds + (16 * rt + ln) * CF::MP + 4 * lg;
@@ -619,11 +628,10 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
         f32x4_t X = zero4();
         X = mfma(mh, qbh, X);
         X = mfma(ml, qbh, X);
-        X = mfma(mh, qbl, X);
         const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + qrow * CF::QP + 16 * rt + 4 * lg);
         dpart += X[0] * qv[0] + X[1] * qv[1] + X[2] * qv[2] + X[3] * qv[3];
       }
-      // intra block: S^T = K_hat Q_hat^T over key tiles kt <= TT; W = (S^T)^2; O += W V.
+      // intra block: S^T = K_hat Q^T over key tiles kt <= TT; W = (S^T)^2; O += W V.
       // Global chunk 0 (denominators of few weights) uses split-bf16 scores; the two
       // variants are separate code so the common one carries no split work.
       auto intra = [&]<bool SPLIT>() {
@@ -644,7 +652,6 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
               split8(xs, kbh, kbl);
               St = mfma(kbh, qbh, St);
               St = mfma(kbl, qbh, St);
-              St = mfma(kbh, qbl, St);
             } else {
               St = mfma(pack8(xs), qbh, St);
             }

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import kernelized_linear_attention_normalize_amd as kata
-from kata_inputs import WORKLOADS, draw_qkv, round_bf16
+from kata_inputs import DECODE, WORKLOADS, draw_decode_history, draw_decode_steps, draw_qkv, round_bf16
 from oracle import kata_oracle as ko
 from tests.gpu_util import TOL, row_rel_err, to_dev, to_np
 
@@ -254,3 +254,40 @@ def test_decode_small_from_prefill():
     assert row_rel_err(got, ref) <= TOL["bf16"]
     assert np.allclose(to_np(S), S_ref, rtol=1e-4, atol=1e-3)
     assert np.allclose(to_np(Z), Z_ref, rtol=1e-4, atol=1e-3)
+
+
+def test_decode_config_sampled_heads():
+    """The decode configuration in its benchmarked launch shape (128 sequences x 16 heads,
+    256 steps, seeded history and steps). Heads are independent, so only sampled heads get
+    their prefilled state (the others start from zero); their outputs at every step and
+    final states are compared with the oracle."""
+    N, H, p, dv, steps = DECODE["N"], DECODE["H"], DECODE["p"], DECODE["dv"], DECODE["steps"]
+    print(f"[case] decode config N={N} H={H} p={p} dv={dv} steps={steps}", flush=True)
+    kh, vh = draw_decode_history(DECODE["hist_seed"], N, H, DECODE["hist"], p, dv)
+    heads = [(0, 0), (37, 5), (127, 15)]
+    n = p * (p + 1) // 2
+    S0 = np.zeros((N, H, n, dv), np.float32)
+    Z0 = np.zeros((N, H, n), np.float32)
+    for (a, b) in heads:
+        s_, z_ = ko.prefill_state(kh[a, b], vh[a, b])
+        S0[a, b], Z0[a, b] = s_, z_
+    del kh, vh
+    qs, ks, vs = draw_decode_steps(DECODE["step_seed"], steps, N, H, p, dv)
+    S = torch.from_numpy(S0).cuda()
+    Z = torch.from_numpy(Z0).cuda()
+    qd, kd, vd = to_dev(qs, "bf16"), to_dev(ks, "bf16"), to_dev(vs, "bf16")
+    out = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda:0")
+    got = np.empty((steps, len(heads), dv), np.float32)
+    for st in range(steps):
+        kata.decode_step(qd[st], kd[st], vd[st], S, Z, out=out)
+        o = out.float()
+        for i, (a, b) in enumerate(heads):
+            got[st, i] = o[a, b].cpu().numpy()
+    S_end, Z_end = to_np(S), to_np(Z)
+    for i, (a, b) in enumerate(heads):
+        ref, S_ref, Z_ref = ko.decode_steps(S0[a, b], Z0[a, b], qs[:, a, b], ks[:, a, b], vs[:, a, b])
+        err = row_rel_err(got[:, i], ref)
+        print(f"  head ({a},{b}) rel_err={err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+        assert np.allclose(S_end[a, b], S_ref, rtol=1e-4, atol=1e-2)
+        assert np.allclose(Z_end[a, b], Z_ref, rtol=1e-4, atol=1e-2)
