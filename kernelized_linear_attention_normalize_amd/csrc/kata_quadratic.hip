@@ -20,6 +20,8 @@
 //     output columns of one query, stored with one 8-byte write, and its own denominator).
 // Weights lie in [0, ||q||^2] and the denominator is a plain sum, so unlike softmax there is
 // no running maximum and no rescaling.
+#include <type_traits>
+
 #include "kata_device.h"
 #include "kata_launch.h"
 
@@ -135,13 +137,18 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
   const int nkb = (kend + BN - 1) / BN;
   prefetch(0);
   stage(0);
+  // The query fragments are complete here; without this wait the counter bookkeeping
+  // (which sees the staging waits only on some paths) keeps them pending into the loop
+  // and waits for the next block's prefetch before the first MFMA of every block.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     const int kb0 = kb * BN;
     if (kb + 1 < nkb) prefetch(kb0 + BN);
-    if (kb0 <= qw0 + QW - 1 && qw0 < T) {
-      const bool diag = kb0 + BN - 1 > qw0;  // some (key > query) pairs in this block
+    // one key block against this wave's queries; DIAG: some (key > query) pairs to mask
+    auto block = [&](auto diag_c) {
+      constexpr bool DIAG = decltype(diag_c)::value;
 #pragma unroll
       for (int kp = 0; kp < NKP; ++kp) {
         // S^T tiles of key pair kp: keys 32 kp + 16 h + 4 lg + r (rows), queries 16 qt + ln
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
             const int h = j >> 2, r = j & 3;
             const float s = St[h][qt][r] * (h ? ik1[r] : ik0[r]);
             w[j] = s * s;
-            if (diag && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[j] = 0.f;
+            if (DIAG && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[j] = 0.f;
           }
           const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])});
 #pragma unroll
@@ -183,6 +190,10 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
           D[qt] = mfma16(ones, wa, D[qt]);
         }
       }
+    };
+    if (kb0 <= qw0 + QW - 1 && qw0 < T) {
+      if (kb0 + BN - 1 > qw0) block(std::true_type{});
+      else block(std::false_type{});
     }
     if (kb + 1 < nkb) stage(buf ^ 1);  // buffer of block kb - 1: every wave is past it
     __syncthreads();
