@@ -376,8 +376,7 @@ struct Stager {
       x[e] = bf16_bits_to_f32(src[e]);
       ss += x[e] * x[e];
     }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
+    ss = group_sum<4>(ss);
     const float inv = inv_norm_fast(ss) * scale;
 #pragma unroll
     for (int e = 0; e < CF::KQ; ++e) x[e] *= inv;
@@ -677,8 +676,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
         intra.template operator()<true>();
       else
         intra.template operator()<false>();
-      dpart += __shfl_xor(dpart, 16, 64);
-      dpart += __shfl_xor(dpart, 32, 64);  // denominator of query qrow, in every lane group
+      dpart = xor32_sum(xor16_sum(dpart));  // denominator of query qrow, in every lane group
     }
     // readout psi(Q) S over pairs [PB, PE): Y[x] = q_hat[qrow][(x & ~15) | ((x + 4 lg) & 15)]
     {

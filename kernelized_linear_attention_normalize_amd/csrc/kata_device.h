@@ -89,11 +89,36 @@ __device__ __forceinline__ void packed_ij(int f, int p, int& i, int& j) {
 
 __device__ __forceinline__ float sqrt2f() { return 1.41421356237309515f; }
 
-// Sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+// x of the lane that DPP control CTRL selects inside this lane's 16-lane row
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+// x + x of lane ^ 16 (gfx950 permlane16 swap: odd rows trade with even rows)
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x + x of lane ^ 32 (gfx950 permlane32 swap: the wave halves trade)
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over aligned groups of G adjacent lanes (G = 1, 2, 4, ..., 64) without LDS traffic:
+// DPP inside 16-lane rows, permlane swaps across rows. Every step adds a symmetric pair,
+// so all lanes of a group end with the bitwise same sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (G >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (G >= 8) x += dpp_f<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if constexpr (G >= 16) x += dpp_f<0x140>(x); // row_mirror: the other half of the row
+  if constexpr (G >= 32) x = xor16_sum(x);
+  if constexpr (G >= 64) x = xor32_sum(x);
   return x;
 }
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
 }  // namespace kata

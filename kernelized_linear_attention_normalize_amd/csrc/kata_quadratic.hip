@@ -27,8 +27,18 @@
 
 namespace kata {
 
+#ifndef KATA_QW
+#define KATA_QW 64
+#endif
+#ifndef KATA_QOCC
+#define KATA_QOCC 2
+#endif
+#ifndef KATA_QBM
+#define KATA_QBM 256
+#endif
 namespace quad {
-constexpr int BM = 256, BN = 64, QW = 64, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
+constexpr int BM = KATA_QBM, BN = 64, QW = KATA_QW, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
+constexpr int NTHR = 64 * (BM / QW);  // threads per workgroup
 constexpr int VTP = 80;  // bf16 pitch of V^T rows (160 bytes: conflict-free 16-byte reads)
 }
 
@@ -37,7 +47,7 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 template <int P, int DV, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v,
                                                                 void* __restrict__ o, int T,
@@ -48,9 +58,9 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
   constexpr int NT = DV / 16;                              // 16-wide output column tiles
   constexpr int KPC = P / 8;                               // 16-byte pieces per key row
   constexpr int KPIECES = BN * KPC;
-  constexpr int KI = (KPIECES + 255) / 256;
+  constexpr int KI = (KPIECES + NTHR - 1) / NTHR;
   constexpr int VPIECES = (BN / 2) * (DV / 8);
-  static_assert(VPIECES <= 256 && KPIECES % 64 == 0, "staging layout");
+  static_assert(VPIECES <= NTHR && KPIECES % 64 == 0, "staging layout");
   __shared__ __align__(16) uint16_t sK[2][BN * KP];
   __shared__ __align__(16) float sInvK[2][BN];
   __shared__ __align__(16) uint16_t sVt[2][DV * VTP];
@@ -85,7 +95,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
   auto prefetch = [&](int kb0) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int pc = tid + 256 * i;
+      const int pc = tid + NTHR * i;
       if (pc < KPIECES)
         kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((kb0 + pc / KPC) * P + 8 * (pc % KPC)) * 2, 0, 0);
     }
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int pc = tid + 256 * i;
+      const int pc = tid + NTHR * i;
       if (pc < KPIECES) {  // whole waves
         const int row = pc / KPC, col = pc % KPC;
         *reinterpret_cast<u32x4_t*>(&sK[buf][row * KP + 8 * col]) = kreg[i];
@@ -108,8 +118,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_bf16_kernel(const uint16_t* 
           const float lo = bf16_bits_to_f32(kreg[i][e] & 0xffffu), hi = __uint_as_float(kreg[i][e] & 0xffff0000u);
           ss += lo * lo + hi * hi;
         }
-#pragma unroll
-        for (int m = 1; m < KPC; m <<= 1) ss += __shfl_xor(ss, m, 64);  // the row's pieces are adjacent lanes
+        ss = group_sum<KPC>(ss);  // the row's pieces are adjacent lanes
         if (col == 0) sInvK[buf][row] = inv_norm_fast(ss);
       }
     }
@@ -222,7 +231,7 @@ template <int P, int DV>
 static hipError_t launch_quad_pd(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int BH, int T, hipStream_t st) {
   const int nqb = (T + quad::BM - 1) / quad::BM;
-  dim3 grid((unsigned)((int64_t)nqb * BH)), block(256);
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
   if (o_bf16) quadratic_bf16_kernel<P, DV, true><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
   else quadratic_bf16_kernel<P, DV, false><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
   return hipGetLastError();

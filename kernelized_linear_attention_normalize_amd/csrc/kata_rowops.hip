@@ -41,8 +41,7 @@ __global__ __launch_bounds__(256) void lift_kernel(const void* __restrict__ u, i
       uh[rr][c] = x;
       ss += x * x;
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+    ss = group_sum<16>(ss);
     const float inv = inv_norm(ss);
     for (int c = l16; c < p; c += 16) uh[rr][c] *= inv;
   }
