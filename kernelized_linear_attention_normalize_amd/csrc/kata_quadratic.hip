@@ -67,8 +67,11 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const int64_t bh = blockIdx.x / nqb;
-  const int qb0 = (nqb - 1 - (int)(blockIdx.x % nqb)) * BM;  // longest rows first
+  // The work of a query block grows with its index, so workgroups go out longest first over
+  // all sequences: workgroup x takes query block nqb - 1 - x / BH of sequence x % BH.
+  const int nbh = (int)(gridDim.x / nqb);
+  const int64_t bh = blockIdx.x % nbh;
+  const int qb0 = (nqb - 1 - (int)(blockIdx.x / nbh)) * BM;
   const int qw0 = qb0 + wave * QW;
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + bh * (int64_t)T * P, (uint32_t)T * P * 2);
   const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + bh * (int64_t)T * P, (uint32_t)T * P * 2);
