@@ -6,7 +6,7 @@
 // Eq. (8)); the normalized readout with explicit denominator (normalized-readout
 // paragraph); inclusive causality of the state S_t (feature-value state display).
 //
-// Per workgroup: 256 queries of one (b,h), 4 waves x 64 queries; key blocks of 64,
+// Per workgroup: 512 queries of one (b,h), 8 waves x 64 queries; key blocks of 64,
 // double-buffered in LDS with one barrier per block (the next block's global loads are in
 // flight during the current block's MFMAs).
 //   * Scores from the raw bf16 inputs: a bf16 x bf16 product is exact in fp32, so the MFMA
@@ -27,14 +27,16 @@
 
 namespace kata {
 
+// Tile shape (compile-time overridable): KATA_QBM queries per workgroup in waves of KATA_QW
+// queries; KATA_QOCC workgroups per CU for the register budget.
 #ifndef KATA_QW
 #define KATA_QW 64
 #endif
 #ifndef KATA_QOCC
-#define KATA_QOCC 2
+#define KATA_QOCC 1
 #endif
 #ifndef KATA_QBM
-#define KATA_QBM 256
+#define KATA_QBM 512
 #endif
 namespace quad {
 constexpr int BM = KATA_QBM, BN = 64, QW = KATA_QW, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
