@@ -845,6 +845,18 @@ __global__ __launch_bounds__(1024, 1) void summary_bf16_kernel(Args a) {
   }
 }
 
+// pass 1 on nblk workgroups (a.nblk_per_bh set by the caller). A template of its own so a
+// translation unit can instantiate it with other code-generation options than the forward.
+template <int P, int DV, int C>
+hipError_t launch_summary(const Args& a, unsigned nblk, hipStream_t st) {
+  using CF = Cfg<P, DV, C>;
+  auto ks = summary_bf16_kernel<P, DV, C>;
+  hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS);
+  if (e != hipSuccess) return e;
+  ks<<<dim3(nblk), dim3(1024), CF::SUM_LDS, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int P, int DV, int C>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                       int B, int H, int T, const SegPlan& plan, float* ws, int passes, hipStream_t st) {
@@ -853,11 +865,8 @@ hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, v
   Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
-    auto ks = summary_bf16_kernel<P, DV, C>;
-    if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS)) != hipSuccess) return e;
     a.nblk_per_bh = plan.nseg - 1;
-    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(1024), CF::SUM_LDS, st>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_summary<P, DV, C>(a, (unsigned)(BH * (plan.nseg - 1)), st)) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN))
     if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;

@@ -226,8 +226,11 @@ def test_quadratic_config_sampled():
         assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("p,dv,T", [(16, 16, 200), (32, 32, 333), (64, 16, 130), (16, 64, 1)])
+@pytest.mark.parametrize("p,dv,T", [(16, 16, 200), (32, 32, 333), (64, 16, 130), (16, 64, 1),
+                                    (64, 64, 1100), (32, 16, 1537), (16, 32, 700)])
 def test_quadratic_shapes(p, dv, T):
+    """Single and several 512-query blocks (the longest-first block order over all (b,h)),
+    ragged key blocks, a zero query row."""
     q, k, v = _case("quadratic-shapes", 14, 2, 2, T, p, dv, "bf16")
     q[1, 1, 3 % T] = 0.0
     ref = ko.naive(q, k, v)
