@@ -140,6 +140,24 @@ kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* 
                                       kata_stream_t stream);
 
 /*
+ * kata_chunked_fwd_state - kata_chunked_fwd that also returns the recurrent state after the
+ * last token of every sequence (feature-value state display: S_T = sum_{s<=T} psi(k_s) v_s^T
+ * and Z_T = sum_{s<=T} psi(k_s), psi the packed lift above), in the layout kata_decode_step
+ * reads and updates, so decoding continues from a chunked prefill:
+ *   S : [B, H, n, dv] float32 and Z : [B, H, n] float32, packed order; written, not
+ *   accumulated (T = 0 writes zeros). The state is the forward's own: built from bf16
+ *   products with fp32 accumulation for bf16 inputs, in fp32 for fp32 inputs.
+ *   Arguments, validation and errors as kata_chunked_fwd; S and Z must be non-NULL (when
+ *   B * H > 0), 16-byte aligned, and must not overlap each other, q, k, v, o or the
+ *   workspace (KATA_ERR_NULL, KATA_ERR_ALIGN, KATA_ERR_ALIAS).
+ */
+kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v,
+                                     kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
+                                     int T, int p, int dv, int C, kata_scan_t scan,
+                                     void* workspace, size_t workspace_bytes, float* S, float* Z,
+                                     kata_stream_t stream);
+
+/*
  * kata_quadratic_fwd - flash-attention-style forward without a state (abstract: the
  * flash-attention-style operating point). For each query block the kernel walks the key
  * blocks s <= t, accumulating sum_s (q_hat . k_hat_s)^2 [v_s | 1] on chip, and divides

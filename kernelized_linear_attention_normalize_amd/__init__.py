@@ -61,6 +61,8 @@ def load():
     lib.kata_chunked_fwd.restype = I
     lib.kata_chunked_fwd_passes.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, I, P]
     lib.kata_chunked_fwd_passes.restype = I
+    lib.kata_chunked_fwd_state.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, P, P, P]
+    lib.kata_chunked_fwd_state.restype = I
     lib.kata_quadratic_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd.restype = I
     lib.kata_decode_step.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P]
@@ -127,10 +129,12 @@ def _scan_code(scan) -> int:
 
 
 def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,
-                workspace=None, passes: int = PASS_ALL):
+                workspace=None, passes: int = PASS_ALL, return_state: bool = False):
     """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv].
     passes: subset of the passes to enqueue (PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS);
-    running them in separate calls needs the same out and workspace each time."""
+    running them in separate calls needs the same out and workspace each time.
+    return_state: also return the state after the last token, (o, S [B,H,n,dv], Z [B,H,n])
+    in float32, the layout decode_step continues from (all passes only)."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -146,6 +150,18 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if return_state:
+        if passes != PASS_ALL:
+            raise ValueError("return_state needs all passes in one call")
+        n = packed_dim(p)
+        S = torch.empty((B, H, n, dv), dtype=torch.float32, device=dev)
+        Z = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        with torch.cuda.device(dev):
+            _check(lib.kata_chunked_fwd_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                              out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc,
+                                              ws_ptr, ws_bytes, S.data_ptr(), Z.data_ptr(),
+                                              _stream(dev)), "kata_chunked_fwd_state")
+        return out, S, Z
     with torch.cuda.device(dev):
         if passes == PASS_ALL:
             _check(lib.kata_chunked_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),

@@ -7,6 +7,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <utility>
 
 #include "kata_launch.h"
 
@@ -144,17 +145,43 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
   return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
 }
 
-kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,
-                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
-                                      int T, int p, int dv, int C, kata_scan_t scan,
-                                      void* workspace, size_t workspace_bytes, int passes,
-                                      kata_stream_t stream) {
+// kata_chunked_fwd_passes, plus the final state when S and Z are given (want_state)
+static kata_status_t chunked_impl(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                  void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                  int C, kata_scan_t scan, void* workspace, size_t workspace_bytes,
+                                  int passes, bool want_state, float* S, float* Z,
+                                  kata_stream_t stream) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
   bool zero = false;
   kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
-  if (s != KATA_OK || zero) return s;
+  if (s != KATA_OK) return s;
+  if (want_state) {
+    if ((int64_t)B * H == 0) return KATA_OK;
+    if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128}))
+      return KATA_ERR_UNSUPPORTED;
+    if (!S || !Z) return KATA_ERR_NULL;
+    if (!aligned16(S) || !aligned16(Z)) return KATA_ERR_ALIGN;
+    const int64_t n = kata_packed_dim(p);
+    if (mul4(B, H, n, dv) < 0) return KATA_ERR_SHAPE;
+    const size_t Sb = (size_t)B * H * n * dv * 4, Zb = (size_t)B * H * n * 4;
+    if (overlap(S, Sb, Z, Zb)) return KATA_ERR_ALIAS;
+    if (T == 0) {  // empty sequences: the zero state
+      hipStream_t st = (hipStream_t)stream;
+      hipError_t e = kata::launch_fill_zero(S, (int64_t)B * H * n * dv, st);
+      if (e == hipSuccess) e = kata::launch_fill_zero(Z, (int64_t)B * H * n, st);
+      return hip_status(e);
+    }
+    const size_t rows = (size_t)B * H * T;
+    const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
+    const size_t ob = rows * dv * dt_size(o_dt);
+    for (const auto& [ptr, bytes] : {std::pair<const void*, size_t>{S, Sb}, {Z, Zb}})
+      if (overlap(ptr, bytes, q, qb) || overlap(ptr, bytes, k, qb) || overlap(ptr, bytes, v, vb) ||
+          overlap(ptr, bytes, o, ob))
+        return KATA_ERR_ALIAS;
+  }
+  if (zero) return KATA_OK;
   if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128}))
     return KATA_ERR_UNSUPPORTED;
   if (in_dt == KATA_DTYPE_F32 && kata::f32_chunked_lds_bytes(p, dv, C) > 160 * 1024)
@@ -168,19 +195,45 @@ kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* 
     if (!aligned16(workspace)) return KATA_ERR_ALIGN;
     const size_t ob = (size_t)B * H * T * dv * dt_size(o_dt);
     if (overlap(o, ob, workspace, need)) return KATA_ERR_ALIAS;
+    if (want_state) {
+      const int64_t n = kata_packed_dim(p);
+      if (overlap(S, (size_t)B * H * n * dv * 4, workspace, need) ||
+          overlap(Z, (size_t)B * H * n * 4, workspace, need))
+        return KATA_ERR_ALIAS;
+    }
   }
   float* ws = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  float* so = want_state ? S : nullptr;
+  float* zo = want_state ? Z : nullptr;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), o, ob16, B, H, T,
-                                                p, dv, C, plan, ws, passes, st));
+                                                p, dv, C, plan, ws, so, zo, passes, st));
   return hip_status(kata::launch_chunked_f32(static_cast<const float*>(q),
                                              static_cast<const float*>(k),
                                              static_cast<const float*>(v), o, ob16, B, H, T, p, dv,
-                                             C, plan, ws, passes, st));
+                                             C, plan, ws, so, zo, passes, st));
+}
+
+kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
+                                      int T, int p, int dv, int C, kata_scan_t scan,
+                                      void* workspace, size_t workspace_bytes, int passes,
+                                      kata_stream_t stream) {
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, workspace, workspace_bytes,
+                      passes, false, nullptr, nullptr, stream);
+}
+
+kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v,
+                                     kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
+                                     int T, int p, int dv, int C, kata_scan_t scan,
+                                     void* workspace, size_t workspace_bytes, float* S, float* Z,
+                                     kata_stream_t stream) {
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, workspace, workspace_bytes,
+                      KATA_PASS_ALL, true, S, Z, stream);
 }
 
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,

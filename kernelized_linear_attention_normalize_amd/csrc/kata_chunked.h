@@ -292,6 +292,8 @@ struct Args {
   float* ws;
   int T, nseg, cps, nblk_per_bh;
   int o_f32;  // output dtype: 1 = fp32, 0 = bf16
+  float* s_out;  // final state S [B,H,n,DV] in the decode layout, or null
+  float* z_out;  // final state Z [B,H,n], or null
 };
 
 
@@ -497,6 +499,69 @@ __device__ __forceinline__ void build_chunk(f32x4_t (&S)[(map_na<MAP, P>(W))][DV
     if constexpr (XDT >= 0) Sx = mfma(build_frag<P, ntiles<P>() - 1>(N, mlow), vbf[XDT], Sx);
     if constexpr (MT >= 0) {  // Gram tile of 2 M = sum 2 k k^T over these 32 tokens (halved when applied)
       Mt = mfma(pack8(N[MRT]), pack8(N[MCT]), Mt);
+    }
+  }
+}
+
+// Packed pair (a, b) of row m of state tile tau (the build side's feature; see build_frag);
+// false for the padding rows of the p = 16 half tile.
+template <int P>
+__device__ __forceinline__ bool feat_pair(int tau, int m, int& a, int& b) {
+  const int kind = tile_kind<P>(tau), h = tile_half<P>(tau), d = tile_delta<P>(tau);
+  if (kind == K_DIAG) {
+    a = b = 16 * h + m;
+  } else if (kind == K_WITHIN) {
+    a = 16 * h + m;
+    b = 16 * h + ((m + d) & 15);
+  } else if (kind == K_WITHIN8) {
+    if (P == 16) {
+      if (m >= 8) return false;
+      a = m;
+      b = m + 8;
+    } else {  // component m (m < 8) or 16 + m, times the rotated partner of the other half
+      const int src = (m + 8) & 15;
+      a = m < 8 ? m : 16 + m;
+      b = src < 8 ? 16 + src : src;
+    }
+  } else {
+    a = m;
+    b = 16 + ((m + d) & 15);
+  }
+  return true;
+}
+
+// The recurrent state after a sequence's last token, in the decode layout (feature-value
+// state display): S[f][d] = sum_s psi_f(k_hat_s) v_s[d], Z[f] = sum_s psi_f(k_hat_s), with f
+// the packed row-major upper-triangle index. The registers hold off-diagonal features with
+// c^2 = 2 folded in (divide by sqrt(2) for psi_f) and the Gram tile as 2 M (Z_f = c_f M_ab).
+template <int P, int DV, int W>
+__device__ __forceinline__ void write_final_state(const Args& a, int64_t bh,
+                                                  const f32x4_t (&S)[wave_na<P>(W)][DV / 16],
+                                                  const f32x4_t& Mt) {
+  constexpr int n = P * (P + 1) / 2, NT = DV / 16, NH = P / 16;
+  constexpr int MT = m_tile<P>(W);
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+  float* so = a.s_out + bh * (int64_t)n * DV;
+#pragma unroll
+  for (int i = 0; i < wave_nt<P>(W); ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int fa, fb;
+      if (!feat_pair<P>(wave_tile<P>(W, i), 4 * lg + r, fa, fb)) continue;
+      const int i0 = fa < fb ? fa : fb, j0 = fa < fb ? fb : fa;
+      const int f = i0 * P - i0 * (i0 - 1) / 2 + (j0 - i0);
+      const float sc = i0 == j0 ? 1.f : 0.70710678118654752f;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) so[(int64_t)f * DV + 16 * dt + ln] = S[i][dt][r] * sc;
+    }
+  if constexpr (MT >= 0) {
+    float* zo = a.z_out + bh * (int64_t)n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * (MT / NH) + 4 * lg + r, col = 16 * (MT % NH) + ln;
+      if (row > col) continue;  // the upper triangle (M is symmetric)
+      const int f = row * P - row * (row - 1) / 2 + (col - row);
+      zo[f] = 0.5f * Mt[r] * (row == col ? 1.f : 1.41421356237309515f);
     }
   }
 }
@@ -751,6 +816,8 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
     write_m();
     __syncthreads();
   }
+  // the last segment of a sequence ends with the state after its last token
+  if (a.s_out != nullptr && seg == a.nblk_per_bh - 1) write_final_state<P, DV, W>(a, bh, S, Mt);
 }
 
 // ---- pass 1: summary [S | M] of one segment after its chunks, to workspace slot seg
@@ -859,10 +926,11 @@ hipError_t launch_summary(const Args& a, unsigned nblk, hipStream_t st) {
 
 template <int P, int DV, int C>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
-                      int B, int H, int T, const SegPlan& plan, float* ws, int passes, hipStream_t st) {
+                      int B, int H, int T, const SegPlan& plan, float* ws, float* s_out, float* z_out,
+                      int passes, hipStream_t st) {
   using CF = Cfg<P, DV, C>;
   const int BH = B * H;
-  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1};
+  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     a.nblk_per_bh = plan.nseg - 1;

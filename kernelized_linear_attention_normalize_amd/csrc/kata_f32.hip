@@ -23,13 +23,14 @@ size_t f32_chunked_lds_bytes(int p, int dv, int C) {
   return 4 * (n * dv + n + 2 * (size_t)C * p + (size_t)C * dv + C + n);
 }
 
-// MODE 0: forward of one segment starting from its prefix state (or zero);
+// MODE 0: forward of one segment starting from its prefix state (or zero); the last
+//         segment of a sequence also writes the final state to s_out / z_out if given;
 // MODE 1: state summary of one segment (psi(K)^T [V | 1]) written to the workspace.
 template <bool OUT_BF16, int MODE>
 __global__ __launch_bounds__(256) void chunked_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     void* __restrict__ o, int T, int p, int dv, int C, int nseg, int cps, int nblk_per_bh,
-    float* __restrict__ ws) {
+    float* __restrict__ ws, float* __restrict__ s_out, float* __restrict__ z_out) {
   extern __shared__ float sm[];
   const int n = p * (p + 1) / 2;
   float* Ss = sm;
@@ -140,13 +141,18 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
     float* dst = ws + (bh * (nseg - 1) + seg) * state_floats;
     for (int e = tid; e < n * dv + n; e += 256) dst[e] = Ss[e];
   }
+  if (MODE == 0 && s_out != nullptr && seg == nblk_per_bh - 1) {  // S then Z: the decode layout
+    __syncthreads();
+    for (int e = tid; e < n * dv; e += 256) s_out[bh * n * dv + e] = Ss[e];
+    for (int f = tid; f < n; f += 256) z_out[bh * n + f] = Zs[f];
+  }
 }
 
 hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st);
 
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, int passes, hipStream_t st) {
+                              float* ws, float* s_out, float* z_out, int passes, hipStream_t st) {
   const int BH = B * H;
   const size_t lds = f32_chunked_lds_bytes(p, dv, C);
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
@@ -154,7 +160,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
-        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws);
+        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN)) {
@@ -166,7 +172,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   kfn<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, plan.nseg,
-                                                              plan.cps, plan.nseg, ws);
+                                                              plan.cps, plan.nseg, ws, s_out, z_out);
   return hipGetLastError();
 }
 

@@ -29,14 +29,19 @@ hipError_t launch_lift(const void* u, bool u_bf16, int64_t rows, int p, void* ps
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf16, float* S,
                          float* Z, void* o, bool o_bf16, int N, int H, int p, int dv,
                          hipStream_t st);
+// s_out / z_out (may be null): the state after the last token of every sequence, in the
+// decode layout (S [B,H,n,dv], Z [B,H,n], fp32, packed order), written by pass 3
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, int passes, hipStream_t st);
+                              float* ws, float* s_out, float* z_out, int passes, hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
-                               const SegPlan& plan, float* ws, int passes, hipStream_t st);
+                               const SegPlan& plan, float* ws, float* s_out, float* z_out,
+                               int passes, hipStream_t st);
+// n float zeros at p (a fill kernel, so the call is safe under graph capture)
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 

@@ -156,4 +156,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf
   return hipGetLastError();
 }
 
+// ---- zero fill (the state of empty sequences)
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
 }  // namespace kata

@@ -101,6 +101,32 @@ def test_chunked_passes_validation(lib):
     assert passes(2, **kw) == E_WS                # every pass needs the workspace of its plan
 
 
+def test_chunked_state_validation(lib):
+    """kata_chunked_fwd_state: the checks of kata_chunked_fwd plus those of the state outputs."""
+    def st(S=A + (1 << 40), Z=A + (1 << 41), **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=1, H=1, T=128,
+                 p=32, dv=64, C=64, scan=SEQ, ws=None, wsb=0)
+        a.update(kw)
+        return lib.kata_chunked_fwd_state(a["q"], a["k"], a["v"], a["in_dt"], a["o"], a["o_dt"], a["B"],
+                                          a["H"], a["T"], a["p"], a["dv"], a["C"], a["scan"], a["ws"],
+                                          a["wsb"], S, Z, None)
+    assert st(in_dt=7) == E_DTYPE
+    assert st(scan=3) == E_SCAN
+    assert st(B=0, S=None, Z=None) == OK             # no sequences: nothing to write
+    assert st(S=None) == E_NULL
+    assert st(Z=None) == E_NULL
+    assert st(p=64) == E_UNSUP
+    assert st(S=A + (1 << 40) + 4) == E_ALIGN
+    n = lib.kata_packed_dim(32)
+    assert st(Z=A + (1 << 40) + n * 64 * 4 - 64) == E_ALIAS      # Z inside S
+    assert st(S=A + 4096) == E_ALIAS                             # S over k
+    assert st(Z=A + (1 << 30)) == E_ALIAS                        # Z over o
+    assert st(q=None) == E_NULL
+    need = lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16)
+    kw = dict(B=1, H=16, T=131072, scan=ASSOC, o=A + (1 << 34), ws=A + (1 << 36), wsb=need)
+    assert st(S=A + (1 << 36) + 1024, **kw) == E_ALIAS           # S inside the workspace
+
+
 def test_workspace_bytes(lib):
     # sequential mode and single-segment problems need none
     assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, SEQ, BF16) == 0

@@ -172,6 +172,60 @@ def test_chunked_deterministic():
     assert torch.equal(a, b)
 
 
+# ------------------------------------------------------------------ prefill -> decode handoff
+def _normwise(got, ref):
+    """max over (b, h) of ||got - ref||_F / ||ref||_F (last one or two axes are the state)."""
+    axes = tuple(range(2, ref.ndim))
+    return float(np.max(np.sqrt(((got - ref) ** 2).sum(axes)) / np.sqrt((ref ** 2).sum(axes))))
+
+
+@pytest.mark.parametrize("dt,p,dv,C,scan,T0", [
+    ("bf16", 32, 64, 128, "associative", 4100), ("bf16", 32, 64, 64, "sequential", 700),
+    ("bf16", 16, 32, 32, "associative", 2000), ("bf16", 32, 16, 64, "associative", 129),
+    ("bf16", 16, 64, 128, "sequential", 300),
+    ("f32", 16, 32, 32, "associative", 1000), ("f32", 16, 16, 64, "sequential", 77)])
+def test_prefill_state_then_decode(dt, p, dv, C, scan, T0):
+    """kata_chunked_fwd_state's final state continues each sequence through kata_decode_step:
+    the prefill outputs, the state after the prefill and every decode output match the
+    oracle over the whole sequence."""
+    steps, B, H = 6, 2, 3
+    q, k, v = _case("handoff", 16, B, H, T0 + steps, p, dv, dt)
+    k[1, 2, :5] = 0.0  # zero keys add nothing to the state
+    ref = ko.naive(q, k, v)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    pre = lambda x: x[:, :, :T0].contiguous()
+    o, S, Z = kata.chunked_fwd(pre(qd), pre(kd), pre(vd), C=C, scan=scan,
+                               out_dtype=torch.float32, return_state=True)
+    assert row_rel_err(to_np(o), ref[:, :, :T0]) <= TOL[dt]
+    S_ref, Z_ref = ko.prefill_state(k[:, :, :T0], v[:, :, :T0])
+    es, ez = _normwise(to_np(S), S_ref), _normwise(to_np(Z), Z_ref)
+    print(f"  state rel err S={es:.2e} Z={ez:.2e}", flush=True)
+    bar = 1e-2 if dt == "bf16" else 1e-5
+    assert es <= bar and ez <= bar
+    for t in range(T0, T0 + steps):
+        step = lambda x: x[:, :, t].contiguous()
+        got = kata.decode_step(step(qd), step(kd), step(vd), S, Z, out_dtype=torch.float32)
+        assert row_rel_err(to_np(got), ref[:, :, t]) <= TOL[dt]
+
+
+def test_prefill_state_empty_sequences():
+    """T = 0: the state is zero (written, whatever the buffers held)."""
+    q = torch.zeros((2, 3, 0, 32), dtype=torch.bfloat16, device="cuda:0")
+    v = torch.zeros((2, 3, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    o, S, Z = kata.chunked_fwd(q, q, v, C=64, return_state=True)
+    assert o.shape == (2, 3, 0, 64) and S.shape == (2, 3, 528, 64) and Z.shape == (2, 3, 528)
+    assert int(torch.count_nonzero(S)) == 0 and int(torch.count_nonzero(Z)) == 0
+
+
+def test_prefill_state_matches_plain_forward():
+    """Asking for the state does not change o (same kernels, bit for bit)."""
+    q, k, v = _case("handoff-o", 17, 1, 4, 3000, 32, 64, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    a = kata.chunked_fwd(qd, kd, vd, C=128)
+    b, _, _ = kata.chunked_fwd(qd, kd, vd, C=128, return_state=True)
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ mid config
 def test_mid_chunked_quadratic_oracle():
     w = WORKLOADS["mid"]
