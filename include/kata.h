@@ -67,8 +67,22 @@ typedef enum {
   KATA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than kata_chunked_workspace_bytes */
   KATA_ERR_HIP = 8,         /* a HIP launch failed */
   KATA_ERR_SCAN = 9,        /* scan is not a kata_scan_t value */
-  KATA_ERR_PASS = 10        /* passes is not a non-empty combination of kata_pass_t bits */
+  KATA_ERR_PASS = 10,       /* passes is not a non-empty combination of kata_pass_t bits */
+  KATA_ERR_FEATURE = 11     /* feature family not a kata_feature_t value, or g does not divide p */
 } kata_status_t;
+
+/* PSD feature families (reduced PSD families paragraph of the HTML page). The projected
+ * query or key, normalised to the unit sphere, is split into g consecutive blocks of
+ * m = p / g components u = (u_1, ..., u_g):
+ *   FULL  : psi(u) = u u^T (g = 1), n = p(p+1)/2, weight (q.k)^2;
+ *   SIGMA : KATA-Sigma g, psi(u) = sum_a u_a u_a^T, n = m(m+1)/2,
+ *           weight sum_{a,b} (q_a . k_b)^2;
+ *   BLOCK : KATA-M g, psi(u) = (u_1 u_1^T, ..., u_g u_g^T), n = g m(m+1)/2,
+ *           weight sum_a (q_a . k_a)^2.
+ * Packing inside an m x m block is the full map's (row-major upper triangle, sqrt(2) off
+ * the diagonal); BLOCK concatenates the blocks, block 1 first. At g = 1 both reduced
+ * families are the full map. */
+typedef enum { KATA_FEAT_FULL = 0, KATA_FEAT_SIGMA = 1, KATA_FEAT_BLOCK = 2 } kata_feature_t;
 
 /* The three passes of the chunked forward (bit mask). */
 typedef enum {
@@ -80,6 +94,10 @@ typedef enum {
 
 /* n = p(p+1)/2 (Eq. (8)); -1 if p < 1. */
 int64_t kata_packed_dim(int p);
+
+/* Packed feature width n of a family (see kata_feature_t); -1 if p < 1, g does not divide
+ * p, or fam is FULL with g != 1. */
+int64_t kata_feature_dim(int p, kata_feature_t fam, int g);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* kata_status_string(kata_status_t s);
@@ -183,6 +201,41 @@ kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, ka
 kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
                                float* S, float* Z, void* o, kata_dtype_t o_dt, int N, int H,
                                int p, int dv, kata_stream_t stream);
+
+/*
+ * The forms above for any feature family (kata_feature_t, block count g). FULL with g = 1
+ * is exactly the corresponding entry point above (same kernels). SIGMA and BLOCK run VALU
+ * kernels (fp32 arithmetic for fp32 or bf16 inputs); the readout, denominator, state and
+ * chunk algebra are the full map's with psi replaced by the family's map, and the weights
+ * of the intra-chunk and quadratic forms are the family's block dot products.
+ * Arguments, layouts, ownership and errors are those of the entry point without the
+ * suffix, with n = kata_feature_dim(p, fam, g) for the state and the lift, plus
+ * KATA_ERR_FEATURE for a bad (fam, g). kata_chunked_fwd_family also takes the optional
+ * final-state outputs of kata_chunked_fwd_state: S [B,H,n,dv] and Z [B,H,n] fp32, both
+ * NULL for none (one NULL alone is KATA_ERR_NULL). Supported for SIGMA / BLOCK: lift 1 <= p <= 128;
+ * decode p <= 64, dv <= 64; quadratic p <= 64, dv <= 64; chunked p <= 64, dv <= 64,
+ * C in {32, 64, 128} while its LDS state fits (160 KB).
+ */
+kata_status_t kata_lift_family(const void* u, kata_dtype_t u_dt, int64_t rows, int p,
+                               kata_feature_t fam, int g, void* psi, kata_dtype_t psi_dt,
+                               kata_stream_t stream);
+size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, int C,
+                                           kata_scan_t scan, kata_dtype_t in_dt,
+                                           kata_feature_t fam, int g);
+kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int T, int p, int dv, int C, kata_scan_t scan,
+                                      kata_feature_t fam, int g, void* workspace,
+                                      size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream);
+kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
+                                        kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                        int H, int T, int p, int dv, kata_feature_t fam, int g,
+                                        kata_stream_t stream);
+kata_status_t kata_decode_step_family(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, kata_feature_t fam, int g, float* S,
+                                      float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
+                                      int dv, kata_stream_t stream);
 
 #ifdef __cplusplus
 }

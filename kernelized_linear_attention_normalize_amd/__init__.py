@@ -17,9 +17,10 @@ import os
 
 import torch
 
-__all__ = ["KataError", "library_path", "load", "packed_dim", "lift", "chunked_workspace_bytes",
-           "chunked_fwd", "quadratic_fwd", "decode_step", "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE",
-           "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS", "PASS_ALL"]
+__all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
+           "chunked_workspace_bytes", "chunked_fwd", "quadratic_fwd", "decode_step",
+           "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
+           "PASS_ALL", "FEATURES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -28,9 +29,12 @@ _lib = None
 DTYPE_F32, DTYPE_BF16 = 0, 1
 SCAN_SEQUENTIAL, SCAN_ASSOCIATIVE = 0, 1
 PASS_SUMMARIES, PASS_SCAN, PASS_SEGMENTS, PASS_ALL = 1, 2, 4, 7
+# PSD feature families: full map, KATA-Sigma g, KATA-M g (kata_feature_t)
+FEATURES = {"full": 0, "sigma": 1, "block": 2}
 _STATUS = {0: "KATA_OK", 1: "KATA_ERR_NULL", 2: "KATA_ERR_SHAPE", 3: "KATA_ERR_DTYPE",
            4: "KATA_ERR_UNSUPPORTED", 5: "KATA_ERR_ALIGN", 6: "KATA_ERR_ALIAS",
-           7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN", 10: "KATA_ERR_PASS"}
+           7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN", 10: "KATA_ERR_PASS",
+           11: "KATA_ERR_FEATURE"}
 
 
 class KataError(RuntimeError):
@@ -67,6 +71,16 @@ def load():
     lib.kata_quadratic_fwd.restype = I
     lib.kata_decode_step.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, P]
     lib.kata_decode_step.restype = I
+    lib.kata_feature_dim.argtypes, lib.kata_feature_dim.restype = [I, I, I], I64
+    lib.kata_lift_family.argtypes, lib.kata_lift_family.restype = [P, I, I64, I, I, I, P, I, P], I
+    lib.kata_chunked_workspace_bytes_family.argtypes = [I, I, I, I, I, I, I, I, I, I]
+    lib.kata_chunked_workspace_bytes_family.restype = SZ
+    lib.kata_chunked_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P, P, P]
+    lib.kata_chunked_fwd_family.restype = I
+    lib.kata_quadratic_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P]
+    lib.kata_quadratic_fwd_family.restype = I
+    lib.kata_decode_step_family.argtypes = [P, P, P, I, I, I, P, P, P, I, I, I, I, I, P]
+    lib.kata_decode_step_family.restype = I
     _lib = lib
     return lib
 
@@ -104,16 +118,36 @@ def packed_dim(p: int) -> int:
     return int(load().kata_packed_dim(p))
 
 
-def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None) -> torch.Tensor:
-    """[..., p] -> [..., p(p+1)/2]: packed psi(u_hat) (rank-one lift, after Eq. (8))."""
+def _fam(family: str, g: int) -> int:
+    if family not in FEATURES:
+        raise ValueError(f"family must be one of {tuple(FEATURES)}")
+    return FEATURES[family]
+
+
+def feature_dim(p: int, family: str = "full", g: int = 1) -> int:
+    """Packed feature width of a family: p(p+1)/2, m(m+1)/2 (Sigma g) or g m(m+1)/2 (M g)."""
+    n = int(load().kata_feature_dim(p, _fam(family, g), g))
+    if n < 0:
+        raise ValueError(f"invalid feature family ({family}, g={g}) for p={p}")
+    return n
+
+
+def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None, family: str = "full",
+         g: int = 1) -> torch.Tensor:
+    """[..., p] -> [..., n]: packed psi(u_hat) (rank-one lift, after Eq. (8)), or the
+    family's map (reduced PSD families paragraph)."""
     lib = load()
     dev = _dev(u)
     p = u.shape[-1]
     rows = u.numel() // p if p else 0
-    out = torch.empty(u.shape[:-1] + (packed_dim(p),), dtype=out_dtype or u.dtype, device=dev)
+    out = torch.empty(u.shape[:-1] + (feature_dim(p, family, g),), dtype=out_dtype or u.dtype, device=dev)
     with torch.cuda.device(dev):
-        _check(lib.kata_lift(u.data_ptr(), _dt(u), rows, p, out.data_ptr(), _dt(out),
-                             _stream(dev)), "kata_lift")
+        if family == "full":
+            _check(lib.kata_lift(u.data_ptr(), _dt(u), rows, p, out.data_ptr(), _dt(out),
+                                 _stream(dev)), "kata_lift")
+        else:
+            _check(lib.kata_lift_family(u.data_ptr(), _dt(u), rows, p, _fam(family, g), g, out.data_ptr(),
+                                        _dt(out), _stream(dev)), "kata_lift_family")
     return out
 
 
@@ -129,12 +163,15 @@ def _scan_code(scan) -> int:
 
 
 def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,
-                workspace=None, passes: int = PASS_ALL, return_state: bool = False):
+                workspace=None, passes: int = PASS_ALL, return_state: bool = False,
+                family: str = "full", g: int = 1):
     """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv].
     passes: subset of the passes to enqueue (PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS);
     running them in separate calls needs the same out and workspace each time.
     return_state: also return the state after the last token, (o, S [B,H,n,dv], Z [B,H,n])
-    in float32, the layout decode_step continues from (all passes only)."""
+    in float32, the layout decode_step continues from (all passes only).
+    family, g: the PSD feature family ("full", "sigma" = KATA-Sigma g, "block" = KATA-M g);
+    the reduced families run all passes in one call."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -145,11 +182,27 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
     _dev(out, q)
-    need = int(lib.kata_chunked_workspace_bytes(B, H, T, p, dv, C, sc, _dt(q)))
+    fam = _fam(family, g)
+    need = int(lib.kata_chunked_workspace_bytes_family(B, H, T, p, dv, C, sc, _dt(q), fam, g))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if family != "full":
+        if passes != PASS_ALL:
+            raise ValueError("the reduced families run all passes in one call")
+        S = Z = None
+        if return_state:
+            n = feature_dim(p, family, g)
+            S = torch.empty((B, H, n, dv), dtype=torch.float32, device=dev)
+            Z = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        with torch.cuda.device(dev):
+            _check(lib.kata_chunked_fwd_family(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                               out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc, fam, g,
+                                               ws_ptr, ws_bytes, S.data_ptr() if S is not None else None,
+                                               Z.data_ptr() if Z is not None else None, _stream(dev)),
+                   "kata_chunked_fwd_family")
+        return (out, S, Z) if return_state else out
     if return_state:
         if passes != PASS_ALL:
             raise ValueError("return_state needs all passes in one call")
@@ -175,8 +228,9 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
     return out
 
 
-def quadratic_fwd(q, k, v, out_dtype=None, out=None):
-    """Flash-style quadratic forward (no state). q, k: [B,H,T,p]; v: [B,H,T,dv]."""
+def quadratic_fwd(q, k, v, out_dtype=None, out=None, family: str = "full", g: int = 1):
+    """Flash-style quadratic forward (no state). q, k: [B,H,T,p]; v: [B,H,T,dv].
+    family, g: the PSD feature family of the weights (see chunked_fwd)."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -187,20 +241,27 @@ def quadratic_fwd(q, k, v, out_dtype=None, out=None):
         out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
     _dev(out, q)
     with torch.cuda.device(dev):
-        _check(lib.kata_quadratic_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
-                                      out.data_ptr(), _dt(out), B, H, T, p, dv, _stream(dev)),
-               "kata_quadratic_fwd")
+        if family == "full":
+            _check(lib.kata_quadratic_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                          out.data_ptr(), _dt(out), B, H, T, p, dv, _stream(dev)),
+                   "kata_quadratic_fwd")
+        else:
+            _check(lib.kata_quadratic_fwd_family(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                                 out.data_ptr(), _dt(out), B, H, T, p, dv,
+                                                 _fam(family, g), g, _stream(dev)),
+                   "kata_quadratic_fwd_family")
     return out
 
 
-def decode_step(q, k, v, S, Z, out_dtype=None, out=None):
+def decode_step(q, k, v, S, Z, out_dtype=None, out=None, family: str = "full", g: int = 1):
     """One recurrent step: S += psi(k) v^T, Z += psi(k), o = psi(q)^T S / psi(q)^T Z.
-    q, k: [N,H,p]; v: [N,H,dv]; S: [N,H,n,dv] fp32 and Z: [N,H,n] fp32 updated in place."""
+    q, k: [N,H,p]; v: [N,H,dv]; S: [N,H,n,dv] fp32 and Z: [N,H,n] fp32 updated in place;
+    family, g: the PSD feature family of psi (n = feature_dim(p, family, g))."""
     lib = load()
     dev = _dev(q, k, v, S, Z)
     N, H, p = q.shape
     dv = v.shape[-1]
-    n = packed_dim(p)
+    n = feature_dim(p, family, g)
     if S.dtype != torch.float32 or Z.dtype != torch.float32:
         raise TypeError("S and Z must be float32")
     if tuple(S.shape) != (N, H, n, dv) or tuple(Z.shape) != (N, H, n):
@@ -209,7 +270,13 @@ def decode_step(q, k, v, S, Z, out_dtype=None, out=None):
         out = torch.empty((N, H, dv), dtype=out_dtype or v.dtype, device=dev)
     _dev(out, q)
     with torch.cuda.device(dev):
-        _check(lib.kata_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
-                                    S.data_ptr(), Z.data_ptr(), out.data_ptr(), _dt(out), N, H, p,
-                                    dv, _stream(dev)), "kata_decode_step")
+        if family == "full":
+            _check(lib.kata_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                        S.data_ptr(), Z.data_ptr(), out.data_ptr(), _dt(out), N, H,
+                                        p, dv, _stream(dev)), "kata_decode_step")
+        else:
+            _check(lib.kata_decode_step_family(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                               _fam(family, g), g, S.data_ptr(), Z.data_ptr(),
+                                               out.data_ptr(), _dt(out), N, H, p, dv, _stream(dev)),
+                   "kata_decode_step_family")
     return out

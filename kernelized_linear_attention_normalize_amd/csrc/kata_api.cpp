@@ -45,6 +45,11 @@ int64_t mul4(int64_t a, int64_t b, int64_t c, int64_t d) {
 
 kata_status_t hip_status(hipError_t e) { return e == hipSuccess ? KATA_OK : KATA_ERR_HIP; }
 
+// (fam, g) valid for width p: KATA_OK or KATA_ERR_FEATURE
+kata_status_t check_feature(int p, kata_feature_t fam, int g) {
+  return kata_feature_dim(p, fam, g) > 0 ? KATA_OK : KATA_ERR_FEATURE;
+}
+
 }  // namespace
 
 namespace kata {
@@ -74,6 +79,14 @@ extern "C" {
 
 int64_t kata_packed_dim(int p) { return p < 1 ? -1 : (int64_t)p * (p + 1) / 2; }
 
+int64_t kata_feature_dim(int p, kata_feature_t fam, int g) {
+  if (p < 1 || g < 1 || p % g != 0) return -1;
+  if (fam == KATA_FEAT_FULL) return g == 1 ? kata_packed_dim(p) : -1;
+  if (fam != KATA_FEAT_SIGMA && fam != KATA_FEAT_BLOCK) return -1;
+  const int64_t m = p / g, nb = m * (m + 1) / 2;
+  return fam == KATA_FEAT_SIGMA ? nb : g * nb;
+}
+
 const char* kata_status_string(kata_status_t s) {
   switch (s) {
     case KATA_OK: return "KATA_OK";
@@ -87,23 +100,41 @@ const char* kata_status_string(kata_status_t s) {
     case KATA_ERR_HIP: return "KATA_ERR_HIP: kernel launch failed";
     case KATA_ERR_SCAN: return "KATA_ERR_SCAN: invalid scan mode";
     case KATA_ERR_PASS: return "KATA_ERR_PASS: invalid pass mask";
+    case KATA_ERR_FEATURE: return "KATA_ERR_FEATURE: invalid feature family or block count";
   }
   return "KATA_ERR_UNKNOWN";
 }
 
-kata_status_t kata_lift(const void* u, kata_dtype_t u_dt, int64_t rows, int p, void* psi,
-                        kata_dtype_t psi_dt, kata_stream_t stream) {
+static kata_status_t lift_impl(const void* u, kata_dtype_t u_dt, int64_t rows, int p,
+                               kata_feature_t fam, int g, void* psi, kata_dtype_t psi_dt,
+                               kata_stream_t stream) {
   if (!valid_dt(u_dt) || !valid_dt(psi_dt)) return KATA_ERR_DTYPE;
   if (rows < 0 || p < 1) return KATA_ERR_SHAPE;
+  kata_status_t s = check_feature(p, fam, g);
+  if (s != KATA_OK) return s;
   if (p > 128) return KATA_ERR_UNSUPPORTED;
   if (rows == 0) return KATA_OK;
-  const int64_t n = kata_packed_dim(p);
+  const int64_t n = kata_feature_dim(p, fam, g);
   if (mul4(rows, n, 1, 1) < 0 || (rows + 15) / 16 > kMaxGrid) return KATA_ERR_SHAPE;
   if (!u || !psi) return KATA_ERR_NULL;
   if (!aligned16(u) || !aligned16(psi)) return KATA_ERR_ALIGN;
   if (overlap(u, rows * p * dt_size(u_dt), psi, rows * n * dt_size(psi_dt))) return KATA_ERR_ALIAS;
+  if (fam != KATA_FEAT_FULL)
+    return hip_status(kata::launch_family_lift(u, u_dt == KATA_DTYPE_BF16, rows, p, (int)fam, g, psi,
+                                               psi_dt == KATA_DTYPE_BF16, (hipStream_t)stream));
   return hip_status(kata::launch_lift(u, u_dt == KATA_DTYPE_BF16, rows, p, psi,
                                       psi_dt == KATA_DTYPE_BF16, (hipStream_t)stream));
+}
+
+kata_status_t kata_lift(const void* u, kata_dtype_t u_dt, int64_t rows, int p, void* psi,
+                        kata_dtype_t psi_dt, kata_stream_t stream) {
+  return lift_impl(u, u_dt, rows, p, KATA_FEAT_FULL, 1, psi, psi_dt, stream);
+}
+
+kata_status_t kata_lift_family(const void* u, kata_dtype_t u_dt, int64_t rows, int p,
+                               kata_feature_t fam, int g, void* psi, kata_dtype_t psi_dt,
+                               kata_stream_t stream) {
+  return lift_impl(u, u_dt, rows, p, fam, g, psi, psi_dt, stream);
 }
 
 // shared checks of the [B,H,T,*] forward entry points; returns KATA_OK to continue,
@@ -146,24 +177,37 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
 }
 
 // kata_chunked_fwd_passes, plus the final state when S and Z are given (want_state)
+// the chunked forward's supported (p, dv, C) for a family and input dtype
+static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
+  if (!in_set(C, {32, 64, 128})) return false;
+  if (fam == KATA_FEAT_FULL) {
+    if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64})) return false;
+    return in_dt == KATA_DTYPE_BF16 || kata::f32_chunked_lds_bytes(p, dv, C) <= 160 * 1024;
+  }
+  return p <= 64 && dv <= 64 && kata::family_chunked_lds_bytes(p, dv, C, (int)fam, g) <= 160 * 1024;
+}
+
+// kata_chunked_fwd_passes for any family, plus the final state when S and Z are given
+// (want_state)
 static kata_status_t chunked_impl(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
                                   void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
-                                  int C, kata_scan_t scan, void* workspace, size_t workspace_bytes,
-                                  int passes, bool want_state, float* S, float* Z,
-                                  kata_stream_t stream) {
+                                  int C, kata_scan_t scan, kata_feature_t fam, int g,
+                                  void* workspace, size_t workspace_bytes, int passes,
+                                  bool want_state, float* S, float* Z, kata_stream_t stream) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
   bool zero = false;
   kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
   if (s != KATA_OK) return s;
+  if ((s = check_feature(p, fam, g)) != KATA_OK) return s;
+  if (fam != KATA_FEAT_FULL && passes != KATA_PASS_ALL) return KATA_ERR_PASS;
   if (want_state) {
     if ((int64_t)B * H == 0) return KATA_OK;
-    if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128}))
-      return KATA_ERR_UNSUPPORTED;
+    if (!chunked_supported(p, dv, C, in_dt, fam, g)) return KATA_ERR_UNSUPPORTED;
     if (!S || !Z) return KATA_ERR_NULL;
     if (!aligned16(S) || !aligned16(Z)) return KATA_ERR_ALIGN;
-    const int64_t n = kata_packed_dim(p);
+    const int64_t n = kata_feature_dim(p, fam, g);
     if (mul4(B, H, n, dv) < 0) return KATA_ERR_SHAPE;
     const size_t Sb = (size_t)B * H * n * dv * 4, Zb = (size_t)B * H * n * 4;
     if (overlap(S, Sb, Z, Zb)) return KATA_ERR_ALIAS;
@@ -182,21 +226,18 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
         return KATA_ERR_ALIAS;
   }
   if (zero) return KATA_OK;
-  if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128}))
-    return KATA_ERR_UNSUPPORTED;
-  if (in_dt == KATA_DTYPE_F32 && kata::f32_chunked_lds_bytes(p, dv, C) > 160 * 1024)
-    return KATA_ERR_UNSUPPORTED;
+  if (!chunked_supported(p, dv, C, in_dt, fam, g)) return KATA_ERR_UNSUPPORTED;
   if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
   const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
-  const size_t need = kata_chunked_workspace_bytes(B, H, T, p, dv, C, scan, in_dt);
+  const size_t need = kata_chunked_workspace_bytes_family(B, H, T, p, dv, C, scan, in_dt, fam, g);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KATA_ERR_ALIGN;
     const size_t ob = (size_t)B * H * T * dv * dt_size(o_dt);
     if (overlap(o, ob, workspace, need)) return KATA_ERR_ALIAS;
     if (want_state) {
-      const int64_t n = kata_packed_dim(p);
+      const int64_t n = kata_feature_dim(p, fam, g);
       if (overlap(S, (size_t)B * H * n * dv * 4, workspace, need) ||
           overlap(Z, (size_t)B * H * n * 4, workspace, need))
         return KATA_ERR_ALIAS;
@@ -207,6 +248,9 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   float* zo = want_state ? Z : nullptr;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (fam != KATA_FEAT_FULL)
+    return hip_status(kata::launch_family_chunked(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
+                                                  dv, C, (int)fam, g, plan, ws, so, zo, st));
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),
@@ -218,13 +262,26 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
                                              C, plan, ws, so, zo, passes, st));
 }
 
+size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, int C,
+                                           kata_scan_t scan, kata_dtype_t in_dt,
+                                           kata_feature_t fam, int g) {
+  if (kata_feature_dim(p, fam, g) <= 0) return 0;
+  if (fam == KATA_FEAT_FULL) return kata_chunked_workspace_bytes(B, H, T, p, dv, C, scan, in_dt);
+  if (!valid_dt(in_dt) || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
+  if (B <= 0 || H <= 0 || T <= 0 || dv < 1 || C < 1) return 0;
+  if (!chunked_supported(p, dv, C, in_dt, fam, g)) return 0;
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  if (plan.nseg <= 1) return 0;
+  return (size_t)B * H * (plan.nseg - 1) * kata::family_state_floats(p, dv, (int)fam, g) * sizeof(float);
+}
+
 kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,
                                       kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B, int H,
                                       int T, int p, int dv, int C, kata_scan_t scan,
                                       void* workspace, size_t workspace_bytes, int passes,
                                       kata_stream_t stream) {
-  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, workspace, workspace_bytes,
-                      passes, false, nullptr, nullptr, stream);
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
+                      workspace_bytes, passes, false, nullptr, nullptr, stream);
 }
 
 kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v,
@@ -232,8 +289,19 @@ kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v
                                      int T, int p, int dv, int C, kata_scan_t scan,
                                      void* workspace, size_t workspace_bytes, float* S, float* Z,
                                      kata_stream_t stream) {
-  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, workspace, workspace_bytes,
-                      KATA_PASS_ALL, true, S, Z, stream);
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
+                      workspace_bytes, KATA_PASS_ALL, true, S, Z, stream);
+}
+
+kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int T, int p, int dv, int C, kata_scan_t scan,
+                                      kata_feature_t fam, int g, void* workspace,
+                                      size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream) {
+  if ((S == nullptr) != (Z == nullptr)) return KATA_ERR_NULL;
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, fam, g, workspace,
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, stream);
 }
 
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
@@ -244,17 +312,22 @@ kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata
                                  workspace_bytes, KATA_PASS_ALL, stream);
 }
 
-kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
-                                 void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
-                                 kata_stream_t stream) {
+static kata_status_t quadratic_impl(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                    void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                    kata_feature_t fam, int g, kata_stream_t stream) {
   bool zero = false;
   kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
-  if (s != KATA_OK || zero) return s;
-  if (!in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) return KATA_ERR_UNSUPPORTED;
+  if (s != KATA_OK) return s;
+  if ((s = check_feature(p, fam, g)) != KATA_OK || zero) return s;
+  if (fam == KATA_FEAT_FULL ? (!in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) : (p > 64 || dv > 64))
+    return KATA_ERR_UNSUPPORTED;
   if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
   if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (fam != KATA_FEAT_FULL)
+    return hip_status(kata::launch_family_quadratic(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
+                                                    dv, (int)fam, g, st));
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_quadratic_bf16(static_cast<const uint16_t*>(q),
                                                   static_cast<const uint16_t*>(k),
@@ -266,19 +339,35 @@ kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, ka
                                                dv, st));
 }
 
-kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
-                               float* S, float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
-                               int dv, kata_stream_t stream) {
+kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                 void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                 kata_stream_t stream) {
+  return quadratic_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, KATA_FEAT_FULL, 1, stream);
+}
+
+kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
+                                        kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                        int H, int T, int p, int dv, kata_feature_t fam, int g,
+                                        kata_stream_t stream) {
+  return quadratic_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, fam, g, stream);
+}
+
+static kata_status_t decode_impl(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                 kata_feature_t fam, int g, float* S, float* Z, void* o,
+                                 kata_dtype_t o_dt, int N, int H, int p, int dv,
+                                 kata_stream_t stream) {
   if (!valid_dt(in_dt) || !valid_dt(o_dt)) return KATA_ERR_DTYPE;
   if (N < 0 || H < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
-  if (p > 64 || dv > 64 || dv % 4 != 0) return KATA_ERR_UNSUPPORTED;
+  kata_status_t s = check_feature(p, fam, g);
+  if (s != KATA_OK) return s;
+  if (p > 64 || dv > 64 || (fam == KATA_FEAT_FULL && dv % 4 != 0)) return KATA_ERR_UNSUPPORTED;
   const int64_t NH = (int64_t)N * H;
   if (NH == 0) return KATA_OK;
   if (NH > kMaxGrid) return KATA_ERR_SHAPE;
   if (!q || !k || !v || !S || !Z || !o) return KATA_ERR_NULL;
   for (const void* ptr : {q, k, v, (const void*)S, (const void*)Z, (const void*)o})
     if (!aligned16(ptr)) return KATA_ERR_ALIGN;
-  const int64_t n = kata_packed_dim(p);
+  const int64_t n = kata_feature_dim(p, fam, g);
   const size_t qb = NH * p * dt_size(in_dt), vb = NH * dv * dt_size(in_dt);
   const size_t ob = NH * dv * dt_size(o_dt), Sb = NH * n * dv * 4, Zb = NH * n * 4;
   const void* outs[3] = {o, S, Z};
@@ -290,9 +379,26 @@ kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata
     for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
   }
+  if (fam != KATA_FEAT_FULL)
+    return hip_status(kata::launch_family_decode(q, k, v, in_dt == KATA_DTYPE_BF16, S, Z, o,
+                                                 o_dt == KATA_DTYPE_BF16, N, H, p, dv, (int)fam, g,
+                                                 (hipStream_t)stream));
   return hip_status(kata::launch_decode(q, k, v, in_dt == KATA_DTYPE_BF16, S, Z, o,
                                         o_dt == KATA_DTYPE_BF16, N, H, p, dv,
                                         (hipStream_t)stream));
+}
+
+kata_status_t kata_decode_step(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                               float* S, float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
+                               int dv, kata_stream_t stream) {
+  return decode_impl(q, k, v, in_dt, KATA_FEAT_FULL, 1, S, Z, o, o_dt, N, H, p, dv, stream);
+}
+
+kata_status_t kata_decode_step_family(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, kata_feature_t fam, int g, float* S,
+                                      float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
+                                      int dv, kata_stream_t stream) {
+  return decode_impl(q, k, v, in_dt, fam, g, S, Z, o, o_dt, N, H, p, dv, stream);
 }
 
 }  // extern "C"

@@ -42,6 +42,22 @@ hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint1
                                int passes, hipStream_t st);
 // n float zeros at p (a fill kernel, so the call is safe under graph capture)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// ---- reduced PSD families (fam 1: Sigma g, 2: M g; m = p / g), VALU kernels
+// floats of one segment summary (n*dv + n, padded to a multiple of 4)
+int64_t family_state_floats(int p, int dv, int fam, int g);
+// dynamic LDS bytes of the family chunked kernel
+size_t family_chunked_lds_bytes(int p, int dv, int C, int fam, int g);
+hipError_t launch_family_lift(const void* u, bool u_bf16, int64_t rows, int p, int fam, int g, void* psi,
+                              bool psi_bf16, hipStream_t st);
+hipError_t launch_family_decode(const void* q, const void* k, const void* v, bool in_bf16, float* S, float* Z,
+                                void* o, bool o_bf16, int N, int H, int p, int dv, int fam, int g,
+                                hipStream_t st);
+hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
+                                 bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
+                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, hipStream_t st);
+hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, bool in_bf16, void* o, bool o_bf16,
+                                   int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st);
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 

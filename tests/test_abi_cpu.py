@@ -18,7 +18,7 @@ from kernelized_linear_attention_normalize_amd import build_lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 F32, BF16 = 0, 1
 SEQ, ASSOC = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN, E_PASS = range(11)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN, E_PASS, E_FEAT = range(12)
 A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never dereferenced)
 
 
@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 def test_packed_dim_and_status_strings(lib):
     assert lib.kata_packed_dim(32) == 528 and lib.kata_packed_dim(64) == 2080
     assert lib.kata_packed_dim(0) == -1
-    for s in range(11):
+    for s in range(12):
         assert lib.kata_status_string(s).startswith(b"KATA_")
 
 
@@ -125,6 +125,44 @@ def test_chunked_state_validation(lib):
     need = lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16)
     kw = dict(B=1, H=16, T=131072, scan=ASSOC, o=A + (1 << 34), ws=A + (1 << 36), wsb=need)
     assert st(S=A + (1 << 36) + 1024, **kw) == E_ALIAS           # S inside the workspace
+
+
+def test_feature_families(lib):
+    """kata_feature_dim matches the widths of the oracle; a bad (family, g) is
+    KATA_ERR_FEATURE before anything else touches the device."""
+    from oracle import kata_families as kf
+    FULL, SIGMA, BLOCK = 0, 1, 2
+    for p, fam, g in [(32, SIGMA, 2), (32, BLOCK, 2), (64, SIGMA, 2), (64, BLOCK, 4), (12, SIGMA, 3), (16, BLOCK, 16)]:
+        assert lib.kata_feature_dim(p, fam, g) == kf.family_dim(p, ("full", "sigma", "block")[fam], g)
+    assert lib.kata_feature_dim(32, FULL, 1) == 528
+    assert lib.kata_feature_dim(32, FULL, 2) == -1 and lib.kata_feature_dim(32, SIGMA, 3) == -1
+    assert lib.kata_feature_dim(32, 7, 1) == -1 and lib.kata_feature_dim(32, SIGMA, 0) == -1
+    fwd = dict(q=A, k=A + 4096, v=A + 8192, o=A + (1 << 30))
+    assert lib.kata_quadratic_fwd_family(fwd["q"], fwd["k"], fwd["v"], BF16, fwd["o"], BF16, 1, 1, 64, 32, 64,
+                                         SIGMA, 3, None) == E_FEAT
+    assert lib.kata_quadratic_fwd_family(fwd["q"], fwd["k"], fwd["v"], BF16, fwd["o"], BF16, 1, 1, 64, 128, 64,
+                                         SIGMA, 2, None) == E_UNSUP
+    assert lib.kata_decode_step_family(A, A + 4096, A + 8192, BF16, BLOCK, 5, A + (1 << 30), A + (1 << 31),
+                                       A + (1 << 32), BF16, 2, 2, 32, 64, None) == E_FEAT
+    assert lib.kata_lift_family(A, F32, 4, 32, FULL, 4, A + (1 << 30), F32, None) == E_FEAT
+
+    def ch(fam=SIGMA, g=2, S=None, Z=None, **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=1, H=1, T=128,
+                 p=32, dv=64, C=64, scan=SEQ, ws=None, wsb=0)
+        a.update(kw)
+        return lib.kata_chunked_fwd_family(a["q"], a["k"], a["v"], a["in_dt"], a["o"], a["o_dt"], a["B"],
+                                           a["H"], a["T"], a["p"], a["dv"], a["C"], a["scan"], fam, g,
+                                           a["ws"], a["wsb"], S, Z, None)
+    assert ch(g=5) == E_FEAT
+    assert ch(S=A + (1 << 40)) == E_NULL               # S without Z
+    assert ch(p=128, g=2) == E_UNSUP
+    assert ch(C=16) == E_UNSUP
+    # associative: the family's summaries need the workspace of their own width
+    need = lib.kata_chunked_workspace_bytes_family(1, 4, 65536, 32, 64, 64, ASSOC, BF16, SIGMA, 2)
+    assert need == 4 * 63 * (136 * 64 + 136) * 4     # 4 heads x 63 summaries (64 segments each)
+    assert lib.kata_chunked_workspace_bytes_family(1, 4, 65536, 32, 64, 64, ASSOC, BF16, FULL, 1) == \
+        lib.kata_chunked_workspace_bytes(1, 4, 65536, 32, 64, 64, ASSOC, BF16)
+    assert ch(B=1, H=4, T=65536, scan=ASSOC, o=A + (1 << 34)) == E_WS
 
 
 def test_workspace_bytes(lib):
