@@ -96,6 +96,10 @@ def main():
     ap.add_argument("--scan", default="associative", choices=["associative", "sequential"])
     ap.add_argument("--workload", default="long", choices=["long", "quadratic", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--family", default="full", choices=["full", "sigma", "block"],
+                    help="PSD feature family of the quadratic workload (sigma = KATA-Sigma g, "
+                         "block = KATA-M g)")
+    ap.add_argument("--g", type=int, default=1, help="feature blocks of --family")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,18 +145,24 @@ def main():
         to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
         qd, kd, vd = to(q), to(k), to(v)
         out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
-        step = [lambda: kata.quadratic_fwd(qd, kd, vd, out=out)]
+        fam, g = args.family, (args.g if args.family != "full" else 1)
+        step = [lambda: kata.quadratic_fwd(qd, kd, vd, out=out, family=fam, g=g)]
         dominant = 0
         kernel_name = "quadratic_bf16_kernel"
         pairs = B * H * T * (T + 1) // 2
-        flops = (2 * p + 2 * (dv + 1)) * pairs
+        # per causal pair: the block dot products of the family (2p for the full map and
+        # M g, 2pg for Sigma g: all g^2 block pairs of length p/g) plus W.[V | 1]
+        flops = ((2 * p * g if fam == "sigma" else 2 * p) + 2 * (dv + 1)) * pairs
         units = B * T
+        fam_txt = "" if fam == "full" else f" family={fam}{g}"
         metric = "flash-style KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
-        config = {"workload": f"quadratic: flash-style forward B={B} H={H} T={T} p={p} dv={dv}",
+        config = {"workload": f"quadratic: flash-style forward B={B} H={H} T={T} p={p} dv={dv}{fam_txt}",
                   "global_batch": B, "seq_len": T, "heads": H, "p": p, "dv": dv,
                   "parallelism": "single-gpu"}
+        if fam != "full":
+            config.update({"family": fam, "g": g})
         bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
-        traffic_file = "quadratic_traffic.txt"
+        traffic_file = "quadratic_traffic.txt" if fam == "full" else f"quadratic_{fam}{g}_traffic.txt"
     elif args.workload == "copy":
         nbytes = 1 << 30
         src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
@@ -251,8 +261,19 @@ def main():
         from oracle import kata_oracle as ko
         res = out.float().cpu().numpy()
         rows = [0, 1, 63, 64, T // 2, T - 1]
-        parity = max(ko.row_rel_err(res[0, h, rows], ko.naive_rows(q[0, h], k[0, h], v[0, h], rows))
-                     for h in (0, H - 1))
+        if args.workload == "quadratic" and args.family != "full":
+            from oracle import kata_families as kf
+
+            def ref_rows(qq, kk, vv):  # the family's definition on the sampled rows
+                qh, kh = ko.normalize(qq), ko.normalize(kk)
+                out_rows = []
+                for t in rows:
+                    w = kf.weights_family(qh[t:t + 1], kh[:t + 1], args.family, args.g)[0]
+                    out_rows.append(w @ vv[:t + 1] / w.sum() if w.sum() > 0 else np.zeros(vv.shape[-1]))
+                return np.asarray(out_rows)
+        else:
+            ref_rows = lambda qq, kk, vv: ko.naive_rows(qq, kk, vv, rows)
+        parity = max(ko.row_rel_err(res[0, h, rows], ref_rows(q[0, h], k[0, h], v[0, h])) for h in (0, H - 1))
 
     cpu = None
     if args.workload == "long" and not args.no_cpu_baseline:

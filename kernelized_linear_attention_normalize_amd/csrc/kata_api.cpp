@@ -325,9 +325,15 @@ static kata_status_t quadratic_impl(const void* q, const void* k, const void* v,
   if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
-  if (fam != KATA_FEAT_FULL)
+  if (fam != KATA_FEAT_FULL) {
+    if (in_dt == KATA_DTYPE_BF16 && kata::quadratic_bf16_family_supported(p, dv, (int)fam, g))
+      return hip_status(kata::launch_quadratic_bf16_family(static_cast<const uint16_t*>(q),
+                                                           static_cast<const uint16_t*>(k),
+                                                           static_cast<const uint16_t*>(v), o, ob16, B, H,
+                                                           T, p, dv, (int)fam, g, st));
     return hip_status(kata::launch_family_quadratic(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
                                                     dv, (int)fam, g, st));
+  }
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_quadratic_bf16(static_cast<const uint16_t*>(q),
                                                   static_cast<const uint16_t*>(k),

@@ -48,7 +48,11 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int P, int DV, bool OUT_BF16>
+// FAM: 0 the full map; 1 KATA-Sigma G, 2 KATA-M G (reduced PSD families paragraph) with
+// blocks of P / G components, a whole number of 32-wide k-steps each: the block dot products
+// q_a . k_b come from pairing the k-steps of block b of the keys with those of block a of the
+// queries, and the weight is the sum of their squares (all pairs for Sigma, a = b for M).
+template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1>
 __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v,
@@ -63,6 +67,8 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   constexpr int KI = (KPIECES + NTHR - 1) / NTHR;
   constexpr int VPIECES = (BN / 2) * (DV / 8);
   static_assert(VPIECES <= NTHR && KPIECES % 64 == 0, "staging layout");
+  constexpr int KM = KS / G;  // k-steps per feature block
+  static_assert(FAM == 0 ? G == 1 : (P % (32 * G) == 0), "feature blocks are whole k-steps");
   __shared__ __align__(16) uint16_t sK[2][BN * KP];
   __shared__ __align__(16) float sInvK[2][BN];
   __shared__ __align__(16) uint16_t sVt[2][DV * VTP];
@@ -163,6 +169,54 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
     // one key block against this wave's queries; DIAG: some (key > query) pairs to mask
     auto block = [&](auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
+      if constexpr (FAM != 0) {  // reduced family: block dot products, squared and summed
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) {
+          u32x4_t a[2][KS];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              a[h][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][(16 * (2 * kp + h) + ln) * KP + 32 * ks + 8 * lg]);
+          const f32x4_t ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
+          const f32x4_t ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
+          const f32x4_t ik2[2] = {ik0 * ik0, ik1 * ik1};
+          bf16x8_t vb[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            vb[nt] = *reinterpret_cast<const bf16x8_t*>(&sVt[buf][vt_row(16 * nt + ln) * VTP + 32 * kp + 8 * lg]);
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) {
+            const int query = qw0 + 16 * qt + ln;
+            float w[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              f32x4_t sq = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int qa = 0; qa < G; ++qa)
+#pragma unroll
+                for (int kb = 0; kb < G; ++kb) {
+                  if (FAM == 2 && kb != qa) continue;
+                  f32x4_t St = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int i = 0; i < KM; ++i)
+                    St = mfma16(__builtin_bit_cast(bf16x8_t, a[h][kb * KM + i]), qf[qt][qa * KM + i], St);
+                  sq += St * St;
+                }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                w[4 * h + r] = sq[r] * ik2[h][r];
+                if (DIAG && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[4 * h + r] = 0.f;
+              }
+            }
+            const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])});
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) O[qt][nt] = mfma16(vb[nt], wa, O[qt][nt]);
+            D[qt] = mfma16(ones, wa, D[qt]);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int kp = 0; kp < NKP; ++kp) {
         // S^T tiles of key pair kp: keys 32 kp + 16 h + 4 lg + r (rows), queries 16 qt + ln
@@ -252,6 +306,36 @@ hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uin
   KATA_QCASE(64, 16) KATA_QCASE(64, 32) KATA_QCASE(64, 64)
 #undef KATA_QCASE
   return hipErrorInvalidValue;
+}
+
+// reduced families with 32-component blocks (p = 64, g = 2); false if not covered here
+bool quadratic_bf16_family_supported(int p, int dv, int fam, int g) {
+  return p == 64 && g == 2 && (fam == 1 || fam == 2) && (dv == 16 || dv == 32 || dv == 64);
+}
+
+template <int DV, int FAM>
+static hipError_t launch_quad_fam(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
+                                  int BH, int T, hipStream_t st) {
+  const int nqb = (T + quad::BM - 1) / quad::BM;
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
+  if (o_bf16) quadratic_bf16_kernel<64, DV, true, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  else quadratic_bf16_kernel<64, DV, false, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                        bool o_bf16, int B, int H, int T, int p, int dv, int fam, int g,
+                                        hipStream_t st) {
+  if (!quadratic_bf16_family_supported(p, dv, fam, g)) return hipErrorInvalidValue;
+  const int BH = B * H;
+  if (fam == 1) {
+    if (dv == 16) return launch_quad_fam<16, 1>(q, k, v, o, o_bf16, BH, T, st);
+    if (dv == 32) return launch_quad_fam<32, 1>(q, k, v, o, o_bf16, BH, T, st);
+    return launch_quad_fam<64, 1>(q, k, v, o, o_bf16, BH, T, st);
+  }
+  if (dv == 16) return launch_quad_fam<16, 2>(q, k, v, o, o_bf16, BH, T, st);
+  if (dv == 32) return launch_quad_fam<32, 2>(q, k, v, o, o_bf16, BH, T, st);
+  return launch_quad_fam<64, 2>(q, k, v, o, o_bf16, BH, T, st);
 }
 
 }  // namespace kata

@@ -75,8 +75,11 @@ def test_family_chunked_many_segments_and_state():
 
 @pytest.mark.parametrize("family,p,g,dv,T,dt", [
     ("sigma", 64, 2, 64, 700, "bf16"), ("block", 64, 2, 64, 513, "bf16"), ("sigma", 32, 4, 16, 200, "f32"),
-    ("block", 16, 2, 32, 65, "f32")])
+    ("block", 16, 2, 32, 65, "f32"), ("sigma", 64, 2, 16, 1100, "bf16"), ("block", 64, 2, 32, 1537, "bf16"),
+    ("sigma", 64, 4, 64, 300, "bf16")])
 def test_family_quadratic(family, p, g, dv, T, dt):
+    """bf16 with p = 64, g = 2 runs the MFMA kernel (32-component blocks, several 512-query
+    blocks, ragged key blocks); the other cases the VALU kernel."""
     q, k, v = _case(f"family-quadratic-{family}{g}", 43, 2, 2, T, p, dv, dt)
     q[1, 1, 2] = 0.0
     ref = kf.naive_family(q, k, v, family, g)
