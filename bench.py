@@ -114,7 +114,36 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.workload == "long":
+    if args.workload == "long" and args.family != "full":
+        # KATA-Sigma g / M g on the long shape: queries and keys of 2 x 32 components
+        # (Sigma 2 at d = 64 has the 528-coordinate state of the full map at p = 32)
+        w = WORKLOADS["long"]
+        fam, g = args.family, args.g
+        B, H, T, p, dv, C = w.B, w.H, w.T, 64, w.dv, args.chunk
+        q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd = to(q), to(k), to(v)
+        out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(kata.chunked_workspace_bytes_family(B, H, T, p, dv, C, kata._scan_code(args.scan),
+                                                                 fam=fam, g=g), 1), dtype=torch.uint8, device=dev)
+        step = [lambda: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws, family=fam, g=g)]
+        dominant = 0
+        s2 = fam == "sigma" and g == 2
+        kernel_name = f"chunked_bf16_kernel<32, {dv}, {C}, true>" if s2 else "family_chunked_kernel"
+        m = p // g
+        n = m * (m + 1) // 2 * (1 if fam == "sigma" else g)
+        Cr = C // 2 if s2 else C  # tokens per chunk (C counts 32-component rows under Sigma 2)
+        pair = 2 * p * g if fam == "sigma" else 2 * p
+        flops = (4 * n * (dv + 1) + (Cr + 1) * (pair // 2 + dv + 1)) * B * H * T
+        units = B * T
+        metric = f"chunked KATA-{'Sigma' if fam == 'sigma' else 'M'}{g} fwd tokens/s at T={T} (1 GPU) + % bf16 MFMA peak"
+        config = {"workload": f"long, KATA-{fam}{g}: chunked forward B={B} H={H} T={T} p={p} (n={n}) dv={dv} "
+                              f"C={C} scan={args.scan}", "global_batch": B, "seq_len": T, "heads": H, "p": p,
+                  "dv": dv, "chunk": C, "scan": args.scan, "family": fam, "g": g,
+                  "parallelism": "single-gpu"}
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        traffic_file = f"chunked_long_{fam}{g}_C{C}_{args.scan}_traffic.txt"
+    elif args.workload == "long":
         w = WORKLOADS["long"]
         B, H, T, p, dv, C = w.B, w.H, w.T, w.p, w.dv, args.chunk
         q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
@@ -261,7 +290,7 @@ def main():
         from oracle import kata_oracle as ko
         res = out.float().cpu().numpy()
         rows = [0, 1, 63, 64, T // 2, T - 1]
-        if args.workload == "quadratic" and args.family != "full":
+        if args.family != "full":
             from oracle import kata_families as kf
 
             def ref_rows(qq, kk, vv):  # the family's definition on the sampled rows
@@ -276,7 +305,7 @@ def main():
         parity = max(ko.row_rel_err(res[0, h, rows], ref_rows(q[0, h], k[0, h], v[0, h])) for h in (0, H - 1))
 
     cpu = None
-    if args.workload == "long" and not args.no_cpu_baseline:
+    if args.workload == "long" and args.family == "full" and not args.no_cpu_baseline:
         cpu = cpu_baseline_long(q, k, v, H)
 
     rec = {"metric": metric, "value": round(value, 1),

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
-           "chunked_workspace_bytes", "chunked_fwd", "quadratic_fwd", "decode_step",
+           "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
            "PASS_ALL", "FEATURES"]
 
@@ -154,6 +154,12 @@ def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None, family: str = "f
 def chunked_workspace_bytes(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16):
     return int(load().kata_chunked_workspace_bytes(B, H, T, p, dv, C, int(scan),
                                                    DTYPE_BF16 if in_dtype == torch.bfloat16 else DTYPE_F32))
+
+
+def chunked_workspace_bytes_family(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16,
+                                   fam: str = "full", g: int = 1):
+    return int(load().kata_chunked_workspace_bytes_family(
+        B, H, T, p, dv, C, int(scan), DTYPE_BF16 if in_dtype == torch.bfloat16 else DTYPE_F32, _fam(fam, g), g))
 
 
 def _scan_code(scan) -> int:

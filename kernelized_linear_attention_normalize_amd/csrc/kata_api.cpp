@@ -177,9 +177,16 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
 }
 
 // kata_chunked_fwd_passes, plus the final state when S and Z are given (want_state)
+// KATA-Sigma 2 at p = 64 with bf16 inputs runs the MFMA kernels over 2T virtual rows
+static bool sigma2_mfma(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
+  return fam == KATA_FEAT_SIGMA && g == 2 && p == 64 && in_dt == KATA_DTYPE_BF16 && in_set(dv, {32, 64}) &&
+         in_set(C, {64, 128});
+}
+
 // the chunked forward's supported (p, dv, C) for a family and input dtype
 static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
   if (!in_set(C, {32, 64, 128})) return false;
+  if (sigma2_mfma(p, dv, C, in_dt, fam, g)) return true;
   if (fam == KATA_FEAT_FULL) {
     if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64})) return false;
     return in_dt == KATA_DTYPE_BF16 || kata::f32_chunked_lds_bytes(p, dv, C) <= 160 * 1024;
@@ -228,7 +235,9 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   if (zero) return KATA_OK;
   if (!chunked_supported(p, dv, C, in_dt, fam, g)) return KATA_ERR_UNSUPPORTED;
   if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
-  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  const bool s2 = sigma2_mfma(p, dv, C, in_dt, fam, g);
+  if (s2 && (int64_t)T * 2 > INT32_MAX) return KATA_ERR_SHAPE;
+  const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
   const size_t need = kata_chunked_workspace_bytes_family(B, H, T, p, dv, C, scan, in_dt, fam, g);
   if (need > 0) {
@@ -248,6 +257,11 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   float* zo = want_state ? Z : nullptr;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (s2)
+    return hip_status(kata::launch_chunked_bf16_sigma2(static_cast<const uint16_t*>(q),
+                                                       static_cast<const uint16_t*>(k),
+                                                       static_cast<const uint16_t*>(v), o, ob16, B, H, T, dv,
+                                                       C, plan, ws, so, zo, st));
   if (fam != KATA_FEAT_FULL)
     return hip_status(kata::launch_family_chunked(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
                                                   dv, C, (int)fam, g, plan, ws, so, zo, st));
@@ -270,9 +284,12 @@ size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, i
   if (!valid_dt(in_dt) || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
   if (B <= 0 || H <= 0 || T <= 0 || dv < 1 || C < 1) return 0;
   if (!chunked_supported(p, dv, C, in_dt, fam, g)) return 0;
-  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  const bool s2 = sigma2_mfma(p, dv, C, in_dt, fam, g);
+  if (s2 && (int64_t)T * 2 > INT32_MAX) return 0;
+  const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if (plan.nseg <= 1) return 0;
-  return (size_t)B * H * (plan.nseg - 1) * kata::family_state_floats(p, dv, (int)fam, g) * sizeof(float);
+  const int64_t sf = s2 ? kata::mfma_state_floats(32, dv) : kata::family_state_floats(p, dv, (int)fam, g);
+  return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
 }
 
 kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* v,

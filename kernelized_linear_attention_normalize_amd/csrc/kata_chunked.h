@@ -298,8 +298,11 @@ struct Args {
 
 
 
-// ---- chunk staging: global bf16 -> registers (load) -> normalised LDS layouts
-template <int P, int DV, int C, bool WITH_Q>
+// ---- chunk staging: global bf16 -> registers (load) -> normalised LDS layouts.
+// S2 (KATA-Sigma 2 on 2P-wide inputs): a token's two P-component blocks are consecutive
+// "virtual" rows of the same memory read as [2T][P] (a.T counts virtual rows); a key is
+// normalised over both blocks, and both virtual rows carry the token's value row.
+template <int P, int DV, int C, bool WITH_Q, bool S2 = false>
 struct Stager {
   using CF = Cfg<P, DV, C>;
   typedef uint16_t row_t __attribute__((ext_vector_type(P / 4)));
@@ -329,7 +332,7 @@ struct Stager {
   __device__ __forceinline__ void init(const Args& a, int64_t bh) {
     qb = a.q + bh * a.T * P;
     kb = a.k + bh * a.T * P;
-    vb = a.v + bh * a.T * DV;
+    vb = a.v + bh * (S2 ? a.T / 2 : a.T) * DV;
     T = a.T;
   }
 
@@ -346,7 +349,8 @@ struct Stager {
     const uint32_t left = (uint32_t)(T - t0);
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)t0 * P, left * P * 2);
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * P, left * P * 2);
-    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vb + (int64_t)t0 * DV, left * DV * 2);
+    const __amdgpu_buffer_rsrc_t rv = S2 ? buf_rsrc(vb + (int64_t)(t0 / 2) * DV, (left / 2) * DV * 2)
+                                         : buf_rsrc(vb + (int64_t)t0 * DV, left * DV * 2);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int pc = qk_piece(i);
@@ -363,14 +367,21 @@ struct Stager {
       if (pc >= 0 && pc < CF::VPIECES) {
         int vp, vd;
         CF::vpiece(pc, vp, vd);
-        const uint32_t voff = (uint32_t)(2 * vp * DV + 8 * vd) * 2;
-        vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
-        vr[i][1] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + DV * 2, 0, 0));
+        if constexpr (S2) {  // key pair vp = the two blocks of token vp: one value row
+          const uint32_t voff = (uint32_t)(vp * DV + 8 * vd) * 2;
+          vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+          vr[i][1] = vr[i][0];
+        } else {
+          const uint32_t voff = (uint32_t)(2 * vp * DV + 8 * vd) * 2;
+          vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+          vr[i][1] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + DV * 2, 0, 0));
+        }
       }
     }
   }
 
-  // normalised row piece (4 consecutive lanes share a row; the norm is combined over them)
+  // normalised row piece (4 consecutive lanes share a row, 8 a token under S2; the norm is
+  // combined over them)
   __device__ __forceinline__ void normalise(const row_t& src, float (&x)[CF::KQ], float scale = 1.f) {
     float ss = 0.f;
 #pragma unroll
@@ -378,7 +389,7 @@ struct Stager {
       x[e] = bf16_bits_to_f32(src[e]);
       ss += x[e] * x[e];
     }
-    ss = group_sum<4>(ss);
+    ss = group_sum<S2 ? 8 : 4>(ss);
     const float inv = inv_norm_fast(ss) * scale;
 #pragma unroll
     for (int e = 0; e < CF::KQ; ++e) x[e] *= inv;
@@ -568,7 +579,10 @@ __device__ __forceinline__ void write_final_state(const Args& a, int64_t bh,
 
 // ---- forward of one segment; W (wave index) is a template parameter so every tile and
 // pair index is a compile-time constant and the lift indexes registers directly.
-template <int P, int DV, int C, int W>
+// S2: KATA-Sigma 2 over virtual rows (see Stager): psi(q)^T S and the denominator of a token
+// are the sums over its two virtual query rows (adjacent lanes), the causal mask compares
+// tokens, and output row t is token t.
+template <int P, int DV, int C, int W, bool S2 = false>
 __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   using CF = Cfg<P, DV, C>;
   constexpr int NT = CF::NT, NH = CF::NH, NTW = wave_nt<P>(W);
@@ -594,7 +608,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
   const int osz = a.o_f32 ? 4 : 2;
-  char* obase = static_cast<char*>(a.o) + bh * a.T * DV * osz;
+  char* obase = static_cast<char*>(a.o) + bh * (S2 ? a.T / 2 : a.T) * DV * osz;
 
   // ---- initial state (exclusive prefix of this segment, or zero)
   f32x4_t S[wave_na<P>(W)][NT];
@@ -645,7 +659,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
     }
   };
 
-  Stager<P, DV, C, true> stg;
+  Stager<P, DV, C, true, S2> stg;
   stg.init(a, bh);
   stg.load(c0 * C);
   stg.stage_rows(lds);
@@ -723,7 +737,8 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float w = St[r] * St[r];
-            if (kt == TT && 4 * lg + r > ln) w = 0.f;  // causal: key <= query on the diagonal tile
+            // causal: key <= query on the diagonal tile (token indices under S2)
+            if (kt == TT && (S2 ? ((4 * lg + r) >> 1) > (ln >> 1) : 4 * lg + r > ln)) w = 0.f;
             wv[4 * half + r] = w;
             dpart += w;
           }
@@ -790,9 +805,13 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
     if constexpr (CF::owns_any(FSI)) {  // add the other splits' sums, normalise, store
       float den = dpart;
       if constexpr (!OWNER) den = pd[TT * 64 + lane];
+      if constexpr (S2) den += dpp_f<0xB1>(den);  // the token's other virtual query row (lane ^ 1)
       const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)t0 * DV * osz, (uint32_t)(a.T - t0) * DV * osz);
-      const uint32_t ob = (uint32_t)((16 * TT + ln) * DV + 4 * lg);  // rows past T are dropped
+      const int orow0 = S2 ? t0 / 2 : t0, orows = S2 ? (a.T - t0) / 2 : a.T - t0;
+      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)orow0 * DV * osz, (uint32_t)orows * DV * osz);
+      // rows past T are dropped; under S2 the even lane of a token stores it
+      const uint32_t ob = (uint32_t)((S2 ? (16 * TT + ln) >> 1 : 16 * TT + ln) * DV + 4 * lg);
+      const bool store = !S2 || (ln & 1) == 0;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
         if (CF::out_owner(dt) != FSI) continue;
@@ -800,11 +819,17 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 #pragma unroll
         for (int f = 0; f < CF::FS; ++f)
           if (f != FSI) o += *reinterpret_cast<const f32x4_t*>(part + (CF::part_slot(TT, dt, f) * 64 + lane) * 16);
+        if constexpr (S2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] += dpp_f<0xB1>(o[r]);
+        }
         o *= inv;
-        if (a.o_f32)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, (ob + 16 * dt) * 4, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pk2(o[0], o[1]), pk2(o[2], o[3])}, ro, (ob + 16 * dt) * 2, 0, 0);
+        if (store) {
+          if (a.o_f32)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, (ob + 16 * dt) * 4, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pk2(o[0], o[1]), pk2(o[2], o[3])}, ro, (ob + 16 * dt) * 2, 0, 0);
+        }
       }
     }
     if (c + 1 < c1) {
@@ -821,7 +846,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 }
 
 // ---- pass 1: summary [S | M] of one segment after its chunks, to workspace slot seg
-template <int P, int DV, int C, int W>
+template <int P, int DV, int C, int W, bool S2 = false>
 __device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
   using CF = Cfg<P, DV, C>;
   constexpr int NT = CF::NT, NTW = Map16::nt<P>(W), MT = Map16::mtile<P>(W);
@@ -841,7 +866,7 @@ __device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) S[i][dt] = zero4();
 
-  Stager<P, DV, C, false> stg;
+  Stager<P, DV, C, false, S2> stg;
   stg.init(a, bh);
   stg.load(c0 * C);
   stg.template stage_kt<false>(lds, OKT);
@@ -873,58 +898,59 @@ __device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
 }
 
 // forward of the segments (8 waves)
-template <int P, int DV, int C>
+template <int P, int DV, int C, bool S2 = false>
 __global__ __launch_bounds__(512, 1) void chunked_bf16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
-    case 0: run_fwd<P, DV, C, 0>(a, lds); break;
-    case 1: run_fwd<P, DV, C, 1>(a, lds); break;
-    case 2: run_fwd<P, DV, C, 2>(a, lds); break;
-    case 3: run_fwd<P, DV, C, 3>(a, lds); break;
-    case 4: run_fwd<P, DV, C, 4>(a, lds); break;
-    case 5: run_fwd<P, DV, C, 5>(a, lds); break;
-    case 6: run_fwd<P, DV, C, 6>(a, lds); break;
-    default: run_fwd<P, DV, C, 7>(a, lds); break;
+    case 0: run_fwd<P, DV, C, 0, S2>(a, lds); break;
+    case 1: run_fwd<P, DV, C, 1, S2>(a, lds); break;
+    case 2: run_fwd<P, DV, C, 2, S2>(a, lds); break;
+    case 3: run_fwd<P, DV, C, 3, S2>(a, lds); break;
+    case 4: run_fwd<P, DV, C, 4, S2>(a, lds); break;
+    case 5: run_fwd<P, DV, C, 5, S2>(a, lds); break;
+    case 6: run_fwd<P, DV, C, 6, S2>(a, lds); break;
+    default: run_fwd<P, DV, C, 7, S2>(a, lds); break;
   }
 }
 
 // segment summaries (16 waves)
-template <int P, int DV, int C>
+template <int P, int DV, int C, bool S2 = false>
 __global__ __launch_bounds__(1024, 1) void summary_bf16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
-    case 0: run_sum16<P, DV, C, 0>(a, lds); break;
-    case 1: run_sum16<P, DV, C, 1>(a, lds); break;
-    case 2: run_sum16<P, DV, C, 2>(a, lds); break;
-    case 3: run_sum16<P, DV, C, 3>(a, lds); break;
-    case 4: run_sum16<P, DV, C, 4>(a, lds); break;
-    case 5: run_sum16<P, DV, C, 5>(a, lds); break;
-    case 6: run_sum16<P, DV, C, 6>(a, lds); break;
-    case 7: run_sum16<P, DV, C, 7>(a, lds); break;
-    case 8: run_sum16<P, DV, C, 8>(a, lds); break;
-    case 9: run_sum16<P, DV, C, 9>(a, lds); break;
-    case 10: run_sum16<P, DV, C, 10>(a, lds); break;
-    case 11: run_sum16<P, DV, C, 11>(a, lds); break;
-    case 12: run_sum16<P, DV, C, 12>(a, lds); break;
-    case 13: run_sum16<P, DV, C, 13>(a, lds); break;
-    case 14: run_sum16<P, DV, C, 14>(a, lds); break;
-    default: run_sum16<P, DV, C, 15>(a, lds); break;
+    case 0: run_sum16<P, DV, C, 0, S2>(a, lds); break;
+    case 1: run_sum16<P, DV, C, 1, S2>(a, lds); break;
+    case 2: run_sum16<P, DV, C, 2, S2>(a, lds); break;
+    case 3: run_sum16<P, DV, C, 3, S2>(a, lds); break;
+    case 4: run_sum16<P, DV, C, 4, S2>(a, lds); break;
+    case 5: run_sum16<P, DV, C, 5, S2>(a, lds); break;
+    case 6: run_sum16<P, DV, C, 6, S2>(a, lds); break;
+    case 7: run_sum16<P, DV, C, 7, S2>(a, lds); break;
+    case 8: run_sum16<P, DV, C, 8, S2>(a, lds); break;
+    case 9: run_sum16<P, DV, C, 9, S2>(a, lds); break;
+    case 10: run_sum16<P, DV, C, 10, S2>(a, lds); break;
+    case 11: run_sum16<P, DV, C, 11, S2>(a, lds); break;
+    case 12: run_sum16<P, DV, C, 12, S2>(a, lds); break;
+    case 13: run_sum16<P, DV, C, 13, S2>(a, lds); break;
+    case 14: run_sum16<P, DV, C, 14, S2>(a, lds); break;
+    default: run_sum16<P, DV, C, 15, S2>(a, lds); break;
   }
 }
 
 // pass 1 on nblk workgroups (a.nblk_per_bh set by the caller). A template of its own so a
 // translation unit can instantiate it with other code-generation options than the forward.
-template <int P, int DV, int C>
+template <int P, int DV, int C, bool S2 = false>
 hipError_t launch_summary(const Args& a, unsigned nblk, hipStream_t st) {
   using CF = Cfg<P, DV, C>;
-  auto ks = summary_bf16_kernel<P, DV, C>;
+  auto ks = summary_bf16_kernel<P, DV, C, S2>;
   hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, CF::SUM_LDS);
   if (e != hipSuccess) return e;
   ks<<<dim3(nblk), dim3(1024), CF::SUM_LDS, st>>>(a);
   return hipGetLastError();
 }
 
-template <int P, int DV, int C>
+// T: rows of q / k (virtual rows, 2x the tokens, under S2)
+template <int P, int DV, int C, bool S2 = false>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                       int B, int H, int T, const SegPlan& plan, float* ws, float* s_out, float* z_out,
                       int passes, hipStream_t st) {
@@ -934,12 +960,12 @@ hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, v
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     a.nblk_per_bh = plan.nseg - 1;
-    if ((e = launch_summary<P, DV, C>(a, (unsigned)(BH * (plan.nseg - 1)), st)) != hipSuccess) return e;
+    if ((e = launch_summary<P, DV, C, S2>(a, (unsigned)(BH * (plan.nseg - 1)), st)) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN))
     if ((e = launch_scan(ws, BH, plan.nseg - 1, CF::STATE_FLOATS, st)) != hipSuccess) return e;
   if (!(passes & PASS_SEGMENTS)) return hipSuccess;
-  auto kf = chunked_bf16_kernel<P, DV, C>;
+  auto kf = chunked_bf16_kernel<P, DV, C, S2>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), CF::LDS, st>>>(a);

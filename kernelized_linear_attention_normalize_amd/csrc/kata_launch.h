@@ -56,6 +56,11 @@ hipError_t launch_family_decode(const void* q, const void* k, const void* v, boo
 hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
                                  const SegPlan& plan, float* ws, float* s_out, float* z_out, hipStream_t st);
+// bf16 MFMA chunked forward of KATA-Sigma 2 at p = 64 (dv in {32, 64}, C in {64, 128}); plan
+// over the 2T virtual rows (two 32-component blocks per token)
+hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                      bool o_bf16, int B, int H, int T, int dv, int C, const SegPlan& plan,
+                                      float* ws, float* s_out, float* z_out, hipStream_t st);
 // bf16 MFMA quadratic form for the reduced families with 32-component blocks
 bool quadratic_bf16_family_supported(int p, int dv, int fam, int g);
 hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,

@@ -43,6 +43,20 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, nm), nm
 
 
+def test_no_unresolved_library_symbols():
+    """Every kata symbol the library references is defined in it (a template declared in one
+    translation unit and instantiated in another under a different signature would only
+    fail when the loader binds it)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", kata.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    assert "kata" not in out, [l for l in out.splitlines() if "kata" in l]
+
+
 def test_packed_dim_and_status_strings(lib):
     assert lib.kata_packed_dim(32) == 528 and lib.kata_packed_dim(64) == 2080
     assert lib.kata_packed_dim(0) == -1

@@ -73,6 +73,47 @@ def test_family_chunked_many_segments_and_state():
         assert row_rel_err(to_np(got), ref[:, :, t]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dv,C,T", [(64, 128, 700), (32, 64, 1000), (64, 64, 333), (32, 128, 129)])
+def test_sigma2_p64_mfma_chunked(dv, C, T):
+    """KATA-Sigma 2 at p = 64 with bf16 inputs: the MFMA kernels over 2T virtual rows (two
+    32-component blocks per token, the key norm over both, token-level causality, the two
+    virtual query rows of a token summed before the division); both scans, ragged T."""
+    q, k, v = _case("sigma2-mfma", 46, 2, 3, T, 64, dv, "bf16")
+    q[0, 2, 4] = 0.0
+    k[1, 1, :2] = 0.0
+    k[0, 0, 7, 32:] = 0.0  # one block of a key zero: the other block still counts
+    ref = kf.naive_family(q, k, v, "sigma", 2)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    for scan in ("sequential", "associative"):
+        for odt in (torch.float32, torch.bfloat16):
+            got = to_np(kata.chunked_fwd(qd, kd, vd, C=C, scan=scan, out_dtype=odt, family="sigma", g=2))
+            err = row_rel_err(got, ref)
+            print(f"  scan={scan} out={odt} rel_err={err:.3e}", flush=True)
+            assert err <= TOL["bf16"]
+
+
+def test_sigma2_p64_mfma_many_segments_and_state():
+    """Many segments, the final Sigma 2 state from the MFMA kernels, decoding on from it."""
+    T0, steps = 5000, 4
+    q, k, v = _case("sigma2-mfma-state", 47, 1, 2, T0 + steps, 64, 64, "bf16")
+    ref = kf.naive_family(q, k, v, "sigma", 2)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    pre = lambda x: x[:, :, :T0].contiguous()
+    o, S, Z = kata.chunked_fwd(pre(qd), pre(kd), pre(vd), C=128, scan="associative", out_dtype=torch.float32,
+                               return_state=True, family="sigma", g=2)
+    assert row_rel_err(to_np(o), ref[:, :, :T0]) <= TOL["bf16"]
+    S_ref, Z_ref = kf.prefill_state_family(k[:, :, :T0], v[:, :, :T0], "sigma", 2)
+    nw = lambda g_, r_: float(np.max(np.sqrt(((g_ - r_) ** 2).sum(axis=tuple(range(2, r_.ndim))))
+                                     / np.sqrt((r_ ** 2).sum(axis=tuple(range(2, r_.ndim))))))
+    es, ez = nw(to_np(S), S_ref), nw(to_np(Z), Z_ref)
+    print(f"  state rel err S={es:.2e} Z={ez:.2e}", flush=True)
+    assert es <= 1e-2 and ez <= 1e-2
+    for t in range(T0, T0 + steps):
+        st = lambda x: x[:, :, t].contiguous()
+        got = kata.decode_step(st(qd), st(kd), st(vd), S, Z, out_dtype=torch.float32, family="sigma", g=2)
+        assert row_rel_err(to_np(got), ref[:, :, t]) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("family,p,g,dv,T,dt", [
     ("sigma", 64, 2, 64, 700, "bf16"), ("block", 64, 2, 64, 513, "bf16"), ("sigma", 32, 4, 16, 200, "f32"),
     ("block", 16, 2, 32, 65, "f32"), ("sigma", 64, 2, 16, 1100, "bf16"), ("block", 64, 2, 32, 1537, "bf16"),
