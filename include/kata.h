@@ -228,6 +228,22 @@ kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* 
                                       kata_feature_t fam, int g, void* workspace,
                                       size_t workspace_bytes, float* S, float* Z,
                                       kata_stream_t stream);
+/*
+ * kata_chunked_fwd_ragged - kata_chunked_fwd_family over sequences of different lengths in
+ * the padded layout: sequence b uses its first lens[b] tokens of q, k, v ([B, H, T, *] as
+ * above); lens is a device array of B int32 (16-byte aligned), values clamped to [0, T].
+ * Output rows t >= lens[b] are not written (they keep what o held). With S, Z (both or
+ * neither) the state after token lens[b] - 1 of every sequence is written (zero for an
+ * empty sequence). Each sequence's result equals a call on that sequence alone (up to the
+ * fp32 summation order of the segments: the segment plan is that of T). Errors as
+ * kata_chunked_fwd_family; lens NULL is KATA_ERR_NULL when B * H * T > 0.
+ */
+kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int T, int p, int dv, int C, kata_scan_t scan,
+                                      kata_feature_t fam, int g, const int32_t* lens,
+                                      void* workspace, size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream);
 kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
                                         kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
                                         int H, int T, int p, int dv, kata_feature_t fam, int g,

@@ -77,6 +77,8 @@ def load():
     lib.kata_chunked_workspace_bytes_family.restype = SZ
     lib.kata_chunked_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, SZ, P, P, P]
     lib.kata_chunked_fwd_family.restype = I
+    lib.kata_chunked_fwd_ragged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
+    lib.kata_chunked_fwd_ragged.restype = I
     lib.kata_quadratic_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd_family.restype = I
     lib.kata_decode_step_family.argtypes = [P, P, P, I, I, I, P, P, P, I, I, I, I, I, P]
@@ -170,14 +172,17 @@ def _scan_code(scan) -> int:
 
 def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,
                 workspace=None, passes: int = PASS_ALL, return_state: bool = False,
-                family: str = "full", g: int = 1):
+                family: str = "full", g: int = 1, lengths=None):
     """Exact O(T) chunked-state forward. q, k: [B,H,T,p]; v: [B,H,T,dv] -> o [B,H,T,dv].
     passes: subset of the passes to enqueue (PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS);
     running them in separate calls needs the same out and workspace each time.
     return_state: also return the state after the last token, (o, S [B,H,n,dv], Z [B,H,n])
     in float32, the layout decode_step continues from (all passes only).
     family, g: the PSD feature family ("full", "sigma" = KATA-Sigma g, "block" = KATA-M g);
-    the reduced families run all passes in one call."""
+    the reduced families run all passes in one call.
+    lengths: optional int32 device tensor [B]; sequence b then uses its first lengths[b]
+    tokens (padded layout), output rows past it are not written, and the returned state is
+    the one after its last token."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -194,6 +199,25 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if lengths is not None:
+        if passes != PASS_ALL:
+            raise ValueError("ragged sequences run all passes in one call")
+        if lengths.dtype != torch.int32 or tuple(lengths.shape) != (B,):
+            raise ValueError("lengths must be an int32 tensor of shape [B]")
+        _dev(lengths, q)
+        S = Z = None
+        if return_state:
+            n = feature_dim(p, family, g)
+            S = torch.empty((B, H, n, dv), dtype=torch.float32, device=dev)
+            Z = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        with torch.cuda.device(dev):
+            _check(lib.kata_chunked_fwd_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                               out.data_ptr(), _dt(out), B, H, T, p, dv, C, sc, fam, g,
+                                               lengths.data_ptr(), ws_ptr, ws_bytes,
+                                               S.data_ptr() if S is not None else None,
+                                               Z.data_ptr() if Z is not None else None, _stream(dev)),
+                   "kata_chunked_fwd_ragged")
+        return (out, S, Z) if return_state else out
     if family != "full":
         if passes != PASS_ALL:
             raise ValueError("the reduced families run all passes in one call")

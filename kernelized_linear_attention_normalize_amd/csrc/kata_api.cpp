@@ -200,7 +200,8 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
                                   void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
                                   int C, kata_scan_t scan, kata_feature_t fam, int g,
                                   void* workspace, size_t workspace_bytes, int passes,
-                                  bool want_state, float* S, float* Z, kata_stream_t stream) {
+                                  bool want_state, float* S, float* Z, const int32_t* lens,
+                                  kata_stream_t stream) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
@@ -261,19 +262,19 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
     return hip_status(kata::launch_chunked_bf16_sigma2(static_cast<const uint16_t*>(q),
                                                        static_cast<const uint16_t*>(k),
                                                        static_cast<const uint16_t*>(v), o, ob16, B, H, T, dv,
-                                                       C, plan, ws, so, zo, st));
+                                                       C, plan, ws, so, zo, lens, st));
   if (fam != KATA_FEAT_FULL)
     return hip_status(kata::launch_family_chunked(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
-                                                  dv, C, (int)fam, g, plan, ws, so, zo, st));
+                                                  dv, C, (int)fam, g, plan, ws, so, zo, lens, st));
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), o, ob16, B, H, T,
-                                                p, dv, C, plan, ws, so, zo, passes, st));
+                                                p, dv, C, plan, ws, so, zo, lens, passes, st));
   return hip_status(kata::launch_chunked_f32(static_cast<const float*>(q),
                                              static_cast<const float*>(k),
                                              static_cast<const float*>(v), o, ob16, B, H, T, p, dv,
-                                             C, plan, ws, so, zo, passes, st));
+                                             C, plan, ws, so, zo, lens, passes, st));
 }
 
 size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, int C,
@@ -298,7 +299,7 @@ kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes, int passes,
                                       kata_stream_t stream) {
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
-                      workspace_bytes, passes, false, nullptr, nullptr, stream);
+                      workspace_bytes, passes, false, nullptr, nullptr, nullptr, stream);
 }
 
 kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v,
@@ -307,7 +308,7 @@ kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v
                                      void* workspace, size_t workspace_bytes, float* S, float* Z,
                                      kata_stream_t stream) {
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
-                      workspace_bytes, KATA_PASS_ALL, true, S, Z, stream);
+                      workspace_bytes, KATA_PASS_ALL, true, S, Z, nullptr, stream);
 }
 
 kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* v,
@@ -318,7 +319,22 @@ kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* 
                                       kata_stream_t stream) {
   if ((S == nullptr) != (Z == nullptr)) return KATA_ERR_NULL;
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, fam, g, workspace,
-                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, stream);
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, nullptr, stream);
+}
+
+kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int T, int p, int dv, int C, kata_scan_t scan,
+                                      kata_feature_t fam, int g, const int32_t* lens,
+                                      void* workspace, size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream) {
+  if ((S == nullptr) != (Z == nullptr)) return KATA_ERR_NULL;
+  if ((int64_t)B * H > 0 && T > 0) {
+    if (lens == nullptr) return KATA_ERR_NULL;
+    if (!aligned16(lens)) return KATA_ERR_ALIGN;
+  }
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, fam, g, workspace,
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, lens, stream);
 }
 
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,

@@ -294,7 +294,18 @@ struct Args {
   int o_f32;  // output dtype: 1 = fp32, 0 = bf16
   float* s_out;  // final state S [B,H,n,DV] in the decode layout, or null
   float* z_out;  // final state Z [B,H,n], or null
+  const int* lens;  // per-sequence lengths [B] (rows beyond are not used), or null: all T
+  int H;
 };
+
+// rows of sequence bh in use (virtual rows under S2): its length clamped to [0, a.T]
+template <bool S2>
+__device__ __forceinline__ int seq_rows(const Args& a, int64_t bh) {
+  if (a.lens == nullptr) return a.T;
+  const int L = a.lens[bh / a.H];
+  const int64_t r = (int64_t)(L < 0 ? 0 : L) * (S2 ? 2 : 1);
+  return r < a.T ? (int)r : a.T;
+}
 
 
 
@@ -333,7 +344,7 @@ struct Stager {
     qb = a.q + bh * a.T * P;
     kb = a.k + bh * a.T * P;
     vb = a.v + bh * (S2 ? a.T / 2 : a.T) * DV;
-    T = a.T;
+    T = seq_rows<S2>(a, bh);  // rows past the sequence's length read as zero
   }
 
   __device__ __forceinline__ row_t load_piece(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -346,7 +357,7 @@ struct Stager {
   // the chunk's rows t0.. as buffers: rows past T read as zero
   __device__ __forceinline__ void load(int t0) {
     const int tid = threadIdx.x;
-    const uint32_t left = (uint32_t)(T - t0);
+    const uint32_t left = (uint32_t)(t0 < T ? T - t0 : 0);  // a chunk past the end reads zeros
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)t0 * P, left * P * 2);
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * P, left * P * 2);
     const __amdgpu_buffer_rsrc_t rv = S2 ? buf_rsrc(vb + (int64_t)(t0 / 2) * DV, (left / 2) * DV * 2)
@@ -604,7 +615,8 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
-  const int nchunks = (a.T + C - 1) / C;
+  const int Tb = seq_rows<S2>(a, bh);  // this sequence's rows
+  const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
   const int osz = a.o_f32 ? 4 : 2;
@@ -807,7 +819,7 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
       if constexpr (!OWNER) den = pd[TT * 64 + lane];
       if constexpr (S2) den += dpp_f<0xB1>(den);  // the token's other virtual query row (lane ^ 1)
       const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
-      const int orow0 = S2 ? t0 / 2 : t0, orows = S2 ? (a.T - t0) / 2 : a.T - t0;
+      const int orow0 = S2 ? t0 / 2 : t0, orows = S2 ? (Tb - t0) / 2 : Tb - t0;
       const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)orow0 * DV * osz, (uint32_t)orows * DV * osz);
       // rows past T are dropped; under S2 the even lane of a token stores it
       const uint32_t ob = (uint32_t)((S2 ? (16 * TT + ln) >> 1 : 16 * TT + ln) * DV + 4 * lg);
@@ -855,7 +867,8 @@ __device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
   const int lane = threadIdx.x & 63;
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
-  const int nchunks = (a.T + C - 1) / C;
+  const int Tb = seq_rows<S2>(a, bh);  // this sequence's rows
+  const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
 
@@ -953,10 +966,10 @@ hipError_t launch_summary(const Args& a, unsigned nblk, hipStream_t st) {
 template <int P, int DV, int C, bool S2 = false>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                       int B, int H, int T, const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                      int passes, hipStream_t st) {
+                      const int* lens, int passes, hipStream_t st) {
   using CF = Cfg<P, DV, C>;
   const int BH = B * H;
-  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out};
+  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out, lens, H};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     a.nblk_per_bh = plan.nseg - 1;

@@ -30,7 +30,8 @@ template <bool OUT_BF16, int MODE>
 __global__ __launch_bounds__(256) void chunked_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     void* __restrict__ o, int T, int p, int dv, int C, int nseg, int cps, int nblk_per_bh,
-    float* __restrict__ ws, float* __restrict__ s_out, float* __restrict__ z_out) {
+    float* __restrict__ ws, float* __restrict__ s_out, float* __restrict__ z_out,
+    const int* __restrict__ lens, int H) {
   extern __shared__ float sm[];
   const int n = p * (p + 1) / 2;
   float* Ss = sm;
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / nblk_per_bh;
   const int seg = blockIdx.x % nblk_per_bh;
-  const int nchunks = (T + C - 1) / C;
+  const int Tb = lens == nullptr ? T : min(max(lens[bh / H], 0), T);  // this sequence's rows
+  const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * cps, c1 = min(nchunks, c0 + cps);
   const int64_t state_floats = (int64_t)n * dv + n;
 
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
 
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
-    const int L = min(C, T - t0);
+    const int L = min(C, Tb - t0);
     __syncthreads();
     // load + normalise rows: thread r < C handles q row r, C <= r < 2C handles k row r-C
     for (int r = tid; r < 2 * C; r += 256) {
@@ -152,7 +154,8 @@ hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st)
 
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, float* s_out, float* z_out, int passes, hipStream_t st) {
+                              float* ws, float* s_out, float* z_out, const int* lens, int passes,
+                              hipStream_t st) {
   const int BH = B * H;
   const size_t lds = f32_chunked_lds_bytes(p, dv, C);
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
@@ -160,7 +163,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
-        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr);
+        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr, lens, H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN)) {
@@ -172,7 +175,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   kfn<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, plan.nseg,
-                                                              plan.cps, plan.nseg, ws, s_out, z_out);
+                                                              plan.cps, plan.nseg, ws, s_out, z_out, lens, H);
   return hipGetLastError();
 }
 

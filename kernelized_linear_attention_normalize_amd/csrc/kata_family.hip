@@ -203,7 +203,8 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
                                                              int T, int p, int dv, int C, Feat F, int nseg,
                                                              int cps, int nblk_per_bh, float* __restrict__ ws,
                                                              int64_t state_floats, float* __restrict__ s_out,
-                                                             float* __restrict__ z_out) {
+                                                             float* __restrict__ z_out, const int* __restrict__ lens,
+                                                             int H) {
   extern __shared__ float sm[];
   const int n = F.n;
   float* Ss = sm;
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / nblk_per_bh;
   const int seg = blockIdx.x % nblk_per_bh;
-  const int nchunks = (T + C - 1) / C;
+  const int Tb = lens == nullptr ? T : min(max(lens[bh / H], 0), T);  // this sequence's rows
+  const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * cps, c1 = min(nchunks, c0 + cps);
 
   for (int f = tid; f < n; f += 256) tab[f] = pair_entry(F, f);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
   }
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
-    const int L = min(C, T - t0);
+    const int L = min(C, Tb - t0);
     __syncthreads();
     for (int r = tid; r < 2 * C; r += 256) {  // rows r < C: queries, C <= r < 2C: keys
       const bool isq = r < C;
@@ -287,7 +289,7 @@ template <bool IN_BF16>
 static hipError_t launch_family_chunked_t(const void* q, const void* k, const void* v, void* o, bool o_bf16,
                                           int B, int H, int T, int p, int dv, int C, int fam, int g,
                                           const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                                          hipStream_t st) {
+                                          const int* lens, hipStream_t st) {
   const Feat F = make_feat(p, fam, g);
   const int BH = B * H;
   const size_t lds = family_chunked_lds_bytes(p, dv, C, fam, g);
@@ -299,7 +301,7 @@ static hipError_t launch_family_chunked_t(const void* q, const void* k, const vo
       return e;
     ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(q, k, v, nullptr, T, p, dv, C, F, plan.nseg,
                                                                        plan.cps, plan.nseg - 1, ws, sf, nullptr,
-                                                                       nullptr);
+                                                                       nullptr, lens, H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_scan(ws, BH, plan.nseg - 1, sf, st)) != hipSuccess) return e;
   }
@@ -307,16 +309,19 @@ static hipError_t launch_family_chunked_t(const void* q, const void* k, const vo
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, F, plan.nseg, plan.cps,
-                                                              plan.nseg, ws, sf, s_out, z_out);
+                                                              plan.nseg, ws, sf, s_out, z_out, lens, H);
   return hipGetLastError();
 }
 
 hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
-                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, hipStream_t st) {
+                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, const int* lens,
+                                 hipStream_t st) {
   if (in_bf16)
-    return launch_family_chunked_t<true>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out, st);
-  return launch_family_chunked_t<false>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out, st);
+    return launch_family_chunked_t<true>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out,
+                                         lens, st);
+  return launch_family_chunked_t<false>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out,
+                                        lens, st);
 }
 
 // ---------------------------------------------------------------------------- quadratic

@@ -30,16 +30,19 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf
                          float* Z, void* o, bool o_bf16, int N, int H, int p, int dv,
                          hipStream_t st);
 // s_out / z_out (may be null): the state after the last token of every sequence, in the
-// decode layout (S [B,H,n,dv], Z [B,H,n], fp32, packed order), written by pass 3
+// decode layout (S [B,H,n,dv], Z [B,H,n], fp32, packed order), written by pass 3.
+// lens (device, [B], may be null): per-sequence lengths; rows t >= lens[b] are not used and
+// their outputs are not written (the segment plan is that of T).
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, float* s_out, float* z_out, int passes, hipStream_t st);
+                              float* ws, float* s_out, float* z_out, const int* lens, int passes,
+                              hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
                                const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                               int passes, hipStream_t st);
+                               const int* lens, int passes, hipStream_t st);
 // n float zeros at p (a fill kernel, so the call is safe under graph capture)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
@@ -55,12 +58,13 @@ hipError_t launch_family_decode(const void* q, const void* k, const void* v, boo
                                 hipStream_t st);
 hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
-                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, hipStream_t st);
+                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, const int* lens,
+                                 hipStream_t st);
 // bf16 MFMA chunked forward of KATA-Sigma 2 at p = 64 (dv in {32, 64}, C in {64, 128}); plan
 // over the 2T virtual rows (two 32-component blocks per token)
 hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                       bool o_bf16, int B, int H, int T, int dv, int C, const SegPlan& plan,
-                                      float* ws, float* s_out, float* z_out, hipStream_t st);
+                                      float* ws, float* s_out, float* z_out, const int* lens, hipStream_t st);
 // bf16 MFMA quadratic form for the reduced families with 32-component blocks
 bool quadratic_bf16_family_supported(int p, int dv, int fam, int g);
 hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
