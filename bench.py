@@ -156,7 +156,7 @@ def main():
         step = [lambda m=m: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws,
                                              passes=m) for m in passes]
         dominant = 2  # the segment pass
-        kernel_name = f"chunked_bf16_kernel<{p}, {dv}, {C}>"
+        kernel_name = f"chunked_bf16_kernel<{p}, {dv}, {C}, false>"
         n = p * (p + 1) // 2
         flops = chunked_flops_per_head_token(n, p, dv, C) * B * H * T
         units = B * T
