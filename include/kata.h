@@ -253,6 +253,27 @@ kata_status_t kata_decode_step_family(const void* q, const void* k, const void* 
                                       float* Z, void* o, kata_dtype_t o_dt, int N, int H, int p,
                                       int dv, kata_stream_t stream);
 
+/*
+ * kata_quadratic_bwd - gradients of the causal forward (any feature family) with respect to
+ * q, k and v, given grad_o = dL/do. The pages describe no backward pass; this is the calculus
+ * of the forward they define (normalized readout, the family's weights, the projection onto
+ * the unit sphere): with D_t = sum_{s<=t} w_ts and delta_t = grad_o_t . o_t,
+ *   dv_s = sum_{t>=s} (w_ts / D_t) grad_o_t,  dw_ts = (grad_o_t . v_s - delta_t) / D_t,
+ *   and dw_ts through the block dot products and the normalisation to dq and dk (zero rows
+ *   and rows with D_t = 0 get zero gradients).
+ *   q, k : [B, H, T, p] and v, grad_o : [B, H, T, dv] in in_dt; dq, dk : [B, H, T, p] and
+ *   dv_out : [B, H, T, dv] float32, written. workspace: at least
+ *   kata_quadratic_bwd_workspace_bytes(B, H, T) bytes (D_t and delta_t per row).
+ *   Flash-style O(T^2) VALU kernels (a reference for training, not a tuned kernel).
+ *   Supported: p <= 64, dv <= 64, at most 16 block pairs (Sigma g: g <= 4). Outputs must not
+ *   overlap each other, the inputs or the workspace.
+ */
+size_t kata_quadratic_bwd_workspace_bytes(int B, int H, int T);
+kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, const void* grad_o,
+                                 kata_dtype_t in_dt, int B, int H, int T, int p, int dv,
+                                 kata_feature_t fam, int g, float* dq, float* dk, float* dv_out,
+                                 void* workspace, size_t workspace_bytes, kata_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

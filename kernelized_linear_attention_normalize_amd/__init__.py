@@ -20,7 +20,7 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -79,6 +79,10 @@ def load():
     lib.kata_chunked_fwd_family.restype = I
     lib.kata_chunked_fwd_ragged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
     lib.kata_chunked_fwd_ragged.restype = I
+    lib.kata_quadratic_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.kata_quadratic_bwd_workspace_bytes.restype = SZ
+    lib.kata_quadratic_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
+    lib.kata_quadratic_bwd.restype = I
     lib.kata_quadratic_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd_family.restype = I
     lib.kata_decode_step_family.argtypes = [P, P, P, I, I, I, P, P, P, I, I, I, I, I, P]
@@ -310,3 +314,53 @@ def decode_step(q, k, v, S, Z, out_dtype=None, out=None, family: str = "full", g
                                                out.data_ptr(), _dt(out), N, H, p, dv, _stream(dev)),
                    "kata_decode_step_family")
     return out
+
+
+def quadratic_bwd(q, k, v, grad_o, family: str = "full", g: int = 1):
+    """Gradients (dq, dk, dv) in float32 of the causal forward with dL/do = grad_o.
+    q, k: [B,H,T,p]; v, grad_o: [B,H,T,dv], in the dtype of q (float32 or bfloat16)."""
+    lib = load()
+    dev = _dev(q, k, v, grad_o)
+    B, H, T, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or grad_o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v and grad_o")
+    if not (k.dtype == v.dtype == grad_o.dtype == q.dtype):
+        raise TypeError("q, k, v and grad_o must share one dtype")
+    dq = torch.empty((B, H, T, p), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dvv = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kata_quadratic_bwd_workspace_bytes(B, H, T))
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_quadratic_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), _dt(q),
+                                      B, H, T, p, dv, _fam(family, g), g, dq.data_ptr(), dk.data_ptr(),
+                                      dvv.data_ptr(), ws.data_ptr(), need, _stream(dev)), "kata_quadratic_bwd")
+    return dq, dk, dvv
+
+
+class _KataAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, C, family, g):
+        ctx.save_for_backward(q, k, v)
+        ctx.family, ctx.g = family, g
+        try:  # the O(T) chunked form where its kernels cover the shape, else the quadratic form
+            return chunked_fwd(q, k, v, C=C, family=family, g=g)
+        except KataError as e:
+            if e.status != 4:  # KATA_ERR_UNSUPPORTED
+                raise
+        return quadratic_fwd(q, k, v, family=family, g=g)
+
+    @staticmethod
+    def backward(ctx, grad_o):
+        q, k, v = ctx.saved_tensors
+        go = grad_o.contiguous().to(q.dtype)
+        dq, dk, dvv = quadratic_bwd(q, k, v, go, family=ctx.family, g=ctx.g)
+        return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
+
+
+def kata_attention(q, k, v, C: int = 64, family: str = "full", g: int = 1):
+    """Differentiable causal KATA attention: the chunked forward (quadratic form where the
+    chunked kernels do not cover the shape) and the gradients of kata_quadratic_bwd."""
+    return _KataAttention.apply(q, k, v, C, family, g)
+

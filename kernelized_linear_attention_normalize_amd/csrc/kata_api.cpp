@@ -440,4 +440,42 @@ kata_status_t kata_decode_step_family(const void* q, const void* k, const void* 
   return decode_impl(q, k, v, in_dt, fam, g, S, Z, o, o_dt, N, H, p, dv, stream);
 }
 
+size_t kata_quadratic_bwd_workspace_bytes(int B, int H, int T) {
+  if (B <= 0 || H <= 0 || T <= 0) return 0;
+  return (size_t)B * H * T * 2 * sizeof(float);
+}
+
+kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, const void* grad_o,
+                                 kata_dtype_t in_dt, int B, int H, int T, int p, int dv,
+                                 kata_feature_t fam, int g, float* dq, float* dk, float* dv_out,
+                                 void* workspace, size_t workspace_bytes, kata_stream_t stream) {
+  if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
+  if (B < 0 || H < 0 || T < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
+  kata_status_t s = check_feature(p, fam, g);
+  if (s != KATA_OK) return s;
+  if (p > 64 || dv > 64 || kata::bwd_pairs(p, (int)fam, g) > 16) return KATA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * T == 0) return KATA_OK;
+  if (mul4(B, H, T, p > dv ? p : dv) < 0 || (int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
+  for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
+    if (!aligned16(ptr)) return KATA_ERR_ALIGN;
+  const size_t need = kata_quadratic_bwd_workspace_bytes(B, H, T);
+  if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KATA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * T;
+  const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
+  const void* outs[4] = {dq, dk, dv_out, workspace};
+  const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], q, qb) || overlap(outs[i], outb[i], k, qb) || overlap(outs[i], outb[i], v, vb) ||
+        overlap(outs[i], outb[i], grad_o, vb))
+      return KATA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
+  }
+  return hip_status(kata::launch_quadratic_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, T, p, dv,
+                                               (int)fam, g, static_cast<float*>(workspace), dq, dk, dv_out,
+                                               (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -65,6 +65,11 @@ hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bo
 hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                       bool o_bf16, int B, int H, int T, int dv, int C, const SegPlan& plan,
                                       float* ws, float* s_out, float* z_out, const int* lens, hipStream_t st);
+// gradients of the quadratic form (VALU): ws holds 2 floats (D_t, g_t . o_t) per row
+int bwd_pairs(int p, int fam, int g);
+hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
+                                int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
+                                float* dvo, hipStream_t st);
 // bf16 MFMA quadratic form for the reduced families with 32-component blocks
 bool quadratic_bf16_family_supported(int p, int dv, int fam, int g);
 hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,

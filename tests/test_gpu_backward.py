@@ -1,0 +1,66 @@
+"""Gradients of the causal forward on the GPU (kata_quadratic_bwd, through the C ABI and the
+autograd wrapper) against the float64 backward oracle (oracle/kata_backward.py).
+
+Bar: normwise ||g_gpu - g_ref|| / ||g_ref|| <= 2e-4 per gradient tensor (fp32 arithmetic on
+fp32 or exact bf16 inputs; the oracle gets the same input values)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import kernelized_linear_attention_normalize_amd as kata
+from kata_inputs import draw_qkv
+from oracle import kata_backward as kb
+from tests.gpu_util import to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _rel(got, ref, floor):
+    """Normwise error relative to the reference, or to `floor` where the exact gradient is
+    (near) zero (e.g. dq at T = 1: o_1 = v_1 for every q)."""
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), floor))
+
+
+@pytest.mark.parametrize("dt,family,g,p,dv,T", [
+    ("f32", "full", 1, 16, 16, 33), ("f32", "full", 1, 32, 64, 257), ("bf16", "full", 1, 64, 48, 200),
+    ("f32", "sigma", 2, 32, 32, 100), ("bf16", "block", 2, 64, 64, 130),
+    ("f32", "sigma", 4, 64, 16, 70)])
+def test_quadratic_bwd_matches_oracle(dt, family, g, p, dv, T):
+    print(f"[case] bwd {dt} {family}{g} p={p} dv={dv} T={T}", flush=True)
+    q, k, v = draw_qkv(49, 2, 2, T, p, dv, dt)
+    go = draw_qkv(50, 2, 2, T, dv, dv, dt)[0]
+    q[0, 1, 0] = 0.0
+    k[1, 0, T // 2] = 0.0
+    ref = kb.backward(q, k, v, go, family, g)
+    got = kata.quadratic_bwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(go, dt), family=family, g=g)
+    floor = 1e-2 * float(np.linalg.norm(go))
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        e = _rel(to_np(a), r, floor)
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 2e-4, name
+    assert np.all(to_np(got[0])[0, 1, 0] == 0.0)
+
+
+def test_single_token():
+    """T = 1: o_1 = v_1 whatever q and k, so dv = grad_o and the exact dq, dk vanish (their
+    fp32 values are rounding noise amplified by 1 / (q_hat . k_hat), so only finiteness is
+    checked for them)."""
+    q, k, v = draw_qkv(53, 2, 3, 1, 32, 64, "bf16")
+    go = draw_qkv(54, 2, 3, 1, 64, 64, "bf16")[0]
+    dq, dk, dvv = kata.quadratic_bwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(go, "bf16"))
+    np.testing.assert_allclose(to_np(dvv), go, rtol=1e-6, atol=1e-6)
+    assert np.all(np.isfinite(to_np(dq))) and np.all(np.isfinite(to_np(dk)))
+
+
+def test_autograd_wrapper():
+    """kata_attention: chunked forward, gradients from kata_quadratic_bwd through autograd."""
+    q, k, v = draw_qkv(51, 1, 2, 300, 32, 64, "f32")
+    go = draw_qkv(52, 1, 2, 300, 64, 64, "f32")[0]
+    qd, kd, vd = (to_dev(x, "f32").requires_grad_(True) for x in (q, k, v))
+    o = kata.kata_attention(qd, kd, vd, C=64)
+    (o * to_dev(go, "f32")).sum().backward()
+    ref = kb.backward(q, k, v, go)
+    for name, t, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
+        assert _rel(to_np(t), r, 1e-2 * float(np.linalg.norm(go))) <= 2e-4, name
