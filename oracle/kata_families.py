@@ -1,4 +1,5 @@
-"""Plain float64 oracle of the reduced PSD feature families KATA-Sigma g and KATA-M g.
+"""Plain float64 oracle of the reduced PSD feature families KATA-Sigma g and KATA-M g, and of
+the higher even-order lifts psi_2r (bottom of the file).
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/`` (and nothing on the product path).
 Imports numpy and the full-map oracle's normalisation and packing helpers only.
@@ -35,7 +36,8 @@ from oracle.kata_oracle import _divide_rows, normalize, packed_dim, packed_pairs
 FAMILIES = ("full", "sigma", "block")
 
 __all__ = ["FAMILIES", "family_dim", "lift_family", "weights_family", "naive_family",
-           "recurrent_family", "prefill_state_family", "decode_steps_family"]
+           "recurrent_family", "prefill_state_family", "decode_steps_family", "order_dim",
+           "order_multisets", "lift_order", "naive_order"]
 
 
 def _check(p: int, family: str, g: int) -> int:
@@ -143,3 +145,60 @@ def decode_steps_family(S0, Z0, q, k, v, family: str, g: int = 1):
         den = np.einsum("...f,...f->...", fq[st], Z)
         outs[st] = _divide_rows(num, den)
     return outs, S, Z
+
+
+# ------------------------------------------------------------------ higher even orders
+# Source: arXiv HTML page, paragraph after the spherical-code discussion (display of
+# psi_2r): the same p-dimensional projection generates psi_2r(u) = u^{(x) 2r}, with
+# <psi_2r(u), psi_2r(v)> = (u . v)^{2r} >= 0 and symmetric ambient dimension
+# binom(p + 2r - 1, 2r); the pages use r = 1.
+# Reading (listed in the design doc): the symmetric tensor is packed over multisets
+# i_1 <= ... <= i_2r in lexicographic order, coordinate sqrt(multinomial) * prod u_i, so the
+# packed Euclidean inner product is the tensor one (r = 1: the full map's packing).
+
+def order_dim(p: int, r: int) -> int:
+    """binom(p + 2r - 1, 2r) packed coordinates of u^{(x) 2r}."""
+    if p < 1 or r < 1:
+        raise ValueError("p and r must be >= 1")
+    return math.comb(p + 2 * r - 1, 2 * r)
+
+
+def order_multisets(p: int, r: int) -> list[tuple[int, ...]]:
+    """Multisets of size 2r over range(p) in lexicographic order."""
+    out = []
+
+    def rec(start, prefix):
+        if len(prefix) == 2 * r:
+            out.append(tuple(prefix))
+            return
+        for i in range(start, p):
+            rec(i, prefix + [i])
+    rec(0, [])
+    return out
+
+
+def lift_order(u: np.ndarray, r: int) -> np.ndarray:
+    """Packed psi_2r of the unit-normalised rows of u: [..., p] -> [..., binom(p+2r-1, 2r)]."""
+    uh = normalize(u)
+    p = uh.shape[-1]
+    cols = []
+    for ms in order_multisets(p, r):
+        counts = np.bincount(np.asarray(ms), minlength=p)
+        coef = math.factorial(2 * r)
+        for c in counts:
+            coef //= math.factorial(int(c))
+        val = np.ones(uh.shape[:-1])
+        for i in ms:
+            val = val * uh[..., i]
+        cols.append(math.sqrt(coef) * val)
+    return np.stack(cols, axis=-1)
+
+
+def naive_order(q: np.ndarray, k: np.ndarray, v: np.ndarray, r: int) -> np.ndarray:
+    """Causal output with weights (q_hat_t . k_hat_s)^{2r}, by the definition, O(T^2)."""
+    qh, kh = normalize(q), normalize(k)
+    v = np.asarray(v, dtype=np.float64)
+    T = qh.shape[-2]
+    a = qh @ np.swapaxes(kh, -1, -2)
+    w = np.where(np.tril(np.ones((T, T), dtype=bool)), a ** (2 * r), 0.0)
+    return _divide_rows(w @ v, w.sum(axis=-1))

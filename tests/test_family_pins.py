@@ -138,3 +138,35 @@ def test_weights_nonnegative_and_outputs_in_hull():
         o = kf.naive_family(q, k, v, fam, g)
         for t in range(40):
             assert (o[t] >= v[: t + 1].min(0) - 1e-12).all() and (o[t] <= v[: t + 1].max(0) + 1e-12).all()
+
+
+# ------------------------------------------------------------------ higher even orders
+def test_order_dims_and_r1_is_the_full_map():
+    # binom(p + 2r - 1, 2r): by hand, p=4 r=2 -> binom(7, 4) = 35; p=16 r=2 -> 3876
+    assert kf.order_dim(4, 2) == 35 and kf.order_dim(16, 2) == 3876 and kf.order_dim(3, 3) == 28
+    assert kf.order_dim(64, 1) == 2080
+    u = RNG.standard_normal((6, 9))
+    np.testing.assert_array_equal(kf.lift_order(u, 1), ko.lift(u))
+
+
+def test_order_worked_example_p2_r2():
+    """u = (a, b) on the circle: psi_4 = (a^4, 2a^3 b, sqrt(6) a^2 b^2, 2 a b^3, b^4) (the
+    multinomial coefficients 1, 4, 6, 4, 1 under square roots)."""
+    a, b = 0.6, 0.8
+    want = [a ** 4, 2 * a ** 3 * b, math.sqrt(6) * a ** 2 * b ** 2, 2 * a * b ** 3, b ** 4]
+    np.testing.assert_allclose(kf.lift_order(np.array([a, b]), 2), want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("p,r", [(3, 2), (4, 2), (5, 3), (2, 4)])
+def test_order_identities(p, r):
+    """||psi_2r(u_hat)|| = 1 and <psi_2r(u), psi_2r(v)> = (u_hat . v_hat)^{2r}; the weights of
+    the naive form equal the packed inner products."""
+    u, v = RNG.standard_normal((7, p)), RNG.standard_normal((5, p))
+    fu, fv = kf.lift_order(u, r), kf.lift_order(v, r)
+    np.testing.assert_allclose(np.linalg.norm(fu, axis=-1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(fu @ fv.T, (ko.normalize(u) @ ko.normalize(v).T) ** (2 * r), rtol=1e-12, atol=1e-15)
+    q, k, vv = RNG.standard_normal((12, p)), RNG.standard_normal((12, p)), RNG.standard_normal((12, 2))
+    fq, fk = kf.lift_order(q, r), kf.lift_order(k, r)
+    w = np.tril(fq @ fk.T)
+    ref = (w @ vv) / w.sum(axis=-1, keepdims=True)
+    np.testing.assert_allclose(kf.naive_order(q, k, vv, r), ref, rtol=1e-11)
