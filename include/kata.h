@@ -254,6 +254,26 @@ kata_status_t kata_decode_step_family(const void* q, const void* k, const void* 
                                       int dv, kata_stream_t stream);
 
 /*
+ * Higher even-order lifts (HTML page, psi_2r display): psi_2r(u) = u_hat^(x 2r), packed over
+ * the multisets i_1 <= ... <= i_2r of range(p) in lexicographic order with coordinate
+ * sqrt((2r)! / prod multiplicity!) prod u_hat_i, so <psi_2r(q), psi_2r(k)> = (q_hat . k_hat)^(2r)
+ * (r = 1: the rank-one lift above). The state binom(p + 2r - 1, 2r) x dv outgrows chip memory
+ * already at r = 2 (the pages use r = 1), so the higher orders come as the lift and the
+ * stateless quadratic form only.
+ *   kata_order_dim: binom(p + 2r - 1, 2r); -1 if p < 1 or r outside 1..4 (or it overflows).
+ *   kata_lift_order: as kata_lift with n = kata_order_dim(p, r); 1 <= p <= 128, r <= 4.
+ *   kata_quadratic_fwd_order: as kata_quadratic_fwd with weights (q_hat . k_hat)^(2r);
+ *   r = 1 is kata_quadratic_fwd; bf16 inputs with r = 2 and (p, dv) of the full map run the
+ *   MFMA kernel, the rest a VALU kernel (p <= 64, dv <= 64). KATA_ERR_FEATURE for r outside 1..4.
+ */
+int64_t kata_order_dim(int p, int r);
+kata_status_t kata_lift_order(const void* u, kata_dtype_t u_dt, int64_t rows, int p, int r, void* psi,
+                              kata_dtype_t psi_dt, kata_stream_t stream);
+kata_status_t kata_quadratic_fwd_order(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                       void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv, int r,
+                                       kata_stream_t stream);
+
+/*
  * kata_quadratic_bwd - gradients of the causal forward (any feature family) with respect to
  * q, k and v, given grad_o = dL/do. The pages describe no backward pass; this is the calculus
  * of the forward they define (normalized readout, the family's weights, the projection onto

@@ -20,7 +20,7 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -79,6 +79,10 @@ def load():
     lib.kata_chunked_fwd_family.restype = I
     lib.kata_chunked_fwd_ragged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
     lib.kata_chunked_fwd_ragged.restype = I
+    lib.kata_order_dim.argtypes, lib.kata_order_dim.restype = [I, I], I64
+    lib.kata_lift_order.argtypes, lib.kata_lift_order.restype = [P, I, I64, I, I, P, I, P], I
+    lib.kata_quadratic_fwd_order.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P]
+    lib.kata_quadratic_fwd_order.restype = I
     lib.kata_quadratic_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.kata_quadratic_bwd_workspace_bytes.restype = SZ
     lib.kata_quadratic_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
@@ -138,14 +142,30 @@ def feature_dim(p: int, family: str = "full", g: int = 1) -> int:
     return n
 
 
+def order_dim(p: int, r: int) -> int:
+    """binom(p + 2r - 1, 2r): packed width of the even-order lift psi_2r."""
+    n = int(load().kata_order_dim(p, r))
+    if n < 0:
+        raise ValueError(f"invalid order r={r} for p={p}")
+    return n
+
+
 def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None, family: str = "full",
-         g: int = 1) -> torch.Tensor:
-    """[..., p] -> [..., n]: packed psi(u_hat) (rank-one lift, after Eq. (8)), or the
-    family's map (reduced PSD families paragraph)."""
+         g: int = 1, order: int = 1) -> torch.Tensor:
+    """[..., p] -> [..., n]: packed psi(u_hat) (rank-one lift, after Eq. (8)), the family's map
+    (reduced PSD families paragraph), or with order = r > 1 the even-order lift psi_2r."""
     lib = load()
     dev = _dev(u)
     p = u.shape[-1]
     rows = u.numel() // p if p else 0
+    if order != 1:
+        if family != "full":
+            raise ValueError("higher orders apply to the full map")
+        out = torch.empty(u.shape[:-1] + (order_dim(p, order),), dtype=out_dtype or u.dtype, device=dev)
+        with torch.cuda.device(dev):
+            _check(lib.kata_lift_order(u.data_ptr(), _dt(u), rows, p, order, out.data_ptr(), _dt(out),
+                                       _stream(dev)), "kata_lift_order")
+        return out
     out = torch.empty(u.shape[:-1] + (feature_dim(p, family, g),), dtype=out_dtype or u.dtype, device=dev)
     with torch.cuda.device(dev):
         if family == "full":
@@ -262,9 +282,10 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
     return out
 
 
-def quadratic_fwd(q, k, v, out_dtype=None, out=None, family: str = "full", g: int = 1):
+def quadratic_fwd(q, k, v, out_dtype=None, out=None, family: str = "full", g: int = 1, order: int = 1):
     """Flash-style quadratic forward (no state). q, k: [B,H,T,p]; v: [B,H,T,dv].
-    family, g: the PSD feature family of the weights (see chunked_fwd)."""
+    family, g: the PSD feature family of the weights (see chunked_fwd); order = r > 1:
+    weights (q_hat . k_hat)^(2r) of the even-order lift psi_2r (full map)."""
     lib = load()
     dev = _dev(q, k, v)
     B, H, T, p = q.shape
@@ -275,7 +296,13 @@ def quadratic_fwd(q, k, v, out_dtype=None, out=None, family: str = "full", g: in
         out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
     _dev(out, q)
     with torch.cuda.device(dev):
-        if family == "full":
+        if order != 1:
+            if family != "full":
+                raise ValueError("higher orders apply to the full map")
+            _check(lib.kata_quadratic_fwd_order(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                                out.data_ptr(), _dt(out), B, H, T, p, dv, order, _stream(dev)),
+                   "kata_quadratic_fwd_order")
+        elif family == "full":
             _check(lib.kata_quadratic_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
                                           out.data_ptr(), _dt(out), B, H, T, p, dv, _stream(dev)),
                    "kata_quadratic_fwd")

@@ -478,4 +478,53 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                                (hipStream_t)stream));
 }
 
+int64_t kata_order_dim(int p, int r) {
+  if (p < 1 || r < 1 || r > 4) return -1;
+  double c = 1.0;  // binom(p + 2r - 1, 2r)
+  for (int i = 1; i <= 2 * r; ++i) c = c * (p + 2 * r - i) / i;
+  if (c > 9.0e15) return -1;
+  return (int64_t)(c + 0.5);
+}
+
+kata_status_t kata_lift_order(const void* u, kata_dtype_t u_dt, int64_t rows, int p, int r, void* psi,
+                              kata_dtype_t psi_dt, kata_stream_t stream) {
+  if (!valid_dt(u_dt) || !valid_dt(psi_dt)) return KATA_ERR_DTYPE;
+  if (rows < 0 || p < 1) return KATA_ERR_SHAPE;
+  if (r < 1 || r > 4) return KATA_ERR_FEATURE;
+  if (r == 1) return kata_lift(u, u_dt, rows, p, psi, psi_dt, stream);
+  if (p > 128) return KATA_ERR_UNSUPPORTED;
+  if (rows == 0) return KATA_OK;
+  const int64_t n = kata_order_dim(p, r);
+  if (n < 0 || n > (int64_t)256 * 65535 || mul4(rows, n, 1, 1) < 0 || (rows + 15) / 16 > 65535)
+    return KATA_ERR_SHAPE;
+  if (!u || !psi) return KATA_ERR_NULL;
+  if (!aligned16(u) || !aligned16(psi)) return KATA_ERR_ALIGN;
+  if (overlap(u, rows * p * dt_size(u_dt), psi, rows * n * dt_size(psi_dt))) return KATA_ERR_ALIAS;
+  return hip_status(kata::launch_order_lift(u, u_dt == KATA_DTYPE_BF16, rows, p, r, n, psi,
+                                            psi_dt == KATA_DTYPE_BF16, (hipStream_t)stream));
+}
+
+kata_status_t kata_quadratic_fwd_order(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                       void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv, int r,
+                                       kata_stream_t stream) {
+  if (r == 1) return kata_quadratic_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, stream);
+  bool zero = false;
+  kata_status_t s = check_fwd(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, zero);
+  if (s != KATA_OK) return s;
+  if (r < 1 || r > 4) return KATA_ERR_FEATURE;
+  if (zero) return KATA_OK;
+  if (p > 64 || dv > 64) return KATA_ERR_UNSUPPORTED;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
+  if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
+  const bool ob16 = o_dt == KATA_DTYPE_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  if (in_dt == KATA_DTYPE_BF16 && r == 2 && in_set(p, {16, 32, 64}) && in_set(dv, {16, 32, 64}))
+    return hip_status(kata::launch_quadratic_bf16_order2(static_cast<const uint16_t*>(q),
+                                                         static_cast<const uint16_t*>(k),
+                                                         static_cast<const uint16_t*>(v), o, ob16, B, H, T, p,
+                                                         dv, st));
+  return hip_status(kata::launch_family_quadratic(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p, dv, 3, r,
+                                                  st));
+}
+
 }  // extern "C"

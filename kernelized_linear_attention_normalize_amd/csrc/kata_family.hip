@@ -22,6 +22,7 @@ namespace {
 struct Feat {
   int sigma;  // 1: Sigma g, 0: M g
   int g, m, nb, n;  // blocks, block width, packed coordinates per block, total coordinates
+  int order;  // r of the weight's even power (q . k)^(2r) per block pair; 1 for the families
 };
 
 // (i, j) of packed coordinate f of an m x m block (f < m(m+1)/2), as a 16:16 table entry
@@ -50,7 +51,10 @@ __device__ __forceinline__ float feat_weight(const Feat& F, const float* q, cons
       if (!F.sigma && b != a) continue;
       float d = 0.f;
       for (int i = 0; i < F.m; ++i) d += q[a * F.m + i] * k[b * F.m + i];
-      w += d * d;
+      const float d2 = d * d;
+      float x = d2;
+      for (int o = 1; o < F.order; ++o) x *= d2;
+      w += x;
     }
   return w;
 }
@@ -75,6 +79,14 @@ Feat make_feat(int p, int fam, int g) {
   F.m = p / g;
   F.nb = F.m * (F.m + 1) / 2;
   F.n = F.sigma ? F.nb : g * F.nb;
+  F.order = 1;
+  return F;
+}
+
+// the full map with weights (q_hat . k_hat)^(2r): one block, no lift (weight form only)
+Feat make_order(int p, int r) {
+  Feat F = make_feat(p, 2, 1);
+  F.order = r;
   return F;
 }
 
@@ -117,6 +129,75 @@ hipError_t launch_family_lift(const void* u, bool u_bf16, int64_t rows, int p, i
   else if (u_bf16) family_lift_kernel<true, false><<<grid, block, 0, st>>>(u, rows, p, F, psi);
   else if (psi_bf16) family_lift_kernel<false, true><<<grid, block, 0, st>>>(u, rows, p, F, psi);
   else family_lift_kernel<false, false><<<grid, block, 0, st>>>(u, rows, p, F, psi);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- psi_2r lift
+// Coordinate f <-> the f-th multiset i_1 <= ... <= i_2r of range(p) in lexicographic order,
+// value sqrt((2r)! / prod mult!) prod u_hat_i (arXiv HTML page, psi_2r display: the packed
+// inner product is (u . v)^(2r)).
+
+// number of multisets of size len over {lo, ..., p-1}: binom(p - lo + len - 1, len)
+__device__ __forceinline__ double n_multisets(int p, int lo, int len) {
+  const int nn = p - lo;
+  if (len == 0) return 1.0;
+  if (nn <= 0) return 0.0;
+  double c = 1.0;
+  for (int i = 1; i <= len; ++i) c = c * (nn + len - i) / i;
+  return c;
+}
+
+template <bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(256) void order_lift_kernel(const void* __restrict__ u, int64_t rows, int p, int r,
+                                                         int64_t n, void* __restrict__ psi) {
+  __shared__ float uh[FL_ROWS][FL_MAXP];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * FL_ROWS;
+  if (tid < FL_ROWS) load_norm_row<IN_BF16>(u, r0 + tid, r0 + tid < rows, p, uh[tid]);
+  __syncthreads();
+  const int64_t f = (int64_t)blockIdx.x * 256 + tid;
+  if (f >= n) return;
+  // unrank f: choose each element as the smallest value whose block of multisets holds f
+  int idx[8];
+  double rank = (double)f;
+  int lo = 0;
+  for (int pos = 0; pos < 2 * r; ++pos) {
+    int i = lo;
+    for (;; ++i) {
+      const double cnt = n_multisets(p, i, 2 * r - pos - 1);
+      if (rank < cnt || i == p - 1) break;
+      rank -= cnt;
+    }
+    idx[pos] = i;
+    lo = i;
+  }
+  double coef = 1.0;  // (2r)! / prod mult!
+  for (int i = 2; i <= 2 * r; ++i) coef *= i;
+  int run = 1;
+  for (int pos = 1; pos <= 2 * r; ++pos) {
+    if (pos < 2 * r && idx[pos] == idx[pos - 1]) {
+      ++run;
+    } else {
+      for (int i = 2; i <= run; ++i) coef /= i;
+      run = 1;
+    }
+  }
+  const float c = (float)sqrt(coef);
+  const int nrows = (int)min<int64_t>(FL_ROWS, rows - r0);
+  for (int rr = 0; rr < nrows; ++rr) {
+    float val = c;
+    for (int pos = 0; pos < 2 * r; ++pos) val *= uh[rr][idx[pos]];
+    store_from_f32<OUT_BF16>(psi, (r0 + rr) * n + f, val);
+  }
+}
+
+hipError_t launch_order_lift(const void* u, bool u_bf16, int64_t rows, int p, int r, int64_t n, void* psi,
+                             bool psi_bf16, hipStream_t st) {
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)((rows + FL_ROWS - 1) / FL_ROWS)), block(256);
+  if (u_bf16 && psi_bf16) order_lift_kernel<true, true><<<grid, block, 0, st>>>(u, rows, p, r, n, psi);
+  else if (u_bf16) order_lift_kernel<true, false><<<grid, block, 0, st>>>(u, rows, p, r, n, psi);
+  else if (psi_bf16) order_lift_kernel<false, true><<<grid, block, 0, st>>>(u, rows, p, r, n, psi);
+  else order_lift_kernel<false, false><<<grid, block, 0, st>>>(u, rows, p, r, n, psi);
   return hipGetLastError();
 }
 
@@ -377,7 +458,8 @@ __global__ __launch_bounds__(256) void family_quadratic_kernel(const void* __res
 
 hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, bool in_bf16, void* o, bool o_bf16,
                                    int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st) {
-  const Feat F = make_feat(p, fam, g);
+  // fam 3: the full map with weights (q_hat . k_hat)^(2g) (order r = g)
+  const Feat F = fam == 3 ? make_order(p, g) : make_feat(p, fam, g);
   const size_t lds = 4 * ((size_t)FQ_BQ * p + (size_t)FQ_BK * p + (size_t)FQ_BK * dv + FQ_BQ * (FQ_BK + 1));
   dim3 grid((unsigned)((int64_t)((T + FQ_BQ - 1) / FQ_BQ) * B * H)), block(256);
   if (in_bf16 && o_bf16) family_quadratic_kernel<true, true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F);

@@ -70,11 +70,18 @@ int bwd_pairs(int p, int fam, int g);
 hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
                                 int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
                                 float* dvo, hipStream_t st);
+// bf16 MFMA quadratic form with weights (q_hat . k_hat)^4 (psi_4), full map's (p, dv) set
+hipError_t launch_quadratic_bf16_order2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                        bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 // bf16 MFMA quadratic form for the reduced families with 32-component blocks
 bool quadratic_bf16_family_supported(int p, int dv, int fam, int g);
 hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                         bool o_bf16, int B, int H, int T, int p, int dv, int fam, int g,
                                         hipStream_t st);
+// packed psi_2r lift (n = binom(p + 2r - 1, 2r) coordinates per row, VALU)
+hipError_t launch_order_lift(const void* u, bool u_bf16, int64_t rows, int p, int r, int64_t n, void* psi,
+                             bool psi_bf16, hipStream_t st);
+// fam 3 selects the full map with weights (q_hat . k_hat)^(2g)
 hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, bool in_bf16, void* o, bool o_bf16,
                                    int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st);
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,

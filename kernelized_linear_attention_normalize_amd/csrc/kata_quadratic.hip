@@ -52,7 +52,9 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // blocks of P / G components, a whole number of 32-wide k-steps each: the block dot products
 // q_a . k_b come from pairing the k-steps of block b of the keys with those of block a of the
 // queries, and the weight is the sum of their squares (all pairs for Sigma, a = b for M).
-template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1>
+// R (full map only): weights (q_hat . k_hat)^(2R), the inner product of the higher even-order
+// lift psi_2R (psi_2r display of the HTML page); R = 1 is the rank-one map.
+template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1>
 __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v,
@@ -249,7 +251,11 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
           for (int j = 0; j < 8; ++j) {
             const int h = j >> 2, r = j & 3;
             const float s = St[h][qt][r] * (h ? ik1[r] : ik0[r]);
-            w[j] = s * s;
+            const float s2 = s * s;
+            float ww = s2;
+#pragma unroll
+            for (int o = 1; o < R; ++o) ww *= s2;
+            w[j] = ww;
             if (DIAG && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[j] = 0.f;
           }
           const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(w[0], w[1]), pk2(w[2], w[3]), pk2(w[4], w[5]), pk2(w[6], w[7])});
@@ -305,6 +311,29 @@ hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uin
   KATA_QCASE(32, 16) KATA_QCASE(32, 32) KATA_QCASE(32, 64)
   KATA_QCASE(64, 16) KATA_QCASE(64, 32) KATA_QCASE(64, 64)
 #undef KATA_QCASE
+  return hipErrorInvalidValue;
+}
+
+template <int P, int DV, int R>
+static hipError_t launch_quad_order(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
+                                    int BH, int T, hipStream_t st) {
+  const int nqb = (T + quad::BM - 1) / quad::BM;
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
+  if (o_bf16) quadratic_bf16_kernel<P, DV, true, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  else quadratic_bf16_kernel<P, DV, false, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  return hipGetLastError();
+}
+
+// weights (q_hat . k_hat)^4 (r = 2) on the MFMA kernel for the full map's (p, dv) set
+hipError_t launch_quadratic_bf16_order2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                        bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st) {
+  const int BH = B * H;
+#define KATA_QOCASE(PP, DD) \
+  if (p == PP && dv == DD) return launch_quad_order<PP, DD, 2>(q, k, v, o, o_bf16, BH, T, st);
+  KATA_QOCASE(16, 16) KATA_QOCASE(16, 32) KATA_QOCASE(16, 64)
+  KATA_QOCASE(32, 16) KATA_QOCASE(32, 32) KATA_QOCASE(32, 64)
+  KATA_QOCASE(64, 16) KATA_QOCASE(64, 32) KATA_QOCASE(64, 64)
+#undef KATA_QOCASE
   return hipErrorInvalidValue;
 }
 

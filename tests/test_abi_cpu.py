@@ -179,6 +179,19 @@ def test_feature_families(lib):
     assert ch(B=1, H=4, T=65536, scan=ASSOC, o=A + (1 << 34)) == E_WS
 
 
+def test_higher_orders(lib):
+    from oracle import kata_families as kf
+    for p, r in [(4, 2), (16, 2), (3, 3), (8, 4), (64, 1)]:
+        assert lib.kata_order_dim(p, r) == kf.order_dim(p, r)
+    assert lib.kata_order_dim(8, 5) == -1 and lib.kata_order_dim(0, 2) == -1
+    assert lib.kata_lift_order(A, F32, 4, 16, 5, A + (1 << 30), F32, None) == E_FEAT
+    assert lib.kata_lift_order(A, F32, 4, 200, 2, A + (1 << 30), F32, None) == E_UNSUP
+    assert lib.kata_quadratic_fwd_order(A, A + 4096, A + 8192, BF16, A + (1 << 30), BF16, 1, 1, 64, 32, 64, 0,
+                                        None) == E_FEAT
+    assert lib.kata_quadratic_fwd_order(A, A + 4096, A + 8192, BF16, A + (1 << 30), BF16, 1, 1, 64, 128, 64, 2,
+                                        None) == E_UNSUP
+
+
 def test_workspace_bytes(lib):
     # sequential mode and single-segment problems need none
     assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, SEQ, BF16) == 0

@@ -158,3 +158,27 @@ def test_family_full_is_the_full_path():
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     assert torch.equal(kata.chunked_fwd(qd, kd, vd, C=64), kata.chunked_fwd(qd, kd, vd, C=64, family="full"))
     assert torch.equal(kata.quadratic_fwd(qd, kd, vd), kata.quadratic_fwd(qd, kd, vd, family="full", g=1))
+
+
+# ------------------------------------------------------------------ higher even orders
+@pytest.mark.parametrize("p,r", [(4, 2), (16, 2), (5, 3), (3, 4), (8, 1)])
+def test_order_lift(p, r):
+    rng = np.random.default_rng(55)
+    u = rng.standard_normal((21, p)).astype(np.float32)
+    u[2] = 0.0
+    got = to_np(kata.lift(to_dev(u, "f32"), order=r))
+    ref = kf.lift_order(u, r)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=0, atol=5e-6)
+
+
+@pytest.mark.parametrize("p,dv,T,r,dt", [(64, 64, 700, 2, "bf16"), (32, 16, 333, 2, "bf16"), (16, 32, 200, 3, "f32"),
+                                         (64, 64, 130, 4, "bf16"), (32, 32, 65, 2, "f32")])
+def test_order_quadratic(p, dv, T, r, dt):
+    """Weights (q_hat . k_hat)^(2r): bf16 with r = 2 runs the MFMA kernel, the rest VALU."""
+    q, k, v = _case(f"order-quadratic-r{r}", 56, 2, 2, T, p, dv, dt)
+    ref = kf.naive_order(q, k, v, r)
+    got = to_np(kata.quadratic_fwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), out_dtype=torch.float32, order=r))
+    err = row_rel_err(got, ref)
+    print(f"  rel_err={err:.3e}", flush=True)
+    assert err <= TOL[dt]
