@@ -795,6 +795,9 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
            constexpr int t1 = 2 * (PB + PI), t2 = t1 + 1;
            constexpr bool has2 = t2 < CF::NTL;
            if constexpr (PB + PI + 1 < PE) load_pair(PB + PI + 1, fr[(PI + 1) & 1]);
+           // keep the next pair's reads ahead of this pair's work: under register pressure the
+           // scheduler otherwise sinks each read to its MFMA and waits out the LDS latency
+           __builtin_amdgcn_sched_barrier(0);
            const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
 #pragma unroll
            for (int dt = 0; dt < NT; ++dt) O[dt] = mfma(fr[PI & 1][dt], af, O[dt]);  // O^T += S^T psi(Q)^T
