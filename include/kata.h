@@ -244,6 +244,32 @@ kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* 
                                       kata_feature_t fam, int g, const int32_t* lens,
                                       void* workspace, size_t workspace_bytes, float* S, float* Z,
                                       kata_stream_t stream);
+/*
+ * kata_chunked_fwd_varlen - kata_chunked_fwd_family over B sequences packed without padding
+ * in the token-major layout: q, k are [total, H, p] and v, o are [total, H, dv] (row-major;
+ * token cu_seqlens[b] + t of sequence b, head h, is row (cu_seqlens[b] + t) * H + h).
+ * cu_seqlens is a device array of B + 1 int32 (4-byte aligned) with cu_seqlens[0] = 0,
+ * non-decreasing, cu_seqlens[B] <= total; max_len must be at least every length
+ * cu_seqlens[b + 1] - cu_seqlens[b] (longer sequences are cut at max_len). The kernels clamp
+ * offsets to [0, total] and lengths to [0, max_len], so invalid contents give unspecified
+ * results but no access outside the tensors. The workspace is that of the padded call with
+ * T = max_len (kata_chunked_workspace_bytes_family(B, H, max_len, ...)). With S, Z (both or
+ * neither) the state after each sequence's last token is written, [B, H, n, dv] and
+ * [B, H, n] as for kata_chunked_fwd_state (zero for an empty sequence). Rows outside every
+ * sequence are not written. The KATA-Sigma 2 MFMA path takes the padded layout only, so
+ * Sigma 2 at p = 64 runs here on the VALU family kernel where its LDS fits (else
+ * KATA_ERR_UNSUPPORTED). Each sequence's result equals the padded call on that sequence
+ * alone (up to the fp32 summation order of the segments: the plan is that of max_len).
+ * Errors as kata_chunked_fwd_family; KATA_ERR_NULL for cu_seqlens NULL when B * H > 0;
+ * KATA_ERR_SHAPE for negative total / max_len or max_len * H * max(p, dv) * 4 >= 2^31.
+ */
+kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int total, int max_len, int p, int dv, int C,
+                                      kata_scan_t scan, kata_feature_t fam, int g,
+                                      const int32_t* cu_seqlens, void* workspace,
+                                      size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream);
 kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
                                         kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
                                         int H, int T, int p, int dv, kata_feature_t fam, int g,

@@ -20,7 +20,7 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -79,6 +79,8 @@ def load():
     lib.kata_chunked_fwd_family.restype = I
     lib.kata_chunked_fwd_ragged.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
     lib.kata_chunked_fwd_ragged.restype = I
+    lib.kata_chunked_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
+    lib.kata_chunked_fwd_varlen.restype = I
     lib.kata_order_dim.argtypes, lib.kata_order_dim.restype = [I, I], I64
     lib.kata_lift_order.argtypes, lib.kata_lift_order.restype = [P, I, I64, I, I, P, I, P], I
     lib.kata_quadratic_fwd_order.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P]
@@ -180,6 +182,48 @@ def lift(u: torch.Tensor, out_dtype: torch.dtype | None = None, family: str = "f
 def chunked_workspace_bytes(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16):
     return int(load().kata_chunked_workspace_bytes(B, H, T, p, dv, C, int(scan),
                                                    DTYPE_BF16 if in_dtype == torch.bfloat16 else DTYPE_F32))
+
+
+def chunked_fwd_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64, scan="associative", out_dtype=None,
+                       out=None, workspace=None, return_state: bool = False, family: str = "full", g: int = 1):
+    """Chunked forward over B sequences packed without padding (token-major, as in varlen
+    attention): q, k [total, H, p]; v [total, H, dv] -> o [total, H, dv]. cu_seqlens: int32
+    device tensor [B + 1] of sequence offsets (0 first, non-decreasing); max_len >= every
+    length. return_state: also return the state after each sequence's last token,
+    (o, S [B,H,n,dv], Z [B,H,n]) in float32. Rows outside every sequence are not written."""
+    lib = load()
+    dev = _dev(q, k, v)
+    total, H, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2]:
+        raise ValueError("shape mismatch between q, k and v")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
+    _dev(cu_seqlens, q)
+    B = cu_seqlens.numel() - 1
+    sc = _scan_code(scan)
+    if out is None:
+        out = torch.empty((total, H, dv), dtype=out_dtype or v.dtype, device=dev)
+    _dev(out, q)
+    fam = _fam(family, g)
+    need = int(lib.kata_chunked_workspace_bytes_family(B, H, max_len, p, dv, C, sc, _dt(q), fam, g))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    S = Z = None
+    if return_state:
+        n = feature_dim(p, family, g)
+        S = torch.empty((B, H, n, dv), dtype=torch.float32, device=dev)
+        Z = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_chunked_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q), out.data_ptr(),
+                                           _dt(out), B, H, total, max_len, p, dv, C, sc, fam, g,
+                                           cu_seqlens.data_ptr(), ws_ptr, ws_bytes,
+                                           S.data_ptr() if S is not None else None,
+                                           Z.data_ptr() if Z is not None else None, _stream(dev)),
+               "kata_chunked_fwd_varlen")
+    return (out, S, Z) if return_state else out
 
 
 def chunked_workspace_bytes_family(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16,

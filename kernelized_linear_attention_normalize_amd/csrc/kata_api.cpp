@@ -155,10 +155,10 @@ static kata_status_t check_fwd(const void* q, const void* k, const void* v, kata
   return KATA_OK;
 }
 
+// rows: rows of q / k / v / o (B*H*T in the padded layout, total*H in the packed one)
 static kata_status_t check_fwd_alias(const void* q, const void* k, const void* v,
-                                     kata_dtype_t in_dt, const void* o, kata_dtype_t o_dt, int B,
-                                     int H, int T, int p, int dv) {
-  const size_t rows = (size_t)B * H * T;
+                                     kata_dtype_t in_dt, const void* o, kata_dtype_t o_dt, size_t rows,
+                                     int p, int dv) {
   const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
   const size_t ob = rows * dv * dt_size(o_dt);
   if (overlap(o, ob, q, qb) || overlap(o, ob, k, qb) || overlap(o, ob, v, vb)) return KATA_ERR_ALIAS;
@@ -184,9 +184,11 @@ static bool sigma2_mfma(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t
 }
 
 // the chunked forward's supported (p, dv, C) for a family and input dtype
-static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
+// (packed: the packed token-major layout, which the Sigma 2 virtual-row kernels do not take)
+static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g,
+                              bool packed = false) {
   if (!in_set(C, {32, 64, 128})) return false;
-  if (sigma2_mfma(p, dv, C, in_dt, fam, g)) return true;
+  if (!packed && sigma2_mfma(p, dv, C, in_dt, fam, g)) return true;
   if (fam == KATA_FEAT_FULL) {
     if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64})) return false;
     return in_dt == KATA_DTYPE_BF16 || kata::f32_chunked_lds_bytes(p, dv, C) <= 160 * 1024;
@@ -201,7 +203,7 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
                                   int C, kata_scan_t scan, kata_feature_t fam, int g,
                                   void* workspace, size_t workspace_bytes, int passes,
                                   bool want_state, float* S, float* Z, const int32_t* lens,
-                                  kata_stream_t stream) {
+                                  const int32_t* cu, int total, kata_stream_t stream) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
@@ -210,22 +212,25 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   if (s != KATA_OK) return s;
   if ((s = check_feature(p, fam, g)) != KATA_OK) return s;
   if (fam != KATA_FEAT_FULL && passes != KATA_PASS_ALL) return KATA_ERR_PASS;
+  const bool packed = cu != nullptr;
+  // rows of q / k / v / o
+  const size_t rows = packed ? (size_t)total * H : (size_t)B * H * T;
+  if (packed && !zero && total == 0) zero = true;
   if (want_state) {
     if ((int64_t)B * H == 0) return KATA_OK;
-    if (!chunked_supported(p, dv, C, in_dt, fam, g)) return KATA_ERR_UNSUPPORTED;
+    if (!chunked_supported(p, dv, C, in_dt, fam, g, packed)) return KATA_ERR_UNSUPPORTED;
     if (!S || !Z) return KATA_ERR_NULL;
     if (!aligned16(S) || !aligned16(Z)) return KATA_ERR_ALIGN;
     const int64_t n = kata_feature_dim(p, fam, g);
     if (mul4(B, H, n, dv) < 0) return KATA_ERR_SHAPE;
     const size_t Sb = (size_t)B * H * n * dv * 4, Zb = (size_t)B * H * n * 4;
     if (overlap(S, Sb, Z, Zb)) return KATA_ERR_ALIAS;
-    if (T == 0) {  // empty sequences: the zero state
+    if (T == 0 || rows == 0) {  // empty sequences: the zero state
       hipStream_t st = (hipStream_t)stream;
       hipError_t e = kata::launch_fill_zero(S, (int64_t)B * H * n * dv, st);
       if (e == hipSuccess) e = kata::launch_fill_zero(Z, (int64_t)B * H * n, st);
       return hip_status(e);
     }
-    const size_t rows = (size_t)B * H * T;
     const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
     const size_t ob = rows * dv * dt_size(o_dt);
     for (const auto& [ptr, bytes] : {std::pair<const void*, size_t>{S, Sb}, {Z, Zb}})
@@ -234,9 +239,11 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
         return KATA_ERR_ALIAS;
   }
   if (zero) return KATA_OK;
-  if (!chunked_supported(p, dv, C, in_dt, fam, g)) return KATA_ERR_UNSUPPORTED;
-  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
-  const bool s2 = sigma2_mfma(p, dv, C, in_dt, fam, g);
+  if (!chunked_supported(p, dv, C, in_dt, fam, g, packed)) return KATA_ERR_UNSUPPORTED;
+  // the kernels address one sequence's rows (H rows apart when packed) with 32-bit byte offsets
+  if (packed && (int64_t)T * H * (p > dv ? p : dv) * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, rows, p, dv)) != KATA_OK) return s;
+  const bool s2 = cu == nullptr && sigma2_mfma(p, dv, C, in_dt, fam, g);
   if (s2 && (int64_t)T * 2 > INT32_MAX) return KATA_ERR_SHAPE;
   const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
@@ -244,7 +251,7 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KATA_ERR_ALIGN;
-    const size_t ob = (size_t)B * H * T * dv * dt_size(o_dt);
+    const size_t ob = rows * dv * dt_size(o_dt);
     if (overlap(o, ob, workspace, need)) return KATA_ERR_ALIAS;
     if (want_state) {
       const int64_t n = kata_feature_dim(p, fam, g);
@@ -263,18 +270,19 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
                                                        static_cast<const uint16_t*>(k),
                                                        static_cast<const uint16_t*>(v), o, ob16, B, H, T, dv,
                                                        C, plan, ws, so, zo, lens, st));
+  const kata::SeqLayout lay{lens, cu, total};
   if (fam != KATA_FEAT_FULL)
     return hip_status(kata::launch_family_chunked(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
-                                                  dv, C, (int)fam, g, plan, ws, so, zo, lens, st));
+                                                  dv, C, (int)fam, g, plan, ws, so, zo, lay, st));
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), o, ob16, B, H, T,
-                                                p, dv, C, plan, ws, so, zo, lens, passes, st));
+                                                p, dv, C, plan, ws, so, zo, lay, passes, st));
   return hip_status(kata::launch_chunked_f32(static_cast<const float*>(q),
                                              static_cast<const float*>(k),
                                              static_cast<const float*>(v), o, ob16, B, H, T, p, dv,
-                                             C, plan, ws, so, zo, lens, passes, st));
+                                             C, plan, ws, so, zo, lay, passes, st));
 }
 
 size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, int C,
@@ -299,7 +307,7 @@ kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes, int passes,
                                       kata_stream_t stream) {
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
-                      workspace_bytes, passes, false, nullptr, nullptr, nullptr, stream);
+                      workspace_bytes, passes, false, nullptr, nullptr, nullptr, nullptr, 0, stream);
 }
 
 kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v,
@@ -308,7 +316,7 @@ kata_status_t kata_chunked_fwd_state(const void* q, const void* k, const void* v
                                      void* workspace, size_t workspace_bytes, float* S, float* Z,
                                      kata_stream_t stream) {
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, workspace,
-                      workspace_bytes, KATA_PASS_ALL, true, S, Z, nullptr, stream);
+                      workspace_bytes, KATA_PASS_ALL, true, S, Z, nullptr, nullptr, 0, stream);
 }
 
 kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* v,
@@ -319,7 +327,7 @@ kata_status_t kata_chunked_fwd_family(const void* q, const void* k, const void* 
                                       kata_stream_t stream) {
   if ((S == nullptr) != (Z == nullptr)) return KATA_ERR_NULL;
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, fam, g, workspace,
-                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, nullptr, stream);
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, nullptr, nullptr, 0, stream);
 }
 
 kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* v,
@@ -334,7 +342,25 @@ kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* 
     if (!aligned16(lens)) return KATA_ERR_ALIGN;
   }
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, fam, g, workspace,
-                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, lens, stream);
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, lens, nullptr, 0, stream);
+}
+
+kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* v,
+                                      kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
+                                      int H, int total, int max_len, int p, int dv, int C,
+                                      kata_scan_t scan, kata_feature_t fam, int g,
+                                      const int32_t* cu_seqlens, void* workspace,
+                                      size_t workspace_bytes, float* S, float* Z,
+                                      kata_stream_t stream) {
+  if ((S == nullptr) != (Z == nullptr)) return KATA_ERR_NULL;
+  if (total < 0 || max_len < 0) return KATA_ERR_SHAPE;
+  if ((int64_t)B * H > 0) {
+    if (cu_seqlens == nullptr) return KATA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
+  }
+  if ((int64_t)total * H * (p > dv ? p : dv) < 0 || mul4(total, H, p > dv ? p : dv, 1) < 0) return KATA_ERR_SHAPE;
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, max_len, p, dv, C, scan, fam, g, workspace,
+                      workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, nullptr, cu_seqlens, total, stream);
 }
 
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
@@ -354,7 +380,7 @@ static kata_status_t quadratic_impl(const void* q, const void* k, const void* v,
   if ((s = check_feature(p, fam, g)) != KATA_OK || zero) return s;
   if (fam == KATA_FEAT_FULL ? (!in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) : (p > 64 || dv > 64))
     return KATA_ERR_UNSUPPORTED;
-  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, (size_t)B * H * T, p, dv)) != KATA_OK) return s;
   if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
@@ -514,7 +540,7 @@ kata_status_t kata_quadratic_fwd_order(const void* q, const void* k, const void*
   if (r < 1 || r > 4) return KATA_ERR_FEATURE;
   if (zero) return KATA_OK;
   if (p > 64 || dv > 64) return KATA_ERR_UNSUPPORTED;
-  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, B, H, T, p, dv)) != KATA_OK) return s;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, (size_t)B * H * T, p, dv)) != KATA_OK) return s;
   if ((int64_t)B * H * ((T + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;

@@ -294,17 +294,27 @@ struct Args {
   int o_f32;  // output dtype: 1 = fp32, 0 = bf16
   float* s_out;  // final state S [B,H,n,DV] in the decode layout, or null
   float* z_out;  // final state Z [B,H,n], or null
-  const int* lens;  // per-sequence lengths [B] (rows beyond are not used), or null: all T
+  SeqLayout lay;     // row layout and per-sequence lengths (S2: padded layout only)
   int H;
 };
 
-// rows of sequence bh in use (virtual rows under S2): its length clamped to [0, a.T]
+// first q/k row, row step and rows in use of sequence bh. Under S2 a.T counts virtual rows
+// (two per token) of the padded layout and a length counts tokens.
 template <bool S2>
-__device__ __forceinline__ int seq_rows(const Args& a, int64_t bh) {
-  if (a.lens == nullptr) return a.T;
-  const int L = a.lens[bh / a.H];
-  const int64_t r = (int64_t)(L < 0 ? 0 : L) * (S2 ? 2 : 1);
-  return r < a.T ? (int)r : a.T;
+__device__ __forceinline__ void seq_view(const Args& a, int64_t bh, int64_t& row0, int& step, int& len) {
+  if constexpr (S2) {
+    row0 = bh * (int64_t)a.T;
+    step = 1;
+    if (a.lay.lens == nullptr) {
+      len = a.T;
+    } else {
+      const int L = a.lay.lens[bh / a.H];
+      const int64_t r = (int64_t)(L < 0 ? 0 : L) * 2;
+      len = r < a.T ? (int)r : a.T;
+    }
+  } else {
+    seq_rows_of(a.lay, bh, a.H, a.T, row0, step, len);
+  }
 }
 
 
@@ -338,13 +348,18 @@ struct Stager {
     return tid - 4 * C;
   }
   const uint16_t *qb, *kb, *vb;
-  int T;
+  int T;           // rows in use
+  uint32_t rsp, rsv;  // elements between consecutive q / k rows and v rows
 
   __device__ __forceinline__ void init(const Args& a, int64_t bh) {
-    qb = a.q + bh * a.T * P;
-    kb = a.k + bh * a.T * P;
-    vb = a.v + bh * (S2 ? a.T / 2 : a.T) * DV;
-    T = seq_rows<S2>(a, bh);  // rows past the sequence's length read as zero
+    int64_t row0;
+    int rs;
+    seq_view<S2>(a, bh, row0, rs, T);  // rows past the sequence's length read as zero
+    rsp = (uint32_t)rs * P;
+    rsv = (uint32_t)rs * DV;
+    qb = a.q + row0 * P;
+    kb = a.k + row0 * P;
+    vb = a.v + (S2 ? bh * (int64_t)(a.T / 2) : row0) * DV;
   }
 
   __device__ __forceinline__ row_t load_piece(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -358,10 +373,13 @@ struct Stager {
   __device__ __forceinline__ void load(int t0) {
     const int tid = threadIdx.x;
     const uint32_t left = (uint32_t)(t0 < T ? T - t0 : 0);  // a chunk past the end reads zeros
-    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)t0 * P, left * P * 2);
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * P, left * P * 2);
+    // byte ranges end with the last row in use (rows are rs rows apart)
+    const uint32_t qk_bytes = left ? ((left - 1) * rsp + P) * 2 : 0;
+    const uint32_t v_bytes = left ? ((left - 1) * rsv + DV) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)t0 * rsp, qk_bytes);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * rsp, qk_bytes);
     const __amdgpu_buffer_rsrc_t rv = S2 ? buf_rsrc(vb + (int64_t)(t0 / 2) * DV, (left / 2) * DV * 2)
-                                         : buf_rsrc(vb + (int64_t)t0 * DV, left * DV * 2);
+                                         : buf_rsrc(vb + (int64_t)t0 * rsv, v_bytes);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int pc = qk_piece(i);
@@ -369,7 +387,7 @@ struct Stager {
       // q or k is uniform across a wave (4C is a multiple of 64)
       const int isq = __builtin_amdgcn_readfirstlane(pc < 4 * C ? 1 : 0);
       const int row = (isq ? pc : pc - 4 * C) >> 2, kq = pc & 3;
-      const uint32_t voff = (uint32_t)(row * P + kq * CF::KQ) * 2;
+      const uint32_t voff = (row * rsp + kq * CF::KQ) * 2;
       if (pc < CF::QK_PIECES && (WITH_Q || !isq)) qk[i] = load_piece(isq ? rq : rk, voff, 0);
     }
 #pragma unroll
@@ -383,9 +401,9 @@ struct Stager {
           vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
           vr[i][1] = vr[i][0];
         } else {
-          const uint32_t voff = (uint32_t)(2 * vp * DV + 8 * vd) * 2;
+          const uint32_t voff = (2 * vp * rsv + 8 * vd) * 2;
           vr[i][0] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
-          vr[i][1] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + DV * 2, 0, 0));
+          vr[i][1] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + rsv * 2, 0, 0));
         }
       }
     }
@@ -615,12 +633,15 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
 
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
-  const int Tb = seq_rows<S2>(a, bh);  // this sequence's rows
+  int64_t row0;
+  int rstep, Tb;  // first row, row step, this sequence's rows
+  seq_view<S2>(a, bh, row0, rstep, Tb);
+  const uint32_t orsv = (uint32_t)rstep * DV;  // elements between consecutive output rows
   const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
   const int osz = a.o_f32 ? 4 : 2;
-  char* obase = static_cast<char*>(a.o) + bh * (S2 ? a.T / 2 : a.T) * DV * osz;
+  char* obase = static_cast<char*>(a.o) + (S2 ? bh * (int64_t)(a.T / 2) : row0) * DV * osz;
 
   // ---- initial state (exclusive prefix of this segment, or zero)
   f32x4_t S[wave_na<P>(W)][NT];
@@ -823,9 +844,10 @@ __device__ __forceinline__ void run_fwd(const Args& a, char* lds) {
       if constexpr (S2) den += dpp_f<0xB1>(den);  // the token's other virtual query row (lane ^ 1)
       const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
       const int orow0 = S2 ? t0 / 2 : t0, orows = S2 ? (Tb - t0) / 2 : Tb - t0;
-      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(obase + (int64_t)orow0 * DV * osz, (uint32_t)orows * DV * osz);
-      // rows past T are dropped; under S2 the even lane of a token stores it
-      const uint32_t ob = (uint32_t)((S2 ? (16 * TT + ln) >> 1 : 16 * TT + ln) * DV + 4 * lg);
+      const __amdgpu_buffer_rsrc_t ro =
+          buf_rsrc(obase + (int64_t)orow0 * orsv * osz, ((uint32_t)(orows - 1) * orsv + DV) * osz);
+      // rows past the length are dropped; under S2 the even lane of a token stores it
+      const uint32_t ob = (uint32_t)(S2 ? (16 * TT + ln) >> 1 : 16 * TT + ln) * orsv + 4 * lg;
       const bool store = !S2 || (ln & 1) == 0;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
@@ -870,7 +892,9 @@ __device__ __forceinline__ void run_sum16(const Args& a, char* lds) {
   const int lane = threadIdx.x & 63;
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
-  const int Tb = seq_rows<S2>(a, bh);  // this sequence's rows
+  int64_t row0;
+  int rstep, Tb;  // this sequence's rows
+  seq_view<S2>(a, bh, row0, rstep, Tb);
   const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(nchunks, c0 + a.cps);
@@ -969,10 +993,10 @@ hipError_t launch_summary(const Args& a, unsigned nblk, hipStream_t st) {
 template <int P, int DV, int C, bool S2 = false>
 hipError_t launch_pdc(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                       int B, int H, int T, const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                      const int* lens, int passes, hipStream_t st) {
+                      SeqLayout lay, int passes, hipStream_t st) {
   using CF = Cfg<P, DV, C>;
   const int BH = B * H;
-  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out, lens, H};
+  Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out, lay, H};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     a.nblk_per_bh = plan.nseg - 1;

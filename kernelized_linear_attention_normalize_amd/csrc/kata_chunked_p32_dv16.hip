@@ -4,10 +4,10 @@
 namespace kata {
 namespace chk {
 template hipError_t launch_pdc<32, 16, 32>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                         int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                         int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 template hipError_t launch_pdc<32, 16, 64>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                         int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                         int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 template hipError_t launch_pdc<32, 16, 128>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                          int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                          int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 }  // namespace chk
 }  // namespace kata

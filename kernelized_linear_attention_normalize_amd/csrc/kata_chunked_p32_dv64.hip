@@ -8,10 +8,10 @@ extern template hipError_t launch_summary<32, 64, 32>(const Args&, unsigned, hip
 extern template hipError_t launch_summary<32, 64, 64>(const Args&, unsigned, hipStream_t);
 extern template hipError_t launch_summary<32, 64, 128>(const Args&, unsigned, hipStream_t);
 template hipError_t launch_pdc<32, 64, 32>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                         int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                         int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 template hipError_t launch_pdc<32, 64, 64>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                         int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                         int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 template hipError_t launch_pdc<32, 64, 128>(const uint16_t*, const uint16_t*, const uint16_t*, void*, bool, int,
-                                          int, int, const SegPlan&, float*, float*, float*, const int*, int, hipStream_t);
+                                          int, int, const SegPlan&, float*, float*, float*, SeqLayout, int, hipStream_t);
 }  // namespace chk
 }  // namespace kata

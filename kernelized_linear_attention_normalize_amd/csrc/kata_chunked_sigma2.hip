@@ -14,8 +14,8 @@ hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, cons
                                       float* ws, float* s_out, float* z_out, const int* lens, hipStream_t st) {
 #define KATA_S2CASE(DD, CC)                                                                        \
   if (dv == DD && C == CC)                                                                         \
-    return chk::launch_pdc<32, DD, CC, true>(q, k, v, o, o_bf16, B, H, 2 * T, plan, ws, s_out, z_out, lens, \
-                                             PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS, st);
+    return chk::launch_pdc<32, DD, CC, true>(q, k, v, o, o_bf16, B, H, 2 * T, plan, ws, s_out, z_out,       \
+                                             SeqLayout{lens, nullptr, 0}, PASS_SUMMARIES | PASS_SCAN | PASS_SEGMENTS, st);
   KATA_S2CASE(32, 64) KATA_S2CASE(32, 128) KATA_S2CASE(64, 64) KATA_S2CASE(64, 128)
 #undef KATA_S2CASE
   return hipErrorInvalidValue;

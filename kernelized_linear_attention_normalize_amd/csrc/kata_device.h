@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kata_launch.h"
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -120,5 +122,25 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+// First row, row step (in rows) and rows in use of sequence bh = (b, h) of a chunked
+// forward (see SeqLayout). Lengths clamp to [0, T] and packed offsets to [0, total], so every
+// row a kernel touches lies inside the tensors whatever the device arrays hold.
+__device__ __forceinline__ void seq_rows_of(const SeqLayout& L, int64_t bh, int H, int T, int64_t& row0,
+                                            int& step, int& len) {
+  const int64_t b = bh / H, h = bh % H;
+  if (L.cu != nullptr) {
+    int s = L.cu[b], e = L.cu[b + 1];
+    s = s < 0 ? 0 : (s > L.total ? L.total : s);
+    e = e < s ? s : (e > L.total ? L.total : e);
+    row0 = (int64_t)s * H + h;
+    step = H;
+    len = e - s < T ? e - s : T;
+  } else {
+    row0 = bh * (int64_t)T;
+    step = 1;
+    len = L.lens == nullptr ? T : min(max(L.lens[b], 0), T);
+  }
+}
 
 }  // namespace kata

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     void* __restrict__ o, int T, int p, int dv, int C, int nseg, int cps, int nblk_per_bh,
     float* __restrict__ ws, float* __restrict__ s_out, float* __restrict__ z_out,
-    const int* __restrict__ lens, int H) {
+    SeqLayout lay, int H) {
   extern __shared__ float sm[];
   const int n = p * (p + 1) / 2;
   float* Ss = sm;
@@ -44,7 +44,9 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / nblk_per_bh;
   const int seg = blockIdx.x % nblk_per_bh;
-  const int Tb = lens == nullptr ? T : min(max(lens[bh / H], 0), T);  // this sequence's rows
+  int64_t row0;
+  int rstep, Tb;  // first row, row step, this sequence's rows
+  seq_rows_of(lay, bh, H, T, row0, rstep, Tb);
   const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * cps, c1 = min(nchunks, c0 + cps);
   const int64_t state_floats = (int64_t)n * dv + n;
@@ -60,9 +62,9 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
   } else {
     for (int e = tid; e < n * dv + n; e += 256) Ss[e] = 0.f;
   }
-  const float* qb = q + bh * (int64_t)T * p;
-  const float* kb = k + bh * (int64_t)T * p;
-  const float* vb = v + bh * (int64_t)T * dv;
+  const float* qb = q + row0 * p;
+  const float* kb = k + row0 * p;
+  const float* vb = v + row0 * dv;
 
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
       const int t = isq ? r : r - C;
       if (MODE == 1 && isq) continue;
       float* dst = (isq ? qh : kh) + t * p;
-      const float* src = (isq ? qb : kb) + (int64_t)(t0 + t) * p;
+      const float* src = (isq ? qb : kb) + (int64_t)(t0 + t) * rstep * p;
       float ss = 0.f;
       for (int i = 0; i < p; ++i) {
         const float x = t < L ? src[i] : 0.f;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
     }
     for (int e = tid; e < C * dv; e += 256) {
       const int t = e / dv;
-      vv[e] = t < L ? vb[(int64_t)t0 * dv + e] : 0.f;
+      vv[e] = t < L ? vb[(int64_t)(t0 + t) * rstep * dv + e % dv] : 0.f;
     }
     __syncthreads();
     if (MODE == 0) {
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
           num += a * a * vv[s * dv + dd];
         }
         const float dn = den[t];
-        store_from_f32<OUT_BF16>(o, (bh * T + t0 + t) * (int64_t)dv + dd, dn > 0.f ? num / dn : 0.f);
+        store_from_f32<OUT_BF16>(o, (row0 + (int64_t)(t0 + t) * rstep) * dv + dd, dn > 0.f ? num / dn : 0.f);
       }
       __syncthreads();
     }
@@ -154,7 +156,7 @@ hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st)
 
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, float* s_out, float* z_out, const int* lens, int passes,
+                              float* ws, float* s_out, float* z_out, SeqLayout lay, int passes,
                               hipStream_t st) {
   const int BH = B * H;
   const size_t lds = f32_chunked_lds_bytes(p, dv, C);
@@ -163,7 +165,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
-        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr, lens, H);
+        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr, lay, H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN)) {
@@ -175,7 +177,7 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   kfn<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, plan.nseg,
-                                                              plan.cps, plan.nseg, ws, s_out, z_out, lens, H);
+                                                              plan.cps, plan.nseg, ws, s_out, z_out, lay, H);
   return hipGetLastError();
 }
 

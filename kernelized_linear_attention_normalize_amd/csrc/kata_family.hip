@@ -284,8 +284,7 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
                                                              int T, int p, int dv, int C, Feat F, int nseg,
                                                              int cps, int nblk_per_bh, float* __restrict__ ws,
                                                              int64_t state_floats, float* __restrict__ s_out,
-                                                             float* __restrict__ z_out, const int* __restrict__ lens,
-                                                             int H) {
+                                                             float* __restrict__ z_out, SeqLayout lay, int H) {
   extern __shared__ float sm[];
   const int n = F.n;
   float* Ss = sm;
@@ -298,7 +297,9 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / nblk_per_bh;
   const int seg = blockIdx.x % nblk_per_bh;
-  const int Tb = lens == nullptr ? T : min(max(lens[bh / H], 0), T);  // this sequence's rows
+  int64_t row0;
+  int rstep, Tb;  // first row, row step, this sequence's rows
+  seq_rows_of(lay, bh, H, T, row0, rstep, Tb);
   const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * cps, c1 = min(nchunks, c0 + cps);
 
@@ -317,10 +318,10 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
       const bool isq = r < C;
       const int t = isq ? r : r - C;
       if (MODE == 1 && isq) continue;
-      load_norm_row<IN_BF16>(isq ? q : k, bh * T + t0 + t, t < L, p, (isq ? qh : kh) + t * p);
+      load_norm_row<IN_BF16>(isq ? q : k, row0 + (int64_t)(t0 + t) * rstep, t < L, p, (isq ? qh : kh) + t * p);
     }
     for (int e = tid; e < C * dv; e += 256)
-      vv[e] = e / dv < L ? load_as_f32<IN_BF16>(v, (bh * T + t0) * dv + e) : 0.f;
+      vv[e] = e / dv < L ? load_as_f32<IN_BF16>(v, (row0 + (int64_t)(t0 + e / dv) * rstep) * dv + e % dv) : 0.f;
     __syncthreads();
     if (MODE == 0) {
       for (int t = tid; t < L; t += 256) {  // denominator: psi(q_t) . Z + intra weights
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(256) void family_chunked_kernel(const void* __restr
         for (int f = 0; f < n; ++f) num += feat_val(F, tab[f], qt) * Ss[f * dv + dd];
         for (int s = 0; s <= t; ++s) num += feat_weight(F, qt, kh + s * p) * vv[s * dv + dd];
         const float dn = den[t];
-        store_from_f32<OUT_BF16>(o, (bh * T + t0 + t) * (int64_t)dv + dd, dn > 0.f ? num / dn : 0.f);
+        store_from_f32<OUT_BF16>(o, (row0 + (int64_t)(t0 + t) * rstep) * dv + dd, dn > 0.f ? num / dn : 0.f);
       }
       __syncthreads();
     }
@@ -370,7 +371,7 @@ template <bool IN_BF16>
 static hipError_t launch_family_chunked_t(const void* q, const void* k, const void* v, void* o, bool o_bf16,
                                           int B, int H, int T, int p, int dv, int C, int fam, int g,
                                           const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                                          const int* lens, hipStream_t st) {
+                                          SeqLayout lay, hipStream_t st) {
   const Feat F = make_feat(p, fam, g);
   const int BH = B * H;
   const size_t lds = family_chunked_lds_bytes(p, dv, C, fam, g);
@@ -382,7 +383,7 @@ static hipError_t launch_family_chunked_t(const void* q, const void* k, const vo
       return e;
     ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(q, k, v, nullptr, T, p, dv, C, F, plan.nseg,
                                                                        plan.cps, plan.nseg - 1, ws, sf, nullptr,
-                                                                       nullptr, lens, H);
+                                                                       nullptr, lay, H);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_scan(ws, BH, plan.nseg - 1, sf, st)) != hipSuccess) return e;
   }
@@ -390,19 +391,19 @@ static hipError_t launch_family_chunked_t(const void* q, const void* k, const vo
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, F, plan.nseg, plan.cps,
-                                                              plan.nseg, ws, sf, s_out, z_out, lens, H);
+                                                              plan.nseg, ws, sf, s_out, z_out, lay, H);
   return hipGetLastError();
 }
 
 hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
-                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, const int* lens,
+                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, SeqLayout lay,
                                  hipStream_t st) {
   if (in_bf16)
     return launch_family_chunked_t<true>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out,
-                                         lens, st);
+                                         lay, st);
   return launch_family_chunked_t<false>(q, k, v, o, o_bf16, B, H, T, p, dv, C, fam, g, plan, ws, s_out, z_out,
-                                        lens, st);
+                                        lay, st);
 }
 
 // ---------------------------------------------------------------------------- quadratic

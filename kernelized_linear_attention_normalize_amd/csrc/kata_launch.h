@@ -14,6 +14,17 @@ struct SegPlan {
 };
 SegPlan seg_plan(int B, int H, int T, int C, int scan);
 
+// Where the rows of sequence bh = (b, h) of a chunked forward live. Padded layout
+// [B, H, T, *] (cu null): rows bh * T + t, cut at lens[b] when lens (device, [B]) is given.
+// Packed token-major layout [total, H, *] (cu: device cu_seqlens[B + 1]): rows
+// (cu[b] + t) * H + h for t < cu[b + 1] - cu[b]. T bounds every length (the segment plan is
+// that of T).
+struct SeqLayout {
+  const int* lens = nullptr;
+  const int* cu = nullptr;
+  int total = 0;  // rows per head of the packed layout
+};
+
 // passes of the chunked forward (the values of kata_pass_t)
 enum : int { PASS_SUMMARIES = 1, PASS_SCAN = 2, PASS_SEGMENTS = 4 };
 
@@ -31,18 +42,18 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf
                          hipStream_t st);
 // s_out / z_out (may be null): the state after the last token of every sequence, in the
 // decode layout (S [B,H,n,dv], Z [B,H,n], fp32, packed order), written by pass 3.
-// lens (device, [B], may be null): per-sequence lengths; rows t >= lens[b] are not used and
-// their outputs are not written (the segment plan is that of T).
+// lay: the row layout (SeqLayout); rows past a sequence's length are not used and their
+// outputs are not written.
 hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, void* o, bool o_bf16,
                               int B, int H, int T, int p, int dv, int C, const SegPlan& plan,
-                              float* ws, float* s_out, float* z_out, const int* lens, int passes,
+                              float* ws, float* s_out, float* z_out, SeqLayout lay, int passes,
                               hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
                                const SegPlan& plan, float* ws, float* s_out, float* z_out,
-                               const int* lens, int passes, hipStream_t st);
+                               SeqLayout lay, int passes, hipStream_t st);
 // n float zeros at p (a fill kernel, so the call is safe under graph capture)
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
@@ -58,7 +69,7 @@ hipError_t launch_family_decode(const void* q, const void* k, const void* v, boo
                                 hipStream_t st);
 hipError_t launch_family_chunked(const void* q, const void* k, const void* v, bool in_bf16, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, int C, int fam, int g,
-                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, const int* lens,
+                                 const SegPlan& plan, float* ws, float* s_out, float* z_out, SeqLayout lay,
                                  hipStream_t st);
 // bf16 MFMA chunked forward of KATA-Sigma 2 at p = 64 (dv in {32, 64}, C in {64, 128}); plan
 // over the 2T virtual rows (two 32-component blocks per token)

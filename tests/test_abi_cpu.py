@@ -179,6 +179,34 @@ def test_feature_families(lib):
     assert ch(B=1, H=4, T=65536, scan=ASSOC, o=A + (1 << 34)) == E_WS
 
 
+def test_varlen_validation(lib):
+    """kata_chunked_fwd_varlen: argument errors come back before any device access."""
+    FULL, SIGMA = 0, 1
+
+    def vl(fam=FULL, g=1, cu=A + (1 << 36), S=None, Z=None, **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=2, H=2, total=300,
+                 max_len=200, p=32, dv=64, C=64, scan=SEQ, ws=None, wsb=0)
+        a.update(kw)
+        return lib.kata_chunked_fwd_varlen(a["q"], a["k"], a["v"], a["in_dt"], a["o"], a["o_dt"], a["B"],
+                                           a["H"], a["total"], a["max_len"], a["p"], a["dv"], a["C"], a["scan"],
+                                           fam, g, cu, a["ws"], a["wsb"], S, Z, None)
+    assert vl(cu=None) == E_NULL
+    assert vl(cu=A + (1 << 36) + 2) == E_ALIGN               # int32 array: 4-byte aligned
+    assert vl(total=-1) == E_SHAPE and vl(max_len=-5) == E_SHAPE
+    assert vl(S=A + (1 << 40)) == E_NULL                     # S without Z
+    assert vl(g=3, fam=SIGMA) == E_FEAT
+    assert vl(total=0) == OK and vl(max_len=0) == OK and vl(B=0) == OK   # nothing to do
+    assert vl(dv=48) == E_UNSUP
+    # the Sigma 2 MFMA path takes the padded layout only; the VALU family kernel's LDS does
+    # not fit this shape
+    assert vl(fam=SIGMA, g=2, p=64, dv=64, C=128) == E_UNSUP
+    # 32-bit offsets of one packed sequence: max_len * H * max(p, dv) * 4 must stay below 2^31
+    assert vl(H=1024, max_len=1 << 14, total=1 << 14) == E_SHAPE
+    # the associative scan's workspace is that of the padded call with T = max_len
+    need = lib.kata_chunked_workspace_bytes(2, 2, 200 * 64, 32, 64, 64, ASSOC, BF16)
+    assert need > 0 and vl(scan=ASSOC, max_len=200 * 64, total=300) == E_WS
+
+
 def test_higher_orders(lib):
     from oracle import kata_families as kf
     for p, r in [(4, 2), (16, 2), (3, 3), (8, 4), (64, 1)]:

@@ -50,3 +50,54 @@ def test_ragged_lengths(dt, family, p, g, dv, C, scan):
         print(f"  seq {b} L={L} rel_err={err:.3e} state S={es:.2e} Z={ez:.2e}", flush=True)
         assert err <= TOL[dt]
         assert es <= bar and ez <= bar
+
+
+# ------------------------------------------------------------------ packed (varlen) layout
+def _pack(x, lens):
+    """padded [B, H, T, d] -> packed token-major [sum(lens), H, d]"""
+    return np.concatenate([np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)], axis=0)
+
+
+@pytest.mark.parametrize("dt,family,p,g,dv,C,scan", [
+    ("bf16", "full", 32, 1, 64, 128, "associative"), ("bf16", "full", 32, 1, 64, 64, "sequential"),
+    ("bf16", "full", 16, 1, 32, 32, "associative"), ("f32", "full", 16, 1, 32, 64, "associative"),
+    ("bf16", "sigma", 32, 2, 32, 64, "associative"), ("f32", "block", 16, 2, 16, 32, "sequential")])
+def test_varlen_packed(dt, family, p, g, dv, C, scan):
+    """Token-major packed sequences (kata_chunked_fwd_varlen): each sequence against the oracle
+    run on it alone, the state after its last token, rows outside every sequence untouched, and
+    bitwise agreement with the padded ragged call on the same data (same kernels and plan)."""
+    B, H, max_len = 4, 3, 1600
+    lens = [1500, 0, 37, 777]
+    print(f"[case] varlen {dt} {family}{g} p={p} dv={dv} C={C} scan={scan} lens={lens}", flush=True)
+    q, k, v = draw_qkv(49, B, H, max_len, p, dv, dt)
+    extra = 5  # rows after the last sequence, outside every sequence
+    pk = [np.concatenate([_pack(x, lens), x[0, :, :extra].transpose(1, 0, 2)], axis=0) for x in (q, k, v)]
+    total = pk[0].shape[0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    out = torch.full((total, H, dv), 7.0, dtype=torch.float32, device="cuda:0")
+    o, S, Z = kata.chunked_fwd_varlen(*(to_dev(x, dt) for x in pk), cu, max_len, C=C, scan=scan, out=out,
+                                      return_state=True, family=family, g=g)
+    o, S, Z = to_np(o), to_np(S), to_np(Z)
+    assert np.all(o[sum(lens):] == 7.0), "rows outside every sequence were written"
+    bar = 1e-2 if dt == "bf16" else 1e-5
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(S[b] == 0.0) and np.all(Z[b] == 0.0)
+            continue
+        got = np.transpose(o[starts[b]:starts[b] + L], (1, 0, 2))  # [H, L, dv]
+        ref = kf.naive_family(q[b, :, :L], k[b, :, :L], v[b, :, :L], family, g)
+        err = row_rel_err(got, ref)
+        S_ref, Z_ref = kf.prefill_state_family(k[b, :, :L], v[b, :, :L], family, g)
+        es, ez = _normwise(S[b], S_ref), _normwise(Z[b], Z_ref)
+        print(f"  seq {b} L={L} rel_err={err:.3e} state S={es:.2e} Z={ez:.2e}", flush=True)
+        assert err <= TOL[dt]
+        assert es <= bar and ez <= bar
+    # the padded ragged call on the same rows gives the same bits
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    op, Sp, Zp = kata.chunked_fwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), C=C, scan=scan,
+                                  out_dtype=torch.float32, return_state=True, family=family, g=g, lengths=ln)
+    op = to_np(op)
+    for b, L in enumerate(lens):
+        assert np.array_equal(np.transpose(o[starts[b]:starts[b] + L], (1, 0, 2)), op[b, :, :L])
+    assert np.array_equal(S, to_np(Sp)) and np.array_equal(Z, to_np(Zp))
