@@ -94,12 +94,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--scan", default="associative", choices=["associative", "sequential"])
-    ap.add_argument("--workload", default="long", choices=["long", "quadratic", "decode", "copy"])
+    ap.add_argument("--workload", default="long",
+                    choices=["long", "quadratic", "decode", "copy", "backward", "varlen"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--family", default="full", choices=["full", "sigma", "block"],
                     help="PSD feature family of the quadratic workload (sigma = KATA-Sigma g, "
                          "block = KATA-M g)")
     ap.add_argument("--g", type=int, default=1, help="feature blocks of --family")
+    ap.add_argument("--order", type=int, default=1,
+                    help="quadratic workload: weights (q_hat . k_hat)^(2r) of the even-order lift psi_2r")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -175,7 +178,8 @@ def main():
         qd, kd, vd = to(q), to(k), to(v)
         out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
         fam, g = args.family, (args.g if args.family != "full" else 1)
-        step = [lambda: kata.quadratic_fwd(qd, kd, vd, out=out, family=fam, g=g)]
+        r = args.order
+        step = [lambda: kata.quadratic_fwd(qd, kd, vd, out=out, family=fam, g=g, order=r)]
         dominant = 0
         kernel_name = "quadratic_bf16_kernel"
         pairs = B * H * T * (T + 1) // 2
@@ -183,15 +187,69 @@ def main():
         # M g, 2pg for Sigma g: all g^2 block pairs of length p/g) plus W.[V | 1]
         flops = ((2 * p * g if fam == "sigma" else 2 * p) + 2 * (dv + 1)) * pairs
         units = B * T
-        fam_txt = "" if fam == "full" else f" family={fam}{g}"
+        fam_txt = ("" if fam == "full" else f" family={fam}{g}") + ("" if r == 1 else f" order r={r}")
         metric = "flash-style KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
         config = {"workload": f"quadratic: flash-style forward B={B} H={H} T={T} p={p} dv={dv}{fam_txt}",
                   "global_batch": B, "seq_len": T, "heads": H, "p": p, "dv": dv,
                   "parallelism": "single-gpu"}
         if fam != "full":
             config.update({"family": fam, "g": g})
+        if r != 1:
+            config["order"] = r
         bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
-        traffic_file = "quadratic_traffic.txt" if fam == "full" else f"quadratic_{fam}{g}_traffic.txt"
+        traffic_file = ("quadratic_traffic.txt" if fam == "full" else f"quadratic_{fam}{g}_traffic.txt") \
+            if r == 1 else f"quadratic_order{r}_traffic.txt"
+    elif args.workload == "backward":
+        # gradients of the quadratic shape (O(T^2) fp32 VALU kernels, any input dtype)
+        w = WORKLOADS["quadratic"]
+        B, H, T, p, dv = w.B, w.H, w.T, w.p, w.dv
+        q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
+        go = np.random.default_rng(w.seed + 100).standard_normal((B, H, T, dv), dtype=np.float32)
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd, gd = to(q), to(k), to(v), to(go)  # the output gradient in the inputs' dtype
+        step = [lambda: kata.quadratic_bwd(qd, kd, vd, gd)]
+        dominant = 0
+        kernel_name = "quadratic_bf16_kernel (statistics) + bwd_keys_kernel + bwd_queries_kernel"
+        pairs = B * H * T * (T + 1) // 2
+        # per causal pair: the forward's statistics (scores 2p, W.[V | 1] 2 (dv + 1)), the
+        # scores once more (2p), dP = g . v (2 dv), dV (2 dv), dK (2p) and dQ (2p)
+        flops = (8 * p + 6 * dv + 2) * pairs
+        units = B * T
+        metric = "quadratic-form KATA backward tokens/s (1 GPU) + % bf16 MFMA peak"
+        config = {"workload": f"backward: gradients of the flash-style forward B={B} H={H} T={T} p={p} dv={dv}, "
+                              "bf16 inputs", "global_batch": B, "seq_len": T, "heads": H,
+                  "p": p, "dv": dv, "parallelism": "single-gpu"}
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        traffic_file = "backward_traffic.txt"
+        args.no_cpu_baseline = True
+    elif args.workload == "varlen":
+        # packed sequences of mixed length (token-major, cu_seqlens): VARLEN in kata_inputs
+        from kata_inputs import VARLEN, draw_varlen
+        H, p, dv, C = VARLEN["H"], VARLEN["p"], VARLEN["dv"], args.chunk
+        lens, q, k, v = draw_varlen(VARLEN)
+        total = int(sum(lens))
+        max_len = int(max(lens))
+        to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        qd, kd, vd = to(q), to(k), to(v)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        out = torch.empty((total, H, dv), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(kata.chunked_workspace_bytes(len(lens), H, max_len, p, dv, C,
+                                                          kata._scan_code(args.scan)), 1),
+                         dtype=torch.uint8, device=dev)
+        step = [lambda: kata.chunked_fwd_varlen(qd, kd, vd, cu, max_len, C=C, scan=args.scan, out=out, workspace=ws)]
+        dominant = 0
+        kernel_name = "kata_chunked_fwd_varlen (all passes)"
+        n = p * (p + 1) // 2
+        flops = chunked_flops_per_head_token(n, p, dv, C) * H * total
+        units = total
+        metric = "packed variable-length chunked KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
+        config = {"workload": f"varlen: chunked forward over {len(lens)} packed sequences of "
+                              f"{min(lens)}..{max_len} tokens ({total} in all), H={H} p={p} (n={n}) dv={dv} "
+                              f"C={C} scan={args.scan}", "global_batch": len(lens), "tokens": total,
+                  "heads": H, "p": p, "dv": dv, "chunk": C, "scan": args.scan, "parallelism": "single-gpu"}
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        traffic_file = f"varlen_C{C}_traffic.txt"
+        args.no_cpu_baseline = True
     elif args.workload == "copy":
         nbytes = 1 << 30
         src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
@@ -301,7 +359,12 @@ def main():
                     out_rows.append(w @ vv[:t + 1] / w.sum() if w.sum() > 0 else np.zeros(vv.shape[-1]))
                 return np.asarray(out_rows)
         else:
-            ref_rows = lambda qq, kk, vv: ko.naive_rows(qq, kk, vv, rows)
+            if args.order != 1:
+                from oracle import kata_families as kf
+                ref_rows = lambda qq, kk, vv: np.asarray([kf.naive_order(qq[:t + 1], kk[:t + 1], vv[:t + 1],
+                                                                         args.order)[t] for t in rows])
+            else:
+                ref_rows = lambda qq, kk, vv: ko.naive_rows(qq, kk, vv, rows)
         parity = max(ko.row_rel_err(res[0, h, rows], ref_rows(q[0, h], k[0, h], v[0, h])) for h in (0, H - 1))
 
     cpu = None

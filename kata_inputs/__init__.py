@@ -15,7 +15,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["round_bf16", "Workload", "WORKLOADS", "draw_qkv", "draw_decode_history",
-           "draw_decode_steps"]
+           "draw_decode_steps", "VARLEN", "draw_varlen"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -56,6 +56,9 @@ WORKLOADS = {
 # Recurrent decode workload: 128 sequences x 16 heads, p=32, dv=64, a 4096-token
 # float32 history (seed 4) that fills the state, then 256 single-token bf16 steps (seed 5).
 DECODE = dict(N=128, H=16, p=32, dv=64, hist=4096, steps=256, hist_seed=4, step_seed=5)
+# packed variable-length batch: B sequences with lengths uniform in [lo, hi] (about the long
+# workload's 131072 tokens in all), token-major q, k [total, H, p], v [total, H, dv]
+VARLEN = dict(B=16, H=16, p=32, dv=64, lo=2048, hi=14336, seed=6)
 
 
 def draw_qkv(seed: int, B: int, H: int, T: int, p: int, dv: int, dtype: str = "bf16"):
@@ -89,3 +92,15 @@ def draw_decode_steps(seed: int, steps: int, N: int, H: int, p: int, dv: int,
     if dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     return q, k, v
+
+
+def draw_varlen(spec=None):
+    """(lens [B] int, q, k [total, H, p], v [total, H, dv]) float32, bf16-exact."""
+    spec = spec or VARLEN
+    rng = np.random.default_rng(spec["seed"])
+    lens = rng.integers(spec["lo"], spec["hi"] + 1, size=spec["B"])
+    total = int(lens.sum())
+    q = round_bf16(rng.standard_normal((total, spec["H"], spec["p"]), dtype=np.float32))
+    k = round_bf16(rng.standard_normal((total, spec["H"], spec["p"]), dtype=np.float32))
+    v = round_bf16(rng.standard_normal((total, spec["H"], spec["dv"]), dtype=np.float32))
+    return [int(x) for x in lens], q, k, v

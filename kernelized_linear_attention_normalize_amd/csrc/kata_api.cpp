@@ -499,6 +499,11 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
   }
+  if (in_dt == KATA_DTYPE_BF16 && fam == KATA_FEAT_FULL && kata::quadratic_bwd_mfma_supported(p, dv))
+    return hip_status(kata::launch_quadratic_bwd_mfma(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<const uint16_t*>(grad_o), B, H, T, p, dv, static_cast<float*>(workspace), dq, dk, dv_out,
+        (hipStream_t)stream));
   return hip_status(kata::launch_quadratic_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, T, p, dv,
                                                (int)fam, g, static_cast<float*>(workspace), dq, dk, dv_out,
                                                (hipStream_t)stream));

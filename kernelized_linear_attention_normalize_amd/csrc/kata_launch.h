@@ -78,6 +78,11 @@ hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, cons
                                       float* ws, float* s_out, float* z_out, const int* lens, hipStream_t st);
 // gradients of the quadratic form (VALU): ws holds 2 floats (D_t, g_t . o_t) per row
 int bwd_pairs(int p, int fam, int g);
+// full map, bf16 q, k, v, gout: MFMA backward (p, dv in {32, 64}); stats: 2 floats per row
+bool quadratic_bwd_mfma_supported(int p, int dv);
+hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,
+                                     int B, int H, int T, int p, int dv, float* stats, float* dq, float* dk,
+                                     float* dvo, hipStream_t st);
 hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
                                 int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
                                 float* dvo, hipStream_t st);

@@ -54,12 +54,15 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // queries, and the weight is the sum of their squares (all pairs for Sigma, a = b for M).
 // R (full map only): weights (q_hat . k_hat)^(2R), the inner product of the higher even-order
 // lift psi_2R (psi_2r display of the HTML page); R = 1 is the rank-one map.
-template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1>
+// STATS (backward, full map): no output; instead row t's denominator D_t = sum_s w_ts (with
+// the raw query, as everywhere here) and delta_t = gout_t . o_t go to stats[2 t], [2 t + 1].
+template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1, bool STATS = false>
 __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v,
                                                                 void* __restrict__ o, int T,
-                                                                int nqb) {
+                                                                int nqb, const uint16_t* __restrict__ gout,
+                                                                float* __restrict__ stats) {
   using namespace quad;
   constexpr int KS = (P + 31) / 32;                        // 32-wide k-steps over components
   constexpr int KP = P == 64 ? 80 : (P == 32 ? 48 : 16);   // bf16 pitch of K rows (8 * odd floats)
@@ -274,6 +277,28 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   }
 
   // ---- epilogue: lane holds columns 16 nt + 4 lg + r of query qw0 + 16 qt + ln
+  if constexpr (STATS) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int query = qw0 + 16 * qt + ln;
+      const float den = D[qt][0];
+      const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
+      float part = 0.f;  // this lane's columns of gout . o
+      if (query < T) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gout + (bh * T + query) * (int64_t)DV + 16 * nt + 4 * lg);
+          const f32x4_t x = O[qt][nt] * inv;
+          part += x[0] * bf16_bits_to_f32(gw[0] & 0xffffu) + x[1] * __uint_as_float(gw[0] & 0xffff0000u) +
+                  x[2] * bf16_bits_to_f32(gw[1] & 0xffffu) + x[3] * __uint_as_float(gw[1] & 0xffff0000u);
+        }
+      }
+      part = xor32_sum(xor16_sum(part));  // over the four lane groups (all lanes take part)
+      if (query < T && lg == 0)
+        *reinterpret_cast<u32x2_t*>(stats + (bh * T + query) * 2) = u32x2_t{__float_as_uint(den), __float_as_uint(part)};
+    }
+    return;
+  }
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int query = qw0 + 16 * qt + ln;
@@ -297,8 +322,8 @@ static hipError_t launch_quad_pd(const uint16_t* q, const uint16_t* k, const uin
                                  bool o_bf16, int BH, int T, hipStream_t st) {
   const int nqb = (T + quad::BM - 1) / quad::BM;
   dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
-  if (o_bf16) quadratic_bf16_kernel<P, DV, true><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
-  else quadratic_bf16_kernel<P, DV, false><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  if (o_bf16) quadratic_bf16_kernel<P, DV, true><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
+  else quadratic_bf16_kernel<P, DV, false><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -319,8 +344,8 @@ static hipError_t launch_quad_order(const uint16_t* q, const uint16_t* k, const 
                                     int BH, int T, hipStream_t st) {
   const int nqb = (T + quad::BM - 1) / quad::BM;
   dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
-  if (o_bf16) quadratic_bf16_kernel<P, DV, true, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
-  else quadratic_bf16_kernel<P, DV, false, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  if (o_bf16) quadratic_bf16_kernel<P, DV, true, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
+  else quadratic_bf16_kernel<P, DV, false, 0, 1, R><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -347,8 +372,8 @@ static hipError_t launch_quad_fam(const uint16_t* q, const uint16_t* k, const ui
                                   int BH, int T, hipStream_t st) {
   const int nqb = (T + quad::BM - 1) / quad::BM;
   dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
-  if (o_bf16) quadratic_bf16_kernel<64, DV, true, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
-  else quadratic_bf16_kernel<64, DV, false, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb);
+  if (o_bf16) quadratic_bf16_kernel<64, DV, true, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
+  else quadratic_bf16_kernel<64, DV, false, FAM, 2><<<grid, block, 0, st>>>(q, k, v, o, T, nqb, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -365,6 +390,23 @@ hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, co
   if (dv == 16) return launch_quad_fam<16, 2>(q, k, v, o, o_bf16, BH, T, st);
   if (dv == 32) return launch_quad_fam<32, 2>(q, k, v, o, o_bf16, BH, T, st);
   return launch_quad_fam<64, 2>(q, k, v, o, o_bf16, BH, T, st);
+}
+
+// backward statistics of the full map (STATS above) for bf16 q, k, v, gout
+hipError_t launch_quadratic_bf16_stats(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,
+                                       float* stats, int B, int H, int T, int p, int dv, hipStream_t st) {
+  const int BH = B * H;
+  const int nqb = (T + quad::BM - 1) / quad::BM;
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
+#define KATA_SCASE(PP, DD)                                                                                        \
+  if (p == PP && dv == DD) {                                                                                      \
+    quadratic_bf16_kernel<PP, DD, false, 0, 1, 1, true><<<grid, block, 0, st>>>(q, k, v, nullptr, T, nqb, gout,  \
+                                                                               stats);                           \
+    return hipGetLastError();                                                                                     \
+  }
+  KATA_SCASE(32, 32) KATA_SCASE(32, 64) KATA_SCASE(64, 32) KATA_SCASE(64, 64)
+#undef KATA_SCASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kata

@@ -64,3 +64,38 @@ def test_autograd_wrapper():
     ref = kb.backward(q, k, v, go)
     for name, t, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
         assert _rel(to_np(t), r, 1e-2 * float(np.linalg.norm(go))) <= 2e-4, name
+
+
+# ------------------------------------------------------------------ MFMA path
+@pytest.mark.parametrize("p,dv,T", [(64, 64, 700), (32, 64, 1030), (64, 32, 257), (32, 32, 64), (64, 64, 600)])
+def test_quadratic_bwd_mfma(p, dv, T):
+    """bf16 inputs of the full map with p, dv in {32, 64} run the bf16 MFMA backward. Its
+    per-pair operands (the weight over D_t and dW_ts S_ts) are rounded to bf16 (relative
+    2^-9) before the fp32 accumulation, as the forward rounds its weights; bar: normwise
+    1e-2 per gradient tensor. Zero query and key rows get zero gradients."""
+    print(f"[case] bwd mfma p={p} dv={dv} T={T}", flush=True)
+    q, k, v = draw_qkv(61, 2, 3, T, p, dv, "bf16")
+    go = draw_qkv(62, 2, 3, T, dv, dv, "bf16")[0]
+    q[1, 2, 5] = 0.0
+    k[0, 1, T // 3] = 0.0
+    ref = kb.backward(q, k, v, go)
+    got = kata.quadratic_bwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(go, "bf16"))
+    floor = 1e-2 * float(np.linalg.norm(go))
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        e = _rel(to_np(a), r, floor)
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 1e-2, name
+    assert np.all(to_np(got[0])[1, 2, 5] == 0.0) and np.all(to_np(got[1])[0, 1, T // 3] == 0.0)
+
+
+def test_quadratic_bwd_mfma_matches_valu_path():
+    """The MFMA path (bf16 inputs) and the fp32 VALU path (the same values as fp32 inputs)
+    agree to the MFMA path's bar."""
+    q, k, v = draw_qkv(63, 1, 2, 333, 64, 64, "bf16")
+    go = draw_qkv(64, 1, 2, 333, 64, 64, "bf16")[0]
+    a = kata.quadratic_bwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(go, "bf16"))
+    b = kata.quadratic_bwd(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), to_dev(go, "f32"))
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        e = _rel(to_np(x), to_np(y), 1e-2 * float(np.linalg.norm(go)))
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 1e-2, name
