@@ -105,7 +105,7 @@ def main():
                     help="quadratic workload: weights (q_hat . k_hat)^(2r) of the even-order lift psi_2r")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -16,7 +16,7 @@ or key is split into g consecutive blocks u = (u_1, ..., u_g) of m components;
 The readout is the same normalised form as for the full map (normalized-readout
 paragraph): o_t = sum_{s<=t} w_ts v_s / sum_{s<=t} w_ts with w_ts = <psi(q_t), psi(k_s)>.
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
   * the whole d-vector is projected onto the unit sphere first (the full map's
     preprocessing), then split into blocks; at g = 1 this is the full map;
   * packed order: Sigma g uses the full map's order for an m x m matrix (row-major upper
@@ -152,7 +152,7 @@ def decode_steps_family(S0, Z0, q, k, v, family: str, g: int = 1):
 # psi_2r): the same p-dimensional projection generates psi_2r(u) = u^{(x) 2r}, with
 # <psi_2r(u), psi_2r(v)> = (u . v)^{2r} >= 0 and symmetric ambient dimension
 # binom(p + 2r - 1, 2r); the pages use r = 1.
-# Reading (listed in the design doc): the symmetric tensor is packed over multisets
+# Reading (the pages give only the dimension): the symmetric tensor is packed over multisets
 # i_1 <= ... <= i_2r in lexicographic order, coordinate sqrt(multinomial) * prod u_i, so the
 # packed Euclidean inner product is the tensor one (r = 1: the full map's packing).
 

@@ -16,7 +16,7 @@ Source: "Kernelized Linear Attention: Breaking the Capacity Wall with Symmetric 
   * chunked-forward paragraph (three kernels, wall-clock model): the inter-chunk
     recurrence is an associative prefix sum of per-chunk (S_loc, Z_loc).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * packed order = row-major upper triangle incl. diagonal; off-diagonals scaled by
     sqrt(2) so that the packed Euclidean inner product equals the Frobenius one;
   * no epsilon in the normalisation (a zero vector lifts to zero) and none in the
@@ -58,7 +58,7 @@ def packed_pairs(p: int) -> tuple[np.ndarray, np.ndarray]:
 
 def normalize(u: np.ndarray) -> np.ndarray:
     """Project rows onto the unit sphere S^{p-1} (rank-one lift paragraph). A zero row
-    stays zero (no epsilon; reading listed in the design doc)."""
+    stays zero (no epsilon: the pages state none)."""
     u = np.asarray(u, dtype=np.float64)
     nrm = np.sqrt(np.sum(u * u, axis=-1, keepdims=True))
     out = np.zeros_like(u)
