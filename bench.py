@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (the figure counts packed dual-rate FMAs)
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_normalize_amd", "csrc")
 
@@ -101,6 +102,10 @@ def main():
                     help="PSD feature family of the quadratic workload (sigma = KATA-Sigma g, "
                          "block = KATA-M g)")
     ap.add_argument("--g", type=int, default=1, help="feature blocks of --family")
+    ap.add_argument("--bwd-form", default="flash", choices=["flash", "chunked"],
+                    help="backward workload: flash-style MFMA kernels or the O(T) state form")
+    ap.add_argument("--bwd-shape", default="quadratic", choices=["quadratic", "long"],
+                    help="backward workload: the quadratic shape or the long shape")
     ap.add_argument("--order", type=int, default=1,
                     help="quadratic workload: weights (q_hat . k_hat)^(2r) of the even-order lift psi_2r")
     args = ap.parse_args()
@@ -200,27 +205,39 @@ def main():
         traffic_file = ("quadratic_traffic.txt" if fam == "full" else f"quadratic_{fam}{g}_traffic.txt") \
             if r == 1 else f"quadratic_order{r}_traffic.txt"
     elif args.workload == "backward":
-        # gradients of the quadratic shape (O(T^2) fp32 VALU kernels, any input dtype)
-        w = WORKLOADS["quadratic"]
+        # gradients on the quadratic shape or the long shape, flash-style or state form
+        w = WORKLOADS[args.bwd_shape]
         B, H, T, p, dv = w.B, w.H, w.T, w.p, w.dv
         q, k, v = draw_qkv(w.seed, B, H, T, p, dv, w.dtype)
         go = np.random.default_rng(w.seed + 100).standard_normal((B, H, T, dv), dtype=np.float32)
         to = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
         qd, kd, vd, gd = to(q), to(k), to(v), to(go)  # the output gradient in the inputs' dtype
-        step = [lambda: kata.quadratic_bwd(qd, kd, vd, gd)]
-        dominant = 0
-        kernel_name = "quadratic_bf16_kernel (statistics) + bwd_keys_kernel + bwd_queries_kernel"
-        pairs = B * H * T * (T + 1) // 2
-        # per causal pair: the forward's statistics (scores 2p, W.[V | 1] 2 (dv + 1)), the
-        # scores once more (2p), dP = g . v (2 dv), dV (2 dv), dK (2p) and dQ (2p)
-        flops = (8 * p + 6 * dv + 2) * pairs
         units = B * T
-        metric = "quadratic-form KATA backward tokens/s (1 GPU) + % bf16 MFMA peak"
-        config = {"workload": f"backward: gradients of the flash-style forward B={B} H={H} T={T} p={p} dv={dv}, "
-                              "bf16 inputs", "global_batch": B, "seq_len": T, "heads": H,
-                  "p": p, "dv": dv, "parallelism": "single-gpu"}
-        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
-        traffic_file = "backward_traffic.txt"
+        if args.bwd_form == "flash":
+            step = [lambda: kata.quadratic_bwd(qd, kd, vd, gd)]
+            kernel_name = "quadratic_bf16_kernel (statistics) + bwd_keys_kernel + bwd_queries_kernel"
+            pairs = B * H * T * (T + 1) // 2
+            # per causal pair: the forward's statistics (scores 2p, W.[V | 1] 2 (dv + 1)), the
+            # scores once more (2p), dP = g . v (2 dv), dV (2 dv), dK (2p) and dQ (2p)
+            flops = (8 * p + 6 * dv + 2) * pairs
+            metric = "quadratic-form KATA backward tokens/s (1 GPU) + % bf16 MFMA peak"
+            bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            Cb = 16
+            step = [lambda: kata.chunked_bwd(qd, kd, vd, gd, C=Cb)]
+            kernel_name = "chunked_bwd_kernel (4 passes) + segment_scan_kernel"
+            n = p * (p + 1) // 2
+            # per head-token, the state form: the forward recompute, X = S a + Z b, the two state
+            # updates, Y = R v + r (2 n (dv + 1) each), dv = R^T psi(k) (2 n dv), the two lift
+            # transposes (4 n each), and the chunk's pairs (about C / 2 of them, 4 (p + dv) each)
+            flops = (10 * n * (dv + 1) + 2 * n * dv + 8 * n + 2 * Cb * (p + dv)) * B * H * T
+            metric = "state-form (O(T)) KATA backward tokens/s (1 GPU) + % fp32 vector peak"
+            bound, peak, unit = "alu", PEAK_FP32_VECTOR_TFLOPS, "TFLOP/s"
+        dominant = 0
+        config = {"workload": f"backward ({args.bwd_form}): gradients of the forward B={B} H={H} T={T} p={p} "
+                              f"dv={dv}, bf16 inputs", "global_batch": B, "seq_len": T, "heads": H,
+                  "p": p, "dv": dv, "form": args.bwd_form, "parallelism": "single-gpu"}
+        traffic_file = f"backward_{args.bwd_form}_{args.bwd_shape}_traffic.txt"
         args.no_cpu_baseline = True
     elif args.workload == "varlen":
         # packed sequences of mixed length (token-major, cu_seqlens): VARLEN in kata_inputs

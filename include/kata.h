@@ -320,6 +320,28 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                  kata_feature_t fam, int g, float* dq, float* dk, float* dv_out,
                                  void* workspace, size_t workspace_bytes, kata_stream_t stream);
 
+/*
+ * kata_chunked_bwd - the same gradients as kata_quadratic_bwd for the full map, in O(T):
+ * the state form of the forward (feature-value state display, normalized readout, chunked
+ * forward paragraph of the HTML page) differentiated. A forward-time pass over the chunks
+ * carries [S | Z] and gives D_t, delta_t and dq; a reverse-time pass carries
+ * [R | r] = sum_{t>=s} psi(q_hat_t) [g_t / D_t | -delta_t / D_t] and gives dk and dv. Both
+ * passes are split into segments whose summaries are scanned like the forward's (scan).
+ *   q, k : [B, H, T, p] and v, grad_o : [B, H, T, dv] in in_dt; dq, dk : [B, H, T, p] and
+ *   dv_out : [B, H, T, dv] float32, written. workspace: at least
+ *   kata_chunked_bwd_workspace_bytes(B, H, T, p, dv, C, scan) bytes (D_t, delta_t per row and
+ *   the two sets of segment summaries); 0 means unsupported arguments.
+ *   fp32 VALU kernels (a correct O(T) path for long sequences; the MFMA kernels of
+ *   kata_quadratic_bwd are faster at moderate T). Supported: p <= 64, dv <= 64, C in
+ *   {16, 32, 64} with the state n (dv + 1) fp32 and the chunk's rows within 160 KB of LDS
+ *   (p = 32, dv = 64 needs C = 16); else KATA_ERR_UNSUPPORTED. Outputs must not overlap each
+ *   other, the inputs or the workspace.
+ */
+size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan);
+kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, const void* grad_o, kata_dtype_t in_dt,
+                               int B, int H, int T, int p, int dv, int C, kata_scan_t scan, float* dq, float* dk,
+                               float* dv_out, void* workspace, size_t workspace_bytes, kata_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

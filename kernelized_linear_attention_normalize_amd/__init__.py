@@ -20,7 +20,7 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -85,6 +85,10 @@ def load():
     lib.kata_lift_order.argtypes, lib.kata_lift_order.restype = [P, I, I64, I, I, P, I, P], I
     lib.kata_quadratic_fwd_order.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd_order.restype = I
+    lib.kata_chunked_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.kata_chunked_bwd_workspace_bytes.restype = SZ
+    lib.kata_chunked_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
+    lib.kata_chunked_bwd.restype = I
     lib.kata_quadratic_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.kata_quadratic_bwd_workspace_bytes.restype = SZ
     lib.kata_quadratic_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
@@ -407,6 +411,32 @@ def quadratic_bwd(q, k, v, grad_o, family: str = "full", g: int = 1):
         _check(lib.kata_quadratic_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), _dt(q),
                                       B, H, T, p, dv, _fam(family, g), g, dq.data_ptr(), dk.data_ptr(),
                                       dvv.data_ptr(), ws.data_ptr(), need, _stream(dev)), "kata_quadratic_bwd")
+    return dq, dk, dvv
+
+
+def chunked_bwd(q, k, v, grad_o, C: int = 32, scan="associative", workspace=None):
+    """O(T) gradients (dq, dk, dv) of the causal full-map forward, float32, from the state form
+    (fp32 VALU kernels). q, k: [B,H,T,p]; v, grad_o: [B,H,T,dv], one dtype."""
+    lib = load()
+    dev = _dev(q, k, v, grad_o)
+    B, H, T, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or grad_o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v and grad_o")
+    if not (q.dtype == k.dtype == v.dtype == grad_o.dtype):
+        raise TypeError("q, k, v and grad_o must share one dtype")
+    sc = _scan_code(scan)
+    dq = torch.empty((B, H, T, p), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dvv = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kata_chunked_bwd_workspace_bytes(B, H, T, p, dv, C, sc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_chunked_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), _dt(q), B, H, T, p,
+                                    dv, C, sc, dq.data_ptr(), dk.data_ptr(), dvv.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(dev)),
+               "kata_chunked_bwd")
     return dq, dk, dvv
 
 

@@ -509,6 +509,55 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                                (hipStream_t)stream));
 }
 
+static bool chunked_bwd_supported(int p, int dv, int C) {
+  return p >= 1 && p <= 64 && dv >= 1 && dv <= 64 && in_set(C, {16, 32, 64}) &&
+         kata::chunked_bwd_lds_bytes(p, dv, C) <= 160 * 1024;
+}
+
+size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan) {
+  if (B <= 0 || H <= 0 || T <= 0 || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
+  if (!chunked_bwd_supported(p, dv, C)) return 0;
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  const size_t rows = (size_t)B * H * T;
+  const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
+  return (rows * 2 + 2 * sums) * sizeof(float);
+}
+
+kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, const void* grad_o, kata_dtype_t in_dt,
+                               int B, int H, int T, int p, int dv, int C, kata_scan_t scan, float* dq, float* dk,
+                               float* dv_out, void* workspace, size_t workspace_bytes, kata_stream_t stream) {
+  if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
+  if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
+  if (B < 0 || H < 0 || T < 0 || p < 1 || dv < 1 || C < 1) return KATA_ERR_SHAPE;
+  if (!chunked_bwd_supported(p, dv, C)) return KATA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * T == 0) return KATA_OK;
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  if (mul4(B, H, T, p > dv ? p : dv) < 0 || (int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
+  for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
+    if (!aligned16(ptr)) return KATA_ERR_ALIGN;
+  const size_t need = kata_chunked_bwd_workspace_bytes(B, H, T, p, dv, C, scan);
+  if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KATA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * T;
+  const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
+  const void* outs[4] = {dq, dk, dv_out, workspace};
+  const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], q, qb) || overlap(outs[i], outb[i], k, qb) || overlap(outs[i], outb[i], v, vb) ||
+        overlap(outs[i], outb[i], grad_o, vb))
+      return KATA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
+  }
+  float* stats = static_cast<float*>(workspace);
+  const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
+  float* fsum = stats + rows * 2;
+  float* rsum = fsum + sums;
+  return hip_status(kata::launch_chunked_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, T, p, dv, C, plan,
+                                             stats, fsum, rsum, dq, dk, dv_out, (hipStream_t)stream));
+}
+
 int64_t kata_order_dim(int p, int r) {
   if (p < 1 || r < 1 || r > 4) return -1;
   double c = 1.0;  // binom(p + 2r - 1, 2r)

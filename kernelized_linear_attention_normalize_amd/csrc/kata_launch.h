@@ -78,6 +78,12 @@ hipError_t launch_chunked_bf16_sigma2(const uint16_t* q, const uint16_t* k, cons
                                       float* ws, float* s_out, float* z_out, const int* lens, hipStream_t st);
 // gradients of the quadratic form (VALU): ws holds 2 floats (D_t, g_t . o_t) per row
 int bwd_pairs(int p, int fam, int g);
+// O(T) chunked backward of the full map (fp32 VALU): LDS bytes, summary floats, launch
+size_t chunked_bwd_lds_bytes(int p, int dv, int C);
+int64_t chunked_bwd_state_floats(int p, int dv);
+hipError_t launch_chunked_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B, int H,
+                              int T, int p, int dv, int C, const SegPlan& plan, float* stats, float* fsum,
+                              float* rsum, float* dq, float* dk, float* dvo, hipStream_t st);
 // full map, bf16 q, k, v, gout: MFMA backward (p, dv in {32, 64}); stats: 2 floats per row
 bool quadratic_bwd_mfma_supported(int p, int dv);
 hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,

@@ -207,6 +207,25 @@ def test_varlen_validation(lib):
     assert need > 0 and vl(scan=ASSOC, max_len=200 * 64, total=300) == E_WS
 
 
+def test_chunked_bwd_validation(lib):
+    need = lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 16, ASSOC)
+    assert need >= 2 * 1000 * 2 * 4
+    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 32, ASSOC) == 0   # LDS: C = 16 only
+    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 96, 64, 16, ASSOC) == 0
+    args = lambda **kw: dict(dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, dt=BF16, B=1, H=2, T=1000, p=32, dv=64,
+                                  C=16, scan=ASSOC, dq=A + (1 << 30), dk=A + (2 << 30), dvo=A + (3 << 30),
+                                  ws=A + (4 << 30), wsb=need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.kata_chunked_bwd(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["T"], a["p"], a["dv"],
+                                    a["C"], a["scan"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"], None)
+    assert call(C=32) == E_UNSUP and call(scan=7) == E_SCAN and call(dt=5) == E_DTYPE
+    assert call(dq=None) == E_NULL and call(wsb=need - 1) == E_WS and call(ws=None) == E_WS
+    assert call(dk=A + (1 << 30)) == E_ALIAS                       # dk on top of dq
+    assert call(T=0) == OK and call(B=0) == OK
+
+
 def test_higher_orders(lib):
     from oracle import kata_families as kf
     for p, r in [(4, 2), (16, 2), (3, 3), (8, 4), (64, 1)]:

@@ -99,3 +99,43 @@ def test_quadratic_bwd_mfma_matches_valu_path():
         e = _rel(to_np(x), to_np(y), 1e-2 * float(np.linalg.norm(go)))
         print(f"  {name} rel={e:.2e}", flush=True)
         assert e <= 1e-2, name
+
+
+# ------------------------------------------------------------------ O(T) chunked path
+@pytest.mark.parametrize("dt,p,dv,C,T,scan", [
+    ("f32", 16, 16, 16, 1, "sequential"), ("f32", 16, 32, 32, 300, "associative"),
+    ("bf16", 32, 64, 16, 517, "associative"), ("bf16", 32, 32, 32, 1000, "sequential"),
+    ("f32", 16, 64, 64, 777, "associative"), ("bf16", 32, 16, 64, 130, "associative")])
+def test_chunked_bwd_matches_oracle(dt, p, dv, C, T, scan):
+    """kata_chunked_bwd (state form, fp32 arithmetic) against the float64 backward oracle:
+    normwise <= 2e-4 per gradient tensor (T = 1: dq, dk are exactly zero, so only dv)."""
+    print(f"[case] chunked bwd {dt} p={p} dv={dv} C={C} T={T} {scan}", flush=True)
+    q, k, v = draw_qkv(81, 2, 3, T, p, dv, dt)
+    go = draw_qkv(82, 2, 3, T, dv, dv, dt)[0]
+    if T > 4:
+        q[0, 2, 3] = 0.0
+        k[1, 1, T // 2] = 0.0
+    ref = kb.backward(q, k, v, go)
+    got = kata.chunked_bwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(go, dt), C=C, scan=scan)
+    floor = 1e-2 * float(np.linalg.norm(go))
+    names = ("dq", "dk", "dv") if T > 1 else ("dv",)
+    for name in names:
+        i = ("dq", "dk", "dv").index(name)
+        e = _rel(to_np(got[i]), ref[i], floor)
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 2e-4, name
+    if T > 4:
+        assert np.all(to_np(got[0])[0, 2, 3] == 0.0) and np.all(to_np(got[1])[1, 1, T // 2] == 0.0)
+
+
+def test_chunked_bwd_long_matches_quadratic_path():
+    """A longer sequence with many segments: the O(T) path and the flash-style VALU path
+    (fp32 inputs) agree."""
+    q, k, v = draw_qkv(83, 1, 2, 3000, 32, 32, "f32")
+    go = draw_qkv(84, 1, 2, 3000, 32, 32, "f32")[0]
+    a = kata.chunked_bwd(*(to_dev(x, "f32") for x in (q, k, v, go)), C=32)
+    b = kata.quadratic_bwd(*(to_dev(x, "f32") for x in (q, k, v, go)))
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        e = _rel(to_np(x), to_np(y), 1e-2 * float(np.linalg.norm(go)))
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 2e-4, name
