@@ -29,6 +29,8 @@
  *     are computed in fp32 throughout.
  *   - Errors are reported only through the returned status; KATA_ERR_HIP means the
  *     kernel launch failed (hipGetLastError) and the outputs are unspecified.
+ *   - The [B, H, T, *] forwards address one sequence with 32-bit byte offsets:
+ *     T * max(p, dv) * 4 must stay below 2^31 (KATA_ERR_SHAPE otherwise).
  */
 #ifndef KATA_H
 #define KATA_H

@@ -150,6 +150,8 @@ static kata_status_t check_fwd(const void* q, const void* k, const void* v, kata
     return KATA_OK;
   }
   if (mul4(B, H, T, p > dv ? p : dv) < 0) return KATA_ERR_SHAPE;
+  // the kernels address one sequence with 32-bit byte offsets (4-byte elements at most)
+  if ((int64_t)T * (p > dv ? p : dv) * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
   if (!q || !k || !v || !o) return KATA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KATA_ERR_ALIGN;
   return KATA_OK;

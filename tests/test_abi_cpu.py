@@ -179,6 +179,14 @@ def test_feature_families(lib):
     assert ch(B=1, H=4, T=65536, scan=ASSOC, o=A + (1 << 34)) == E_WS
 
 
+def test_sequence_length_limit(lib):
+    """One sequence is addressed with 32-bit byte offsets: T * max(p, dv) * 4 < 2^31."""
+    T = (1 << 31) // (64 * 4)  # exactly at the limit for dv = 64
+    assert lib.kata_quadratic_fwd(A, A + 4096, A + 8192, BF16, A + (1 << 40), BF16, 1, 1, T, 32, 64, None) == E_SHAPE
+    assert lib.kata_chunked_fwd(A, A + 4096, A + 8192, BF16, A + (1 << 40), BF16, 1, 1, T, 32, 64, 64, SEQ, None, 0,
+                                None) == E_SHAPE
+
+
 def test_varlen_validation(lib):
     """kata_chunked_fwd_varlen: argument errors come back before any device access."""
     FULL, SIGMA = 0, 1
