@@ -333,11 +333,15 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
  *   dv_out : [B, H, T, dv] float32, written. workspace: at least
  *   kata_chunked_bwd_workspace_bytes(B, H, T, p, dv, C, scan) bytes (D_t, delta_t per row and
  *   the two sets of segment summaries); 0 means unsupported arguments.
- *   fp32 VALU kernels (a correct O(T) path for long sequences; the MFMA kernels of
- *   kata_quadratic_bwd are faster at moderate T). Supported: p <= 64, dv <= 64, C in
- *   {16, 32, 64} with the state n (dv + 1) fp32 and the chunk's rows within 160 KB of LDS
- *   (p = 32, dv = 64 needs C = 16); else KATA_ERR_UNSUPPORTED. Outputs must not overlap each
- *   other, the inputs or the workspace.
+ *   bf16 inputs with p in {16, 32} and dv in {32, 64} run bf16 MFMA kernels: the bf16
+ *   chunked forward (o in fp32 and its segment prefixes, in the workspace), then 32-token
+ *   chunks whose state contractions, lift and lift transpose stay on chip; C only has to be
+ *   in {16, 32, 64} there, and products are rounded to bf16 before fp32 accumulation as in
+ *   the forward (normwise error about 1e-3 against the exact gradients). Other shapes and
+ *   fp32 inputs run fp32 VALU kernels with the state n (dv + 1) fp32 and the chunk's rows
+ *   within 160 KB of LDS (p <= 64, dv <= 64; p = 32, dv = 64 needs C = 16). Otherwise
+ *   KATA_ERR_UNSUPPORTED. The workspace size depends on the shape, not on in_dt, and covers
+ *   both paths. Outputs must not overlap each other, the inputs or the workspace.
  */
 size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan);
 kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, const void* grad_o, kata_dtype_t in_dt,

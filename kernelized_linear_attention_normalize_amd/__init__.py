@@ -415,8 +415,9 @@ def quadratic_bwd(q, k, v, grad_o, family: str = "full", g: int = 1):
 
 
 def chunked_bwd(q, k, v, grad_o, C: int = 32, scan="associative", workspace=None):
-    """O(T) gradients (dq, dk, dv) of the causal full-map forward, float32, from the state form
-    (fp32 VALU kernels). q, k: [B,H,T,p]; v, grad_o: [B,H,T,dv], one dtype."""
+    """O(T) gradients (dq, dk, dv) of the causal full-map forward, float32, from the state form:
+    bf16 MFMA kernels for bf16 inputs with p in {16, 32} and dv in {32, 64}, fp32 VALU kernels
+    (chunk C) otherwise. q, k: [B,H,T,p]; v, grad_o: [B,H,T,dv], one dtype."""
     lib = load()
     dev = _dev(q, k, v, grad_o)
     B, H, T, p = q.shape

@@ -511,18 +511,31 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                                (hipStream_t)stream));
 }
 
-static bool chunked_bwd_supported(int p, int dv, int C) {
+// fp32 VALU state-form kernels: the chunk's rows and the fp32 state within LDS
+static bool chunked_bwd_valu_supported(int p, int dv, int C) {
   return p >= 1 && p <= 64 && dv >= 1 && dv <= 64 && in_set(C, {16, 32, 64}) &&
          kata::chunked_bwd_lds_bytes(p, dv, C) <= 160 * 1024;
+}
+// a shape one of the two paths runs (the bf16 MFMA kernels choose their own chunking)
+static bool chunked_bwd_supported(int p, int dv, int C) {
+  return in_set(C, {16, 32, 64}) && (chunked_bwd_valu_supported(p, dv, C) || kata::chunked_bwd_mfma_supported(p, dv));
 }
 
 size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan) {
   if (B <= 0 || H <= 0 || T <= 0 || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
   if (!chunked_bwd_supported(p, dv, C)) return 0;
-  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
-  const size_t rows = (size_t)B * H * T;
-  const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
-  return (rows * 2 + 2 * sums) * sizeof(float);
+  size_t need = 0;
+  if (chunked_bwd_valu_supported(p, dv, C)) {
+    const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+    const size_t rows = (size_t)B * H * T;
+    const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
+    need = (rows * 2 + 2 * sums) * sizeof(float);
+  }
+  if (kata::chunked_bwd_mfma_supported(p, dv)) {  // the size does not depend on the input dtype
+    const size_t m = kata::chunked_bwd_mfma_workspace_floats(B, H, T, p, dv, scan) * sizeof(float);
+    need = m > need ? m : need;
+  }
+  return need;
 }
 
 kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, const void* grad_o, kata_dtype_t in_dt,
@@ -532,9 +545,13 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (B < 0 || H < 0 || T < 0 || p < 1 || dv < 1 || C < 1) return KATA_ERR_SHAPE;
   if (!chunked_bwd_supported(p, dv, C)) return KATA_ERR_UNSUPPORTED;
+  const bool mfma = in_dt == KATA_DTYPE_BF16 && kata::chunked_bwd_mfma_supported(p, dv);
+  if (!mfma && !chunked_bwd_valu_supported(p, dv, C)) return KATA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * T == 0) return KATA_OK;
-  const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
+  const kata::SegPlan plan = kata::seg_plan(B, H, T, mfma ? kata::CHUNKED_BWD_FWD_C : C, scan);
   if (mul4(B, H, T, p > dv ? p : dv) < 0 || (int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
+  // the forward that the MFMA path runs first addresses a sequence with 32-bit byte offsets
+  if (mfma && (int64_t)T * (p > dv ? p : dv) * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
   if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
   for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
     if (!aligned16(ptr)) return KATA_ERR_ALIGN;
@@ -552,6 +569,11 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
   }
+  if (mfma)
+    return hip_status(kata::launch_chunked_bwd_mfma(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<const uint16_t*>(grad_o), B, H, T, p, dv, (int)scan, static_cast<float*>(workspace), dq, dk,
+        dv_out, (hipStream_t)stream));
   float* stats = static_cast<float*>(workspace);
   const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
   float* fsum = stats + rows * 2;

@@ -84,6 +84,14 @@ int64_t chunked_bwd_state_floats(int p, int dv);
 hipError_t launch_chunked_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B, int H,
                               int T, int p, int dv, int C, const SegPlan& plan, float* stats, float* fsum,
                               float* rsum, float* dq, float* dk, float* dvo, hipStream_t st);
+// O(T) chunked backward of the full map on bf16 MFMA (p in {16, 32}, dv in {32, 64}); the
+// forward it runs first (for o and the segment prefixes) uses chunks of CHUNKED_BWD_FWD_C
+constexpr int CHUNKED_BWD_FWD_C = 128;
+bool chunked_bwd_mfma_supported(int p, int dv);
+size_t chunked_bwd_mfma_workspace_floats(int B, int H, int T, int p, int dv, int scan);
+hipError_t launch_chunked_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* go,
+                                   int B, int H, int T, int p, int dv, int scan, float* ws, float* dq, float* dk,
+                                   float* dvo, hipStream_t st);
 // full map, bf16 q, k, v, gout: MFMA backward (p, dv in {32, 64}); stats: 2 floats per row
 bool quadratic_bwd_mfma_supported(int p, int dv);
 hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,

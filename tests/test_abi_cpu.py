@@ -217,9 +217,15 @@ def test_varlen_validation(lib):
 
 def test_chunked_bwd_validation(lib):
     need = lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 16, ASSOC)
-    assert need >= 2 * 1000 * 2 * 4
-    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 32, ASSOC) == 0   # LDS: C = 16 only
+    # covers the bf16 MFMA path: stats and two sets of segment summaries (8 segments of 128
+    # tokens per head here, 34,816 floats each at p = 32, dv = 64)
+    assert need >= (2 * 1000 * 2 + 2 * 2 * 7 * 34816) * 4
+    # p = 32, dv = 64 at C = 32: the bf16 MFMA path runs it (any C in {16, 32, 64}), the fp32
+    # VALU path does not (its LDS holds that state with C = 16 only)
+    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 32, ASSOC) > 0
+    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 32, 64, 8, ASSOC) == 0
     assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 96, 64, 16, ASSOC) == 0
+    assert lib.kata_chunked_bwd_workspace_bytes(1, 2, 1000, 48, 48, 32, ASSOC) == 0  # neither path
     args = lambda **kw: dict(dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, dt=BF16, B=1, H=2, T=1000, p=32, dv=64,
                                   C=16, scan=ASSOC, dq=A + (1 << 30), dk=A + (2 << 30), dvo=A + (3 << 30),
                                   ws=A + (4 << 30), wsb=need), **kw)
@@ -228,7 +234,8 @@ def test_chunked_bwd_validation(lib):
         a = args(**kw)
         return lib.kata_chunked_bwd(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["T"], a["p"], a["dv"],
                                     a["C"], a["scan"], a["dq"], a["dk"], a["dvo"], a["ws"], a["wsb"], None)
-    assert call(C=32) == E_UNSUP and call(scan=7) == E_SCAN and call(dt=5) == E_DTYPE
+    assert call(C=32, dt=F32) == E_UNSUP and call(C=8) == E_UNSUP
+    assert call(scan=7) == E_SCAN and call(dt=5) == E_DTYPE
     assert call(dq=None) == E_NULL and call(wsb=need - 1) == E_WS and call(ws=None) == E_WS
     assert call(dk=A + (1 << 30)) == E_ALIAS                       # dk on top of dq
     assert call(T=0) == OK and call(B=0) == OK
