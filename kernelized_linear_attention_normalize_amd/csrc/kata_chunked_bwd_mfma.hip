@@ -24,7 +24,9 @@
 //          must vanish (at t = 0, o_0 = v_0 whatever q_0 is);
 //   rsum : [R | 2N] of every segment but the first, scanned in reversed slot order so that a
 //          slot holds the suffix of the segments after one;
-//   rdk  : reverse time from each segment's suffix: dk and dv.
+//   rdk  : reverse time from each segment's suffix, two kernels that each rebuild R: dk (R v_s
+//          through the lift's transpose) and dv (R^T psi(k_hat_s), one value-column tile of
+//          one key tile per wave, so no sums across waves).
 //
 // Layouts. States use the feature tiles of the forward (33 tiles of 16 rows at p = 32, each
 // row a pair (i, j) of components; see kata_chunked.h) but are built with the forward
@@ -36,7 +38,8 @@
 // Y[x] = u[(x & ~15) | ((x + 4 g) & 15)] as in the forward readout, every feature row of
 // a tile is a product Y_a Y_b of two compile-time registers, and its gradient adds x Y_b to
 // G[a] and x Y_a to G[b] of an equally rotated accumulator (the state carries c_f^2 like the
-// forward's, so the lift's constants cancel). The lanes' G are summed through LDS adds.
+// forward's, so the lift's constants cancel). The lanes' G are summed in registers (lane groups g and g + 2,
+// whose rotations differ by 8) and then across waves through per-wave LDS partials.
 #include "kata_chunked.h"
 
 namespace kata {
@@ -44,7 +47,6 @@ namespace cbm {
 using namespace chk;
 
 constexpr int CB = 32;   // tokens per chunk
-constexpr int AP = 36;   // pitch of the transposed gradient accumulators (2-way LDS add banks)
 
 template <int P, int DV>
 struct Lay {
@@ -186,14 +188,29 @@ __device__ __forceinline__ void gram_apply(const uint16_t* mm, bf16x8_t ub, int 
     X[rt] = mfma(__builtin_bit_cast(bf16x8_t, u32x4_t{l0[0], l0[1], l1[0], l1[1]}), ub, X[rt]);
   }
 }
-// G (rotated by 4 lg) added into the transposed accumulator acc[comp][AP] at token column t
+// Lanes 0..31 end with the sum of this lane's G and that of lane + 32 (lane group lg + 2,
+// whose rotation differs by 8: its element x ^ 8 is this lane's element x); the upper half's
+// G is left as it was.
 template <int P>
-__device__ __forceinline__ void add_rotated(float* acc, const float (&G)[P], int t, int lg) {
+__device__ __forceinline__ void pair_sum_lo(float (&G)[P]) {
+  float H[P];
 #pragma unroll
   for (int x = 0; x < P; ++x) {
-    const int comp = (x & ~15) | ((x + 4 * lg) & 15);
-    __hip_atomic_fetch_add(acc + comp * AP + t, G[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(G[x ^ 8]), __float_as_uint(G[x]), false, false);
+    H[x] = __uint_as_float(r[1]);  // lanes 0..31: G[x ^ 8] of lane + 32
   }
+#pragma unroll
+  for (int x = 0; x < P; ++x) G[x] += H[x];
+}
+// rotated G of lane group lg (< 2) stored un-rotated as row t of a [rows][P + 4] fp32 slot
+template <int P>
+__device__ __forceinline__ void store_rotated(float* slot, const float (&G)[P], int t, int lg) {
+#pragma unroll
+  for (int h = 0; h < P / 16; ++h)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<f32x4_t*>(slot + t * (P + 4) + 16 * h + ((4 * u + 4 * lg) & 15)) =
+          f32x4_t{G[16 * h + 4 * u], G[16 * h + 4 * u + 1], G[16 * h + 4 * u + 2], G[16 * h + 4 * u + 3]};
 }
 
 // ---- per-thread staging of one chunk: waves 0-1 q pieces, 2-3 k pieces (4 threads per row),
@@ -247,11 +264,13 @@ struct FL {
   static constexpr int VR = VT + DV * LY::VTP * 2;             // v rows bf16 [CB][RP]
   static constexpr int GR = VR + CB * LY::RP * 2;              // g rows bf16
   static constexpr int MM = GR + CB * LY::RP * 2;              // Gram halves bf16 [2][P][MP]
-  static constexpr int DQ = MM + 2 * P * LY::MP * 2;           // dq_hat fp32 [P][AP]
-  static constexpr int IQ = DQ + P * AP * 4;                   // 1 / |q| [2][CB]
-  static constexpr int DL = IQ + 2 * CB * 4;                   // psi(q_hat)^T S g partial sums [CB]
-  static constexpr int ID = DL + CB * 4;                       // 1 / D [CB]
+  static constexpr int GP = MM + 2 * P * LY::MP * 2;           // dq_hat partials fp32 [8 waves x 2][CB][P + 4]
+  static constexpr int G2 = GP + 16 * CB * (P + 4) * 4;        // the owners' part of dq_hat [CB][P + 4]
+  static constexpr int IQ = G2 + CB * (P + 4) * 4;             // 1 / |q| [2][CB]
+  static constexpr int DL = IQ + 2 * CB * 4;                   // psi(q_hat)^T S g partials [8 waves][CB]
+  static constexpr int ID = DL + 8 * CB * 4;                   // 1 / D [CB]
   static constexpr int BYTES = ID + CB * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <int P, int DV, int W>
@@ -333,7 +352,8 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + FLY::VR);
   const uint16_t* gr = reinterpret_cast<const uint16_t*>(lds + FLY::GR);
   uint16_t* mm = reinterpret_cast<uint16_t*>(lds + FLY::MM);
-  float* dqa = reinterpret_cast<float*>(lds + FLY::DQ);
+  float* gp = reinterpret_cast<float*>(lds + FLY::GP);
+  float* g2s = reinterpret_cast<float*>(lds + FLY::G2);
   const float* iq = reinterpret_cast<const float*>(lds + FLY::IQ);
   float* dla = reinterpret_cast<float*>(lds + FLY::DL);
   float* idl = reinterpret_cast<float*>(lds + FLY::ID);
@@ -363,8 +383,6 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
   stg.load(a, row0, c0 * CB);
   stg.stage(lds, c0 & 1);
   write_gram<P, MT>(mm, Mt, ln, lg);
-  for (int e = threadIdx.x; e < P * AP; e += 512) dqa[e] = 0.f;
-  if (threadIdx.x < CB) dla[threadIdx.x] = 0.f;
   __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
@@ -446,16 +464,19 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
          ...);
       }(std::make_integer_sequence<int, NTW>{});
       {
-        // psi(q_hat_t)^T (S g_t) = (1/2) sum_x Y[x] G[x] (psi is homogeneous of degree 2)
+        // psi(q_hat_t)^T (S g_t) = (1/2) sum_x Y[x] G[x] (psi is homogeneous of degree 2),
+        // summed over this wave's feature rows
         float ds = 0.f;
 #pragma unroll
         for (int x = 0; x < P; ++x) ds += Y[x] * G[x];
-        __hip_atomic_fetch_add(dla + t, 0.5f * ds, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        ds = xor32_sum(xor16_sum(ds));
+        if (lg == 0) dla[W * CB + t] = 0.5f * ds;
         const float s = idl[t];
 #pragma unroll
         for (int x = 0; x < P; ++x) G[x] *= s;
       }
-      add_rotated<P>(dqa, G, t, lg);
+      pair_sum_lo<P>(G);
+      if (lg < 2) store_rotated<P>(gp + (2 * W + lg) * CB * (P + 4), G, t, lg);
     }
     {  // build: S^T += V^T psi(K), 2 M += (sqrt2 K)^T (sqrt2 K)
       float N[NH][8];
@@ -480,7 +501,10 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
     // (v_s . g_t - delta_t) / D_t 2 (q_hat_t . k_hat_s) k_hat_s over keys s <= t
     if constexpr (OWN) {
       const int t = 16 * TT + ln;
-      const float delta = (dla[t] + dintra) * invD;
+      float sd = dintra;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) sd += dla[w * CB + t];
+      const float delta = sd * invD;
       const float bt = -delta * invD;
       float G2[NH][4];
 #pragma unroll
@@ -501,11 +525,10 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) G2[h][r] += out[r];
       }
-      // components 16 h + 4 lg + r of token t: one lane each, after every wave's adds
+      // components 16 h + 4 lg + r of token t: one lane each
 #pragma unroll
       for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dqa[(16 * h + 4 * lg + r) * AP + t] += G2[h][r];
+        *reinterpret_cast<f32x4_t*>(g2s + t * (P + 4) + 16 * h + 4 * lg) = f32x4_t{G2[h][0], G2[h][1], G2[h][2], G2[h][3]};
       if (lg == 0 && t0 + t < a.T)
         *reinterpret_cast<f32x2_t*>(a.stats + (row0 + t0 + t) * 2) = f32x2_t{Dt, delta};
     }
@@ -516,13 +539,10 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
       const int u = threadIdx.x - 256;
       if (u < CB * TPR) {
         const int r = u / TPR, c4 = (u % TPR) * 4;
-        float d[4];
+        f32x4_t dsum = *reinterpret_cast<const f32x4_t*>(g2s + r * (P + 4) + c4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[e] = dqa[(c4 + e) * AP + r];
-          dqa[(c4 + e) * AP + r] = 0.f;
-        }
-        if (c4 == 0) dla[r] = 0.f;
+        for (int j = 0; j < 16; ++j) dsum += *reinterpret_cast<const f32x4_t*>(gp + (j * CB + r) * (P + 4) + c4);
+        const float d[4] = {dsum[0], dsum[1], dsum[2], dsum[3]};
         const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + r * LY::QP + c4);
         const float pr = group_sum<TPR>(qv[0] * d[0] + qv[1] * d[1] + qv[2] * d[2] + qv[3] * d[3]);
         const float s = iq[buf * CB + r];
@@ -547,34 +567,38 @@ struct RArgs {
   int T, nseg, seg_chunks;
 };
 
-template <int P, int DV>
+// reverse-time kernels: segment summaries [R | 2N], dk, dv (each rebuilds R over its chunks)
+enum : int { RM_SUM = 0, RM_DK = 1, RM_DV = 2 };
+
+template <int P, int DV, int MODE>
 struct RL {
   using LY = Lay<P, DV>;
-  static constexpr int SB_BYTES = LY::NPAIR * LY::NT * 64 * 16;
-  static constexpr int QH = 0;                                 // q_hat rows fp32 [CB][QP]
-  static constexpr int QT = QH + CB * LY::QP * 4;              // sqrt2 q_hat^T fp32 [P][TP]
-  static constexpr int QD = QT + P * LY::TP * 4;               // sqrt2 q_hat^T / sqrt(D) fp32 [P][TP]
-  static constexpr int KR = QD + P * LY::TP * 4;               // raw k rows fp32 [CB][QP]
-  static constexpr int KH = KR + CB * LY::QP * 4;              // k_hat rows fp32 [2][CB][QP]
-  static constexpr int GT = KH + 2 * CB * LY::QP * 4;          // G^T bf16 [DV][VTP]
-  static constexpr int GR = GT + DV * LY::VTP * 2;             // g rows bf16 [CB][RP]
-  static constexpr int VR = GR + CB * LY::RP * 2;              // v rows bf16 [CB][RP]
-  static constexpr int SB = VR + CB * LY::RP * 2;              // R, readout fragment order
-  static constexpr int NN = SB + SB_BYTES;                     // weighted Gram halves bf16 [2][P][MP]
-  static constexpr int DK = NN + 2 * P * LY::MP * 2;           // dk_hat fp32 [P][AP]
-  static constexpr int DVA = DK + P * AP * 4;                  // dv fp32 [DV][AP]
-  static constexpr int IK = DVA + DV * AP * 4;                 // 1 / |k| [2][CB]
-  static constexpr int DL = IK + 2 * CB * 4;                   // delta [CB]
-  static constexpr int ID = DL + CB * 4;                       // 1 / D [CB]
+  static constexpr bool DK = MODE == RM_DK, DVM = MODE == RM_DV, SCORES = MODE != RM_SUM;
+  static constexpr int SB_BYTES = DVM ? LY::NPAIR * LY::NT * 64 * 16 : 0;
+  static constexpr int QD = 0;                                        // sqrt2 q_hat^T / sqrt(D) fp32 [P][TP]
+  static constexpr int GT = QD + P * LY::TP * 4;                      // G^T bf16 [DV][VTP]
+  static constexpr int QH = GT + DV * LY::VTP * 2;                    // q_hat rows fp32 [CB][QP]
+  static constexpr int KR = QH + (SCORES ? CB * LY::QP * 4 : 0);      // raw k rows fp32 [CB][QP]
+  static constexpr int KH = KR + (SCORES ? CB * LY::QP * 4 : 0);      // k_hat rows fp32 [2][CB][QP]
+  static constexpr int QT = KH + (SCORES ? 2 * CB * LY::QP * 4 : 0);  // sqrt2 q_hat^T fp32 [P][TP]
+  static constexpr int GR = QT + (DK ? P * LY::TP * 4 : 0);           // g rows bf16 [CB][RP]
+  static constexpr int VR = GR + (DK ? CB * LY::RP * 2 : 0);          // v rows bf16 [CB][RP]
+  static constexpr int NN = VR + (DK ? CB * LY::RP * 2 : 0);          // weighted Gram halves bf16 [2][P][MP]
+  static constexpr int GP = NN + (DK ? 2 * P * LY::MP * 2 : 0);       // dk_hat partials [8 waves x 2][CB][P + 4]
+  static constexpr int SB = GP + (DK ? 16 * CB * (P + 4) * 4 : 0);    // R, readout fragment order
+  static constexpr int IK = SB + SB_BYTES;                            // 1 / |k| [2][CB]
+  static constexpr int DL = IK + 2 * CB * 4;                          // delta [CB]
+  static constexpr int ID = DL + CB * 4;                              // 1 / D [CB]
   static constexpr int BYTES = ID + CB * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int P, int DV, int W, bool SUM>
+template <int P, int DV, int W, int MODE>
 struct RStage : Piece<P, DV, W> {
   using B = Piece<P, DV, W>;
   using LY = Lay<P, DV>;
-  using RLY = RL<P, DV>;
+  using RLY = RL<P, DV, MODE>;
+  static constexpr bool SCORES = MODE != RM_SUM, DK = MODE == RM_DK;
   typename B::row_t x;
   u16x8_t vv, gg;
   f32x2_t st;  // D_t, delta_t of the piece's row
@@ -583,11 +607,11 @@ struct RStage : Piece<P, DV, W> {
     const bool ok = t < a.T;
     if constexpr (B::ISQ || B::ISV) st = ok ? *reinterpret_cast<const f32x2_t*>(a.stats + (row0 + t) * 2) : f32x2_t{0.f, 0.f};
     if constexpr (B::ISQ) x = B::load_qk(a.q, row0 + t, ok);
-    if constexpr (B::ISK && !SUM) x = B::load_qk(a.k, row0 + t, ok);
+    if constexpr (B::ISK && SCORES) x = B::load_qk(a.k, row0 + t, ok);
     if constexpr (B::ISV) {
       if (ok) {
         const int64_t off = (row0 + t) * DV + 8 * B::sub();
-        if constexpr (!SUM) vv = *reinterpret_cast<const u16x8_t*>(a.v + off);
+        if constexpr (DK) vv = *reinterpret_cast<const u16x8_t*>(a.v + off);
         gg = *reinterpret_cast<const u16x8_t*>(a.g + off);
       } else {
         for (int e = 0; e < 8; ++e) vv[e] = gg[e] = 0;
@@ -607,14 +631,12 @@ struct RStage : Piece<P, DV, W> {
 #pragma unroll
       for (int e = 0; e < B::KQ; ++e) {
         const float u = f[e] * inv * 1.41421356237309515f;
-        if constexpr (!SUM) {
-          qh[e] = f[e] * inv;
-          qt[e * LY::TP] = u;
-        }
+        if constexpr (SCORES) qh[e] = f[e] * inv;
+        if constexpr (DK) qt[e * LY::TP] = u;
         qd[e * LY::TP] = u * isd;
       }
     }
-    if constexpr (B::ISK && !SUM) {
+    if constexpr (B::ISK && SCORES) {
       float f[B::KQ];
       const float inv = B::unpack(x, f);
       float* kr = reinterpret_cast<float*>(lds + RLY::KR) + r * LY::QP + s * B::KQ;
@@ -627,7 +649,7 @@ struct RStage : Piece<P, DV, W> {
       if (s == 0) reinterpret_cast<float*>(lds + RLY::IK)[buf * CB + r] = inv;
     }
     if constexpr (B::ISV) {
-      if constexpr (!SUM) {
+      if constexpr (DK) {
         *reinterpret_cast<u16x8_t*>(lds + RLY::VR + (r * LY::RP + 8 * s) * 2) = vv;
         *reinterpret_cast<u16x8_t*>(lds + RLY::GR + (r * LY::RP + 8 * s) * 2) = gg;
       }
@@ -663,34 +685,56 @@ __device__ __forceinline__ void write_sb(uint16_t* sb, const f32x4_t (&R)[wave_n
   }
 }
 
-template <int P, int DV, int W, bool SUM>
+// scores q_hat_t . k_hat_s of the query tile q2 against key s of this lane (q_hat as bf16
+// hi + lo, the raw key exact), masked to t >= s: lane (s, lg) holds queries 16 q2 + 4 lg + r
+template <int P>
+__device__ __forceinline__ f32x4_t rev_scores(const float* qhr, bf16x8_t kb, float invk, int q2, int kt, int ln, int lg) {
+  constexpr int QP = P + 8;
+  f32x4_t Sc = zero4();
+  if (q2 >= kt) {
+    float qs[8];
+    comp8<P>(qhr + (16 * q2 + ln) * QP, lg, qs);
+    bf16x8_t qhi, qlo;
+    split8(qs, qhi, qlo);
+    Sc = mfma(qlo, kb, mfma(qhi, kb, zero4()));
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Sc[r] *= invk;
+    if (q2 < kt || (q2 == kt && 4 * lg + r < ln)) Sc[r] = 0.f;  // causal: query >= key
+  }
+  return Sc;
+}
+
+template <int P, int DV, int W, int MODE>
 __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   using LY = Lay<P, DV>;
-  using RLY = RL<P, DV>;
+  using RLY = RL<P, DV, MODE>;
+  constexpr bool SUM = MODE == RM_SUM, DK = MODE == RM_DK, DVM = MODE == RM_DV;
   constexpr int NT = LY::NT, NH = LY::NH, NKS = LY::NKS, NTW = wave_nt<P>(W), MT = m_tile<P>(W);
-  constexpr bool OWN = !SUM && W >= 6;  // waves 6, 7: intra block of key tile W - 6
+  constexpr bool OWN = DK && W >= 6;  // dk: waves 6, 7 take the r part and intra block of key tile W - 6
   constexpr int KO = OWN ? W - 6 : 0;
-  constexpr int KR_ = W & 1, FSI = W >> 1;  // readout: key tile, pair split
-  constexpr int PB = FSI * LY::NPAIR / 4, PE = (FSI + 1) * LY::NPAIR / 4;
+  constexpr int KV = W & 1, DTV = W >> 1;  // dv: key tile, value column tile of this wave
+  constexpr bool RDV = DVM && DTV < NT;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const bool glow = lg < 2, mlow = ln < 8;
-  const int64_t bh = blockIdx.x / (SUM ? a.nseg - 1 : a.nseg);
-  const int seg = (int)(blockIdx.x % (SUM ? a.nseg - 1 : a.nseg)) + (SUM ? 1 : 0);
+  const int nblk = SUM ? a.nseg - 1 : a.nseg;
+  const int64_t bh = blockIdx.x / nblk;
+  const int seg = (int)(blockIdx.x % nblk) + (SUM ? 1 : 0);
   const int64_t row0 = bh * (int64_t)a.T;
   const int nch = (a.T + CB - 1) / CB;
   const int c0 = seg * a.seg_chunks, c1 = min(nch, c0 + a.seg_chunks);
 
-  const float* qhr = reinterpret_cast<const float*>(lds + RLY::QH);
-  const float* qt = reinterpret_cast<const float*>(lds + RLY::QT);
-  const float* kr = reinterpret_cast<const float*>(lds + RLY::KR);
   const float* qd = reinterpret_cast<const float*>(lds + RLY::QD);
   const uint16_t* gt = reinterpret_cast<const uint16_t*>(lds + RLY::GT);
+  const float* qhr = reinterpret_cast<const float*>(lds + RLY::QH);
+  const float* kr = reinterpret_cast<const float*>(lds + RLY::KR);
+  const float* qt = reinterpret_cast<const float*>(lds + RLY::QT);
   const uint16_t* gr = reinterpret_cast<const uint16_t*>(lds + RLY::GR);
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + RLY::VR);
-  uint16_t* sb = reinterpret_cast<uint16_t*>(lds + RLY::SB);
   uint16_t* nn = reinterpret_cast<uint16_t*>(lds + RLY::NN);
-  float* dka = reinterpret_cast<float*>(lds + RLY::DK);
-  float* dva = reinterpret_cast<float*>(lds + RLY::DVA);
+  float* gp = reinterpret_cast<float*>(lds + RLY::GP);
+  uint16_t* sb = reinterpret_cast<uint16_t*>(lds + RLY::SB);
   const float* ik = reinterpret_cast<const float*>(lds + RLY::IK);
   const float* dl = reinterpret_cast<const float*>(lds + RLY::DL);
   const float* idl = reinterpret_cast<const float*>(lds + RLY::ID);
@@ -712,16 +756,13 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
     if constexpr (MT >= 0) Nt = *reinterpret_cast<const f32x4_t*>(src + LY::NTL * NT * 256 + (MT * 64 + lane) * 4);
   }
 
-  RStage<P, DV, W, SUM> stg;
+  RStage<P, DV, W, MODE> stg;
   const int cl = c1 - 1;  // chunks run from the last to the first
-  if (c0 <= cl) {
-    stg.load(a, row0, cl * CB);
-    stg.stage(lds, cl & 1);
-  }
-  if constexpr (!SUM) {
+  stg.load(a, row0, cl * CB);
+  stg.stage(lds, cl & 1);
+  if constexpr (DK) write_gram<P, MT>(nn, Nt, ln, lg);
+  if constexpr (DVM) {
     write_sb<P, DV, W>(sb, R, ln, lg);
-    write_gram<P, MT>(nn, Nt, ln, lg);
-    for (int e = threadIdx.x; e < P * AP + DV * AP; e += 512) dka[e] = 0.f;  // dk_hat and dv accumulators
     if constexpr (LY::NTL & 1) {  // the odd last tile has no partner: its half of the fragments stays zero
       for (int e = threadIdx.x; e < NT * 64 * 4; e += 512)
         sb[(((LY::NPAIR - 1) * NT + e / 256) * 64 + (e / 4) % 64) * 8 + 4 + (e & 3)] = 0;
@@ -732,9 +773,9 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   for (int c = cl; c >= c0; --c) {
     const int t0 = c * CB, buf = c & 1;
     if (c - 1 >= c0) stg.load(a, row0, t0 - CB);
-    if constexpr (!SUM) {
-      const float* kh = reinterpret_cast<const float*>(lds + RLY::KH) + buf * CB * LY::QP;
-      // ================= phase A: dk_hat, dv of the chunk's keys
+    const float* kh = reinterpret_cast<const float*>(lds + RLY::KH) + buf * CB * LY::QP;
+    // ================= phase A
+    if constexpr (DK) {  // dk_hat of the chunk's keys
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const int s = 16 * k2 + ln;
@@ -760,44 +801,34 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
            }()),
            ...);
         }(std::make_integer_sequence<int, NTW>{});
-        float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // intra w_ts / D_t (owner, its key tile)
         if constexpr (OWN) {
           if (k2 == KO) {
             float xs[8];
             comp8<P>(kr + s * LY::QP, lg, xs);
             const bf16x8_t kb = pack8(xs);  // the raw key: exact in bf16
             const float invk = ik[buf * CB + s];
-            // r part: 2 N k_hat_s
+            // r part: 2 N k_hat_s (components 16 rt + 4 lg + r are G[16 rt + r])
             f32x4_t Xn[NH];
             gram_apply<P>(nn, kb, ln, lg, Xn);
 #pragma unroll
             for (int rt = 0; rt < NH; ++rt)
 #pragma unroll
               for (int r = 0; r < 4; ++r) G[16 * rt + r] += 2.f * invk * Xn[rt][r];
-            // intra block over queries t >= s: scores (q_hat as bf16 hi + lo), w_ts / D_t and
-            // e_ts = (v_s . g_t - delta_t) / D_t 2 (q_hat_t . k_hat_s) (v_s . g_t exact)
+            // intra block over queries t >= s: e_ts = (v_s . g_t - delta_t) / D_t 2 (q_hat_t . k_hat_s)
+            // (v_s . g_t exact), times q_hat_t
             float pw[8];
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
-              f32x4_t Sc = zero4(), E = zero4();
+              const f32x4_t Sc = rev_scores<P>(qhr, kb, invk, q2, KO, ln, lg);
+              f32x4_t E = zero4();
               if (q2 >= KO) {
-                float qs[8];
-                comp8<P>(qhr + (16 * q2 + ln) * LY::QP, lg, qs);
-                bf16x8_t qhi, qlo;
-                split8(qs, qhi, qlo);
-                Sc = mfma(qlo, kb, mfma(qhi, kb, zero4()));
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) E = mfma(row_frag(gr + (16 * q2 + ln) * LY::RP, ks, lg), vf[ks], E);
               }
               const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(dl + 16 * q2 + 4 * lg);
               const f32x4_t id4 = *reinterpret_cast<const f32x4_t*>(idl + 16 * q2 + 4 * lg);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                float sc = Sc[r] * invk;
-                if (q2 < KO || (q2 == KO && 4 * lg + r < ln)) sc = 0.f;  // causal: query >= key
-                wv[4 * q2 + r] = sc * sc * id4[r];
-                pw[4 * q2 + r] = (E[r] - dq4[r]) * id4[r] * sc * 1.41421356237309515f;
-              }
+              for (int r = 0; r < 4; ++r) pw[4 * q2 + r] = (E[r] - dq4[r]) * id4[r] * Sc[r] * 1.41421356237309515f;
             }
             const bf16x8_t pb = pack8(pw);
             float Nq[NH][8];
@@ -810,38 +841,40 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
             }
           }
         }
-        add_rotated<P>(dka, G, s, lg);
-        if (k2 == KR_) {
-          // dv_s = R^T psi(k_hat_s) over pairs [PB, PE), plus the owner's sum_t (w_ts / D_t) g_t
-          f32x4_t O[NT];
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) O[dt] = zero4();
-          [&]<int... PI>(std::integer_sequence<int, PI...>) {
-            (([&] {
-               constexpr int t1 = 2 * (PB + PI), t2 = t1 + 1;
-               constexpr bool has2 = t2 < LY::NTL;
-               const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
-#pragma unroll
-               for (int dt = 0; dt < NT; ++dt)
-                 O[dt] = mfma(*reinterpret_cast<const bf16x8_t*>(sb + (((PB + PI) * NT + dt) * 64 + lane) * 8), af, O[dt]);
-             }()),
-             ...);
-          }(std::make_integer_sequence<int, PE - PB>{});
-          if constexpr (OWN) {
-            const bf16x8_t wb = pack8(wv);
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt)
-              O[dt] = mfma(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(gt + vt_row(16 * dt + ln) * LY::VTP + 8 * lg)),
-                           wb, O[dt]);
-          }
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              __hip_atomic_fetch_add(dva + (16 * dt + 4 * lg + r) * AP + s, O[dt][r], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
+        pair_sum_lo<P>(G);
+        if (lg < 2) store_rotated<P>(gp + (2 * W + lg) * CB * (P + 4), G, s, lg);
       }
+    }
+    if constexpr (RDV) {  // dv of key tile KV, value columns 16 DTV .. + 15: R^T psi(k_hat_s) + sum_t (w_ts / D_t) g_t
+      const int s = 16 * KV + ln;
+      float Y[P];
+      rot_row<P>(kh + s * LY::QP, lg, Y);
+      f32x4_t O = zero4();
+      [&]<int... PI>(std::integer_sequence<int, PI...>) {
+        (([&] {
+           constexpr int t1 = 2 * PI, t2 = t1 + 1;
+           constexpr bool has2 = t2 < LY::NTL;
+           const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
+           O = mfma(*reinterpret_cast<const bf16x8_t*>(sb + ((PI * NT + DTV) * 64 + lane) * 8), af, O);
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, LY::NPAIR>{});
+      float xs[8];
+      comp8<P>(kr + s * LY::QP, lg, xs);
+      const bf16x8_t kb = pack8(xs);
+      const float invk = ik[buf * CB + s];
+      float wv[8];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const f32x4_t Sc = rev_scores<P>(qhr, kb, invk, q2, KV, ln, lg);
+        const f32x4_t id4 = *reinterpret_cast<const f32x4_t*>(idl + 16 * q2 + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[4 * q2 + r] = Sc[r] * Sc[r] * id4[r];
+      }
+      O = mfma(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(gt + vt_row(16 * DTV + ln) * LY::VTP + 8 * lg)),
+               pack8(wv), O);
+      if (t0 + s < a.T)  // lane (s, lg) holds columns 16 DTV + 4 lg .. + 3
+        *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + s) * DV + 16 * DTV + 4 * lg) = O;
     }
     {  // build: R^T += G^T psi(Q / sqrt(D)) (= A^T psi(Q)), 2 N += (-delta sqrt2 Q')^T (sqrt2 Q'), Q' = Q / sqrt(D)
       float Nq[NH][8];
@@ -858,7 +891,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
          }()),
          ...);
       }(std::make_integer_sequence<int, NTW>{});
-      if constexpr (MT >= 0) {
+      if constexpr (MT >= 0 && !DVM) {
         const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(dl + 4 * lg);
         const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(dl + 16 + 4 * lg);
         float nw[8];
@@ -871,46 +904,25 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
       }
     }
     __syncthreads();
-    // ================= phase B: dk and dv of the chunk (waves 4-7), staging of chunk c - 1
-    if constexpr (!SUM && W >= 4) {
-      const float* kh = reinterpret_cast<const float*>(lds + RLY::KH) + buf * CB * LY::QP;
+    // ================= phase B: dk of the chunk (waves 4-7), staging of chunk c - 1, state after c
+    if constexpr (DK && W >= 4) {
       constexpr int TPR = P / 4;
       const int u = threadIdx.x - 256;
       if (u < CB * TPR) {
         const int r = u / TPR, c4 = (u % TPR) * 4;
-        float d[4];
+        f32x4_t dsum = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[e] = dka[(c4 + e) * AP + r];
-          dka[(c4 + e) * AP + r] = 0.f;
-        }
+        for (int j = 0; j < 16; ++j) dsum += *reinterpret_cast<const f32x4_t*>(gp + (j * CB + r) * (P + 4) + c4);
         const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kh + r * LY::QP + c4);
-        const float pr = group_sum<TPR>(kv[0] * d[0] + kv[1] * d[1] + kv[2] * d[2] + kv[3] * d[3]);
+        const float pr = group_sum<TPR>(kv[0] * dsum[0] + kv[1] * dsum[1] + kv[2] * dsum[2] + kv[3] * dsum[3]);
         const float s = ik[buf * CB + r];
         if (t0 + r < a.T)
-          *reinterpret_cast<f32x4_t*>(a.dk + (row0 + t0 + r) * P + c4) =
-              f32x4_t{(d[0] - kv[0] * pr) * s, (d[1] - kv[1] * pr) * s, (d[2] - kv[2] * pr) * s, (d[3] - kv[3] * pr) * s};
-      }
-      if (u < CB * LY::NV8) {
-        const int r = u / LY::NV8, c8 = (u % LY::NV8) * 8;
-        float d[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          d[e] = dva[(c8 + e) * AP + r];
-          dva[(c8 + e) * AP + r] = 0.f;
-        }
-        if (t0 + r < a.T) {
-          float* dst = a.dv + (row0 + t0 + r) * DV + c8;
-          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{d[0], d[1], d[2], d[3]};
-          *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{d[4], d[5], d[6], d[7]};
-        }
+          *reinterpret_cast<f32x4_t*>(a.dk + (row0 + t0 + r) * P + c4) = (dsum - kv * pr) * s;
       }
     }
     if (c - 1 >= c0) stg.stage(lds, buf ^ 1);
-    if constexpr (!SUM) {
-      write_sb<P, DV, W>(sb, R, ln, lg);
-      write_gram<P, MT>(nn, Nt, ln, lg);
-    }
+    if constexpr (DK) write_gram<P, MT>(nn, Nt, ln, lg);
+    if constexpr (DVM) write_sb<P, DV, W>(sb, R, ln, lg);
     __syncthreads();
   }
   if constexpr (SUM) {  // segment summary to slot nseg - 1 - seg (reversed, so the scan gives suffixes)
@@ -943,10 +955,10 @@ __global__ __launch_bounds__(512, 1) void fdq_kernel(FArgs a) {
   KATA_CBM_SWITCH(KATA_FDQ)
 #undef KATA_FDQ
 }
-template <int P, int DV, bool SUM>
+template <int P, int DV, int MODE>
 __global__ __launch_bounds__(512, 1) void rev_kernel(RArgs a) {
   extern __shared__ __align__(16) char lds[];
-#define KATA_REV(WW) run_rev<P, DV, WW, SUM>(a, lds)
+#define KATA_REV(WW) run_rev<P, DV, WW, MODE>(a, lds)
   KATA_CBM_SWITCH(KATA_REV)
 #undef KATA_REV
 }
@@ -976,19 +988,18 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), FL<P, DV>::BYTES, st>>>(fa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   RArgs ra{q, k, v, go, stats, rsum, dk, dvo, T, plan.nseg, seg_chunks};
+  auto rev = [&](auto kern, int lds, int nblk) -> hipError_t {
+    hipError_t r = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (r != hipSuccess) return r;
+    kern<<<dim3((unsigned)(BH * nblk)), dim3(512), lds, st>>>(ra);
+    return hipGetLastError();
+  };
   if (plan.nseg > 1) {
-    auto ks = rev_kernel<P, DV, true>;
-    if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, RL<P, DV>::BYTES)) != hipSuccess)
-      return e;
-    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(512), RL<P, DV>::BYTES, st>>>(ra);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = rev(rev_kernel<P, DV, RM_SUM>, RL<P, DV, RM_SUM>::BYTES, plan.nseg - 1)) != hipSuccess) return e;
     if ((e = launch_scan(rsum, (int)BH, plan.nseg - 1, LY::STATE, st)) != hipSuccess) return e;
   }
-  auto kr = rev_kernel<P, DV, false>;
-  if ((e = hipFuncSetAttribute((const void*)kr, hipFuncAttributeMaxDynamicSharedMemorySize, RL<P, DV>::BYTES)) != hipSuccess)
-    return e;
-  kr<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), RL<P, DV>::BYTES, st>>>(ra);
-  return hipGetLastError();
+  if ((e = rev(rev_kernel<P, DV, RM_DK>, RL<P, DV, RM_DK>::BYTES, plan.nseg)) != hipSuccess) return e;
+  return rev(rev_kernel<P, DV, RM_DV>, RL<P, DV, RM_DV>::BYTES, plan.nseg);
 }
 
 }  // namespace cbm
