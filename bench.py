@@ -222,6 +222,19 @@ def main():
             flops = (8 * p + 6 * dv + 2) * pairs
             metric = "quadratic-form KATA backward tokens/s (1 GPU) + % bf16 MFMA peak"
             bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        elif p in (16, 32) and dv in (32, 64):  # bf16 inputs of these shapes: the MFMA state form
+            step = [lambda: kata.chunked_bwd(qd, kd, vd, gd, C=32)]
+            kernel_name = ("summary_bf16_kernel + segment_scan_kernel (forward prefixes), fdq_kernel, "
+                           "rev_kernel<.., 0> + segment_scan_kernel (reverse summaries), rev_kernel<.., 1> (dk), "
+                           "rev_kernel<.., 2> (dv)")
+            n, Cm = p * (p + 1) // 2, 32
+            # per head-token: five state contractions (the S and R builds, S g_t, R v_s and
+            # R^T psi(k_hat_s), 2 n dv each), four n-vector terms (psi^T S g for delta_t, D_t, Z b_t
+            # and r_s, 2 n each) and the chunk's causal pairs ((C + 1) / 2 per token: scores,
+            # v . g, dq, dk and dv at 2p, 2dv, 2p, 2p and 2dv)
+            flops = (10 * n * dv + 8 * n + (Cm + 1) * (6 * p + 4 * dv) // 2) * B * H * T
+            metric = "state-form (O(T)) KATA backward tokens/s (1 GPU) + % bf16 MFMA peak"
+            bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
         else:
             Cb = 16
             step = [lambda: kata.chunked_bwd(qd, kd, vd, gd, C=Cb)]

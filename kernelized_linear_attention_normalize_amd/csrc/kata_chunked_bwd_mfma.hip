@@ -389,7 +389,7 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
     const int t0 = c * CB, buf = c & 1;
     const float* qh = reinterpret_cast<const float*>(lds + FLY::QH) + buf * CB * LY::QP;
     if (c + 1 < c1) stg.load(a, row0, t0 + CB);
-    // ================= phase 1 (owners): D_t; scores and v_s . g_t kept for phase 3
+    // ================= phase 1 (owners): D_t; scores and v_s . g_t kept for phase 2
     f32x4_t Sc[2], Ev[2], Xm[NH];
     float invq = 0.f, invD = 0.f, dintra = 0.f, Dt = 0.f;
     if constexpr (OWN) {
@@ -436,19 +436,19 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
       invD = Dt > 0.f ? 1.f / Dt : 0.f;
       if (lg == 0) idl[t] = invD;
     }
-    __syncthreads();
-    // ================= phase 2: dq_hat of the chunk's tokens, then the build
+    // ================= phase 1, all waves: D_t-free parts of dq_hat (1 / D_t is applied to their
+    // sum), then the build
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = 16 * tt + ln;
-      bf16x8_t af[NKS];  // g_t, exact in bf16; 1 / D_t is applied to the contraction
+      bf16x8_t af[NKS];  // g_t, exact in bf16
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) af[ks] = row_frag(gr + t * LY::RP, ks, lg);
       float Y[P], G[P];
       rot_row<P>(qh + t * LY::QP, lg, Y);
 #pragma unroll
       for (int x = 0; x < P; ++x) G[x] = 0.f;
-      // x = S g_t / D_t over this wave's feature tiles, through the lift's transpose
+      // x = S g_t over this wave's feature tiles, through the lift's transpose
       [&]<int... TI>(std::integer_sequence<int, TI...>) {
         (([&] {
            constexpr int tau = wave_tile<P>(W, TI);
@@ -471,9 +471,6 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
         for (int x = 0; x < P; ++x) ds += Y[x] * G[x];
         ds = xor32_sum(xor16_sum(ds));
         if (lg == 0) dla[W * CB + t] = 0.5f * ds;
-        const float s = idl[t];
-#pragma unroll
-        for (int x = 0; x < P; ++x) G[x] *= s;
       }
       pair_sum_lo<P>(G);
       if (lg < 2) store_rotated<P>(gp + (2 * W + lg) * CB * (P + 4), G, t, lg);
@@ -496,7 +493,7 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
       if constexpr (MT >= 0) Mt = mfma(pack8(N[MT / NH]), pack8(N[MT % NH]), Mt);
     }
     __syncthreads();
-    // ================= phase 2b (owners): delta_t, then the parts of dq_hat that carry it:
+    // ================= phase 2 (owners): delta_t, then the parts of dq_hat that carry it:
     // b_t J^T Z = -delta_t / D_t 2 M q_hat_t, and the intra block
     // (v_s . g_t - delta_t) / D_t 2 (q_hat_t . k_hat_s) k_hat_s over keys s <= t
     if constexpr (OWN) {
@@ -539,9 +536,10 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
       const int u = threadIdx.x - 256;
       if (u < CB * TPR) {
         const int r = u / TPR, c4 = (u % TPR) * 4;
-        f32x4_t dsum = *reinterpret_cast<const f32x4_t*>(g2s + r * (P + 4) + c4);
+        f32x4_t dsum = zero4();
 #pragma unroll
         for (int j = 0; j < 16; ++j) dsum += *reinterpret_cast<const f32x4_t*>(gp + (j * CB + r) * (P + 4) + c4);
+        dsum = dsum * idl[r] + *reinterpret_cast<const f32x4_t*>(g2s + r * (P + 4) + c4);
         const float d[4] = {dsum[0], dsum[1], dsum[2], dsum[3]};
         const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + r * LY::QP + c4);
         const float pr = group_sum<TPR>(qv[0] * d[0] + qv[1] * d[1] + qv[2] * d[2] + qv[3] * d[3]);
@@ -665,23 +663,22 @@ struct RStage : Piece<P, DV, W> {
   }
 };
 
-// R (swapped accumulators) into the readout's fragment order: lane L = (d, g) of pair
-// fragment (pair, dt) holds features 4 g .. + 3 of tile 2 pair, then of tile 2 pair + 1, at
-// value column 16 dt + d
+// R built in the forward's orientation (lane (d, g) holds feature rows 4 g + r at value column
+// 16 dt + d) into the readout's fragment order: contiguous 16-byte fragments of tile pairs
 template <int P, int DV, int W>
-__device__ __forceinline__ void write_sb(uint16_t* sb, const f32x4_t (&R)[wave_na<P>(W)][DV / 16], int ln, int lg) {
-  constexpr int NT = DV / 16;
+__device__ __forceinline__ void write_pairs(uint16_t* sb, const f32x4_t (&R)[wave_na<P>(W)][DV / 16], int lane) {
+  constexpr int NT = DV / 16, NTW = wave_nt<P>(W);
 #pragma unroll
-  for (int i = 0; i < wave_nt<P>(W); ++i) {
-    const int tau = wave_tile<P>(W, i);
-    const int pair = tau >> 1, half = tau & 1;
+  for (int i = 0; i < NTW; i += 2) {
+    const int pair = wave_tile<P>(W, i) >> 1;
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int L = ((ln >> 2) << 4) | (4 * lg + r);
-        sb[((pair * NT + dt) * 64 + L) * 8 + half * 4 + (ln & 3)] = f32_to_bf16_bits(R[i][dt][r]);
-      }
+    for (int dt = 0; dt < NT; ++dt) {
+      const f32x4_t& x = R[i][dt];
+      const f32x4_t& y = R[i + 1 < NTW ? i + 1 : i][dt];
+      const bool two = i + 1 < NTW;  // the odd last tile of a wave has no partner
+      *reinterpret_cast<u32x4_t*>(sb + ((pair * NT + dt) * 64 + lane) * 8) =
+          u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), two ? pk2(y[0], y[1]) : 0u, two ? pk2(y[2], y[3]) : 0u};
+    }
   }
 }
 
@@ -751,8 +748,15 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-        R[i][dt] = *reinterpret_cast<const f32x4_t*>(src + ((wave_tile<P>(W, i) * NT + dt) * 64 + lane) * 4);
+      for (int dt = 0; dt < NT; ++dt) {
+        if constexpr (DVM) {  // dv builds R in the forward's orientation: transposed load
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            R[i][dt][r] = src[((wave_tile<P>(W, i) * NT + dt) * 64 + (((ln >> 2) << 4) | (4 * lg + r))) * 4 + (ln & 3)];
+        } else {
+          R[i][dt] = *reinterpret_cast<const f32x4_t*>(src + ((wave_tile<P>(W, i) * NT + dt) * 64 + lane) * 4);
+        }
+      }
     if constexpr (MT >= 0) Nt = *reinterpret_cast<const f32x4_t*>(src + LY::NTL * NT * 256 + (MT * 64 + lane) * 4);
   }
 
@@ -761,13 +765,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   stg.load(a, row0, cl * CB);
   stg.stage(lds, cl & 1);
   if constexpr (DK) write_gram<P, MT>(nn, Nt, ln, lg);
-  if constexpr (DVM) {
-    write_sb<P, DV, W>(sb, R, ln, lg);
-    if constexpr (LY::NTL & 1) {  // the odd last tile has no partner: its half of the fragments stays zero
-      for (int e = threadIdx.x; e < NT * 64 * 4; e += 512)
-        sb[(((LY::NPAIR - 1) * NT + e / 256) * 64 + (e / 4) % 64) * 8 + 4 + (e & 3)] = 0;
-    }
-  }
+  if constexpr (DVM) write_pairs<P, DV, W>(sb, R, lane);
   __syncthreads();
 
   for (int c = cl; c >= c0; --c) {
@@ -887,7 +885,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
         (([&] {
            const bf16x8_t bfr = build_frag<P, wave_tile<P>(W, TI)>(Nq, mlow);
 #pragma unroll
-           for (int dt = 0; dt < NT; ++dt) R[TI][dt] = mfma(abf[dt], bfr, R[TI][dt]);
+           for (int dt = 0; dt < NT; ++dt) R[TI][dt] = DVM ? mfma(bfr, abf[dt], R[TI][dt]) : mfma(abf[dt], bfr, R[TI][dt]);
          }()),
          ...);
       }(std::make_integer_sequence<int, NTW>{});
@@ -922,7 +920,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
     }
     if (c - 1 >= c0) stg.stage(lds, buf ^ 1);
     if constexpr (DK) write_gram<P, MT>(nn, Nt, ln, lg);
-    if constexpr (DVM) write_sb<P, DV, W>(sb, R, ln, lg);
+    if constexpr (DVM) write_pairs<P, DV, W>(sb, R, lane);
     __syncthreads();
   }
   if constexpr (SUM) {  // segment summary to slot nseg - 1 - seg (reversed, so the scan gives suffixes)
