@@ -336,8 +336,9 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
  *   bf16 inputs with p in {16, 32} and dv in {32, 64} run bf16 MFMA kernels: the bf16
  *   chunked forward (o in fp32 and its segment prefixes, in the workspace), then 32-token
  *   chunks whose state contractions, lift and lift transpose stay on chip; C only has to be
- *   in {16, 32, 64} there, and products are rounded to bf16 before fp32 accumulation as in
- *   the forward (normwise error about 1e-3 against the exact gradients). Other shapes and
+ *   in {16, 32, 64} there, and states, lifted features and per-pair weights are rounded to bf16
+ *   before fp32 accumulation as in the forward (normwise error about 2e-3 to 3e-3 against the
+ *   exact gradients). Other shapes and
  *   fp32 inputs run fp32 VALU kernels with the state n (dv + 1) fp32 and the chunk's rows
  *   within 160 KB of LDS (p <= 64, dv <= 64; p = 32, dv = 64 needs C = 16). Otherwise
  *   KATA_ERR_UNSUPPORTED. The workspace size depends on the shape, not on in_dt, and covers

@@ -105,14 +105,6 @@ __device__ __forceinline__ bf16x8_t sfrag(const f32x4_t (&Sd)[NT], int ks) {
   const f32x4_t& y = Sd[2 * ks + 1];
   return __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(y[0], y[1]), pk2(y[2], y[3])});
 }
-// the same k-slots as bf16 hi + lo (the contractions S g_t and R v_s are differences of
-// nearly equal parts, so the state enters them at about fp32 precision)
-template <int NT>
-__device__ __forceinline__ void sfrag2(const f32x4_t (&Sd)[NT], int ks, bf16x8_t& hi, bf16x8_t& lo) {
-  const float x[8] = {Sd[2 * ks][0],     Sd[2 * ks][1],     Sd[2 * ks][2],     Sd[2 * ks][3],
-                      Sd[2 * ks + 1][0], Sd[2 * ks + 1][1], Sd[2 * ks + 1][2], Sd[2 * ks + 1][3]};
-  split8(x, hi, lo);
-}
 // the same k-slots of a bf16 row (columns 32 ks + 4 lg .. + 3 and 32 ks + 16 + 4 lg .. + 3)
 __device__ __forceinline__ bf16x8_t row_frag(const uint16_t* row, int ks, int lg) {
   const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 32 * ks + 4 * lg);
@@ -454,11 +446,7 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
            constexpr int tau = wave_tile<P>(W, TI);
            f32x4_t X = zero4();
 #pragma unroll
-           for (int ks = 0; ks < NKS; ++ks) {
-             bf16x8_t sh, sl;
-             sfrag2<NT>(S[TI], ks, sh, sl);
-             X = mfma(sl, af[ks], mfma(sh, af[ks], X));
-           }
+           for (int ks = 0; ks < NKS; ++ks) X = mfma(sfrag<NT>(S[TI], ks), af[ks], X);
            tr_tile<P, tau>(G, Y, X, glow);
          }()),
          ...);
@@ -790,11 +778,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
              constexpr int tau = wave_tile<P>(W, TI);
              f32x4_t X = zero4();
 #pragma unroll
-             for (int ks = 0; ks < NKS; ++ks) {
-               bf16x8_t rh, rl;
-               sfrag2<NT>(R[TI], ks, rh, rl);
-               X = mfma(rl, vf[ks], mfma(rh, vf[ks], X));
-             }
+             for (int ks = 0; ks < NKS; ++ks) X = mfma(sfrag<NT>(R[TI], ks), vf[ks], X);
              tr_tile<P, tau>(G, Y, X, glow);
            }()),
            ...);
