@@ -25,8 +25,8 @@
 //   rsum : [R | 2N] of every segment but the first, scanned in reversed slot order so that a
 //          slot holds the suffix of the segments after one;
 //   rdk  : reverse time from each segment's suffix, two kernels that each rebuild R: dk (R v_s
-//          through the lift's transpose) and dv (R^T psi(k_hat_s), one value-column tile of
-//          one key tile per wave, so no sums across waves).
+//          through the lift's transpose) and dv (R^T psi(k_hat_s), a quarter of the feature
+//          pairs of one key tile per wave, summed through LDS).
 //
 // Layouts. States use the feature tiles of the forward (33 tiles of 16 rows at p = 32, each
 // row a pair (i, j) of components; see kata_chunked.h) but are built with the forward
@@ -572,7 +572,8 @@ struct RL {
   static constexpr int NN = VR + (DK ? CB * LY::RP * 2 : 0);          // weighted Gram halves bf16 [2][P][MP]
   static constexpr int GP = NN + (DK ? 2 * P * LY::MP * 2 : 0);       // dk_hat partials [8 waves x 2][CB][P + 4]
   static constexpr int SB = GP + (DK ? 16 * CB * (P + 4) * 4 : 0);    // R, readout fragment order
-  static constexpr int IK = SB + SB_BYTES;                            // 1 / |k| [2][CB]
+  static constexpr int VP = SB + SB_BYTES;                            // dv partials [4 pair ranges][CB][DV + 4]
+  static constexpr int IK = VP + (DVM ? 4 * CB * (DV + 4) * 4 : 0);   // 1 / |k| [2][CB]
   static constexpr int DL = IK + 2 * CB * 4;                          // delta [CB]
   static constexpr int ID = DL + CB * 4;                              // 1 / D [CB]
   static constexpr int BYTES = ID + CB * 4;
@@ -699,8 +700,10 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   constexpr int NT = LY::NT, NH = LY::NH, NKS = LY::NKS, NTW = wave_nt<P>(W), MT = m_tile<P>(W);
   constexpr bool OWN = DK && W >= 6;  // dk: waves 6, 7 take the r part and intra block of key tile W - 6
   constexpr int KO = OWN ? W - 6 : 0;
-  constexpr int KV = W & 1, DTV = W >> 1;  // dv: key tile, value column tile of this wave
-  constexpr bool RDV = DVM && DTV < NT;
+  // dv: key tile KV, readout pairs [VPB, VPE) over all value columns; the intra term on the
+  // waves of the last pair range
+  constexpr int KV = W & 1, FV = W >> 1;
+  constexpr int VPB = FV * LY::NPAIR / 4, VPE = (FV + 1) * LY::NPAIR / 4;
   const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
   const bool glow = lg < 2, mlow = ln < 8;
   const int nblk = SUM ? a.nseg - 1 : a.nseg;
@@ -720,6 +723,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   uint16_t* nn = reinterpret_cast<uint16_t*>(lds + RLY::NN);
   float* gp = reinterpret_cast<float*>(lds + RLY::GP);
   uint16_t* sb = reinterpret_cast<uint16_t*>(lds + RLY::SB);
+  float* vp = reinterpret_cast<float*>(lds + RLY::VP);
   const float* ik = reinterpret_cast<const float*>(lds + RLY::IK);
   const float* dl = reinterpret_cast<const float*>(lds + RLY::DL);
   const float* idl = reinterpret_cast<const float*>(lds + RLY::ID);
@@ -827,36 +831,47 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
         if (lg < 2) store_rotated<P>(gp + (2 * W + lg) * CB * (P + 4), G, s, lg);
       }
     }
-    if constexpr (RDV) {  // dv of key tile KV, value columns 16 DTV .. + 15: R^T psi(k_hat_s) + sum_t (w_ts / D_t) g_t
+    if constexpr (DVM) {  // dv of key tile KV over pairs [VPB, VPE): R^T psi(k_hat_s) (+ sum_t (w_ts / D_t) g_t)
       const int s = 16 * KV + ln;
       float Y[P];
       rot_row<P>(kh + s * LY::QP, lg, Y);
-      f32x4_t O = zero4();
+      f32x4_t O[NT];
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) O[dt] = zero4();
       [&]<int... PI>(std::integer_sequence<int, PI...>) {
         (([&] {
-           constexpr int t1 = 2 * PI, t2 = t1 + 1;
+           constexpr int t1 = 2 * (VPB + PI), t2 = t1 + 1;
            constexpr bool has2 = t2 < LY::NTL;
            const bf16x8_t af = readout_frag<P, t1, has2 ? t2 : t1, has2>(Y, glow);
-           O = mfma(*reinterpret_cast<const bf16x8_t*>(sb + ((PI * NT + DTV) * 64 + lane) * 8), af, O);
+#pragma unroll
+           for (int dt = 0; dt < NT; ++dt)
+             O[dt] = mfma(*reinterpret_cast<const bf16x8_t*>(sb + (((VPB + PI) * NT + dt) * 64 + lane) * 8), af, O[dt]);
          }()),
          ...);
-      }(std::make_integer_sequence<int, LY::NPAIR>{});
-      float xs[8];
-      comp8<P>(kr + s * LY::QP, lg, xs);
-      const bf16x8_t kb = pack8(xs);
-      const float invk = ik[buf * CB + s];
-      float wv[8];
+      }(std::make_integer_sequence<int, VPE - VPB>{});
+      if constexpr (FV == 3) {
+        float xs[8];
+        comp8<P>(kr + s * LY::QP, lg, xs);
+        const bf16x8_t kb = pack8(xs);
+        const float invk = ik[buf * CB + s];
+        float wv[8];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const f32x4_t Sc = rev_scores<P>(qhr, kb, invk, q2, KV, ln, lg);
-        const f32x4_t id4 = *reinterpret_cast<const f32x4_t*>(idl + 16 * q2 + 4 * lg);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const f32x4_t Sc = rev_scores<P>(qhr, kb, invk, q2, KV, ln, lg);
+          const f32x4_t id4 = *reinterpret_cast<const f32x4_t*>(idl + 16 * q2 + 4 * lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wv[4 * q2 + r] = Sc[r] * Sc[r] * id4[r];
+          for (int r = 0; r < 4; ++r) wv[4 * q2 + r] = Sc[r] * Sc[r] * id4[r];
+        }
+        const bf16x8_t wb = pack8(wv);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+          O[dt] = mfma(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(gt + vt_row(16 * dt + ln) * LY::VTP + 8 * lg)),
+                       wb, O[dt]);
       }
-      O = mfma(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(gt + vt_row(16 * DTV + ln) * LY::VTP + 8 * lg)),
-               pack8(wv), O);
-      if (t0 + s < a.T)  // lane (s, lg) holds columns 16 DTV + 4 lg .. + 3
-        *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + s) * DV + 16 * DTV + 4 * lg) = O;
+      // lane (s, lg) holds columns 16 dt + 4 lg .. + 3
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+        *reinterpret_cast<f32x4_t*>(vp + (FV * CB + s) * (DV + 4) + 16 * dt + 4 * lg) = O[dt];
     }
     {  // build: R^T += G^T psi(Q / sqrt(D)) (= A^T psi(Q)), 2 N += (-delta sqrt2 Q')^T (sqrt2 Q'), Q' = Q / sqrt(D)
       float Nq[NH][8];
@@ -886,7 +901,7 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
       }
     }
     __syncthreads();
-    // ================= phase B: dk of the chunk (waves 4-7), staging of chunk c - 1, state after c
+    // ================= phase B: dk or dv of the chunk (waves 4-7), staging of chunk c - 1, state after c
     if constexpr (DK && W >= 4) {
       constexpr int TPR = P / 4;
       const int u = threadIdx.x - 256;
@@ -900,6 +915,22 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
         const float s = ik[buf * CB + r];
         if (t0 + r < a.T)
           *reinterpret_cast<f32x4_t*>(a.dk + (row0 + t0 + r) * P + c4) = (dsum - kv * pr) * s;
+      }
+    }
+    if constexpr (DVM && W >= 4) {  // dv of the chunk: the four pair ranges' sums
+      const int u = threadIdx.x - 256;
+      if (u < CB * LY::NV8) {
+        const int r = u / LY::NV8, c8 = (u % LY::NV8) * 8;
+        f32x4_t d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          d0 += *reinterpret_cast<const f32x4_t*>(vp + (f * CB + r) * (DV + 4) + c8);
+          d1 += *reinterpret_cast<const f32x4_t*>(vp + (f * CB + r) * (DV + 4) + c8 + 4);
+        }
+        if (t0 + r < a.T) {
+          *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + r) * DV + c8) = d0;
+          *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + r) * DV + c8 + 4) = d1;
+        }
       }
     }
     if (c - 1 >= c0) stg.stage(lds, buf ^ 1);
