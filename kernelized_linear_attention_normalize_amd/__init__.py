@@ -20,7 +20,8 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd",
+           "STATE_BWD_MIN_T"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -441,6 +442,12 @@ def chunked_bwd(q, k, v, grad_o, C: int = 32, scan="associative", workspace=None
     return dq, dk, dvv
 
 
+# From this length on, bf16 gradients of the full map (p in {16, 32}, dv in {32, 64}) come from
+# the O(T) state form: it costs about 1.7 ns per head-token against 1.3 ps per causal pair for
+# the flash form on one MI355X, which puts the crossover near T = 2600.
+STATE_BWD_MIN_T = 3072
+
+
 class _KataAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, C, family, g):
@@ -457,12 +464,18 @@ class _KataAttention(torch.autograd.Function):
     def backward(ctx, grad_o):
         q, k, v = ctx.saved_tensors
         go = grad_o.contiguous().to(q.dtype)
-        dq, dk, dvv = quadratic_bwd(q, k, v, go, family=ctx.family, g=ctx.g)
+        if (ctx.family == "full" and q.dtype == torch.bfloat16 and q.shape[-1] in (16, 32)
+                and v.shape[-1] in (32, 64) and q.shape[2] >= STATE_BWD_MIN_T):
+            dq, dk, dvv = chunked_bwd(q, k, v, go, C=32)  # O(T): the bf16 MFMA state form
+        else:
+            dq, dk, dvv = quadratic_bwd(q, k, v, go, family=ctx.family, g=ctx.g)
         return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
 
 
 def kata_attention(q, k, v, C: int = 64, family: str = "full", g: int = 1):
     """Differentiable causal KATA attention: the chunked forward (quadratic form where the
-    chunked kernels do not cover the shape) and the gradients of kata_quadratic_bwd."""
+    chunked kernels do not cover the shape); gradients from kata_chunked_bwd's bf16 MFMA
+    state form for long bf16 sequences (T >= STATE_BWD_MIN_T, full map, p in {16, 32}, dv in
+    {32, 64}), else from kata_quadratic_bwd."""
     return _KataAttention.apply(q, k, v, C, family, g)
 

@@ -66,6 +66,22 @@ def test_autograd_wrapper():
         assert _rel(to_np(t), r, 1e-2 * float(np.linalg.norm(go))) <= 2e-4, name
 
 
+def test_autograd_wrapper_long_bf16():
+    """kata_attention on a long bf16 sequence: the gradients come from the O(T) state form
+    (T >= STATE_BWD_MIN_T), at the bf16 MFMA backward's bar against the oracle."""
+    T = kata.STATE_BWD_MIN_T + 29
+    q, k, v = draw_qkv(53, 1, 2, T, 32, 64, "bf16")
+    go = draw_qkv(54, 1, 2, T, 64, 64, "bf16")[0]
+    qd, kd, vd = (to_dev(x, "bf16").requires_grad_(True) for x in (q, k, v))
+    o = kata.kata_attention(qd, kd, vd, C=64)
+    (o.float() * to_dev(go, "f32")).sum().backward()
+    ref = kb.backward(q, k, v, go)
+    for name, t, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
+        e = _rel(to_np(t.float()), r, 1e-2 * float(np.linalg.norm(go)))
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 1.2e-2, name  # the bf16 MFMA bar plus the gradients' rounding to bf16
+
+
 # ------------------------------------------------------------------ MFMA path
 @pytest.mark.parametrize("p,dv,T", [(64, 64, 700), (32, 64, 1030), (64, 32, 257), (32, 32, 64), (64, 64, 600)])
 def test_quadratic_bwd_mfma(p, dv, T):
