@@ -87,3 +87,31 @@ def test_graph_quadratic_and_decode():
         torch.cuda.synchronize()
         assert torch.equal(o, oe) and torch.equal(S, Se) and torch.equal(Z, Ze), f"decode replay {rep}"
         assert torch.equal(oq, kata.quadratic_fwd(qq, kq, vq, out_dtype=torch.float32)), f"quadratic replay {rep}"
+
+
+def test_graph_chunked_backward():
+    """The O(T) backward (bf16 MFMA state form: forward summaries, scans, three kernels) under
+    capture with a caller-provided workspace: every replay equals the eager call."""
+    B, H, T, p, dv = 1, 2, 1500, 32, 64
+    print("[case] graph chunked backward", flush=True)
+    q, k, v = (to_dev(x, "bf16") for x in draw_qkv(77, B, H, T, p, dv, "bf16"))
+    go = to_dev(draw_qkv(78, B, H, T, dv, dv, "bf16")[0], "bf16")
+    lib = kata.load()
+    ws = torch.empty(int(lib.kata_chunked_bwd_workspace_bytes(B, H, T, p, dv, 32, kata.SCAN_ASSOCIATIVE)),
+                     dtype=torch.uint8, device="cuda:0")
+    outs = []
+
+    def step():
+        outs[:] = kata.chunked_bwd(q, k, v, go, C=32, workspace=ws)
+
+    g = _capture(step)
+    for rep in range(3):
+        nq, nk, nv = (to_dev(x, "bf16") for x in draw_qkv(79 + rep, B, H, T, p, dv, "bf16"))
+        q.copy_(nq), k.copy_(nk), v.copy_(nv)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in outs]
+        ref = kata.chunked_bwd(nq, nk, nv, go, C=32)  # eager, between replays
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
