@@ -349,6 +349,25 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
                                int B, int H, int T, int p, int dv, int C, kata_scan_t scan, float* dq, float* dk,
                                float* dv_out, void* workspace, size_t workspace_bytes, kata_stream_t stream);
 
+/*
+ * kata_chunked_bwd_varlen - kata_chunked_bwd over B sequences packed without padding in the
+ * token-major layout of kata_chunked_fwd_varlen: q, k, dq, dk are [total, H, p] and v,
+ * grad_o, dv_out are [total, H, dv] (token cu_seqlens[b] + t of sequence b, head h, is row
+ * (cu_seqlens[b] + t) * H + h). cu_seqlens: device int32 [B + 1], 4-byte aligned, as for the
+ * forward; max_len bounds every length (longer sequences are cut). Each sequence's gradients
+ * equal the padded call's on that sequence alone; rows outside every sequence are not
+ * written. bf16 inputs with p in {16, 32} and dv in {32, 64} (the bf16 MFMA state form; else
+ * KATA_ERR_UNSUPPORTED). workspace: kata_chunked_bwd_varlen_workspace_bytes (D_t and delta_t
+ * of the total H rows and the segment summaries of the plan of max_len); 0 means unsupported
+ * arguments. Errors as kata_chunked_bwd; KATA_ERR_NULL for cu_seqlens NULL when B H > 0;
+ * KATA_ERR_SHAPE for negative sizes or max_len * H * max(p, dv) * 4 >= 2^31.
+ */
+size_t kata_chunked_bwd_varlen_workspace_bytes(int B, int H, int total, int max_len, int p, int dv, kata_scan_t scan);
+kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* v, const void* grad_o,
+                                      kata_dtype_t in_dt, int B, int H, int total, int max_len, int p, int dv,
+                                      kata_scan_t scan, const int32_t* cu_seqlens, float* dq, float* dk,
+                                      float* dv_out, void* workspace, size_t workspace_bytes, kata_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

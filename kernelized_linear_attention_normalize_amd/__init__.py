@@ -21,7 +21,7 @@ __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "li
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
            "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd",
-           "STATE_BWD_MIN_T"]
+           "chunked_bwd_varlen", "STATE_BWD_MIN_T"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -90,6 +90,10 @@ def load():
     lib.kata_chunked_bwd_workspace_bytes.restype = SZ
     lib.kata_chunked_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
     lib.kata_chunked_bwd.restype = I
+    lib.kata_chunked_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.kata_chunked_bwd_varlen_workspace_bytes.restype = SZ
+    lib.kata_chunked_bwd_varlen.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P, SZ, P]
+    lib.kata_chunked_bwd_varlen.restype = I
     lib.kata_quadratic_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.kata_quadratic_bwd_workspace_bytes.restype = SZ
     lib.kata_quadratic_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
@@ -446,6 +450,38 @@ def chunked_bwd(q, k, v, grad_o, C: int = 32, scan="associative", workspace=None
 # the O(T) state form: it costs about 1.7 ns per head-token against 1.3 ps per causal pair for
 # the flash form on one MI355X, which puts the crossover near T = 2600.
 STATE_BWD_MIN_T = 3072
+
+
+def chunked_bwd_varlen(q, k, v, grad_o, cu_seqlens, max_len: int, scan="associative", workspace=None):
+    """O(T) gradients (dq, dk, dv), float32, of the forward over B sequences packed without
+    padding (the layout of chunked_fwd_varlen): q, k [total, H, p]; v, grad_o [total, H, dv],
+    bf16, p in {16, 32}, dv in {32, 64}. Rows outside every sequence come back as zeros."""
+    lib = load()
+    dev = _dev(q, k, v, grad_o)
+    total, H, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or grad_o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v and grad_o")
+    if not (q.dtype == k.dtype == v.dtype == grad_o.dtype):
+        raise TypeError("q, k, v and grad_o must share one dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
+    _dev(cu_seqlens, q)
+    B = cu_seqlens.numel() - 1
+    sc = _scan_code(scan)
+    dq = torch.zeros((total, H, p), dtype=torch.float32, device=dev)
+    dk = torch.zeros_like(dq)
+    dvv = torch.zeros((total, H, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kata_chunked_bwd_varlen_workspace_bytes(B, H, total, max(max_len, 1), p, dv, sc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_chunked_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), _dt(q), B, H,
+                                           total, max_len, p, dv, sc, cu_seqlens.data_ptr(), dq.data_ptr(),
+                                           dk.data_ptr(), dvv.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream(dev)),
+               "kata_chunked_bwd_varlen")
+    return dq, dk, dvv
 
 
 class _KataAttention(torch.autograd.Function):

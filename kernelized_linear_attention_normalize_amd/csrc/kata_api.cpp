@@ -532,7 +532,7 @@ size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int 
     need = (rows * 2 + 2 * sums) * sizeof(float);
   }
   if (kata::chunked_bwd_mfma_supported(p, dv)) {  // the size does not depend on the input dtype
-    const size_t m = kata::chunked_bwd_mfma_workspace_floats(B, H, T, p, dv, scan) * sizeof(float);
+    const size_t m = kata::chunked_bwd_mfma_workspace_floats(B, H, T, p, dv, scan, (int64_t)B * H * T) * sizeof(float);
     need = m > need ? m : need;
   }
   return need;
@@ -572,14 +572,62 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
   if (mfma)
     return hip_status(kata::launch_chunked_bwd_mfma(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-        static_cast<const uint16_t*>(grad_o), B, H, T, p, dv, (int)scan, static_cast<float*>(workspace), dq, dk,
-        dv_out, (hipStream_t)stream));
+        static_cast<const uint16_t*>(grad_o), B, H, T, p, dv, (int)scan, kata::SeqLayout{}, (int64_t)B * H * T,
+        static_cast<float*>(workspace), dq, dk, dv_out, (hipStream_t)stream));
   float* stats = static_cast<float*>(workspace);
   const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
   float* fsum = stats + rows * 2;
   float* rsum = fsum + sums;
   return hip_status(kata::launch_chunked_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, T, p, dv, C, plan,
                                              stats, fsum, rsum, dq, dk, dv_out, (hipStream_t)stream));
+}
+
+size_t kata_chunked_bwd_varlen_workspace_bytes(int B, int H, int total, int max_len, int p, int dv, kata_scan_t scan) {
+  if (B <= 0 || H <= 0 || total < 0 || max_len <= 0 || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE))
+    return 0;
+  if (!kata::chunked_bwd_mfma_supported(p, dv)) return 0;
+  return kata::chunked_bwd_mfma_workspace_floats(B, H, max_len, p, dv, scan, (int64_t)total * H) * sizeof(float);
+}
+
+kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* v, const void* grad_o,
+                                      kata_dtype_t in_dt, int B, int H, int total, int max_len, int p, int dv,
+                                      kata_scan_t scan, const int32_t* cu_seqlens, float* dq, float* dk,
+                                      float* dv_out, void* workspace, size_t workspace_bytes, kata_stream_t stream) {
+  if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
+  if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
+  if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
+  if (in_dt != KATA_DTYPE_BF16 || !kata::chunked_bwd_mfma_supported(p, dv)) return KATA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
+  if (cu_seqlens == nullptr) return KATA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
+  const int w = p > dv ? p : dv;
+  if (mul4(total, H, w, 1) < 0 || (int64_t)max_len * H * w * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
+  const kata::SegPlan plan = kata::seg_plan(B, H, max_len, kata::CHUNKED_BWD_FWD_C, scan);
+  if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
+  for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
+    if (!aligned16(ptr)) return KATA_ERR_ALIGN;
+  const size_t need = kata_chunked_bwd_varlen_workspace_bytes(B, H, total, max_len, p, dv, scan);
+  if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KATA_ERR_ALIGN;
+  const size_t rows = (size_t)total * H;
+  const size_t qb = rows * p * 2, vb = rows * dv * 2;
+  const void* outs[4] = {dq, dk, dv_out, workspace};
+  const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], q, qb) || overlap(outs[i], outb[i], k, qb) || overlap(outs[i], outb[i], v, vb) ||
+        overlap(outs[i], outb[i], grad_o, vb))
+      return KATA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
+  }
+  kata::SeqLayout lay;
+  lay.cu = cu_seqlens;
+  lay.total = total;
+  return hip_status(kata::launch_chunked_bwd_mfma(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(grad_o), B, H, max_len, p, dv, (int)scan, lay, (int64_t)rows,
+      static_cast<float*>(workspace), dq, dk, dv_out, (hipStream_t)stream));
 }
 
 int64_t kata_order_dim(int p, int r) {

@@ -243,6 +243,8 @@ struct FArgs {
   float* stats;       // [rows][2]: D_t, delta_t
   float* dq;          // [rows][P]
   int T, nseg, seg_chunks;
+  SeqLayout lay;      // row layout (padded [B, H, T] or packed token-major) and lengths
+  int H;
 };
 
 template <int P, int DV>
@@ -272,14 +274,16 @@ struct FStage : Piece<P, DV, W> {
   using FLY = FL<P, DV>;
   typename B::row_t x;
   u16x8_t vv, gg;
-  __device__ __forceinline__ void load(const FArgs& a, int64_t row0, int t0) {
+  // rows t0 .. of the sequence at row0 + t step (rows at or past len read as zero)
+  __device__ __forceinline__ void load(const FArgs& a, int64_t row0, int step, int len, int t0) {
     const int t = t0 + B::row();
-    const bool ok = t < a.T;
-    if constexpr (B::ISQ) x = B::load_qk(a.q, row0 + t, ok);
-    if constexpr (B::ISK) x = B::load_qk(a.k, row0 + t, ok);
+    const bool ok = t >= 0 && t < len;
+    const int64_t row = row0 + (int64_t)t * step;
+    if constexpr (B::ISQ) x = B::load_qk(a.q, row, ok);
+    if constexpr (B::ISK) x = B::load_qk(a.k, row, ok);
     if constexpr (B::ISV) {
       if (ok) {
-        const int64_t off = (row0 + t) * DV + 8 * B::sub();
+        const int64_t off = row * DV + 8 * B::sub();
         vv = *reinterpret_cast<const u16x8_t*>(a.v + off);
         gg = *reinterpret_cast<const u16x8_t*>(a.g + off);
       } else {
@@ -333,8 +337,10 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
   const bool glow = lg < 2, mlow = ln < 8;
   const int64_t bh = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
-  const int64_t row0 = bh * (int64_t)a.T;
-  const int nch = (a.T + CB - 1) / CB;
+  int64_t row0;
+  int rstep, Tb;  // first row, row step, this sequence's length
+  seq_rows_of(a.lay, bh, a.H, a.T, row0, rstep, Tb);
+  const int nch = (Tb + CB - 1) / CB;
   const int c0 = seg * a.seg_chunks, c1 = min(nch, c0 + a.seg_chunks);
 
   const float* qr = reinterpret_cast<const float*>(lds + FLY::QR);
@@ -372,7 +378,7 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
   }
 
   FStage<P, DV, W> stg;
-  stg.load(a, row0, c0 * CB);
+  stg.load(a, row0, rstep, Tb, c0 * CB);
   stg.stage(lds, c0 & 1);
   write_gram<P, MT>(mm, Mt, ln, lg);
   __syncthreads();
@@ -380,7 +386,7 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * CB, buf = c & 1;
     const float* qh = reinterpret_cast<const float*>(lds + FLY::QH) + buf * CB * LY::QP;
-    if (c + 1 < c1) stg.load(a, row0, t0 + CB);
+    if (c + 1 < c1) stg.load(a, row0, rstep, Tb, t0 + CB);
     // ================= phase 1 (owners): D_t; scores and v_s . g_t kept for phase 2
     f32x4_t Sc[2], Ev[2], Xm[NH];
     float invq = 0.f, invD = 0.f, dintra = 0.f, Dt = 0.f;
@@ -514,8 +520,8 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
 #pragma unroll
       for (int h = 0; h < NH; ++h)
         *reinterpret_cast<f32x4_t*>(g2s + t * (P + 4) + 16 * h + 4 * lg) = f32x4_t{G2[h][0], G2[h][1], G2[h][2], G2[h][3]};
-      if (lg == 0 && t0 + t < a.T)
-        *reinterpret_cast<f32x2_t*>(a.stats + (row0 + t0 + t) * 2) = f32x2_t{Dt, delta};
+      if (lg == 0 && t0 + t < Tb)
+        *reinterpret_cast<f32x2_t*>(a.stats + (row0 + (int64_t)(t0 + t) * rstep) * 2) = f32x2_t{Dt, delta};
     }
     __syncthreads();
     // ================= phase 3: dq of the chunk (waves 4-7), staging of chunk c + 1, M after c
@@ -532,8 +538,8 @@ __device__ __forceinline__ void run_fdq(const FArgs& a, char* lds) {
         const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qh + r * LY::QP + c4);
         const float pr = group_sum<TPR>(qv[0] * d[0] + qv[1] * d[1] + qv[2] * d[2] + qv[3] * d[3]);
         const float s = iq[buf * CB + r];
-        if (t0 + r < a.T)
-          *reinterpret_cast<f32x4_t*>(a.dq + (row0 + t0 + r) * P + c4) =
+        if (t0 + r < Tb)
+          *reinterpret_cast<f32x4_t*>(a.dq + (row0 + (int64_t)(t0 + r) * rstep) * P + c4) =
               f32x4_t{(d[0] - qv[0] * pr) * s, (d[1] - qv[1] * pr) * s, (d[2] - qv[2] * pr) * s, (d[3] - qv[3] * pr) * s};
       }
     }
@@ -551,6 +557,8 @@ struct RArgs {
   float* dk;           // [rows][P]
   float* dv;           // [rows][DV]
   int T, nseg, seg_chunks;
+  SeqLayout lay;
+  int H;
 };
 
 // reverse-time kernels: segment summaries [R | 2N], dk, dv (each rebuilds R over its chunks)
@@ -589,15 +597,17 @@ struct RStage : Piece<P, DV, W> {
   typename B::row_t x;
   u16x8_t vv, gg;
   f32x2_t st;  // D_t, delta_t of the piece's row
-  __device__ __forceinline__ void load(const RArgs& a, int64_t row0, int t0) {
+  // rows t0 .. of the sequence at row0 + t step (rows at or past len read as zero)
+  __device__ __forceinline__ void load(const RArgs& a, int64_t row0, int step, int len, int t0) {
     const int t = t0 + B::row();
-    const bool ok = t < a.T;
-    if constexpr (B::ISQ || B::ISV) st = ok ? *reinterpret_cast<const f32x2_t*>(a.stats + (row0 + t) * 2) : f32x2_t{0.f, 0.f};
-    if constexpr (B::ISQ) x = B::load_qk(a.q, row0 + t, ok);
-    if constexpr (B::ISK && SCORES) x = B::load_qk(a.k, row0 + t, ok);
+    const bool ok = t >= 0 && t < len;
+    const int64_t row = row0 + (int64_t)t * step;
+    if constexpr (B::ISQ || B::ISV) st = ok ? *reinterpret_cast<const f32x2_t*>(a.stats + row * 2) : f32x2_t{0.f, 0.f};
+    if constexpr (B::ISQ) x = B::load_qk(a.q, row, ok);
+    if constexpr (B::ISK && SCORES) x = B::load_qk(a.k, row, ok);
     if constexpr (B::ISV) {
       if (ok) {
-        const int64_t off = (row0 + t) * DV + 8 * B::sub();
+        const int64_t off = row * DV + 8 * B::sub();
         if constexpr (DK) vv = *reinterpret_cast<const u16x8_t*>(a.v + off);
         gg = *reinterpret_cast<const u16x8_t*>(a.g + off);
       } else {
@@ -709,8 +719,10 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   const int nblk = SUM ? a.nseg - 1 : a.nseg;
   const int64_t bh = blockIdx.x / nblk;
   const int seg = (int)(blockIdx.x % nblk) + (SUM ? 1 : 0);
-  const int64_t row0 = bh * (int64_t)a.T;
-  const int nch = (a.T + CB - 1) / CB;
+  int64_t row0;
+  int rstep, Tb;  // first row, row step, this sequence's length
+  seq_rows_of(a.lay, bh, a.H, a.T, row0, rstep, Tb);
+  const int nch = (Tb + CB - 1) / CB;
   const int c0 = seg * a.seg_chunks, c1 = min(nch, c0 + a.seg_chunks);
 
   const float* qd = reinterpret_cast<const float*>(lds + RLY::QD);
@@ -753,16 +765,18 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
   }
 
   RStage<P, DV, W, MODE> stg;
-  const int cl = c1 - 1;  // chunks run from the last to the first
-  stg.load(a, row0, cl * CB);
-  stg.stage(lds, cl & 1);
+  const int cl = c1 - 1;  // chunks run from the last to the first (none past the sequence's end)
+  if (c0 <= cl) {
+    stg.load(a, row0, rstep, Tb, cl * CB);
+    stg.stage(lds, cl & 1);
+  }
   if constexpr (DK) write_gram<P, MT>(nn, Nt, ln, lg);
   if constexpr (DVM) write_pairs<P, DV, W>(sb, R, lane);
   __syncthreads();
 
   for (int c = cl; c >= c0; --c) {
     const int t0 = c * CB, buf = c & 1;
-    if (c - 1 >= c0) stg.load(a, row0, t0 - CB);
+    if (c - 1 >= c0) stg.load(a, row0, rstep, Tb, t0 - CB);
     const float* kh = reinterpret_cast<const float*>(lds + RLY::KH) + buf * CB * LY::QP;
     // ================= phase A
     if constexpr (DK) {  // dk_hat of the chunk's keys
@@ -913,8 +927,8 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
         const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kh + r * LY::QP + c4);
         const float pr = group_sum<TPR>(kv[0] * dsum[0] + kv[1] * dsum[1] + kv[2] * dsum[2] + kv[3] * dsum[3]);
         const float s = ik[buf * CB + r];
-        if (t0 + r < a.T)
-          *reinterpret_cast<f32x4_t*>(a.dk + (row0 + t0 + r) * P + c4) = (dsum - kv * pr) * s;
+        if (t0 + r < Tb)
+          *reinterpret_cast<f32x4_t*>(a.dk + (row0 + (int64_t)(t0 + r) * rstep) * P + c4) = (dsum - kv * pr) * s;
       }
     }
     if constexpr (DVM && W >= 4) {  // dv of the chunk: the four pair ranges' sums
@@ -927,9 +941,10 @@ __device__ __forceinline__ void run_rev(const RArgs& a, char* lds) {
           d0 += *reinterpret_cast<const f32x4_t*>(vp + (f * CB + r) * (DV + 4) + c8);
           d1 += *reinterpret_cast<const f32x4_t*>(vp + (f * CB + r) * (DV + 4) + c8 + 4);
         }
-        if (t0 + r < a.T) {
-          *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + r) * DV + c8) = d0;
-          *reinterpret_cast<f32x4_t*>(a.dv + (row0 + t0 + r) * DV + c8 + 4) = d1;
+        if (t0 + r < Tb) {
+          float* dst = a.dv + (row0 + (int64_t)(t0 + r) * rstep) * DV + c8;
+          *reinterpret_cast<f32x4_t*>(dst) = d0;
+          *reinterpret_cast<f32x4_t*>(dst + 4) = d1;
         }
       }
     }
@@ -979,10 +994,10 @@ __global__ __launch_bounds__(512, 1) void rev_kernel(RArgs a) {
 
 template <int P, int DV>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* go, int B, int H, int T,
-                  int scan, float* ws, float* dq, float* dk, float* dvo, hipStream_t st) {
+                  int scan, SeqLayout lay, int64_t rows, float* ws, float* dq, float* dk, float* dvo, hipStream_t st) {
   using LY = Lay<P, DV>;
   const SegPlan plan = seg_plan(B, H, T, CHUNKED_BWD_FWD_C, scan);
-  const int64_t BH = (int64_t)B * H, rows = BH * T;
+  const int64_t BH = (int64_t)B * H;
   const int64_t sums = plan.nseg > 1 ? BH * (plan.nseg - 1) * LY::STATE : 0;
   float* stats = ws;
   float* fws = stats + ((rows * 2 + 3) & ~(int64_t)3);
@@ -991,16 +1006,16 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   // the forward's segment summaries [S | 2M], scanned into prefixes
   if (plan.nseg > 1 &&
       (e = launch_chunked_bf16(q, k, v, nullptr, false, B, H, T, P, DV, CHUNKED_BWD_FWD_C, plan, fws, nullptr,
-                               nullptr, SeqLayout{}, PASS_SUMMARIES | PASS_SCAN, st)) != hipSuccess)
+                               nullptr, lay, PASS_SUMMARIES | PASS_SCAN, st)) != hipSuccess)
     return e;
   const int seg_chunks = plan.cps * (CHUNKED_BWD_FWD_C / CB);
-  FArgs fa{q, k, v, go, fws, stats, dq, T, plan.nseg, seg_chunks};
+  FArgs fa{q, k, v, go, fws, stats, dq, T, plan.nseg, seg_chunks, lay, H};
   auto kf = fdq_kernel<P, DV>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, FL<P, DV>::BYTES)) != hipSuccess)
     return e;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), FL<P, DV>::BYTES, st>>>(fa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  RArgs ra{q, k, v, go, stats, rsum, dk, dvo, T, plan.nseg, seg_chunks};
+  RArgs ra{q, k, v, go, stats, rsum, dk, dvo, T, plan.nseg, seg_chunks, lay, H};
   auto rev = [&](auto kern, int lds, int nblk) -> hipError_t {
     hipError_t r = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (r != hipSuccess) return r;
@@ -1019,20 +1034,20 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
 
 bool chunked_bwd_mfma_supported(int p, int dv) { return (p == 16 || p == 32) && (dv == 32 || dv == 64); }
 
-size_t chunked_bwd_mfma_workspace_floats(int B, int H, int T, int p, int dv, int scan) {
+size_t chunked_bwd_mfma_workspace_floats(int B, int H, int T, int p, int dv, int scan, int64_t rows) {
   const SegPlan plan = seg_plan(B, H, T, CHUNKED_BWD_FWD_C, scan);
-  const size_t BH = (size_t)B * H, rows = BH * T;
+  const size_t BH = (size_t)B * H;
   const size_t sums = plan.nseg > 1 ? BH * (plan.nseg - 1) * (size_t)mfma_state_floats(p, dv) : 0;
   return ((rows * 2 + 3) & ~(size_t)3) + 2 * sums;
 }
 
 hipError_t launch_chunked_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* go,
-                                   int B, int H, int T, int p, int dv, int scan, float* ws, float* dq, float* dk,
-                                   float* dvo, hipStream_t st) {
-  if (p == 16 && dv == 32) return cbm::launch<16, 32>(q, k, v, go, B, H, T, scan, ws, dq, dk, dvo, st);
-  if (p == 16 && dv == 64) return cbm::launch<16, 64>(q, k, v, go, B, H, T, scan, ws, dq, dk, dvo, st);
-  if (p == 32 && dv == 32) return cbm::launch<32, 32>(q, k, v, go, B, H, T, scan, ws, dq, dk, dvo, st);
-  if (p == 32 && dv == 64) return cbm::launch<32, 64>(q, k, v, go, B, H, T, scan, ws, dq, dk, dvo, st);
+                                   int B, int H, int T, int p, int dv, int scan, SeqLayout lay, int64_t rows,
+                                   float* ws, float* dq, float* dk, float* dvo, hipStream_t st) {
+#define KATA_CBM_CASE(PP, DD) \
+  if (p == PP && dv == DD) return cbm::launch<PP, DD>(q, k, v, go, B, H, T, scan, lay, rows, ws, dq, dk, dvo, st);
+  KATA_CBM_CASE(16, 32) KATA_CBM_CASE(16, 64) KATA_CBM_CASE(32, 32) KATA_CBM_CASE(32, 64)
+#undef KATA_CBM_CASE
   return hipErrorInvalidValue;
 }
 

@@ -88,10 +88,12 @@ hipError_t launch_chunked_bwd(const void* q, const void* k, const void* v, const
 // forward it runs first (for o and the segment prefixes) uses chunks of CHUNKED_BWD_FWD_C
 constexpr int CHUNKED_BWD_FWD_C = 128;
 bool chunked_bwd_mfma_supported(int p, int dv);
-size_t chunked_bwd_mfma_workspace_floats(int B, int H, int T, int p, int dv, int scan);
+// workspace floats: D_t, delta_t for `rows` rows (B H T padded, total H packed) and the two
+// sets of segment summaries of the plan of T
+size_t chunked_bwd_mfma_workspace_floats(int B, int H, int T, int p, int dv, int scan, int64_t rows);
 hipError_t launch_chunked_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* go,
-                                   int B, int H, int T, int p, int dv, int scan, float* ws, float* dq, float* dk,
-                                   float* dvo, hipStream_t st);
+                                   int B, int H, int T, int p, int dv, int scan, SeqLayout lay, int64_t rows,
+                                   float* ws, float* dq, float* dk, float* dvo, hipStream_t st);
 // full map, bf16 q, k, v, gout: MFMA backward (p, dv in {32, 64}); stats: 2 floats per row
 bool quadratic_bwd_mfma_supported(int p, int dv);
 hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,

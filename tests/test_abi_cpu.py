@@ -241,6 +241,32 @@ def test_chunked_bwd_validation(lib):
     assert call(T=0) == OK and call(B=0) == OK
 
 
+def test_chunked_bwd_varlen_validation(lib):
+    """kata_chunked_bwd_varlen: argument errors come back before any device access."""
+    need = lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 64, ASSOC)
+    assert need >= 300 * 2 * 2 * 4                                  # at least D_t, delta_t per row
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 64, 64, ASSOC) == 0   # p = 64: no MFMA form
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 16, ASSOC) == 0
+    # D_t, delta_t are kept for every row of the packed tensor, including rows past the last sequence
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 3000, 200, 32, 64, ASSOC) > need
+
+    def vb(cu=A + (1 << 36), **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, dt=BF16, B=2, H=2, total=300, max_len=200, p=32, dv=64,
+                 scan=ASSOC, dq=A + (1 << 30), dk=A + (2 << 30), dvo=A + (3 << 30), ws=A + (4 << 30), wsb=need)
+        a.update(kw)
+        return lib.kata_chunked_bwd_varlen(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["total"],
+                                           a["max_len"], a["p"], a["dv"], a["scan"], cu, a["dq"], a["dk"], a["dvo"],
+                                           a["ws"], a["wsb"], None)
+    assert vb(dt=F32) == E_UNSUP and vb(p=64) == E_UNSUP and vb(dv=48) == E_UNSUP
+    assert vb(scan=7) == E_SCAN and vb(dt=5) == E_DTYPE
+    assert vb(cu=None) == E_NULL and vb(cu=A + (1 << 36) + 2) == E_ALIGN
+    assert vb(total=-1) == E_SHAPE and vb(max_len=-3) == E_SHAPE
+    assert vb(wsb=need - 1) == E_WS and vb(ws=None) == E_WS and vb(dq=None) == E_NULL
+    assert vb(dk=A + (1 << 30)) == E_ALIAS                        # dk on top of dq
+    assert vb(H=1024, max_len=1 << 14, total=1 << 14) == E_SHAPE  # 32-bit offsets of one sequence
+    assert vb(total=0) == OK and vb(max_len=0) == OK and vb(B=0) == OK
+
+
 def test_higher_orders(lib):
     from oracle import kata_families as kf
     for p, r in [(4, 2), (16, 2), (3, 3), (8, 4), (64, 1)]:

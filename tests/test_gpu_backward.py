@@ -206,3 +206,36 @@ def test_chunked_bwd_long_matches_quadratic_path():
         e = _rel(to_np(x), to_np(y), 1e-2 * float(np.linalg.norm(go)))
         print(f"  {name} rel={e:.2e}", flush=True)
         assert e <= 2e-4, name
+
+
+@pytest.mark.parametrize("p,dv,scan", [(32, 64, "associative"), (16, 32, "sequential"), (32, 32, "associative")])
+def test_chunked_bwd_varlen(p, dv, scan):
+    """Packed sequences (token-major, cu_seqlens; kata_chunked_bwd_varlen): each sequence's
+    gradients against the oracle run on it alone, at the bf16 MFMA bar. An empty sequence, a
+    short one (its later segments are empty) and rows after the last sequence (left at zero)."""
+    B, H, max_len = 4, 2, 1400
+    lens = [1300, 0, 45, 700]
+    extra = 3
+    print(f"[case] chunked bwd varlen p={p} dv={dv} {scan} lens={lens}", flush=True)
+    q, k, v = draw_qkv(91, B, H, max_len, p, dv, "bf16")
+    go = draw_qkv(92, B, H, max_len, dv, dv, "bf16")[0]
+
+    def pack(x):
+        rows = [np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)]
+        return np.concatenate(rows + [np.transpose(x[0, :, :extra], (1, 0, 2))], axis=0)
+
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    got = kata.chunked_bwd_varlen(*(to_dev(pack(x), "bf16") for x in (q, k, v, go)), cu, max_len, scan=scan)
+    got = [to_np(x) for x in got]
+    n = sum(lens)
+    assert all(np.all(x[n:] == 0.0) for x in got), "rows outside every sequence were written"
+    start = 0
+    for b, L in enumerate(lens):
+        if L:
+            ref = kb.backward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], go[b:b + 1, :, :L])
+            for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+                e = _rel(np.transpose(x[start:start + L], (1, 0, 2))[None], r,
+                         1e-2 * float(np.linalg.norm(go[b, :, :L])))
+                print(f"  seq {b} L={L} {name} rel={e:.2e}", flush=True)
+                assert e <= MFMA_BWD_BAR, (b, name)
+        start += L
