@@ -178,13 +178,14 @@ struct Map8 {
   template <int P> static constexpr int xdt(int, int) { return -1; }
 };
 // Map16: pass 1 (segment summaries) on 16 waves, 4 per SIMD. p=32: wave w builds tiles
-// 2w, 2w+1; tile 32 is split by output column tile over waves 0..NT-1; Gram tiles on waves
-// 4..7. p=16: wave w < 9 builds tile w; the Gram tile is on wave 9.
+// 2w, 2w+1; tile 32 is split by output column tile over waves 8..8+NT-1 and the Gram tiles
+// sit on waves 12..15 (waves 0-7 also normalise the chunk's keys, 8-15 only write V^T).
+// p=16: wave w < 9 builds tile w; the Gram tile is on wave 9.
 struct Map16 {
   template <int P> static constexpr int nt(int w) { return P == 32 ? 2 : (w < 9 ? 1 : 0); }
   template <int P> static constexpr int tile(int w, int i) { return P == 32 ? 2 * w + i : (w < 9 ? w : 0); }
-  template <int P> static constexpr int mtile(int w) { return P == 32 ? (w >= 4 && w < 8 ? w - 4 : -1) : (w == 9 ? 0 : -1); }
-  template <int P> static constexpr int xdt(int w, int nt) { return P == 32 && w < nt ? w : -1; }
+  template <int P> static constexpr int mtile(int w) { return P == 32 ? (w >= 12 ? w - 12 : -1) : (w == 9 ? 0 : -1); }
+  template <int P> static constexpr int xdt(int w, int nt) { return P == 32 && w >= 8 && w < 8 + nt ? w - 8 : -1; }
 };
 template <class MAP, int P> constexpr int map_na(int w) { return MAP::template nt<P>(w) > 0 ? MAP::template nt<P>(w) : 1; }
 
