@@ -81,3 +81,33 @@ def test_sweep_packed(i):
             print(f"  seq {b} L={L} rel_err={e:.2e}", flush=True)
             assert e <= TOL[c["dt"]]
         start += L
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_sweep_chunked_backward(i):
+    """The O(T) backward on bf16 MFMA (kata_chunked_bwd, and kata_chunked_bwd_varlen on odd
+    cases) at seeded shapes: p, dv from its set, lengths rarely a multiple of the 32-token
+    chunk, both scans. Bar: the bf16 MFMA backward's, normwise 1e-2 per gradient tensor
+    against the float64 oracle."""
+    from oracle import kata_backward as kb
+    rng = np.random.default_rng(4000 + i)
+    p, dv = int(rng.choice([16, 32])), int(rng.choice([32, 64]))
+    T = int(rng.integers(2, 1800))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    scan = ("sequential", "associative")[int(rng.integers(0, 2))]
+    print(f"[case] backward sweep {i}: p={p} dv={dv} T={T} B={B} H={H} {scan}", flush=True)
+    q, k, v = draw_qkv(5000 + i, B, H, T, p, dv, "bf16")
+    go = draw_qkv(6000 + i, B, H, T, dv, dv, "bf16")[0]
+    ref = kb.backward(q, k, v, go)
+    if i % 2 == 0:
+        got = [to_np(x) for x in kata.chunked_bwd(*(to_dev(x, "bf16") for x in (q, k, v, go)), C=32, scan=scan)]
+    else:  # the same batch packed token-major, every sequence of length T
+        pack = lambda x: np.concatenate([np.transpose(x[b], (1, 0, 2)) for b in range(B)], axis=0)
+        cu = torch.tensor([b * T for b in range(B + 1)], dtype=torch.int32, device="cuda:0")
+        out = kata.chunked_bwd_varlen(*(to_dev(pack(x), "bf16") for x in (q, k, v, go)), cu, T, scan=scan)
+        got = [np.stack([np.transpose(to_np(x)[b * T:(b + 1) * T], (1, 0, 2)) for b in range(B)]) for x in out]
+    floor = 1e-2 * float(np.linalg.norm(go))
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        e = float(np.linalg.norm(a - r) / max(np.linalg.norm(r), floor))
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= 1e-2, name
