@@ -29,17 +29,21 @@
 //          pairs of one key tile per wave, summed through LDS).
 //
 // Layouts. States use the feature tiles of the forward (33 tiles of 16 rows at p = 32, each
-// row a pair (i, j) of components; see kata_chunked.h) but are built with the forward
-// build's MFMA operands swapped, S^T = V^T psi(K): lane (m, g) of a 16 x 16 accumulator tile
-// holds feature row m at value columns 16 dt + 4 g + r. Two column tiles of a feature tile
-// are then directly an MFMA operand whose k-slots are 32 value columns, so x = S a_t and
-// R v_s run from registers, and their result X^T (feature rows 4 g + r, one token per lane)
-// goes through the lift's transpose inside the lane: the token's row is held rotated,
-// Y[x] = u[(x & ~15) | ((x + 4 g) & 15)] as in the forward readout, every feature row of
-// a tile is a product Y_a Y_b of two compile-time registers, and its gradient adds x Y_b to
-// G[a] and x Y_a to G[b] of an equally rotated accumulator (the state carries c_f^2 like the
-// forward's, so the lift's constants cancel). The lanes' G are summed in registers (lane groups g and g + 2,
-// whose rotations differ by 8) and then across waves through per-wave LDS partials.
+// row a pair (i, j) of components; see kata_chunked.h). fdq and the dk kernel build them with
+// the forward build's MFMA operands swapped, S^T = V^T psi(K): lane (m, g) of a 16 x 16
+// accumulator tile holds feature row m at value columns 16 dt + 4 g + r. Two column tiles of a
+// feature tile are then directly an MFMA operand whose k-slots are 32 value columns, so S g_t
+// and R v_s run from registers (g_t and v_s exact in bf16; 1 / D_t is applied to the summed
+// result). Their result X^T (feature rows 4 g + r, one token per lane) goes through the lift's
+// transpose inside the lane: the token's row is held rotated,
+// Y[x] = u[(x & ~15) | ((x + 4 g) & 15)] as in the forward readout, every feature row of a tile
+// is a product Y_a Y_b of two compile-time registers, and its gradient adds x Y_b to G[a] and
+// x Y_a to G[b] of an equally rotated accumulator (the state carries c_f^2 like the forward's,
+// so the lift's constants cancel). The lanes' G are summed in registers (lane groups g and
+// g + 2, whose rotations differ by 8) and then across waves through per-wave LDS partials.
+// R = sum_t psi(q_hat_t / sqrt(D_t)) g_t^T, which is A^T psi(Q) with the exact g_t as values.
+// The dv kernel reads R only through the forward readout's fragments, so it builds R in the
+// forward's orientation.
 #include "kata_chunked.h"
 
 namespace kata {
