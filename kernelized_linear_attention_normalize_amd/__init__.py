@@ -21,7 +21,7 @@ __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "li
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
            "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd",
-           "chunked_bwd_varlen", "STATE_BWD_MIN_T"]
+           "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -506,6 +506,32 @@ class _KataAttention(torch.autograd.Function):
         else:
             dq, dk, dvv = quadratic_bwd(q, k, v, go, family=ctx.family, g=ctx.g)
         return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
+
+
+class _KataAttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_len, C):
+        ctx.save_for_backward(q, k, v, cu_seqlens)
+        ctx.max_len = max_len
+        return chunked_fwd_varlen(q, k, v, cu_seqlens, max_len, C=C)
+
+    @staticmethod
+    def backward(ctx, grad_o):
+        q, k, v, cu = ctx.saved_tensors
+        dq, dk, dvv = chunked_bwd_varlen(q, k, v, grad_o.contiguous().to(q.dtype), cu, ctx.max_len)
+        return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
+
+
+def kata_attention_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64):
+    """Differentiable causal KATA attention over B sequences packed without padding (the
+    layout of chunked_fwd_varlen: q, k [total, H, p]; v [total, H, dv]; cu_seqlens int32
+    [B + 1]): the packed chunked forward and the packed O(T) backward (bf16 inputs, full map,
+    p in {16, 32}, dv in {32, 64}). Rows outside every sequence get zero gradients."""
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise TypeError("kata_attention_varlen takes bf16 q, k, v")
+    if q.shape[-1] not in (16, 32) or v.shape[-1] not in (32, 64):
+        raise ValueError("kata_attention_varlen: p must be 16 or 32 and dv 32 or 64")
+    return _KataAttentionVarlen.apply(q, k, v, cu_seqlens, max_len, C)
 
 
 def kata_attention(q, k, v, C: int = 64, family: str = "full", g: int = 1):

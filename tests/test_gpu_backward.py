@@ -239,3 +239,27 @@ def test_chunked_bwd_varlen(p, dv, scan):
                 print(f"  seq {b} L={L} {name} rel={e:.2e}", flush=True)
                 assert e <= MFMA_BWD_BAR, (b, name)
         start += L
+
+
+def test_autograd_varlen():
+    """kata_attention_varlen: the packed forward and the packed O(T) backward through autograd,
+    each sequence against the oracle at the bf16 MFMA bar (gradients rounded to bf16 add 2^-9)."""
+    B, H, max_len, p, dv = 3, 2, 900, 32, 64
+    lens = [900, 0, 333]
+    q, k, v = draw_qkv(95, B, H, max_len, p, dv, "bf16")
+    go = draw_qkv(96, B, H, max_len, dv, dv, "bf16")[0]
+    pack = lambda x: np.concatenate([np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)], axis=0)
+    qd, kd, vd = (to_dev(pack(x), "bf16").requires_grad_(True) for x in (q, k, v))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    o = kata.kata_attention_varlen(qd, kd, vd, cu, max_len)
+    (o.float() * to_dev(pack(go), "f32")).sum().backward()
+    start = 0
+    for b, L in enumerate(lens):
+        if L:
+            ref = kb.backward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], go[b:b + 1, :, :L])
+            for name, t, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
+                got = np.transpose(to_np(t.float())[start:start + L], (1, 0, 2))[None]
+                e = _rel(got, r, 1e-2 * float(np.linalg.norm(go[b, :, :L])))
+                print(f"  seq {b} {name} rel={e:.2e}", flush=True)
+                assert e <= 1.2e-2, (b, name)
+        start += L
