@@ -263,3 +263,20 @@ def test_autograd_varlen():
                 print(f"  seq {b} {name} rel={e:.2e}", flush=True)
                 assert e <= 1.2e-2, (b, name)
         start += L
+
+
+@pytest.mark.parametrize("B,H,T,p,dv,scan", [(4, 16, 128, 32, 64, "associative"), (3, 8, 33, 16, 32, "associative"),
+                                             (2, 16, 256, 32, 32, "sequential")])
+def test_chunked_bwd_mfma_many_heads(B, H, T, p, dv, scan):
+    """The O(T) backward with many sequence-heads (up to 64) and lengths at or just past a
+    chunk or segment boundary (T = 128, 33, 256), at the bf16 MFMA bar against the oracle."""
+    print(f"[case] chunked bwd mfma heads B={B} H={H} T={T} p={p} dv={dv} {scan}", flush=True)
+    q, k, v = draw_qkv(97, B, H, T, p, dv, "bf16")
+    go = draw_qkv(98, B, H, T, dv, dv, "bf16")[0]
+    ref = kb.backward(q, k, v, go)
+    got = kata.chunked_bwd(*(to_dev(x, "bf16") for x in (q, k, v, go)), C=32, scan=scan)
+    floor = 1e-2 * float(np.linalg.norm(go))
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        e = _rel(to_np(a), r, floor)
+        print(f"  {name} rel={e:.2e}", flush=True)
+        assert e <= MFMA_BWD_BAR, name
