@@ -106,6 +106,8 @@ def main():
                     help="backward workload: flash-style MFMA kernels or the O(T) state form")
     ap.add_argument("--bwd-shape", default="quadratic", choices=["quadratic", "long"],
                     help="backward workload: the quadratic shape or the long shape")
+    ap.add_argument("--varlen-form", default="chunked", choices=["chunked", "quadratic"],
+                    help="varlen workload: the chunked (O(T)) form or the flash-style quadratic form")
     ap.add_argument("--order", type=int, default=1,
                     help="quadratic workload: weights (q_hat . k_hat)^(2r) of the even-order lift psi_2r")
     args = ap.parse_args()
@@ -266,19 +268,32 @@ def main():
         ws = torch.empty(max(kata.chunked_workspace_bytes(len(lens), H, max_len, p, dv, C,
                                                           kata._scan_code(args.scan)), 1),
                          dtype=torch.uint8, device=dev)
-        step = [lambda: kata.chunked_fwd_varlen(qd, kd, vd, cu, max_len, C=C, scan=args.scan, out=out, workspace=ws)]
-        dominant = 0
-        kernel_name = "kata_chunked_fwd_varlen (all passes)"
         n = p * (p + 1) // 2
-        flops = chunked_flops_per_head_token(n, p, dv, C) * H * total
         units = total
-        metric = "packed variable-length chunked KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
-        config = {"workload": f"varlen: chunked forward over {len(lens)} packed sequences of "
-                              f"{min(lens)}..{max_len} tokens ({total} in all), H={H} p={p} (n={n}) dv={dv} "
-                              f"C={C} scan={args.scan}", "global_batch": len(lens), "tokens": total,
-                  "heads": H, "p": p, "dv": dv, "chunk": C, "scan": args.scan, "parallelism": "single-gpu"}
+        dominant = 0
+        if args.varlen_form == "chunked":
+            step = [lambda: kata.chunked_fwd_varlen(qd, kd, vd, cu, max_len, C=C, scan=args.scan, out=out,
+                                                    workspace=ws)]
+            kernel_name = "kata_chunked_fwd_varlen (all passes)"
+            flops = chunked_flops_per_head_token(n, p, dv, C) * H * total
+            metric = "packed variable-length chunked KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
+            form = f"chunked forward, C={C} scan={args.scan}"
+            traffic_file = f"varlen_C{C}_traffic.txt"
+        else:
+            step = [lambda: kata.quadratic_fwd_varlen(qd, kd, vd, cu, max_len, out=out)]
+            kernel_name = "quadratic_bf16_kernel (packed)"
+            # per causal pair of a sequence: scores 2p, W.[V | 1] 2 (dv + 1)
+            flops = (2 * p + 2 * (dv + 1)) * H * int(sum(L * (L + 1) // 2 for L in lens))
+            metric = "packed variable-length quadratic-form KATA fwd tokens/s (1 GPU) + % bf16 MFMA peak"
+            form = "flash-style quadratic forward"
+            traffic_file = "varlen_quadratic_traffic.txt"
+        config = {"workload": f"varlen: {form} over {len(lens)} packed sequences of "
+                              f"{min(lens)}..{max_len} tokens ({total} in all), H={H} p={p} (n={n}) dv={dv}",
+                  "global_batch": len(lens), "tokens": total, "heads": H, "p": p, "dv": dv,
+                  "form": args.varlen_form, "parallelism": "single-gpu"}
+        if args.varlen_form == "chunked":
+            config.update({"chunk": C, "scan": args.scan})
         bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
-        traffic_file = f"varlen_C{C}_traffic.txt"
         args.no_cpu_baseline = True
     elif args.workload == "copy":
         nbytes = 1 << 30

@@ -272,6 +272,28 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
                                       const int32_t* cu_seqlens, void* workspace,
                                       size_t workspace_bytes, float* S, float* Z,
                                       kata_stream_t stream);
+/*
+ * kata_quadratic_fwd_varlen - kata_quadratic_fwd (full map) over B sequences packed without
+ * padding, in the token-major layout of kata_chunked_fwd_varlen: q, k are [total, H, p] and
+ * v, o are [total, H, dv]; token cu_seqlens[b] + t of sequence b, head h, is row
+ * (cu_seqlens[b] + t) * H + h. Every sequence attends causally to its own tokens only
+ * (abstract: flash-attention-style operating point; normalized-readout paragraph).
+ * cu_seqlens is a device array of B + 1 int32 (4-byte aligned), cu_seqlens[0] = 0,
+ * non-decreasing, cu_seqlens[B] <= total; max_len must be at least every length (longer
+ * sequences are cut at max_len). Offsets are clamped to [0, total] and lengths to
+ * [0, max_len], so invalid contents give unspecified results but no access outside the
+ * tensors. No workspace, no state. Rows outside every sequence are not written. Each
+ * sequence's rows equal, bit for bit, kata_quadratic_fwd on that sequence alone.
+ *   Supported: bf16 inputs (else KATA_ERR_UNSUPPORTED); p in {16, 32, 64}; dv in {16, 32, 64};
+ *   o in o_dt, must not overlap q, k, v (KATA_ERR_ALIAS).
+ *   Errors: KATA_ERR_NULL for a NULL tensor or cu_seqlens when B * H, total and max_len are
+ *   all positive (otherwise nothing is done); KATA_ERR_ALIGN for a tensor not 16-byte or
+ *   cu_seqlens not 4-byte aligned; KATA_ERR_SHAPE for negative sizes or
+ *   (max_len + 512) * H * max(p, dv) * 4 >= 2^31.
+ */
+kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                        void* o, kata_dtype_t o_dt, int B, int H, int total, int max_len,
+                                        int p, int dv, const int32_t* cu_seqlens, kata_stream_t stream);
 kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
                                         kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
                                         int H, int T, int p, int dv, kata_feature_t fam, int g,

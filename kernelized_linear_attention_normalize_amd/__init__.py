@@ -20,8 +20,8 @@ import torch
 __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "lift",
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
-           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen", "chunked_bwd",
-           "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T"]
+           "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen",
+           "quadratic_fwd_varlen", "chunked_bwd", "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -82,6 +82,8 @@ def load():
     lib.kata_chunked_fwd_ragged.restype = I
     lib.kata_chunked_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
     lib.kata_chunked_fwd_varlen.restype = I
+    lib.kata_quadratic_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    lib.kata_quadratic_fwd_varlen.restype = I
     lib.kata_order_dim.argtypes, lib.kata_order_dim.restype = [I, I], I64
     lib.kata_lift_order.argtypes, lib.kata_lift_order.restype = [P, I, I64, I, I, P, I, P], I
     lib.kata_quadratic_fwd_order.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P]
@@ -233,6 +235,31 @@ def chunked_fwd_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64, scan="ass
                                            Z.data_ptr() if Z is not None else None, _stream(dev)),
                "kata_chunked_fwd_varlen")
     return (out, S, Z) if return_state else out
+
+
+def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=None):
+    """Flash-style quadratic forward (full map, bf16 inputs) over B sequences packed without
+    padding: q, k [total, H, p]; v [total, H, dv] -> o [total, H, dv], each sequence causal over
+    its own tokens. cu_seqlens: int32 device tensor [B + 1] of sequence offsets (0 first,
+    non-decreasing); max_len >= every length. Rows outside every sequence are not written."""
+    lib = load()
+    dev = _dev(q, k, v)
+    total, H, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2]:
+        raise ValueError("shape mismatch between q, k and v")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
+    _dev(cu_seqlens, q)
+    B = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((total, H, dv), dtype=out_dtype or v.dtype, device=dev)
+    _dev(out, q)
+    with torch.cuda.device(dev):
+        _check(lib.kata_quadratic_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q), out.data_ptr(),
+                                             _dt(out), B, H, total, max_len, p, dv, cu_seqlens.data_ptr(),
+                                             _stream(dev)), "kata_quadratic_fwd_varlen")
+    return out
 
 
 def chunked_workspace_bytes_family(B, H, T, p, dv, C, scan=SCAN_ASSOCIATIVE, in_dtype=torch.bfloat16,

@@ -56,14 +56,16 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // lift psi_2R (psi_2r display of the HTML page); R = 1 is the rank-one map.
 // STATS (backward, full map): no output; instead row t's denominator D_t = sum_s w_ts (with
 // the raw query, as everywhere here) and delta_t = gout_t . o_t go to stats[2 t], [2 t + 1].
-template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1, bool STATS = false>
+template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1, bool STATS = false, bool PK = false>
 __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v,
                                                                 void* __restrict__ o, int T,
                                                                 int nqb, const uint16_t* __restrict__ gout,
-                                                                float* __restrict__ stats) {
+                                                                float* __restrict__ stats,
+                                                                SeqLayout lay = SeqLayout{}, int H = 0) {
   using namespace quad;
+  static_assert(!(PK && STATS), "statistics take the padded layout");
   constexpr int KS = (P + 31) / 32;                        // 32-wide k-steps over components
   constexpr int KP = P == 64 ? 80 : (P == 32 ? 48 : 16);   // bf16 pitch of K rows (8 * odd floats)
   constexpr int NT = DV / 16;                              // 16-wide output column tiles
@@ -86,9 +88,19 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   const int64_t bh = blockIdx.x % nbh;
   const int qb0 = (nqb - 1 - (int)(blockIdx.x / nbh)) * BM;
   const int qw0 = qb0 + wave * QW;
-  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
+  // Rows of this sequence: row0 + t * stp for t < len. Padded [B, H, T]: contiguous, all T
+  // rows. Packed token-major (PK): H rows apart, the length from cu_seqlens (T = max_len).
+  int64_t row0 = bh * (int64_t)T;
+  int stp = 1, len = T;
+  if constexpr (PK) {
+    seq_rows_of(lay, bh, H, T, row0, stp, len);
+    if (qb0 >= len) return;  // uniform over the workgroup: no query of this block exists
+  }
+  const int RQ = PK ? stp * P : P, RV = PK ? stp * DV : DV;  // elements from one row to the next
+  // rows at or past len lie outside the resources and read as zero
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + row0 * DV, (uint32_t)len * RV * 2);
 
   // ---- raw query fragments (B operand of S^T): query qw0 + 16 qt + ln, comps 32 ks + 8 lg..
   bf16x8_t qf[NQT][KS];
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t raw = {0u, 0u, 0u, 0u};
       if (P >= 32 || lg < 2)  // rows past T read as zero
-        raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)((qw0 + 16 * qt + ln) * P + 32 * ks + 8 * lg) * 2, 0, 0);
+        raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)((qw0 + 16 * qt + ln) * RQ + 32 * ks + 8 * lg) * 2, 0, 0);
       qf[qt][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
 
@@ -113,12 +125,12 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
     for (int i = 0; i < KI; ++i) {
       const int pc = tid + NTHR * i;
       if (pc < KPIECES)
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((kb0 + pc / KPC) * P + 8 * (pc % KPC)) * 2, 0, 0);
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((kb0 + pc / KPC) * RQ + 8 * (pc % KPC)) * 2, 0, 0);
     }
     if (tid < VPIECES) {
-      const uint32_t off = (uint32_t)((kb0 + 2 * vp) * DV + 8 * vd) * 2;
+      const uint32_t off = (uint32_t)((kb0 + 2 * vp) * RV + 8 * vd) * 2;
       vreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-      vreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + DV * 2, 0, 0);
+      vreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + RV * 2, 0, 0);
     }
   };
   auto stage = [&](int buf) {
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   }
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  const int kend = min(T, qb0 + BM);
+  const int kend = min(len, qb0 + BM);
   const int nkb = (kend + BN - 1) / BN;
   prefetch(0);
   stage(0);
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
         }
       }
     };
-    if (kb0 <= qw0 + QW - 1 && qw0 < T) {
+    if (kb0 <= qw0 + QW - 1 && qw0 < len) {
       if (kb0 + BN - 1 > qw0) block(std::true_type{});
       else block(std::false_type{});
     }
@@ -302,13 +314,13 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int query = qw0 + 16 * qt + ln;
-    if (query >= T) continue;
+    if (query >= len) continue;
     const float den = D[qt][0];
     const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const f32x4_t x = O[qt][nt] * inv;
-      const int64_t idx = (bh * T + query) * (int64_t)DV + 16 * nt + 4 * lg;
+      const int64_t idx = (row0 + (int64_t)query * stp) * DV + 16 * nt + 4 * lg;
       if constexpr (OUT_BF16)
         *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + idx) = u32x2_t{pk2(x[0], x[1]), pk2(x[2], x[3])};
       else
@@ -336,6 +348,35 @@ hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uin
   KATA_QCASE(32, 16) KATA_QCASE(32, 32) KATA_QCASE(32, 64)
   KATA_QCASE(64, 16) KATA_QCASE(64, 32) KATA_QCASE(64, 64)
 #undef KATA_QCASE
+  return hipErrorInvalidValue;
+}
+
+// packed token-major sequences (SeqLayout with cu set), full map: grid of the padded call
+// with T = max_len; query blocks past a sequence's length return at once
+template <int P, int DV>
+static hipError_t launch_quad_packed(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
+                                     int BH, int H, int max_len, SeqLayout lay, hipStream_t st) {
+  const int nqb = (max_len + quad::BM - 1) / quad::BM;
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
+  if (o_bf16)
+    quadratic_bf16_kernel<P, DV, true, 0, 1, 1, false, true>
+        <<<grid, block, 0, st>>>(q, k, v, o, max_len, nqb, nullptr, nullptr, lay, H);
+  else
+    quadratic_bf16_kernel<P, DV, false, 0, 1, 1, false, true>
+        <<<grid, block, 0, st>>>(q, k, v, o, max_len, nqb, nullptr, nullptr, lay, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_quadratic_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                                        bool o_bf16, int B, int H, int max_len, int p, int dv, SeqLayout lay,
+                                        hipStream_t st) {
+  const int BH = B * H;
+#define KATA_QVCASE(PP, DD) \
+  if (p == PP && dv == DD) return launch_quad_packed<PP, DD>(q, k, v, o, o_bf16, BH, H, max_len, lay, st);
+  KATA_QVCASE(16, 16) KATA_QVCASE(16, 32) KATA_QVCASE(16, 64)
+  KATA_QVCASE(32, 16) KATA_QVCASE(32, 32) KATA_QVCASE(32, 64)
+  KATA_QVCASE(64, 16) KATA_QVCASE(64, 32) KATA_QVCASE(64, 64)
+#undef KATA_QVCASE
   return hipErrorInvalidValue;
 }
 

@@ -267,6 +267,25 @@ def test_chunked_bwd_varlen_validation(lib):
     assert vb(total=0) == OK and vb(max_len=0) == OK and vb(B=0) == OK
 
 
+def test_quadratic_varlen_validation(lib):
+    """kata_quadratic_fwd_varlen: argument errors come back before any device access."""
+    def qv(cu=A + (1 << 36), **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, dt=BF16, o=A + (1 << 30), odt=BF16, B=2, H=2, total=300,
+                 max_len=200, p=32, dv=64)
+        a.update(kw)
+        return lib.kata_quadratic_fwd_varlen(a["q"], a["k"], a["v"], a["dt"], a["o"], a["odt"], a["B"], a["H"],
+                                             a["total"], a["max_len"], a["p"], a["dv"], cu, None)
+    assert qv(dt=F32) == E_UNSUP and qv(p=48) == E_UNSUP and qv(dv=8) == E_UNSUP
+    assert qv(dt=5) == E_DTYPE and qv(odt=2) == E_DTYPE
+    assert qv(cu=None) == E_NULL and qv(cu=A + (1 << 36) + 2) == E_ALIGN
+    assert qv(total=-1) == E_SHAPE and qv(max_len=-3) == E_SHAPE and qv(H=-1) == E_SHAPE
+    assert qv(q=None) == E_NULL and qv(o=None) == E_NULL and qv(v=A + 8) == E_ALIGN
+    assert qv(o=A + 4096) == E_ALIAS                              # o on top of k
+    assert qv(H=1024, max_len=1 << 14, total=1 << 14) == E_SHAPE  # 32-bit offsets of one sequence
+    assert qv(H=16, max_len=(1 << 19) - 256, total=100) == E_SHAPE  # a query block past the end counts
+    assert qv(total=0) == OK and qv(max_len=0) == OK and qv(B=0) == OK and qv(H=0) == OK
+
+
 def test_higher_orders(lib):
     from oracle import kata_families as kf
     for p, r in [(4, 2), (16, 2), (3, 3), (8, 4), (64, 1)]:
