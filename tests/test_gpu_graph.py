@@ -115,3 +115,46 @@ def test_graph_chunked_backward():
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv"), got, ref):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_graph_packed_sequences_new_lengths():
+    """The packed forms (chunked and quadratic) in one graph. cu_seqlens is device memory read
+    by the kernels, so every replay takes new sequence lengths as well as new tokens without a
+    new capture (the grid is sized by max_len); each replay equals the eager calls bit for bit."""
+    H, p, dv, C, max_len = 2, 32, 64, 64, 700
+    total = 1500
+    print("[case] graph packed sequences", flush=True)
+    rng = np.random.default_rng(83)
+
+    def draw(lens):
+        x = [torch.from_numpy(rng.standard_normal((total, H, w), dtype=np.float32)).to(torch.bfloat16).cuda()
+             for w in (p, p, dv)]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+        return x, cu
+
+    (q, k, v), cu = draw([700, 0, 300, 500])
+    oc = torch.empty((total, H, dv), dtype=torch.float32, device="cuda:0")
+    oq = torch.empty((total, H, dv), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(kata.chunked_workspace_bytes(4, H, max_len, p, dv, C, kata.SCAN_ASSOCIATIVE), 1),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        kata.chunked_fwd_varlen(q, k, v, cu, max_len, C=C, out=oc, workspace=ws)
+        kata.quadratic_fwd_varlen(q, k, v, cu, max_len, out=oq)
+
+    g = _capture(step)
+    for rep, lens in enumerate([[1, 699, 0, 700], [350, 350, 77, 123], [700, 700, 0, 0]]):
+        (nq, nk, nv), ncu = draw(lens)
+        q.copy_(nq), k.copy_(nk), v.copy_(nv), cu.copy_(ncu)
+        oc.fill_(7.0), oq.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        gc, gq = oc.clone(), oq.clone()
+        rc = torch.full_like(oc, 7.0)
+        rq = torch.full_like(oq, 7.0)
+        kata.chunked_fwd_varlen(nq, nk, nv, ncu, max_len, C=C, out=rc)  # eager, between replays
+        kata.quadratic_fwd_varlen(nq, nk, nv, ncu, max_len, out=rq)
+        torch.cuda.synchronize()
+        n = sum(lens)
+        assert torch.equal(gc, rc) and torch.equal(gq, rq), f"replay {rep} differs from the eager calls"
+        assert bool((gc[n:] == 7.0).all()) and bool((gq[n:] == 7.0).all()), f"replay {rep}: rows past the sequences"
