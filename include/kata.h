@@ -273,7 +273,7 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
                                       size_t workspace_bytes, float* S, float* Z,
                                       kata_stream_t stream);
 /*
- * kata_quadratic_fwd_varlen - kata_quadratic_fwd (full map) over B sequences packed without
+ * kata_quadratic_fwd_varlen - kata_quadratic_fwd_family over B sequences packed without
  * padding, in the token-major layout of kata_chunked_fwd_varlen: q, k are [total, H, p] and
  * v, o are [total, H, dv]; token cu_seqlens[b] + t of sequence b, head h, is row
  * (cu_seqlens[b] + t) * H + h. Every sequence attends causally to its own tokens only
@@ -283,9 +283,11 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
  * sequences are cut at max_len). Offsets are clamped to [0, total] and lengths to
  * [0, max_len], so invalid contents give unspecified results but no access outside the
  * tensors. No workspace, no state. Rows outside every sequence are not written. Each
- * sequence's rows equal, bit for bit, kata_quadratic_fwd on that sequence alone.
- *   Supported: bf16 inputs (else KATA_ERR_UNSUPPORTED); p in {16, 32, 64}; dv in {16, 32, 64};
- *   o in o_dt, must not overlap q, k, v (KATA_ERR_ALIAS).
+ * sequence's rows equal, bit for bit, kata_quadratic_fwd_family on that sequence alone.
+ *   Supported: bf16 inputs (else KATA_ERR_UNSUPPORTED); dv in {16, 32, 64}; the full map with
+ *   p in {16, 32, 64}, or KATA-Sigma g / KATA-M g with p = 64, g = 2 (reduced PSD families
+ *   paragraph); fam, g as for kata_quadratic_fwd_family (KATA_ERR_FEATURE when g does not
+ *   fit the family); o in o_dt, must not overlap q, k, v (KATA_ERR_ALIAS).
  *   Errors: KATA_ERR_NULL for a NULL tensor or cu_seqlens when B * H, total and max_len are
  *   all positive (otherwise nothing is done); KATA_ERR_ALIGN for a tensor not 16-byte or
  *   cu_seqlens not 4-byte aligned; KATA_ERR_SHAPE for negative sizes or
@@ -293,7 +295,8 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
  */
 kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
                                         void* o, kata_dtype_t o_dt, int B, int H, int total, int max_len,
-                                        int p, int dv, const int32_t* cu_seqlens, kata_stream_t stream);
+                                        int p, int dv, kata_feature_t fam, int g, const int32_t* cu_seqlens,
+                                        kata_stream_t stream);
 kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,
                                         kata_dtype_t in_dt, void* o, kata_dtype_t o_dt, int B,
                                         int H, int T, int p, int dv, kata_feature_t fam, int g,

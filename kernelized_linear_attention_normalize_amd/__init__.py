@@ -82,7 +82,7 @@ def load():
     lib.kata_chunked_fwd_ragged.restype = I
     lib.kata_chunked_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, I, P, P, SZ, P, P, P]
     lib.kata_chunked_fwd_varlen.restype = I
-    lib.kata_quadratic_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    lib.kata_quadratic_fwd_varlen.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, I, P, P]
     lib.kata_quadratic_fwd_varlen.restype = I
     lib.kata_order_dim.argtypes, lib.kata_order_dim.restype = [I, I], I64
     lib.kata_lift_order.argtypes, lib.kata_lift_order.restype = [P, I, I64, I, I, P, I, P], I
@@ -237,11 +237,13 @@ def chunked_fwd_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64, scan="ass
     return (out, S, Z) if return_state else out
 
 
-def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=None):
-    """Flash-style quadratic forward (full map, bf16 inputs) over B sequences packed without
-    padding: q, k [total, H, p]; v [total, H, dv] -> o [total, H, dv], each sequence causal over
-    its own tokens. cu_seqlens: int32 device tensor [B + 1] of sequence offsets (0 first,
-    non-decreasing); max_len >= every length. Rows outside every sequence are not written."""
+def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=None, family: str = "full",
+                         g: int = 1):
+    """Flash-style quadratic forward (bf16 inputs) over B sequences packed without padding:
+    q, k [total, H, p]; v [total, H, dv] -> o [total, H, dv], each sequence causal over its own
+    tokens. cu_seqlens: int32 device tensor [B + 1] of sequence offsets (0 first,
+    non-decreasing); max_len >= every length. family, g: the full map, or KATA-Sigma 2 /
+    KATA-M 2 at p = 64. Rows outside every sequence are not written."""
     lib = load()
     dev = _dev(q, k, v)
     total, H, p = q.shape
@@ -257,7 +259,8 @@ def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=
     _dev(out, q)
     with torch.cuda.device(dev):
         _check(lib.kata_quadratic_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q), out.data_ptr(),
-                                             _dt(out), B, H, total, max_len, p, dv, cu_seqlens.data_ptr(),
+                                             _dt(out), B, H, total, max_len, p, dv, _fam(family, g), g,
+                                             cu_seqlens.data_ptr(),
                                              _stream(dev)), "kata_quadratic_fwd_varlen")
     return out
 

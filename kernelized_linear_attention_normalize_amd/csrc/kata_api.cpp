@@ -414,10 +414,15 @@ kata_status_t kata_quadratic_fwd(const void* q, const void* k, const void* v, ka
 
 kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
                                         void* o, kata_dtype_t o_dt, int B, int H, int total, int max_len, int p,
-                                        int dv, const int32_t* cu_seqlens, kata_stream_t stream) {
+                                        int dv, kata_feature_t fam, int g, const int32_t* cu_seqlens,
+                                        kata_stream_t stream) {
   if (!valid_dt(in_dt) || !valid_dt(o_dt)) return KATA_ERR_DTYPE;
   if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
-  if (in_dt != KATA_DTYPE_BF16 || !in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) return KATA_ERR_UNSUPPORTED;
+  kata_status_t s = check_feature(p, fam, g);
+  if (s != KATA_OK) return s;
+  if (in_dt != KATA_DTYPE_BF16 || !in_set(dv, {16, 32, 64})) return KATA_ERR_UNSUPPORTED;
+  if (fam == KATA_FEAT_FULL ? !in_set(p, {16, 32, 64}) : !kata::quadratic_bf16_family_supported(p, dv, (int)fam, g))
+    return KATA_ERR_UNSUPPORTED;
   if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
   if (cu_seqlens == nullptr) return KATA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
@@ -428,16 +433,15 @@ kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void
   if ((int64_t)B * H * ((max_len + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
   if (!q || !k || !v || !o) return KATA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KATA_ERR_ALIGN;
-  kata_status_t s = check_fwd_alias(q, k, v, in_dt, o, o_dt, (size_t)total * H, p, dv);
-  if (s != KATA_OK) return s;
+  if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, (size_t)total * H, p, dv)) != KATA_OK) return s;
   kata::SeqLayout lay;
   lay.cu = cu_seqlens;
   lay.total = total;
   return hip_status(kata::launch_quadratic_bf16_varlen(static_cast<const uint16_t*>(q),
                                                        static_cast<const uint16_t*>(k),
                                                        static_cast<const uint16_t*>(v), o,
-                                                       o_dt == KATA_DTYPE_BF16, B, H, max_len, p, dv, lay,
-                                                       (hipStream_t)stream));
+                                                       o_dt == KATA_DTYPE_BF16, B, H, max_len, p, dv, (int)fam,
+                                                       g, lay, (hipStream_t)stream));
 }
 
 kata_status_t kata_quadratic_fwd_family(const void* q, const void* k, const void* v,

@@ -118,9 +118,10 @@ hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, 
                                    int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st);
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
-// the same over packed token-major sequences (lay.cu set; T = max_len), full map
+// the same over packed token-major sequences (lay.cu set; T = max_len): the full map (fam 0)
+// or a reduced family that quadratic_bf16_family_supported covers
 hipError_t launch_quadratic_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
-                                        bool o_bf16, int B, int H, int max_len, int p, int dv, SeqLayout lay,
-                                        hipStream_t st);
+                                        bool o_bf16, int B, int H, int max_len, int p, int dv, int fam, int g,
+                                        SeqLayout lay, hipStream_t st);
 
 }  // namespace kata

@@ -351,26 +351,35 @@ hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uin
   return hipErrorInvalidValue;
 }
 
-// packed token-major sequences (SeqLayout with cu set), full map: grid of the padded call
-// with T = max_len; query blocks past a sequence's length return at once
-template <int P, int DV>
+// packed token-major sequences (SeqLayout with cu set): grid of the padded call with
+// T = max_len; query blocks past a sequence's length return at once
+template <int P, int DV, int FAM = 0, int G = 1>
 static hipError_t launch_quad_packed(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16,
                                      int BH, int H, int max_len, SeqLayout lay, hipStream_t st) {
   const int nqb = (max_len + quad::BM - 1) / quad::BM;
   dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
   if (o_bf16)
-    quadratic_bf16_kernel<P, DV, true, 0, 1, 1, false, true>
+    quadratic_bf16_kernel<P, DV, true, FAM, G, 1, false, true>
         <<<grid, block, 0, st>>>(q, k, v, o, max_len, nqb, nullptr, nullptr, lay, H);
   else
-    quadratic_bf16_kernel<P, DV, false, 0, 1, 1, false, true>
+    quadratic_bf16_kernel<P, DV, false, FAM, G, 1, false, true>
         <<<grid, block, 0, st>>>(q, k, v, o, max_len, nqb, nullptr, nullptr, lay, H);
   return hipGetLastError();
 }
 
 hipError_t launch_quadratic_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
-                                        bool o_bf16, int B, int H, int max_len, int p, int dv, SeqLayout lay,
-                                        hipStream_t st) {
+                                        bool o_bf16, int B, int H, int max_len, int p, int dv, int fam, int g,
+                                        SeqLayout lay, hipStream_t st) {
   const int BH = B * H;
+  if (fam != 0) {  // the reduced families with 32-component blocks (p = 64, g = 2)
+    if (!quadratic_bf16_family_supported(p, dv, fam, g)) return hipErrorInvalidValue;
+#define KATA_QVFCASE(DD, FF) \
+  if (dv == DD && fam == FF) return launch_quad_packed<64, DD, FF, 2>(q, k, v, o, o_bf16, BH, H, max_len, lay, st);
+    KATA_QVFCASE(16, 1) KATA_QVFCASE(32, 1) KATA_QVFCASE(64, 1)
+    KATA_QVFCASE(16, 2) KATA_QVFCASE(32, 2) KATA_QVFCASE(64, 2)
+#undef KATA_QVFCASE
+    return hipErrorInvalidValue;
+  }
 #define KATA_QVCASE(PP, DD) \
   if (p == PP && dv == DD) return launch_quad_packed<PP, DD>(q, k, v, o, o_bf16, BH, H, max_len, lay, st);
   KATA_QVCASE(16, 16) KATA_QVCASE(16, 32) KATA_QVCASE(16, 64)

@@ -271,11 +271,13 @@ def test_quadratic_varlen_validation(lib):
     """kata_quadratic_fwd_varlen: argument errors come back before any device access."""
     def qv(cu=A + (1 << 36), **kw):
         a = dict(q=A, k=A + 4096, v=A + 8192, dt=BF16, o=A + (1 << 30), odt=BF16, B=2, H=2, total=300,
-                 max_len=200, p=32, dv=64)
+                 max_len=200, p=32, dv=64, fam=0, g=1)
         a.update(kw)
         return lib.kata_quadratic_fwd_varlen(a["q"], a["k"], a["v"], a["dt"], a["o"], a["odt"], a["B"], a["H"],
-                                             a["total"], a["max_len"], a["p"], a["dv"], cu, None)
+                                             a["total"], a["max_len"], a["p"], a["dv"], a["fam"], a["g"], cu, None)
     assert qv(dt=F32) == E_UNSUP and qv(p=48) == E_UNSUP and qv(dv=8) == E_UNSUP
+    assert qv(fam=1, g=2) == E_UNSUP and qv(fam=2, g=4, p=64) == E_UNSUP   # families: p = 64, g = 2 only
+    assert qv(fam=1, g=3) == E_FEAT and qv(fam=0, g=2) == E_FEAT and qv(fam=9) == E_FEAT
     assert qv(dt=5) == E_DTYPE and qv(odt=2) == E_DTYPE
     assert qv(cu=None) == E_NULL and qv(cu=A + (1 << 36) + 2) == E_ALIGN
     assert qv(total=-1) == E_SHAPE and qv(max_len=-3) == E_SHAPE and qv(H=-1) == E_SHAPE

@@ -103,9 +103,11 @@ def test_varlen_packed(dt, family, p, g, dv, C, scan):
     assert np.array_equal(S, to_np(Sp)) and np.array_equal(Z, to_np(Zp))
 
 
-@pytest.mark.parametrize("p,dv,odt,cut", [(32, 64, torch.float32, False), (64, 64, torch.bfloat16, False),
-                                          (16, 16, torch.float32, False), (64, 32, torch.float32, True)])
-def test_quadratic_varlen_packed(p, dv, odt, cut):
+@pytest.mark.parametrize("family,g,p,dv,odt,cut", [
+    ("full", 1, 32, 64, torch.float32, False), ("full", 1, 64, 64, torch.bfloat16, False),
+    ("full", 1, 16, 16, torch.float32, False), ("full", 1, 64, 32, torch.float32, True),
+    ("sigma", 2, 64, 64, torch.float32, False), ("block", 2, 64, 32, torch.bfloat16, True)])
+def test_quadratic_varlen_packed(family, g, p, dv, odt, cut):
     """Token-major packed sequences on the quadratic form (kata_quadratic_fwd_varlen, bf16):
     each sequence against the oracle on it alone, lengths across several 512-query blocks and
     ragged 64-key blocks (0, 1, 37, 513, ...), rows outside every sequence untouched, and
@@ -114,7 +116,7 @@ def test_quadratic_varlen_packed(p, dv, odt, cut):
     B, H = 6, 3
     lens = [1100, 0, 1, 37, 600, 513]
     max_len = 1024 if cut else 1200
-    print(f"[case] quadratic varlen p={p} dv={dv} out={odt} lens={lens} max_len={max_len}", flush=True)
+    print(f"[case] quadratic varlen {family}{g} p={p} dv={dv} out={odt} lens={lens} max_len={max_len}", flush=True)
     q, k, v = draw_qkv(53, B, H, max(lens), p, dv, "bf16")
     extra = 5
     pk = [np.concatenate([_pack(x, lens), x[0, :, :extra].transpose(1, 0, 2)], axis=0) for x in (q, k, v)]
@@ -122,7 +124,7 @@ def test_quadratic_varlen_packed(p, dv, odt, cut):
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
     out = torch.full((total, H, dv), 7.0, dtype=odt, device="cuda:0")
     qd, kd, vd = (to_dev(x, "bf16") for x in pk)
-    o = to_np(kata.quadratic_fwd_varlen(qd, kd, vd, cu, max_len, out=out))
+    o = to_np(kata.quadratic_fwd_varlen(qd, kd, vd, cu, max_len, out=out, family=family, g=g))
     starts = np.concatenate([[0], np.cumsum(lens)])
     assert np.all(o[starts[-1]:] == 7.0), "rows outside every sequence were written"
     for b, L in enumerate(lens):
@@ -132,10 +134,10 @@ def test_quadratic_varlen_packed(p, dv, odt, cut):
         if Lc == 0:
             continue
         got = np.transpose(o[starts[b]:starts[b] + Lc], (1, 0, 2))
-        ref = kf.naive_family(q[b, :, :Lc], k[b, :, :Lc], v[b, :, :Lc], "full", 1)
+        ref = kf.naive_family(q[b, :, :Lc], k[b, :, :Lc], v[b, :, :Lc], family, g)
         err = row_rel_err(got, ref)
         print(f"  seq {b} L={Lc} rel_err={err:.3e}", flush=True)
         assert err <= TOL["bf16"]
         alone = kata.quadratic_fwd(*(to_dev(np.ascontiguousarray(x[b:b + 1, :, :Lc]), "bf16") for x in (q, k, v)),
-                                   out_dtype=odt)
+                                   out_dtype=odt, family=family, g=g)
         assert np.array_equal(got, to_np(alone)[0]), f"seq {b} differs from the padded call"
