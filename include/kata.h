@@ -16,6 +16,8 @@
  *     row-major, 16-byte aligned. The library never allocates, never frees, never
  *     synchronises and keeps no mutable global state; calls only enqueue work on
  *     `stream` and return. Results are valid once the stream has executed the work.
+ *     One exception, by design: kata_chunked_fwd_noalloc keeps its workspace in a fixed
+ *     device array of the library (one per GPU, shared by every call on that GPU).
  *   - Arguments are validated on the host before any HIP call. A call with a zero-sized
  *     problem (rows, B, H, T or N equal to 0) does nothing and returns KATA_OK; its
  *     pointers may then be NULL.
@@ -70,7 +72,9 @@ typedef enum {
   KATA_ERR_HIP = 8,         /* a HIP launch failed */
   KATA_ERR_SCAN = 9,        /* scan is not a kata_scan_t value */
   KATA_ERR_PASS = 10,       /* passes is not a non-empty combination of kata_pass_t bits */
-  KATA_ERR_FEATURE = 11     /* feature family not a kata_feature_t value, or g does not divide p */
+  KATA_ERR_FEATURE = 11,    /* feature family not a kata_feature_t value, or g does not divide p */
+  KATA_ERR_SCRATCH = 12     /* kata_chunked_fwd_noalloc: the call needs more workspace than
+                             * KATA_NOALLOC_SCRATCH_BYTES */
 } kata_status_t;
 
 /* PSD feature families (reduced PSD families paragraph of the HTML page). The projected
@@ -158,6 +162,31 @@ kata_status_t kata_chunked_fwd_passes(const void* q, const void* k, const void* 
                                       int T, int p, int dv, int C, kata_scan_t scan,
                                       void* workspace, size_t workspace_bytes, int passes,
                                       kata_stream_t stream);
+
+/* Size of the library's fixed device scratch array used by kata_chunked_fwd_noalloc. */
+#define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * kata_chunked_fwd_noalloc - kata_chunked_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * caller passes inputs and outputs only; the workspace kata_chunked_fwd would take is a
+ * static device array of KATA_NOALLOC_SCRATCH_BYTES (64 MiB) owned by the library. Each GPU
+ * the library runs on holds its own copy from the first call on that device (whose address is
+ * resolved then, with hipGetSymbolAddress, while that device is current) until the process
+ * ends. The call allocates and frees nothing, and no library routine it calls does.
+ *   Arguments, validation, results and errors as kata_chunked_fwd (bit-identical output);
+ *   the current device must be the one holding q, k, v, o and the stream. Arguments are
+ *   validated before any HIP call; then a call whose workspace would exceed
+ *   KATA_NOALLOC_SCRATCH_BYTES returns KATA_ERR_SCRATCH without enqueueing anything (every
+ *   supported shape needs at most about 36 MB). The summaries in the array are written
+ *   before they are read, so no call depends on what a previous one left there.
+ *   Concurrency: every call on one GPU shares that GPU's array; calls whose work overlaps on
+ *   one GPU (different streams, or different host threads without ordering) race on it and
+ *   give unspecified results. Calls ordered on one stream are safe.
+ */
+kata_status_t kata_chunked_fwd_noalloc(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                       void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                       int C, kata_scan_t scan, kata_stream_t stream);
 
 /*
  * kata_chunked_fwd_state - kata_chunked_fwd that also returns the recurrent state after the

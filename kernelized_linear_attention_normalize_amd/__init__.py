@@ -21,7 +21,8 @@ __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "li
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
            "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen",
-           "quadratic_fwd_varlen", "chunked_bwd", "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T"]
+           "quadratic_fwd_varlen", "chunked_bwd", "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T",
+           "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkata.so")
@@ -35,7 +36,7 @@ FEATURES = {"full": 0, "sigma": 1, "block": 2}
 _STATUS = {0: "KATA_OK", 1: "KATA_ERR_NULL", 2: "KATA_ERR_SHAPE", 3: "KATA_ERR_DTYPE",
            4: "KATA_ERR_UNSUPPORTED", 5: "KATA_ERR_ALIGN", 6: "KATA_ERR_ALIAS",
            7: "KATA_ERR_WORKSPACE", 8: "KATA_ERR_HIP", 9: "KATA_ERR_SCAN", 10: "KATA_ERR_PASS",
-           11: "KATA_ERR_FEATURE"}
+           11: "KATA_ERR_FEATURE", 12: "KATA_ERR_SCRATCH"}
 
 
 class KataError(RuntimeError):
@@ -64,6 +65,8 @@ def load():
     lib.kata_chunked_workspace_bytes.restype = SZ
     lib.kata_chunked_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, P]
     lib.kata_chunked_fwd.restype = I
+    lib.kata_chunked_fwd_noalloc.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P]
+    lib.kata_chunked_fwd_noalloc.restype = I
     lib.kata_chunked_fwd_passes.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, I, P]
     lib.kata_chunked_fwd_passes.restype = I
     lib.kata_chunked_fwd_state.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P, SZ, P, P, P]
@@ -275,6 +278,26 @@ def _scan_code(scan) -> int:
     if isinstance(scan, str):
         return {"sequential": SCAN_SEQUENTIAL, "associative": SCAN_ASSOCIATIVE}[scan]
     return int(scan)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KATA_NOALLOC_SCRATCH_BYTES
+
+
+def chunked_fwd_noalloc(q, k, v, out, C: int = 64, scan="associative"):
+    """kata_chunked_fwd_noalloc: the chunked forward with the library's fixed device scratch as
+    its workspace (nothing is allocated by the call). The caller passes the output tensor
+    out [B,H,T,dv] (float32 or bfloat16). Calls overlapping on one GPU race on the scratch."""
+    lib = load()
+    dev = _dev(q, k, v, out)
+    B, H, T, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or tuple(out.shape) != (B, H, T, dv):
+        raise ValueError("shape mismatch between q, k, v and out")
+    with torch.cuda.device(dev):
+        _check(lib.kata_chunked_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
+                                            out.data_ptr(), _dt(out), B, H, T, p, dv, C, _scan_code(scan),
+                                            _stream(dev)), "kata_chunked_fwd_noalloc")
+    return out
 
 
 def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=None,

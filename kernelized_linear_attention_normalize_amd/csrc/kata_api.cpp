@@ -101,6 +101,8 @@ const char* kata_status_string(kata_status_t s) {
     case KATA_ERR_SCAN: return "KATA_ERR_SCAN: invalid scan mode";
     case KATA_ERR_PASS: return "KATA_ERR_PASS: invalid pass mask";
     case KATA_ERR_FEATURE: return "KATA_ERR_FEATURE: invalid feature family or block count";
+    case KATA_ERR_SCRATCH:
+      return "KATA_ERR_SCRATCH: the call needs more workspace than the fixed no-allocation scratch holds";
   }
   return "KATA_ERR_UNKNOWN";
 }
@@ -205,7 +207,8 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
                                   int C, kata_scan_t scan, kata_feature_t fam, int g,
                                   void* workspace, size_t workspace_bytes, int passes,
                                   bool want_state, float* S, float* Z, const int32_t* lens,
-                                  const int32_t* cu, int total, kata_stream_t stream) {
+                                  const int32_t* cu, int total, kata_stream_t stream,
+                                  bool use_scratch = false) {
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (passes < 1 || passes > KATA_PASS_ALL) return KATA_ERR_PASS;
   if (C < 1) return KATA_ERR_SHAPE;
@@ -250,7 +253,13 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
   const size_t need = kata_chunked_workspace_bytes_family(B, H, T, p, dv, C, scan, in_dt, fam, g);
-  if (need > 0) {
+  if (need > 0 && use_scratch) {
+    // the library's own scratch array: cannot overlap caller buffers; resolved only after
+    // every argument has been validated
+    if (need > KATA_NOALLOC_SCRATCH_BYTES) return KATA_ERR_SCRATCH;
+    if (kata::noalloc_scratch(&workspace) != hipSuccess) return KATA_ERR_HIP;
+    workspace_bytes = need;
+  } else if (need > 0) {
     if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KATA_ERR_ALIGN;
     const size_t ob = rows * dv * dt_size(o_dt);
@@ -363,6 +372,13 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
   if ((int64_t)total * H * (p > dv ? p : dv) < 0 || mul4(total, H, p > dv ? p : dv, 1) < 0) return KATA_ERR_SHAPE;
   return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, max_len, p, dv, C, scan, fam, g, workspace,
                       workspace_bytes, KATA_PASS_ALL, S != nullptr, S, Z, nullptr, cu_seqlens, total, stream);
+}
+
+kata_status_t kata_chunked_fwd_noalloc(const void* q, const void* k, const void* v, kata_dtype_t in_dt,
+                                       void* o, kata_dtype_t o_dt, int B, int H, int T, int p, int dv,
+                                       int C, kata_scan_t scan, kata_stream_t stream) {
+  return chunked_impl(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, KATA_FEAT_FULL, 1, nullptr, 0,
+                      KATA_PASS_ALL, false, nullptr, nullptr, nullptr, nullptr, 0, stream, true);
 }
 
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,

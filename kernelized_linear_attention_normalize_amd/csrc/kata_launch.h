@@ -14,6 +14,10 @@ struct SegPlan {
 };
 SegPlan seg_plan(int B, int H, int T, int C, int scan);
 
+// device address of the library's fixed scratch array on the current device (resolved once
+// per device; see kata_chunked_fwd_noalloc)
+hipError_t noalloc_scratch(void** out);
+
 // Where the rows of sequence bh = (b, h) of a chunked forward live. Padded layout
 // [B, H, T, *] (cu null): rows bh * T + t, cut at lens[b] when lens (device, [B]) is given.
 // Packed token-major layout [total, H, *] (cu: device cu_seqlens[B + 1]): rows

@@ -18,7 +18,7 @@ from kernelized_linear_attention_normalize_amd import build_lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 F32, BF16 = 0, 1
 SEQ, ASSOC = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN, E_PASS, E_FEAT = range(12)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_HIP, E_SCAN, E_PASS, E_FEAT, E_SCRATCH = range(13)
 A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never dereferenced)
 
 
@@ -60,7 +60,7 @@ def test_no_unresolved_library_symbols():
 def test_packed_dim_and_status_strings(lib):
     assert lib.kata_packed_dim(32) == 528 and lib.kata_packed_dim(64) == 2080
     assert lib.kata_packed_dim(0) == -1
-    for s in range(12):
+    for s in range(13):
         assert lib.kata_status_string(s).startswith(b"KATA_")
 
 
@@ -330,3 +330,38 @@ def test_quadratic_and_lift_and_decode_validation(lib):
     assert d(N=0) == OK and d(p=65) == E_UNSUP and d(dv=62) == E_UNSUP
     assert d(S=None) == E_NULL and d(Z=A + (1 << 30) + 16) == E_ALIAS
     assert d(o=A + 4096) == E_ALIAS and d(S=A + (1 << 30) + 4) == E_ALIGN
+
+
+def _noalloc(lib, q=A, k=A + 4096, v=A + 8192, in_dt=BF16, o=A + (1 << 30), o_dt=BF16, B=1, H=1, T=128,
+             p=32, dv=64, C=64, scan=ASSOC):
+    return lib.kata_chunked_fwd_noalloc(q, k, v, in_dt, o, o_dt, B, H, T, p, dv, C, scan, None)
+
+
+def test_noalloc_validates_before_any_hip_call(lib):
+    """kata_chunked_fwd_noalloc rejects bad arguments exactly as kata_chunked_fwd does, before
+    it resolves its scratch array (no HIP call happens on these paths: there is no GPU here)."""
+    assert _noalloc(lib, in_dt=7) == E_DTYPE
+    assert _noalloc(lib, scan=5) == E_SCAN
+    assert _noalloc(lib, T=-1) == E_SHAPE
+    assert _noalloc(lib, q=None) == E_NULL
+    assert _noalloc(lib, o=A + 8) == E_ALIGN
+    assert _noalloc(lib, o=A) == E_ALIAS
+    assert _noalloc(lib, p=48) == E_UNSUP
+    assert _noalloc(lib, T=0, q=None, k=None, v=None, o=None) == OK
+
+
+def test_noalloc_scratch_covers_every_supported_shape(lib):
+    """The fixed scratch (64 MiB) holds the workspace of every supported shape: the segment
+    plan keeps B*H*(segments-1) near one workgroup per compute unit, so the largest need is a
+    few hundred summaries whatever B, H and T are."""
+    cap = kata.NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for p in (16, 32):
+        for dv in (16, 32, 64):
+            for C in (32, 64, 128):
+                for dt in (F32, BF16):
+                    for BH in (1, 2, 3, 5, 8, 16, 31, 64, 100, 128, 200, 255, 256, 257, 1000):
+                        for T in (C + 1, 4096, 131072, 1 << 20):
+                            need = lib.kata_chunked_workspace_bytes(1, BH, T, p, dv, C, ASSOC, dt)
+                            worst = max(worst, need)
+    assert 0 < worst <= cap, worst
