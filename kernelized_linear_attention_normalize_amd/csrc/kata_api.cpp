@@ -176,7 +176,9 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
   if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128})) return 0;
   const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
   if (plan.nseg <= 1) return 0;
-  const int64_t sf = in_dt == KATA_DTYPE_BF16 ? kata::mfma_state_floats(p, dv) : kata::f32_state_floats(p, dv);
+  const int64_t sf = in_dt != KATA_DTYPE_BF16            ? kata::f32_state_floats(p, dv)
+                     : kata::chunked_f16_supported(p, dv, C) ? kata::f16_state_floats(dv)
+                                                             : kata::mfma_state_floats(p, dv);
   return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
 }
 
@@ -285,6 +287,10 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   if (fam != KATA_FEAT_FULL)
     return hip_status(kata::launch_family_chunked(q, k, v, in_dt == KATA_DTYPE_BF16, o, ob16, B, H, T, p,
                                                   dv, C, (int)fam, g, plan, ws, so, zo, lay, st));
+  if (in_dt == KATA_DTYPE_BF16 && kata::chunked_f16_supported(p, dv, C))
+    return hip_status(kata::launch_chunked_f16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                               static_cast<const uint16_t*>(v), o, ob16, B, H, T, p, dv, C, plan, ws,
+                                               so, zo, lay, passes, st));
   if (in_dt == KATA_DTYPE_BF16)
     return hip_status(kata::launch_chunked_bf16(static_cast<const uint16_t*>(q),
                                                 static_cast<const uint16_t*>(k),

@@ -54,6 +54,12 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
                               hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
                                 bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
+// fp16-operand chunked forward (kata_chunked16.h): p = 32, dv = 64, C in {64, 128}
+bool chunked_f16_supported(int p, int dv, int C);
+int64_t f16_state_floats(int dv);
+hipError_t launch_chunked_f16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16, int B,
+                              int H, int T, int p, int dv, int C, const SegPlan& plan, float* ws, float* s_out,
+                              float* z_out, SeqLayout lay, int passes, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
                                const SegPlan& plan, float* ws, float* s_out, float* z_out,

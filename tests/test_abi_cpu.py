@@ -306,8 +306,12 @@ def test_workspace_bytes(lib):
     assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, SEQ, BF16) == 0
     assert lib.kata_chunked_workspace_bytes(1, 1, 64, 32, 64, 64, ASSOC, BF16) == 0
     assert lib.kata_chunked_workspace_bytes(1, 1, 64, 33, 64, 64, ASSOC, BF16) == 0   # unsupported
-    # long config: 16 heads x 16 segments, 15 summaries each of (33 tiles x 4 + 4) x 256 floats
-    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16) == 16 * 15 * (33 * 4 * 256 + 4 * 256) * 4
+    # long config (fp16-operand kernels): 16 heads x 16 segments, 15 summaries each of
+    # 18 feature tiles x 2 value tiles x 1024 floats plus the 1024-float Gram tile
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 64, ASSOC, BF16) == 16 * 15 * (18 * 2 * 1024 + 1024) * 4
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 128, ASSOC, BF16) == 16 * 15 * (18 * 2 * 1024 + 1024) * 4
+    # bf16 MFMA kernels of the other shapes: (33 tiles x dv/16 + 4) x 256 floats
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 32, 64, ASSOC, BF16) == 16 * 15 * (33 * 2 * 256 + 4 * 256) * 4
     # fp32 layout: n*dv + n floats per summary
     w = lib.kata_chunked_workspace_bytes(1, 1, 256, 16, 16, 32, ASSOC, F32)
     assert w == 7 * (136 * 16 + 136) * 4
