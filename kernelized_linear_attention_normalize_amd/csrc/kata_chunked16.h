@@ -35,28 +35,29 @@
 // off-diagonal coordinate appears once, with c^2 = 2 folded into the build (partner copies
 // are staged at 2 k_hat), and the within-block pairs twice at weight 1 (tiles 1-3 are built
 // at 2x and halved when the state is handed to the readout).
-//   * Build (ψ(K)^T V on 32x32x16 MFMA): lane = (row, 8 tokens). The staged key rows come
-//     in five copies (own; partner x2 with XOR 0..3 inside each 4-component block), so that
-//     ds_read_b64_tr_b16 transposed reads give every lane its own and its partner component
-//     for 4 tokens at a time: 4 consecutive lanes read 4 consecutive components, which is
-//     exactly a quad's (4a + c, 4B + (c XOR r)).
+//   * Build (psi(K)^T V on 16x16x32 MFMA, 16-row tiles u = 2 t + half): lane = (row,
+//     8 tokens). Keys and values are staged transposed (component-major k_hat^T, a x2
+//     partner copy, sigma V^T), so each operand of a 32-token step is one 16-byte LDS read:
+//     own component, partner component, value column. The row and piece placement (the
+//     tpos comment) keeps those reads free of bank conflicts for ds_read_b128's lane groups.
 //   * Readout (O^T = S^T psi(Q)^T): lane = (token, lane half). A lane holds its token's 32
 //     components as 16 packed fp16 pairs, rotated by one block in the upper lane half, so
 //     one instruction stream serves quads 4s, 4s+2 (lower half) and 4s+1, 4s+3 (upper);
 //     each pair of slots is one v_pk_mul_f16 with op_sel choosing the partner's halves.
-//   * The readout's state fragment of k-step s is the build accumulator's registers
-//     8s..8s+7 of the same lane: the build lane converts and writes 16 bytes, the readout
-//     lane reads them back.
+//   * State fragments: build lane (value column, quad g) of tile u converts its 4
+//     accumulators to fp16 and writes 8 bytes, placed so that readout lane (value row, half h)
+//     reads quads h and h + 2 of the tile as one 16-byte piece.
 //   * Denominator psi(q)^T Z = q^T M q (Gram matrix, fp32-accurate as hi + lo); the
 //     intra-chunk block computes (q_hat . k_hat)^2 from the components (weight identity of
 //     the lift display) and sums the same fp16 weights that multiply V.
 //
-// Waves: 0-3 read out (token group of 32, or a share of the tiles of one), 4-7 build
-// (tiles 0-4, 5-9, 10-13 with the Gram tile, 14-17); wave w and w + 4 share a SIMD. Per
-// chunk: phase 1 = readout of chunk c from the state before it and build of chunk c |
-// barrier | phase 2 = output, staging of chunk c + 1, state after chunk c to LDS | barrier.
-// ASSOCIATIVE runs a summary pass (build only, 8 waves), the segment scan and the segments;
-// SEQUENTIAL runs one segment per sequence.
+// Segment pass waves: 0-3 read out (token group of 32, or a share of the tiles of one), 4-11
+// build (nine 16-row tiles per SIMD, waves w and w + 4 share one) and stage the keys and
+// values. Per chunk: phase 1 = readout of chunk c from the state before it and build of
+// chunk c | barrier | phase 2 = output, staging of chunk c + 1, state after chunk c to LDS |
+// barrier. ASSOCIATIVE runs a summary pass (8 build waves and 4 staging waves over a double
+// buffer, one barrier per chunk), the segment scan and the segments; SEQUENTIAL runs one
+// segment per sequence.
 #pragma once
 #include <utility>
 
@@ -135,66 +136,80 @@ __device__ __forceinline__ h8_t ld8(const char* p) { return *reinterpret_cast<co
 __device__ __forceinline__ void st4(char* p, h4_t x) { *reinterpret_cast<h4_t*>(p) = x; }
 __device__ __forceinline__ void st8(char* p, h8_t x) { *reinterpret_cast<h8_t*>(p) = x; }
 
-// transposed LDS read: lane i of each 16-lane group gets element i % 4 of the 8-byte
-// chunks addressed by lanes i / 4 + 4 j, j = 0..3 (ds_read_b64_tr_b16)
-__device__ __forceinline__ h4_t tr16(const char* lds, uint32_t off) {
-  const s4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(lds + off));
-  return __builtin_bit_cast(h4_t, r);
-}
-__device__ __forceinline__ h8_t tr16x2(const char* lds, uint32_t off0, uint32_t off1) {
-  return cat44(tr16(lds, off0), tr16(lds, off1));
-}
-
 // ---- LDS layout and work split
+// 12 waves: 0-3 read out, 4-11 build; wave w runs on SIMD w % 4, so every SIMD hosts one
+// readout wave and two build waves.
+constexpr int NU = 2 * NTL;  // 16-row build tiles: u = 2 t + half holds quads 4 half .. 4 half + 3 of tile t
+
 template <int DV, int C>
 struct Lay {
-  static constexpr int NDT = DV / 32;          // 32-column value tiles
+  static constexpr int NDT = DV / 32;          // 32-column value tiles of the readout
+  static constexpr int NDV = DV / 16;          // 16-column value tiles of the build
   static constexpr int NG = C / 32;            // 32-token groups per chunk
   static constexpr int FS = 4 / NG;            // readout waves per token group
-  static constexpr int NSTEP = C / 16;         // 16-token build steps
+  static constexpr int NS = C / 32;            // 32-token build steps
   static constexpr int QPB = 72;               // q_hat row pitch, bytes (8-byte block reads conflict-free)
-  static constexpr int KPB = 64;               // key row pitch per copy, bytes
-  static constexpr int VPB = 2 * DV + 16;      // value row pitch, bytes
+  static constexpr int KPB = 64;               // row-major key rows (unscaled k_hat), bytes
+  static constexpr int RPB = 256;              // transposed rows (one component or value column), bytes
   static constexpr int MPB = 80;               // Gram row pitch, bytes
-  static constexpr int ST = NTL * 2 * NDT * 1024;  // state fragments (fp16)
+  static constexpr int ST = NU * NDV * 64 * 8;  // state fragments: [u][value tile][lane half][column] x 8 fp16
   static constexpr int OFF_Q = ST;
-  static constexpr int OFF_K = OFF_Q + C * QPB;
-  static constexpr int KCOPY = C * KPB;
-  static constexpr int OFF_V = OFF_K + 5 * KCOPY;
-  static constexpr int OFF_M = OFF_V + C * VPB;  // hi, lo
+  static constexpr int OFF_KR = OFF_Q + C * QPB;     // k_hat rows (intra-chunk scores)
+  static constexpr int OFF_KT = OFF_KR + C * KPB;    // k_hat^T (own operands, Gram)
+  static constexpr int OFF_KT2 = OFF_KT + 32 * RPB;  // 2 k_hat^T (partner operands)
+  static constexpr int OFF_VT = OFF_KT2 + 32 * RPB;  // sigma V^T
+  static constexpr int OFF_M = OFF_VT + DV * RPB;    // Gram hi, lo
   static constexpr int OFF_PART = OFF_M + 2 * 32 * MPB;
   static constexpr int PART = FS > 1 ? NG * (FS - 1) * NDT * 64 * 64 : 0;
-  static constexpr int OFF_RED = OFF_PART + PART;  // 8 reduction slots (uint32)
+  static constexpr int OFF_RED = OFF_PART + PART;  // [8 prefix maxima][8 value maxima] (uint32)
   static constexpr int LDS = OFF_RED + 64;
   // first-chunk split operands alias the state area (there is no readout at chunk 0)
   static constexpr int OFF_QLO = 0;
   static constexpr int OFF_KLO = C * QPB;
   static_assert(OFF_KLO + C * KPB <= ST, "split operands fit the state area");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  // summary pass: key copies and values, double-buffered
-  static constexpr int SUM_BUF = 5 * KCOPY + C * VPB;
+  static_assert(C <= 128, "four 64-byte blocks per transposed row");
+  static_assert(OFF_KT % 256 == 0 && OFF_KT2 % 256 == 0 && OFF_VT % 256 == 0, "step reads XOR the address");
+    // summary pass: [k_hat^T | 2 k_hat^T | sigma V^T], double-buffered; value maxima
+  // [2 parities][4 staging waves]
+  static constexpr int SUM_BUF = (64 + DV) * RPB;
   static constexpr int SUM_RED = 2 * SUM_BUF;
-  static constexpr int SUM_LDS = SUM_RED + 64;
+  static constexpr int SUM_LDS = SUM_RED + 128;
   static_assert(SUM_LDS <= 160 * 1024, "LDS budget (summaries)");
-  // workspace summary: state tiles in accumulator layout, then the Gram tile
-  static constexpr int64_t STATE_FLOATS = (int64_t)NTL * NDT * 1024 + 1024;
+  // workspace summary: build tiles in accumulator layout, then the four Gram blocks
+  static constexpr int64_t STATE_FLOATS = (int64_t)NU * NDV * 256 + 1024;
   // readout tile range of split f (the last split also runs the intra block and the
   // denominator, so it takes fewer tiles)
   static constexpr int rb(int f) {
     return FS == 1 ? (f == 0 ? 0 : NTL) : (FS == 2 ? (f == 0 ? 0 : (f == 1 ? 10 : NTL)) : (f <= 2 ? 5 * f : (f == 3 ? 14 : NTL)));
   }
+  // Byte offset of (row, token position) in a transposed buffer (rows of 256 bytes, buffers
+  // 256-byte aligned). Tokens sit at position pi(t) (bits 2 and 3 of t swapped), so that the
+  // intra-chunk product finds its k-slots, keys 16s + 4h + j and 16s + 8 + 4h + j, at 8
+  // consecutive positions. The 64-byte block of positions 32b .. 32b + 31 is stored at block
+  // b ^ (row / 4) % 4 of the row and its 16-byte piece g at piece g ^ row % 4: a 16-byte
+  // MFMA operand read serves 16 lanes per cycle, lanes {0-3, 12-15, 20-27} together and
+  // {4-11, 16-19, 28-31} together (and both + 32), and with this placement every such lane
+  // set meets 16 distinct piece slots of the 256-byte bank window, for own, partner and value
+  // rows alike, while the staging writes of one row stay contiguous. Step b of a read adds
+  // nothing but XOR 64 b to the address of step 0.
+  __device__ static __forceinline__ int tpos(int row, int pos) {
+    return row * RPB + 64 * (((pos >> 5) ^ (row >> 2)) & 3) + 16 * (((pos >> 3) & 3) ^ (row & 3)) + 2 * (pos & 7);
+  }
+  __device__ static __forceinline__ int pi(int t) { return (t & ~12) | ((t >> 1) & 4) | ((t << 1) & 8); }
 };
 
-// build tiles of wave j: forward (4 build waves) and summary pass (8 build waves)
-struct Fwd4 {
-  static constexpr int NW = 4;
-  static constexpr int tb(int j) { return j == 0 ? 0 : (j == 1 ? 5 : (j == 2 ? 10 : (j == 3 ? 14 : 18))); }
-  static constexpr bool gram(int j) { return j == 2; }
-};
-struct Sum8 {
-  static constexpr int NW = 8;
-  static constexpr int tb(int j) { return j == 0 ? 0 : (j == 8 ? 18 : (j < 8 ? 1 + 2 * j : 18)); }
-  static constexpr bool gram(int j) { return j == 2; }
+// Build tiles of build wave j: u = first(j) + 2 i, i < count(j), all of one parity (one own
+// operand per step). Forward: 8 build waves, even tiles on waves 0-3 (5, 4, 5, 4), odd tiles
+// on waves 4-7 (4, 5, 4, 5), 9 tiles per SIMD (waves j and j + 4 share a SIMD). The summary
+// pass uses the same map.
+struct Fwd8 {
+  static constexpr int cnt(int j) { return (j < 4 ? (j % 2 == 0) : (j % 2 == 1)) ? 5 : 4; }
+  static constexpr int first(int j) {
+    int idx = 0;
+    for (int w = (j < 4 ? 0 : 4); w < j; ++w) idx += cnt(w);
+    return 2 * idx + (j < 4 ? 0 : 1);
+  }
 };
 
 struct Args {
@@ -210,6 +225,12 @@ struct Args {
   SeqLayout lay;
   int H;
 };
+
+typedef float acc4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ acc4_t mfma16(h8_t a, h8_t b, acc4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ acc4_t zero4a() { return acc4_t{0.f, 0.f, 0.f, 0.f}; }
 
 // ---- value scale sigma = 2^e from the running bound beta (see the header comment)
 __device__ __forceinline__ int scale_exp(float beta, int e_cur) {
@@ -233,13 +254,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 }
 
 // ---- staging of a chunk (global bf16 -> registers -> scaled fp16 LDS layouts)
+// LDS targets of the key/value staging (byte offsets; kr < 0: no row-major key copy)
+struct KVTarget {
+  int kr, kt, kt2, vt, klo;
+};
+
 template <int DV, int C, int NTHR>
-struct KVStage {  // keys (five copies) and values, staged by NTHR threads (tid 0..NTHR-1)
+struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..NTHR-1)
   using L = Lay<DV, C>;
-  static constexpr int KP = (4 * C + NTHR - 1) / NTHR;       // key pieces (8 components) per thread
-  static constexpr int VP = (C * DV / 8 + NTHR - 1) / NTHR;  // value pieces (8 columns) per thread
-  u32x4_t kr[KP];
-  u32x4_t vr[VP];
+  // key item = (token pair p, component quarter cq): the 8 items of a pair are adjacent lanes
+  static constexpr int KI = 4 * C;
+  static constexpr int KP = (KI + NTHR - 1) / NTHR;
+  // value item = (8-column group dg, token pair p), pairs fastest (row writes of whole lanes)
+  static constexpr int VI = (C / 2) * (DV / 8);
+  static constexpr int VP = (VI + NTHR - 1) / NTHR;
+  u32x2_t kr[KP][2];
+  u32x4_t vr[VP][2];
   const uint16_t *kb, *vb;
   int len;
   uint32_t rsp, rsv;
@@ -259,15 +289,22 @@ struct KVStage {  // keys (five copies) and values, staged by NTHR threads (tid 
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + NTHR * i;
-      if (pc < 4 * C)
-        kr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ((pc >> 2) * rsp + 8 * (pc & 3)) * 2, 0, 0));
+      if (pc < KI) {
+        const int p = pc >> 3, cq = pc & 7;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          kr[i][u] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, ((2 * p + u) * rsp + 4 * cq) * 2, 0, 0));
+      }
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int pc = tid + NTHR * i;
-      constexpr int VPR = DV / 8;
-      if (pc < C * VPR)
-        vr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ((pc / VPR) * rsv + 8 * (pc % VPR)) * 2, 0, 0));
+      if (pc < VI) {
+        const int dg = pc / (C / 2), p = pc % (C / 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          vr[i][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * p + u) * rsv + 8 * dg) * 2, 0, 0));
+      }
     }
   }
   // max |v| of the loaded values as bf16 magnitude bits (ordered like the values)
@@ -276,70 +313,79 @@ struct KVStage {  // keys (five copies) and values, staged by NTHR threads (tid 
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int pc = tid + NTHR * i;
-      if (pc < C * (DV / 8)) {
+      if (pc < VI) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = vr[i][e] & 0x7fff7fffu;
-          const uint32_t lo = x & 0xffffu, hi = x >> 16;
-          m = m > lo ? m : lo;
-          m = m > hi ? m : hi;
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = vr[i][u][e] & 0x7fff7fffu;
+            const uint32_t lo = x & 0xffffu, hi = x >> 16;
+            m = m > lo ? m : lo;
+            m = m > hi ? m : hi;
+          }
       }
     }
     return m;
   }
-  // LDS writes: own copy (unscaled k_hat), four doubled XOR copies, sigma v; the optional
-  // lo part of the own copy (first chunk of a sequence)
+  // LDS writes: k_hat rows (if tg.kr >= 0) and their lo parts (LO), k_hat^T, 2 k_hat^T,
+  // sigma V^T
   template <bool LO>
-  __device__ __forceinline__ void store(char* lds, int off_k, int off_v, float sig, int tid, int off_klo) const {
+  __device__ __forceinline__ void store(char* lds, const KVTarget& tg, float sig, int tid) const {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + NTHR * i;
-      if (pc >= 4 * C) continue;
-      const int row = pc >> 2, e4 = pc & 3;
-      float x[8];
-      float ss = 0.f;
+      if (pc >= KI) continue;
+      const int p = pc >> 3, cq = pc & 7;
+      float x[2][4], inv[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(kr[i][e] << 16);
-        x[2 * e + 1] = __uint_as_float(kr[i][e] & 0xffff0000u);
-        ss += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
+      for (int u = 0; u < 2; ++u) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          x[u][2 * e] = __uint_as_float(kr[i][u][e] << 16);
+          x[u][2 * e + 1] = __uint_as_float(kr[i][u][e] & 0xffff0000u);
+          ss += x[u][2 * e] * x[u][2 * e] + x[u][2 * e + 1] * x[u][2 * e + 1];
+        }
+        inv[u] = inv_norm_fast(group_sum<8>(ss));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[u][e] *= inv[u];
       }
-      ss = group_sum<4>(ss);
-      const float inv = inv_norm_fast(ss);
-      h2_t own[4], dbl[4], sw[4];
+      if (tg.kr >= 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        own[e] = cvt2(x[2 * e] * inv, x[2 * e + 1] * inv);
-        dbl[e] = own[e] * h2_t{(_Float16)2.f, (_Float16)2.f};
-        sw[e] = swp(dbl[e]);
+        for (int u = 0; u < 2; ++u) {
+          const h2_t a = cvt2(x[u][0], x[u][1]), b = cvt2(x[u][2], x[u][3]);
+          st4(lds + tg.kr + (2 * p + u) * L::KPB + 8 * cq, cat2(a, b));
+          if constexpr (LO)
+            st4(lds + tg.klo + (2 * p + u) * L::KPB + 8 * cq,
+                cat2(cvt2(x[u][0] - (float)a[0], x[u][1] - (float)a[1]), cvt2(x[u][2] - (float)b[0], x[u][3] - (float)b[1])));
+        }
       }
-      char* base = lds + off_k + row * L::KPB + 16 * e4;
-      st8(base, cat4(own[0], own[1], own[2], own[3]));
-      // XOR r inside each 4-component block (two registers): r=1 swaps halves, r=2 swaps
-      // registers, r=3 both
-      st8(base + 1 * L::KCOPY, cat4(dbl[0], dbl[1], dbl[2], dbl[3]));
-      st8(base + 2 * L::KCOPY, cat4(sw[0], sw[1], sw[2], sw[3]));
-      st8(base + 3 * L::KCOPY, cat4(dbl[1], dbl[0], dbl[3], dbl[2]));
-      st8(base + 4 * L::KCOPY, cat4(sw[1], sw[0], sw[3], sw[2]));
-      if constexpr (LO) {
-        h2_t lo[4];
+      const int pos = L::pi(2 * p);  // tokens 2p, 2p + 1 share a 4-byte word
+      // lanes cq >= 4 write their components in the order 2, 3, 0, 1: rows 4 cq + c and
+      // 4 (cq + 4) + c share bank slots
+      const bool sw = cq >= 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          lo[e] = cvt2(x[2 * e] * inv - (float)own[e][0], x[2 * e + 1] * inv - (float)own[e][1]);
-        st8(lds + off_klo + row * L::KPB + 16 * e4, cat4(lo[0], lo[1], lo[2], lo[3]));
+      for (int i = 0; i < 4; ++i) {
+        const int c = i ^ (sw ? 2 : 0);
+        const h2_t y = sw ? cvt2(x[0][i ^ 2], x[1][i ^ 2]) : cvt2(x[0][i], x[1][i]);
+        const int off = L::tpos(4 * cq + c, pos);
+        *reinterpret_cast<h2_t*>(lds + tg.kt + off) = y;
+        *reinterpret_cast<h2_t*>(lds + tg.kt2 + off) = y * h2_t{(_Float16)2.f, (_Float16)2.f};
       }
     }
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int pc = tid + NTHR * i;
-      constexpr int VPR = DV / 8;
-      if (pc >= C * VPR) continue;
-      h2_t y[4];
+      if (pc >= VI) continue;
+      const int dg = pc / (C / 2), p = pc % (C / 2);
+      const int pos = L::pi(2 * p);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        y[e] = cvt2(__uint_as_float(vr[i][e] << 16) * sig, __uint_as_float(vr[i][e] & 0xffff0000u) * sig);
-      st8(lds + off_v + (pc / VPR) * L::VPB + 16 * (pc % VPR), cat4(y[0], y[1], y[2], y[3]));
+      for (int e = 0; e < 4; ++e) {
+        const h2_t ya = cvt2(__uint_as_float(vr[i][0][e] << 16) * sig, __uint_as_float(vr[i][1][e] << 16) * sig);
+        const h2_t yb = cvt2(__uint_as_float(vr[i][0][e] & 0xffff0000u) * sig, __uint_as_float(vr[i][1][e] & 0xffff0000u) * sig);
+        *reinterpret_cast<h2_t*>(lds + tg.vt + L::tpos(8 * dg + 2 * e, pos)) = ya;
+        *reinterpret_cast<h2_t*>(lds + tg.vt + L::tpos(8 * dg + 2 * e + 1, pos)) = yb;
+      }
     }
   }
 };
@@ -405,125 +451,146 @@ struct QStage {
   }
 };
 
-// ---- build: S[tile][dt] += psi(K_tile)^T (sigma V) over one chunk; Gram M += K^T K
-template <int DV, int C, int NTW, int TB, bool GRAM>
-__device__ __forceinline__ void build_chunk(acc_t (&S)[NTW > 0 ? NTW : 1][DV / 32], acc_t& Mt, const char* lds,
-                                            int off_k, int off_v) {
+// ---- build (16x16x32 MFMA, 32-token steps): S[u][dv] += psi(K_u)^T (sigma V) for the
+// wave's tiles u = UB, UB + 2, .. (quads 4 HALF .. 4 HALF + 3). A operand lane = (tile row m,
+// 8 token positions of group g): own component 16 HALF + m from k_hat^T times the row's
+// partner component from 2 k_hat^T (k_hat^T for tile 0), one 16-byte read each; B operand
+// lane = (value column, the same 8 positions) from sigma V^T. Accumulator lane (column n,
+// group g) holds quad g of the tile.
+template <int DV, int C, int NU_W, int UB>
+__device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const char* lds, int off_kt, int off_kt2,
+                                            int off_vt) {
   using L = Lay<DV, C>;
-  constexpr int NDT = L::NDT;
-  const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
-  const int qs = 4 * (g & 1) + (i & 3);             // quad of the row this lane addresses
-  const int tok = 8 * (g >> 1) + (i >> 2);          // token this lane addresses (+ 4 for the second read)
-  const uint32_t own = (uint32_t)(off_k + tok * L::KPB + 8 * qs);
-  const uint32_t vl = (uint32_t)(off_v + tok * L::VPB + 2 * (16 * (g & 1) + 4 * (i & 3)));
-  uint32_t part[NTW > 0 ? NTW : 1];
-  [&]<int... TI>(std::integer_sequence<int, TI...>) {
-    ((part[TI] = (uint32_t)(off_k + tile_copy(TB + TI, qs) * L::KCOPY + tok * L::KPB + 8 * tile_partner(TB + TI, qs))), ...);
-  }(std::make_integer_sequence<int, NTW>{});
+  constexpr int NDV = L::NDV, HALF = UB % 2;
+  const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+  const uint32_t own = (uint32_t)(off_kt + L::tpos(16 * HALF + m, 8 * g));
+  uint32_t vl[NDV];
 #pragma unroll
-  for (int st = 0; st < L::NSTEP; ++st) {
-    const uint32_t k0 = 16 * st * L::KPB, k1 = k0 + 4 * L::KPB;
-    const h8_t ko = tr16x2(lds, own + k0, own + k1);
-    h8_t vf[NDT];
+  for (int dv = 0; dv < NDV; ++dv) vl[dv] = (uint32_t)(off_vt + L::tpos(16 * dv + m, 8 * g));
+  uint32_t part[NU_W];
+  [&]<int... UI>(std::integer_sequence<int, UI...>) {
+    ((part[UI] = (uint32_t)((UB + 2 * UI) / 2 == 0 ? off_kt + L::tpos(16 * HALF + m, 8 * g)
+                                                   : off_kt2 + L::tpos(4 * tile_partner((UB + 2 * UI) / 2, 4 * HALF + (m >> 2)) +
+                                                                           ((m & 3) ^ tile_xor((UB + 2 * UI) / 2, 4 * HALF + (m >> 2))),
+                                                                       8 * g))),
+     ...);
+  }(std::make_integer_sequence<int, NU_W>{});
+  // steps stay a loop: unrolled, the scheduler hoists every step's operand reads and the
+  // live ranges exceed the register budget of three waves per SIMD
+#pragma unroll 1
+  for (int st = 0; st < L::NS; ++st) {
+    const uint32_t so = 64 * st;
+    const h8_t ko = ld8(lds + (own ^ so));
+    h8_t vf[NDV];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      vf[dt] = tr16x2(lds, vl + 16 * st * L::VPB + 64 * dt, vl + (16 * st + 4) * L::VPB + 64 * dt);
+    for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8(lds + (vl[dv] ^ so));
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const h8_t kp = tr16x2(lds, part[t] + k0, part[t] + k1);
-      const h8_t psi = ko * kp;
+    for (int u = 0; u < NU_W; ++u) {
+      const h8_t psi = ko * ld8(lds + (part[u] ^ so));
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) S[t][dt] = mfma(psi, vf[dt], S[t][dt]);
+      for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
     }
-    if constexpr (GRAM) Mt = mfma(ko, ko, Mt);
   }
 }
 
-// state fragments of this wave's tiles (sigma S, fp16) for the readout
-template <int DV, int C, int NTW, int TB>
-__device__ __forceinline__ void write_state(const acc_t (&S)[NTW > 0 ? NTW : 1][DV / 32], char* lds) {
+// Gram blocks M_ab = K_a^T K_b (components 16a.., 16b..) of one chunk, a, b in {0, 1}
+template <int DV, int C>
+__device__ __forceinline__ void gram_chunk(acc4_t (&Mg)[4], const char* lds, int off_kt) {
   using L = Lay<DV, C>;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < NTW; ++t)
-#pragma unroll
-    for (int dt = 0; dt < L::NDT; ++dt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        h2_t y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = cvt2(S[t][dt][8 * s + 2 * e], S[t][dt][8 * s + 2 * e + 1]);
-          if (tile_doubled(TB + t)) y[e] = y[e] * h2_t{(_Float16)0.5f, (_Float16)0.5f};
-        }
-        st8(lds + (((TB + t) * 2 + s) * L::NDT + dt) * 1024 + lane * 16, cat4(y[0], y[1], y[2], y[3]));
-      }
+  const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+  const uint32_t o0 = (uint32_t)(off_kt + L::tpos(m, 8 * g)), o1 = (uint32_t)(off_kt + L::tpos(16 + m, 8 * g));
+#pragma unroll 1
+  for (int st = 0; st < L::NS; ++st) {
+    const h8_t olo = ld8(lds + (o0 ^ (64 * st))), ohi = ld8(lds + (o1 ^ (64 * st)));
+    Mg[0] = mfma16(olo, olo, Mg[0]);
+    Mg[1] = mfma16(olo, ohi, Mg[1]);
+    Mg[2] = mfma16(ohi, olo, Mg[2]);
+    Mg[3] = mfma16(ohi, ohi, Mg[3]);
+  }
 }
 
-// Gram matrix to LDS as fp16 hi + lo of M 2^-ge, columns permuted so that the denominator's
-// operand reads its k-slots (components 16s + 8(e/4) + 4h + e%4) as 16 bytes
-template <int DV, int C>
-__device__ __forceinline__ void write_gram(const acc_t& Mt, char* lds, int ge) {
+// state fragments of this wave's tiles (sigma S, fp16) for the readout: build lane (column
+// n, group g) writes 8 bytes at [u][value tile][g % 2][n] + 8 (g / 2), so readout lane
+// (value row, half h) reads quads h and h + 2 of tile u as one 16-byte piece
+template <int DV, int C, int NU_W, int UB>
+__device__ __forceinline__ void write_state(const acc4_t (&S)[NU_W][DV / 16], char* lds) {
   using L = Lay<DV, C>;
-  const int lane = threadIdx.x & 63, n = lane & 31, h = lane >> 5;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int lo = (g & 1) * 256 + n * 16 + (g >> 1) * 8;
+#pragma unroll
+  for (int u = 0; u < NU_W; ++u)
+#pragma unroll
+    for (int dv = 0; dv < L::NDV; ++dv) {
+      h2_t y0 = cvt2(S[u][dv][0], S[u][dv][1]), y1 = cvt2(S[u][dv][2], S[u][dv][3]);
+      if (tile_doubled((UB + 2 * u) / 2)) {
+        y0 = y0 * h2_t{(_Float16)0.5f, (_Float16)0.5f};
+        y1 = y1 * h2_t{(_Float16)0.5f, (_Float16)0.5f};
+      }
+      st4(lds + ((UB + 2 * u) * L::NDV + dv) * 512 + lo, cat2(y0, y1));
+    }
+}
+
+// Gram matrix to LDS as fp16 hi + lo of M 2^-ge. Row r holds the denominator operand's
+// k-slots (components 16s + 8(e/4) + 4h + e%4 at position 16s + 8h + e: bits 2 and 3 of
+// the column swapped); by symmetry block (a, b) writes rows 16b + n, columns 16a + 4g + j.
+template <int DV, int C>
+__device__ __forceinline__ void write_gram(const acc4_t (&Mg)[4], char* lds, int ge) {
+  using L = Lay<DV, C>;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int gs = ((g & 1) << 1) | (g >> 1);
   const float sc = pow2f(-ge);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {  // accumulator rows 8i + 4h + j, i = 2 half, 2 half + 1
-    h2_t hi[4], lo[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = Mt[8 * half + 2 * e] * sc, b = Mt[8 * half + 2 * e + 1] * sc;
-      hi[e] = cvt2(a, b);
-      lo[e] = cvt2(a - (float)hi[e][0], b - (float)hi[e][1]);
-    }
-    char* row = lds + L::OFF_M + n * L::MPB + 2 * (16 * half + 8 * h);
-    st8(row, cat4(hi[0], hi[1], hi[2], hi[3]));
-    st8(row + 32 * L::MPB, cat4(lo[0], lo[1], lo[2], lo[3]));
+  for (int ab = 0; ab < 4; ++ab) {
+    const int a = ab >> 1, b = ab & 1;
+    const float x0 = Mg[ab][0] * sc, x1 = Mg[ab][1] * sc, x2 = Mg[ab][2] * sc, x3 = Mg[ab][3] * sc;
+    const h2_t h0 = cvt2(x0, x1), h1 = cvt2(x2, x3);
+    const h2_t l0 = cvt2(x0 - (float)h0[0], x1 - (float)h0[1]), l1 = cvt2(x2 - (float)h1[0], x3 - (float)h1[1]);
+    char* row = lds + L::OFF_M + (16 * b + n) * L::MPB + 2 * (16 * a + 4 * gs);
+    st4(row, cat2(h0, h1));
+    st4(row + 32 * L::MPB, cat2(l0, l1));
   }
 }
 
 // final state in the decode layout: S[f][d] = sum_s psi_f(k_hat_s) v_s[d] (packed order,
-// sqrt(2) off the diagonal), Z[f] = sum_s psi_f(k_hat_s), from registers holding sigma S
-template <int DV, int NTW, int TB, bool GRAM>
-__device__ __forceinline__ void write_final_state(const Args& a, int64_t bh, const acc_t (&S)[NTW > 0 ? NTW : 1][DV / 32],
-                                                  const acc_t& Mt, float inv_sig) {
+// sqrt(2) off the diagonal) from registers holding sigma S; Z[f] = sum_s psi_f(k_hat_s) from
+// the Gram blocks
+template <int DV, int NU_W, int UB>
+__device__ __forceinline__ void write_final_s(const Args& a, int64_t bh, const acc4_t (&S)[NU_W][DV / 16], float inv_sig) {
   constexpr int n = P * (P + 1) / 2;
-  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   float* so = a.s_out + bh * (int64_t)n * DV;
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
+  for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int j = 0; j < 4; ++j) {
+      const int tt = (UB + 2 * u) / 2, qa = 4 * (UB % 2) + g, c = j;
+      const int r = tile_xor(tt, qa);
+      const int fa = 4 * qa + c, fb = 4 * tile_partner(tt, qa) + (c ^ r);
+      if (tile_doubled(tt) && c > (c ^ r)) continue;  // the other copy of this pair
+      const int i0 = fa < fb ? fa : fb, j0 = fa < fb ? fb : fa;
+      const int f = i0 * P - i0 * (i0 - 1) / 2 + (j0 - i0);
+      const float sc = (tt == 0 ? 1.f : 0.70710678118654752f) * inv_sig;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = 8 * ii + 4 * h + j, qa = m >> 2, c = m & 3;
-        const int tt = TB + t;
-        const int r = tile_xor(tt, qa);
-        const int fa = 4 * qa + c, fb = 4 * tile_partner(tt, qa) + (c ^ r);
-        if (tile_doubled(tt) && c > (c ^ r)) continue;  // the other copy of this pair
-        const int i0 = fa < fb ? fa : fb, j0 = fa < fb ? fb : fa;
-        const int f = i0 * P - i0 * (i0 - 1) / 2 + (j0 - i0);
-        const float sc = (tt == 0 ? 1.f : 0.70710678118654752f) * inv_sig;
+      for (int dv = 0; dv < DV / 16; ++dv) so[(int64_t)f * DV + 16 * dv + col] = S[u][dv][j] * sc;
+    }
+}
+__device__ __forceinline__ void write_final_z(const Args& a, int64_t bh, const acc4_t (&Mg)[4]) {
+  constexpr int n = P * (P + 1) / 2;
+  const int lane = threadIdx.x & 63, col16 = lane & 15, g = lane >> 4;
+  float* zo = a.z_out + bh * (int64_t)n;
 #pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt) so[(int64_t)f * DV + 32 * dt + col] = S[t][dt][4 * ii + j] * sc;
-      }
-  }
-  if constexpr (GRAM) {
-    float* zo = a.z_out + bh * (int64_t)n;
+  for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 8 * ii + 4 * h + j;
-        if (row > col) continue;
-        const int f = row * P - row * (row - 1) / 2 + (col - row);
-        zo[f] = Mt[4 * ii + j] * (row == col ? 1.f : 1.41421356237309515f);
-      }
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * (ab >> 1) + 4 * g + j, col = 16 * (ab & 1) + col16;
+      if (row > col) continue;
+      const int f = row * P - row * (row - 1) / 2 + (col - row);
+      zo[f] = Mg[ab][j] * (row == col ? 1.f : 1.41421356237309515f);
+    }
 }
 
 // ---- readout wave: token group G, tiles [TB, TE); OWNER also runs the intra block, the
-// denominator and the output
+// denominator and the output; wave 0 also accumulates the Gram blocks of the denominator
 template <int DV, int C, int W>
 struct Reader {
   using L = Lay<DV, C>;
@@ -531,6 +598,7 @@ struct Reader {
   static constexpr int G = W / L::FS, F = W % L::FS;
   static constexpr int TB = L::rb(F), TE = L::rb(F + 1);
   static constexpr bool OWNER = F == L::FS - 1;
+  static constexpr bool GRAM = W == 0;
 
   // psi'(q) slots of quad a (lower-half view) for tile T: (c0, c1) and (c2, c3)
   template <int T, int A>
@@ -553,8 +621,22 @@ struct Reader {
     const int osz = a.o_f32 ? 4 : 2;
     char* obase = static_cast<char*>(a.o) + row0 * DV * osz;
     const uint32_t orsv = (uint32_t)rstep * DV;
-    uint32_t* red = reinterpret_cast<uint32_t*>(lds + L::OFF_RED);
+    const uint32_t* red = reinterpret_cast<const uint32_t*>(lds + L::OFF_RED);
+    // this lane's state fragment: readout lane (value row t, half h) reads quads h and h + 2
+    // of build tile u, value tile 2 dt + t / 16, as one 16-byte piece
+    const uint32_t fbase = (uint32_t)((t >> 4) * 512 + h * 256 + (t & 15) * 16);
 
+    acc4_t Mg[4] = {zero4a(), zero4a(), zero4a(), zero4a()};
+    if constexpr (GRAM) {
+      if (seg > 0) {
+        const float* p = a.ws + (bh * (a.nseg - 1) + (seg - 1)) * L::STATE_FLOATS + (int64_t)NU * L::NDV * 256 + lane * 4;
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p + ab * 256);
+          Mg[ab] = acc4_t{x[0], x[1], x[2], x[3]};
+        }
+      }
+    }
     QStage<DV, C, 64 * L::FS> qs;
     qs.init(a.q, row0, rstep, Tb);
     const int qtid = F * 64 + lane;
@@ -564,14 +646,20 @@ struct Reader {
     float beta;
     int e_sig;
     {
-      const float pm = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-      const uint32_t vb = max(max(red[4], red[5]), max(red[6], red[7]));
-      beta = pm + (float)C * __uint_as_float(vb << 16);
+      uint32_t pm = 0, vb = 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        pm = max(pm, red[w]);
+        vb = max(vb, red[8 + w]);
+      }
+      beta = __uint_as_float(pm) + (float)C * __uint_as_float(vb << 16);
       e_sig = scale_exp(beta, 100);
     }
     if (c0 < c1) {
       if (c0 == 0) qs.template store<true>(lds, 32 * G, qtid);
       else qs.template store<false>(lds, 32 * G, qtid);
+      if constexpr (GRAM)
+        if (c0 > 0) write_gram<DV, C>(Mg, lds, gram_exp(c0 * C));
     }
     __syncthreads();  // prologue 2: chunk c0 staged, state before it in LDS
 
@@ -593,22 +681,35 @@ struct Reader {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) O[dt] = zero_acc();
       if (c > 0) {
-        [&]<int... TI>(std::integer_sequence<int, TI...>) {
+        constexpr int NP = 2 * (TE - TB);
+        auto frag = [&](int T, int s, int dt) -> h8_t {
+          return ld8(lds + fbase + (uint32_t)(((2 * T + s) * L::NDV + 2 * dt) * 512));
+        };
+        h8_t fr[2][NDT];
+        if constexpr (NP > 0) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) fr[0][dt] = frag(TB, 0, dt);
+        }
+        [&]<int... PI>(std::integer_sequence<int, PI...>) {
           (([&] {
-             constexpr int T = TB + TI / 2, s = TI % 2;
+             constexpr int T = TB + PI / 2, s = PI % 2;
+             if constexpr (PI + 1 < NP) {
+#pragma unroll
+               for (int dt = 0; dt < NDT; ++dt) fr[(PI + 1) & 1][dt] = frag(TB + (PI + 1) / 2, (PI + 1) % 2, dt);
+             }
+             // keep the next fragments' reads ahead of this step's work
+             __builtin_amdgcn_sched_barrier(0);
              h2_t p0, p1, p2, p3;
              quad_slots<T, 4 * s>(R, p0, p1);
              quad_slots<T, 4 * s + 2>(R, p2, p3);
              const h8_t psi = cat4(p0, p1, p2, p3);
 #pragma unroll
-             for (int dt = 0; dt < NDT; ++dt) {
-               const h8_t sf = ld8(lds + ((T * 2 + s) * NDT + dt) * 1024 + lane * 16);
-               O[dt] = mfma(sf, psi, O[dt]);
-             }
+             for (int dt = 0; dt < NDT; ++dt) O[dt] = mfma(fr[PI & 1][dt], psi, O[dt]);
            }()),
            ...);
-        }(std::make_integer_sequence<int, 2 * (TE - TB)>{});
+        }(std::make_integer_sequence<int, NP>{});
       }
+      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, L::OFF_KT);
       float den = 0.f;
       if constexpr (OWNER) {
         // query operand of the component contractions: k-slots 16s + 8(e/4) + 4h + e%4
@@ -636,12 +737,10 @@ struct Reader {
 #pragma unroll
             for (int s = 0; s < 2; ++s) qlo[s] = cat44(ld4(lrow + 8 * (4 * s + h)), ld4(lrow + 8 * (4 * s + 2 + h)));
           }
-          const int lg = lane >> 4, li = lane & 15;
-          const uint32_t vrow = (uint32_t)(L::OFF_V + (4 * (lg >> 1) + (li >> 2)) * L::VPB + 2 * (16 * (lg & 1) + 4 * (li & 3)));
 #pragma unroll
           for (int kg = 0; kg <= G; ++kg) {
             acc_t Sc = zero_acc();
-            const char* krow = lds + L::OFF_K + (32 * kg + t) * L::KPB;
+            const char* krow = lds + L::OFF_KR + (32 * kg + t) * L::KPB;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const h8_t kop = cat44(ld4(krow + 8 * (4 * s + h)), ld4(krow + 8 * (4 * s + 2 + h)));
@@ -674,8 +773,8 @@ struct Reader {
               const h8_t wop = cat4(wv[4 * s], wv[4 * s + 1], wv[4 * s + 2], wv[4 * s + 3]);
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt) {
-                const uint32_t o0 = vrow + (32 * kg + 16 * s) * L::VPB + 64 * dt;
-                const h8_t vfr = tr16x2(lds, o0, o0 + 8 * L::VPB);
+                // keys 16s + 4h + j, 16s + 8 + 4h + j sit at positions 16s + 8h .. + 7
+                const h8_t vfr = ld8(lds + L::OFF_VT + L::tpos(32 * dt + t, 32 * kg + 16 * s + 8 * h));
                 O[dt] = mfma(vfr, wop, O[dt]);
               }
             }
@@ -731,27 +830,32 @@ struct Reader {
       }
       if (c + 1 < c1) {
         // the bound grows by at most C max|v| per chunk (|psi_f| <= 1 with c^2 folded in)
-        const uint32_t vb = max(max(red[4], red[5]), max(red[6], red[7]));
+        uint32_t vb = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + w]);
         beta += (float)C * __uint_as_float(vb << 16);
         e_sig = scale_exp(beta, e_sig);
         qs.template store<false>(lds, 32 * G, qtid);
+        if constexpr (GRAM) write_gram<DV, C>(Mg, lds, gram_exp(t0 + C));
       }
       __syncthreads();
     }
+    if constexpr (GRAM)
+      if (a.z_out != nullptr && seg == a.nblk_per_bh - 1) write_final_z(a, bh, Mg);
   }
 };
 
-// ---- build wave j of the forward (tiles Fwd4::tb(j) .. tb(j+1))
+// ---- build wave j of the forward (tiles Fwd8::ub(j) .. ub(j + 1)), which also stages the
+// keys and values of the next chunk
 template <int DV, int C, int J>
 struct Builder {
   using L = Lay<DV, C>;
-  static constexpr int NDT = L::NDT;
-  static constexpr int TB = Fwd4::tb(J), NTW = Fwd4::tb(J + 1) - Fwd4::tb(J);
-  static constexpr bool GRAM = Fwd4::gram(J);
+  static constexpr int NDV = L::NDV;
+  static constexpr int UB = Fwd8::first(J), NU_W = Fwd8::cnt(J);
 
   __device__ static __forceinline__ void run(const Args& a, char* lds) {
     const int lane = threadIdx.x & 63;
-    const int btid = J * 64 + lane;  // 0..255 over the build waves
+    const int btid = J * 64 + lane;  // 0..511 over the build waves
     const int64_t bh = blockIdx.x / a.nblk_per_bh;
     const int seg = blockIdx.x % a.nblk_per_bh;
     int64_t row0;
@@ -761,41 +865,25 @@ struct Builder {
     const int c0 = seg * a.cps, c1 = min(nchunks, c0 + a.cps);
     uint32_t* red = reinterpret_cast<uint32_t*>(lds + L::OFF_RED);
 
-    acc_t S[NTW > 0 ? NTW : 1][NDT];
-    acc_t Mt = zero_acc();
+    acc4_t S[NU_W][NDV];
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) S[i][dt] = zero_acc();
+      for (int dv = 0; dv < NDV; ++dv) S[u][dv] = zero4a();
     float pmax = 0.f;
     if (seg > 0) {  // exclusive prefix of this segment (true units)
       const float* src = a.ws + (bh * (a.nseg - 1) + (seg - 1)) * L::STATE_FLOATS;
 #pragma unroll
-      for (int i = 0; i < NTW; ++i)
+      for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const float* p = src + ((TB + i) * NDT + dt) * 1024 + lane * 16;
+        for (int dv = 0; dv < NDV; ++dv) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (((UB + 2 * u) * NDV + dv) * 64 + lane) * 4);
+          S[u][dv] = acc4_t{x[0], x[1], x[2], x[3]};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p + 4 * u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              S[i][dt][4 * u + e] = x[e];
-              pmax = fmaxf(pmax, fabsf(x[e]));
-            }
-          }
+          for (int e = 0; e < 4; ++e) pmax = fmaxf(pmax, fabsf(x[e]));
         }
-      if constexpr (GRAM) {
-        const float* p = src + (int64_t)NTL * NDT * 1024 + lane * 16;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p + 4 * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Mt[4 * u + e] = x[e];
-        }
-      }
     }
-    KVStage<DV, C, 256> kv;
+    KVStage<DV, C, 512> kv;
     kv.init(a.k, a.v, row0, rstep, Tb);
     if (c0 < c1) kv.load(c0 * C, btid);
     {
@@ -803,32 +891,35 @@ struct Builder {
       const uint32_t vm = wave_max_u32(c0 < c1 ? kv.vmax_bits(btid) : 0u);
       if (lane == 0) {
         red[J] = pm;
-        red[4 + J] = vm;
+        red[8 + J] = vm;
       }
     }
     __syncthreads();  // prologue 1
     float beta;
     int e_sig;
     {
-      const float pm = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-      const uint32_t vb = max(max(red[4], red[5]), max(red[6], red[7]));
-      beta = pm + (float)C * __uint_as_float(vb << 16);
+      uint32_t pm = 0, vb = 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        pm = max(pm, red[w]);
+        vb = max(vb, red[8 + w]);
+      }
+      beta = __uint_as_float(pm) + (float)C * __uint_as_float(vb << 16);
       e_sig = scale_exp(beta, 100);
     }
     if (seg > 0) {
       const float sg = pow2f(e_sig);
 #pragma unroll
-      for (int i = 0; i < NTW; ++i)
+      for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) S[i][dt] *= sg;
+        for (int dv = 0; dv < NDV; ++dv) S[u][dv] *= sg;
     }
     if (c0 < c1) {
       if (c0 == 0) {
-        kv.template store<true>(lds, L::OFF_K, L::OFF_V, pow2f(e_sig), btid, L::OFF_KLO);
+        kv.template store<true>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, L::OFF_KLO}, pow2f(e_sig), btid);
       } else {
-        kv.template store<false>(lds, L::OFF_K, L::OFF_V, pow2f(e_sig), btid, 0);
-        write_state<DV, C, NTW, TB>(S, lds);
-        if constexpr (GRAM) write_gram<DV, C>(Mt, lds, gram_exp(c0 * C));
+        kv.template store<false>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, 0}, pow2f(e_sig), btid);
+        write_state<DV, C, NU_W, UB>(S, lds);
       }
     }
     __syncthreads();  // prologue 2
@@ -837,45 +928,51 @@ struct Builder {
       const int t0 = c * C;
       if (c + 1 < c1) kv.load(t0 + C, btid);
       // ---- phase 1: build of chunk c
-      build_chunk<DV, C, NTW, TB, GRAM>(S, Mt, lds, L::OFF_K, L::OFF_V);
+      build_chunk<DV, C, NU_W, UB>(S, lds, L::OFF_KT, L::OFF_KT2, L::OFF_VT);
       if (c + 1 < c1) {
         const uint32_t vm = wave_max_u32(kv.vmax_bits(btid));
-        if (lane == 0) red[4 + J] = vm;
+        if (lane == 0) red[8 + J] = vm;
       }
       __syncthreads();
       // ---- phase 2: state after chunk c (scaled for chunk c + 1), staging of chunk c + 1
       if (c + 1 < c1) {
-        const uint32_t vb = max(max(red[4], red[5]), max(red[6], red[7]));
+        uint32_t vb = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + w]);
         beta += (float)C * __uint_as_float(vb << 16);
         const int e_new = scale_exp(beta, e_sig);
         if (e_new != e_sig) {
           const float f = pow2f(e_new - e_sig);
 #pragma unroll
-          for (int i = 0; i < NTW; ++i)
+          for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) S[i][dt] *= f;
+            for (int dv = 0; dv < NDV; ++dv) S[u][dv] *= f;
           e_sig = e_new;
         }
-        kv.template store<false>(lds, L::OFF_K, L::OFF_V, pow2f(e_sig), btid, 0);
-        write_state<DV, C, NTW, TB>(S, lds);
-        if constexpr (GRAM) write_gram<DV, C>(Mt, lds, gram_exp(t0 + C));
+        kv.template store<false>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, 0}, pow2f(e_sig), btid);
+        write_state<DV, C, NU_W, UB>(S, lds);
       }
       __syncthreads();
     }
-    if (a.s_out != nullptr && seg == a.nblk_per_bh - 1)
-      write_final_state<DV, NTW, TB, GRAM>(a, bh, S, Mt, pow2f(-e_sig));
+    if (a.s_out != nullptr && seg == a.nblk_per_bh - 1) write_final_s<DV, NU_W, UB>(a, bh, S, pow2f(-e_sig));
   }
 };
 
-// ---- summary pass: [S | M] of one segment after its chunks (8 build waves, key and value
-// staging double-buffered, one barrier per chunk), written in true units
+// ---- summary pass: [S | M] of one segment after its chunks, written in true units. Waves
+// 0-7 build (tiles of Fwd8, one build pair per SIMD) and wave 0 also forms the Gram matrix;
+// waves 8-11, one per SIMD, load and stage the keys and values of the next chunk into the
+// other half of a double buffer, so their conversion work runs beside the build MFMAs. One
+// barrier per chunk.
 template <int DV, int C, int J>
 __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   using L = Lay<DV, C>;
-  constexpr int NDT = L::NDT;
-  constexpr int TB = Sum8::tb(J), NTW = Sum8::tb(J + 1) - Sum8::tb(J);
-  constexpr bool GRAM = Sum8::gram(J);
-  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  constexpr int NDV = L::NDV;
+  constexpr bool STAGER = J >= 8;
+  constexpr int JB = STAGER ? 0 : J;
+  constexpr int UB = Fwd8::first(JB), NU_W = STAGER ? 1 : Fwd8::cnt(JB);
+  constexpr bool GRAM = J == 0;
+  const int lane = threadIdx.x & 63;
+  const int stid = (J - 8) * 64 + lane;  // 0..255 over the staging waves
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
   int64_t row0;
@@ -883,89 +980,101 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   seq_rows_of(a.lay, bh, a.H, a.T, row0, rstep, Tb);
   const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * a.cps, c1 = min(nchunks, c0 + a.cps);
-  uint32_t* red = reinterpret_cast<uint32_t*>(lds + L::SUM_RED);  // [2 parities][8 waves]
+  uint32_t* red = reinterpret_cast<uint32_t*>(lds + L::SUM_RED);  // [2 parities][4 staging waves]
 
-  acc_t S[NTW > 0 ? NTW : 1][NDT];
-  acc_t Mt = zero_acc();
-#pragma unroll
-  for (int i = 0; i < NTW; ++i)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[i][dt] = zero_acc();
-  KVStage<DV, C, 512> kv;
-  kv.init(a.k, a.v, row0, rstep, Tb);
+  KVStage<DV, C, 256> kv;
   auto publish = [&](int chunk) {  // max |v| of the loaded chunk into slot set chunk & 1
-    const uint32_t vm = wave_max_u32(kv.vmax_bits(tid));
-    if (lane == 0) red[8 * (chunk & 1) + J] = vm;
+    const uint32_t vm = wave_max_u32(kv.vmax_bits(stid));
+    if (lane == 0) red[4 * (chunk & 1) + (J - 8)] = vm;
   };
   auto vmax_of = [&](int chunk) {
-    const uint32_t* r = red + 8 * (chunk & 1);
-    uint32_t m = 0;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) m = max(m, r[w]);
+    const uint32_t* r = red + 4 * (chunk & 1);
+    const uint32_t m = max(max(r[0], r[1]), max(r[2], r[3]));
     return __uint_as_float(m << 16);
   };
+  auto target = [&](int buf) {
+    const int b = buf * L::SUM_BUF;
+    return KVTarget{-1, b, b + 32 * L::RPB, b + 64 * L::RPB, 0};
+  };
+  if constexpr (STAGER) {
+    kv.init(a.k, a.v, row0, rstep, Tb);
+    if (c0 < c1) {
+      kv.load(c0 * C, stid);
+      publish(c0);
+    }
+  }
+  __syncthreads();
   float beta = 0.f;
   int e_sig = 100;
   if (c0 < c1) {
-    kv.load(c0 * C, tid);
-    publish(c0);
-  }
-  __syncthreads();
-  if (c0 < c1) {
     beta = (float)C * vmax_of(c0);
     e_sig = scale_exp(beta, e_sig);
-    kv.template store<false>(lds, 0, 5 * L::KCOPY, pow2f(e_sig), tid, 0);
-    if (c0 + 1 < c1) {
-      kv.load((c0 + 1) * C, tid);
-      publish(c0 + 1);
+    if constexpr (STAGER) {
+      kv.template store<false>(lds, target(0), pow2f(e_sig), stid);
+      if (c0 + 1 < c1) {
+        kv.load((c0 + 1) * C, stid);
+        publish(c0 + 1);
+      }
     }
   }
   __syncthreads();
-  for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    build_chunk<DV, C, NTW, TB, GRAM>(S, Mt, lds, buf * L::SUM_BUF, buf * L::SUM_BUF + 5 * L::KCOPY);
-    if (c + 1 < c1) {
-      beta += (float)C * vmax_of(c + 1);
-      const int e_new = scale_exp(beta, e_sig);
-      if (e_new != e_sig) {
-        const float f = pow2f(e_new - e_sig);
-#pragma unroll
-        for (int i = 0; i < NTW; ++i)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) S[i][dt] *= f;
-        e_sig = e_new;
+  if constexpr (STAGER) {
+    for (int c = c0; c < c1; ++c) {
+      if (c + 1 < c1) {
+        beta += (float)C * vmax_of(c + 1);
+        e_sig = scale_exp(beta, e_sig);
+        kv.template store<false>(lds, target((c - c0 + 1) & 1), pow2f(e_sig), stid);
+        if (c + 2 < c1) {
+          kv.load((c + 2) * C, stid);
+          publish(c + 2);
+        }
       }
-      const int nb = (buf ^ 1) * L::SUM_BUF;
-      kv.template store<false>(lds, nb, nb + 5 * L::KCOPY, pow2f(e_sig), tid, 0);
-      if (c + 2 < c1) {
-        kv.load((c + 2) * C, tid);
-        publish(c + 2);
+      __syncthreads();
+    }
+  } else {
+    acc4_t S[NU_W][NDV];
+#pragma unroll
+    for (int u = 0; u < NU_W; ++u)
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv) S[u][dv] = zero4a();
+    acc4_t Mg[4] = {zero4a(), zero4a(), zero4a(), zero4a()};
+    for (int c = c0; c < c1; ++c) {
+      const KVTarget tg = target((c - c0) & 1);
+      build_chunk<DV, C, NU_W, UB>(S, lds, tg.kt, tg.kt2, tg.vt);
+      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, tg.kt);
+      if (c + 1 < c1) {
+        beta += (float)C * vmax_of(c + 1);
+        const int e_new = scale_exp(beta, e_sig);
+        if (e_new != e_sig) {
+          const float f = pow2f(e_new - e_sig);
+#pragma unroll
+          for (int u = 0; u < NU_W; ++u)
+#pragma unroll
+            for (int dv = 0; dv < NDV; ++dv) S[u][dv] *= f;
+          e_sig = e_new;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  float* dst = a.ws + (bh * (a.nseg - 1) + seg) * L::STATE_FLOATS;
-  const float inv = pow2f(-e_sig);
+    float* dst = a.ws + (bh * (a.nseg - 1) + seg) * L::STATE_FLOATS;
+    const float inv = pow2f(-e_sig);
 #pragma unroll
-  for (int i = 0; i < NTW; ++i)
+    for (int u = 0; u < NU_W; ++u)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      float* p = dst + ((TB + i) * NDT + dt) * 1024 + lane * 16;
+      for (int dv = 0; dv < NDV; ++dv)
+        *reinterpret_cast<f32x4_t*>(dst + (((UB + 2 * u) * NDV + dv) * 64 + lane) * 4) =
+            f32x4_t{S[u][dv][0] * inv, S[u][dv][1] * inv, S[u][dv][2] * inv, S[u][dv][3] * inv};
+    if constexpr (GRAM) {
+      float* p = dst + (int64_t)NU * NDV * 256 + lane * 4;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<f32x4_t*>(p + 4 * u) =
-            f32x4_t{S[i][dt][4 * u] * inv, S[i][dt][4 * u + 1] * inv, S[i][dt][4 * u + 2] * inv, S[i][dt][4 * u + 3] * inv};
+      for (int ab = 0; ab < 4; ++ab)
+        *reinterpret_cast<f32x4_t*>(p + ab * 256) = f32x4_t{Mg[ab][0], Mg[ab][1], Mg[ab][2], Mg[ab][3]};
     }
-  if constexpr (GRAM) {
-    float* p = dst + (int64_t)NTL * NDT * 1024 + lane * 16;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<f32x4_t*>(p + 4 * u) = f32x4_t{Mt[4 * u], Mt[4 * u + 1], Mt[4 * u + 2], Mt[4 * u + 3]};
   }
 }
 
 template <int DV, int C>
-__global__ __launch_bounds__(512, 1) void summary_f16_kernel(Args a) {
+__global__ __launch_bounds__(768, 1) void summary_f16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
     case 0: run_summary<DV, C, 0>(a, lds); break;
@@ -975,12 +1084,16 @@ __global__ __launch_bounds__(512, 1) void summary_f16_kernel(Args a) {
     case 4: run_summary<DV, C, 4>(a, lds); break;
     case 5: run_summary<DV, C, 5>(a, lds); break;
     case 6: run_summary<DV, C, 6>(a, lds); break;
-    default: run_summary<DV, C, 7>(a, lds); break;
+    case 7: run_summary<DV, C, 7>(a, lds); break;
+    case 8: run_summary<DV, C, 8>(a, lds); break;
+    case 9: run_summary<DV, C, 9>(a, lds); break;
+    case 10: run_summary<DV, C, 10>(a, lds); break;
+    default: run_summary<DV, C, 11>(a, lds); break;
   }
 }
 
 template <int DV, int C>
-__global__ __launch_bounds__(512, 1) void chunked_f16_kernel(Args a) {
+__global__ __launch_bounds__(768, 1) void chunked_f16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
     case 0: Reader<DV, C, 0>::run(a, lds); break;
@@ -990,14 +1103,16 @@ __global__ __launch_bounds__(512, 1) void chunked_f16_kernel(Args a) {
     case 4: Builder<DV, C, 0>::run(a, lds); break;
     case 5: Builder<DV, C, 1>::run(a, lds); break;
     case 6: Builder<DV, C, 2>::run(a, lds); break;
-    default: Builder<DV, C, 3>::run(a, lds); break;
+    case 7: Builder<DV, C, 3>::run(a, lds); break;
+    case 8: Builder<DV, C, 4>::run(a, lds); break;
+    case 9: Builder<DV, C, 5>::run(a, lds); break;
+    case 10: Builder<DV, C, 6>::run(a, lds); break;
+    default: Builder<DV, C, 7>::run(a, lds); break;
   }
 }
 
 }  // namespace c16
-}  // namespace kata
 
-namespace kata {
 namespace c16 {
 
 template <int DV, int C>
@@ -1013,7 +1128,7 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void*
     auto ks = summary_f16_kernel<DV, C>;
     if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, L::SUM_LDS)) != hipSuccess)
       return e;
-    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(512), L::SUM_LDS, st>>>(a);
+    ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(768), L::SUM_LDS, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (plan.nseg > 1 && (passes & PASS_SCAN))
@@ -1022,7 +1137,7 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void*
   auto kf = chunked_f16_kernel<DV, C>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;
-  kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(512), L::LDS, st>>>(a);
+  kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(768), L::LDS, st>>>(a);
   return hipGetLastError();
 }
 
