@@ -121,7 +121,8 @@ kata_status_t kata_lift(const void* u, kata_dtype_t u_dt, int64_t rows, int p,
 /*
  * Workspace bytes kata_chunked_fwd needs for these arguments (0 if none). Depends only
  * on its arguments, not on the device. Returns 0 for arguments kata_chunked_fwd would
- * reject.
+ * reject. in_dt is needed because the segment summaries' layout depends on the kernel the
+ * input dtype selects (fp32 VALU, or bf16 MFMA with fp16 or bf16 operands).
  */
 size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C,
                                     kata_scan_t scan, kata_dtype_t in_dt);
@@ -136,7 +137,10 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C,
  *   workspace: device buffer of at least kata_chunked_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry are ignored and on exit unspecified.
  *   It may be NULL when that size is 0.
- *   Supported: p in {16, 32}; dv in {16, 32, 64}; C in {32, 64, 128}.
+ *   Supported: p in {16, 32}; dv in {16, 32, 64}; C in {32, 64, 128}, for both input
+ *   dtypes (fp32 inputs at p = 32, dv = 64, whose state does not fit in LDS at once, run in
+ *   two halves of the value columns; each output column has the same denominator, so the
+ *   split is exact).
  *   o must not overlap q, k, v or the workspace.
  */
 kata_status_t kata_chunked_fwd(const void* q, const void* k, const void* v, kata_dtype_t in_dt,

@@ -176,7 +176,8 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
   if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64}) || !in_set(C, {32, 64, 128})) return 0;
   const kata::SegPlan plan = kata::seg_plan(B, H, T, C, scan);
   if (plan.nseg <= 1) return 0;
-  const int64_t sf = in_dt != KATA_DTYPE_BF16            ? kata::f32_state_floats(p, dv)
+  if (in_dt != KATA_DTYPE_BF16 && kata::f32_chunked_parts(p, dv, C) == 0) return 0;
+  const int64_t sf = in_dt != KATA_DTYPE_BF16            ? kata::f32_chunked_state_floats(p, dv, C)
                      : kata::chunked_f16_supported(p, dv, C) ? kata::f16_state_floats(dv)
                                                              : kata::mfma_state_floats(p, dv);
   return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
@@ -197,7 +198,7 @@ static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_fea
   if (!packed && sigma2_mfma(p, dv, C, in_dt, fam, g)) return true;
   if (fam == KATA_FEAT_FULL) {
     if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64})) return false;
-    return in_dt == KATA_DTYPE_BF16 || kata::f32_chunked_lds_bytes(p, dv, C) <= 160 * 1024;
+    return in_dt == KATA_DTYPE_BF16 || kata::f32_chunked_parts(p, dv, C) > 0;
   }
   return p <= 64 && dv <= 64 && kata::family_chunked_lds_bytes(p, dv, C, (int)fam, g) <= 160 * 1024;
 }

@@ -23,15 +23,32 @@ size_t f32_chunked_lds_bytes(int p, int dv, int C) {
   return 4 * (n * dv + n + 2 * (size_t)C * p + (size_t)C * dv + C + n);
 }
 
+// Value-column parts of the fp32 chunked forward: 1 when the whole state fits in LDS, 2 when
+// only half of the value columns do (each output column is its own ratio with the same
+// denominator, so the columns split exactly), 0 when neither fits.
+int f32_chunked_parts(int p, int dv, int C) {
+  if (f32_chunked_lds_bytes(p, dv, C) <= 160 * 1024) return 1;
+  if (dv % 2 == 0 && f32_chunked_lds_bytes(p, dv / 2, C) <= 160 * 1024) return 2;
+  return 0;
+}
+
+// workspace floats per (sequence-head, segment summary) over all parts
+int64_t f32_chunked_state_floats(int p, int dv, int C) {
+  const int parts = f32_chunked_parts(p, dv, C);
+  return parts > 0 ? parts * f32_state_floats(p, dv / parts) : 0;
+}
+
 // MODE 0: forward of one segment starting from its prefix state (or zero); the last
 //         segment of a sequence also writes the final state to s_out / z_out if given;
 // MODE 1: state summary of one segment (psi(K)^T [V | 1]) written to the workspace.
+// The kernel handles value columns col0 .. col0 + dv - 1 of rows ldv wide (v, o and the
+// final state S); a part of the columns when the whole state does not fit in LDS.
 template <bool OUT_BF16, int MODE>
 __global__ __launch_bounds__(256) void chunked_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     void* __restrict__ o, int T, int p, int dv, int C, int nseg, int cps, int nblk_per_bh,
     float* __restrict__ ws, float* __restrict__ s_out, float* __restrict__ z_out,
-    SeqLayout lay, int H) {
+    SeqLayout lay, int H, int ldv, int col0) {
   extern __shared__ float sm[];
   const int n = p * (p + 1) / 2;
   float* Ss = sm;
@@ -64,7 +81,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
   }
   const float* qb = q + row0 * p;
   const float* kb = k + row0 * p;
-  const float* vb = v + row0 * dv;
+  const float* vb = v + row0 * ldv + col0;
 
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * C;
@@ -88,7 +105,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
     }
     for (int e = tid; e < C * dv; e += 256) {
       const int t = e / dv;
-      vv[e] = t < L ? vb[(int64_t)(t0 + t) * rstep * dv + e % dv] : 0.f;
+      vv[e] = t < L ? vb[(int64_t)(t0 + t) * rstep * ldv + e % dv] : 0.f;
     }
     __syncthreads();
     if (MODE == 0) {
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
           num += a * a * vv[s * dv + dd];
         }
         const float dn = den[t];
-        store_from_f32<OUT_BF16>(o, (row0 + (int64_t)(t0 + t) * rstep) * dv + dd, dn > 0.f ? num / dn : 0.f);
+        store_from_f32<OUT_BF16>(o, (row0 + (int64_t)(t0 + t) * rstep) * ldv + col0 + dd, dn > 0.f ? num / dn : 0.f);
       }
       __syncthreads();
     }
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(256) void chunked_f32_kernel(
   }
   if (MODE == 0 && s_out != nullptr && seg == nblk_per_bh - 1) {  // S then Z: the decode layout
     __syncthreads();
-    for (int e = tid; e < n * dv; e += 256) s_out[bh * n * dv + e] = Ss[e];
+    for (int e = tid; e < n * dv; e += 256) s_out[(bh * n + e / dv) * ldv + col0 + e % dv] = Ss[e];
     for (int f = tid; f < n; f += 256) z_out[bh * n + f] = Zs[f];
   }
 }
@@ -159,26 +176,38 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
                               float* ws, float* s_out, float* z_out, SeqLayout lay, int passes,
                               hipStream_t st) {
   const int BH = B * H;
-  const size_t lds = f32_chunked_lds_bytes(p, dv, C);
+  const int parts = f32_chunked_parts(p, dv, C);
+  if (parts == 0) return hipErrorInvalidValue;
+  const int dvp = dv / parts;
+  const size_t lds = f32_chunked_lds_bytes(p, dvp, C);
+  const int64_t part_ws = plan.nseg > 1 ? (int64_t)BH * (plan.nseg - 1) * f32_state_floats(p, dvp) : 0;
+  hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     auto kfn = chunked_f32_kernel<false, 1>;
-    hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
-        q, k, v, nullptr, T, p, dv, C, plan.nseg, plan.cps, plan.nseg - 1, ws, nullptr, nullptr, lay, H);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+      return e;
+    for (int part = 0; part < parts; ++part) {
+      kfn<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(256), lds, st>>>(
+          q, k, v, nullptr, T, p, dvp, C, plan.nseg, plan.cps, plan.nseg - 1, ws + part * part_ws, nullptr, nullptr,
+          lay, H, dv, part * dvp);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  if (plan.nseg > 1 && (passes & PASS_SCAN)) {
-    hipError_t e = launch_scan(ws, BH, plan.nseg - 1, f32_state_floats(p, dv), st);
-    if (e != hipSuccess) return e;
-  }
+  if (plan.nseg > 1 && (passes & PASS_SCAN))
+    for (int part = 0; part < parts; ++part)
+      if ((e = launch_scan(ws + part * part_ws, BH, plan.nseg - 1, f32_state_floats(p, dvp), st)) != hipSuccess)
+        return e;
   if (!(passes & PASS_SEGMENTS)) return hipSuccess;
   auto kfn = o_bf16 ? chunked_f32_kernel<true, 0> : chunked_f32_kernel<false, 0>;
-  hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  kfn<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dv, C, plan.nseg,
-                                                              plan.cps, plan.nseg, ws, s_out, z_out, lay, H);
-  return hipGetLastError();
+  if ((e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+    return e;
+  for (int part = 0; part < parts; ++part) {
+    kfn<<<dim3((unsigned)(BH * plan.nseg)), dim3(256), lds, st>>>(q, k, v, o, T, p, dvp, C, plan.nseg, plan.cps,
+                                                                plan.nseg, ws + part * part_ws, s_out, z_out, lay,
+                                                                H, dv, part * dvp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------- quadratic

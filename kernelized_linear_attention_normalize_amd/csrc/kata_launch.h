@@ -38,6 +38,10 @@ int64_t mfma_state_floats(int p, int dv);
 int64_t f32_state_floats(int p, int dv);
 // dynamic LDS bytes of the fp32 chunked kernel (0 if it cannot run)
 size_t f32_chunked_lds_bytes(int p, int dv, int C);
+// value-column parts of the fp32 chunked forward (0: unsupported) and its workspace floats per
+// segment summary over all parts
+int f32_chunked_parts(int p, int dv, int C);
+int64_t f32_chunked_state_floats(int p, int dv, int C);
 
 hipError_t launch_lift(const void* u, bool u_bf16, int64_t rows, int p, void* psi, bool psi_bf16,
                        hipStream_t st);

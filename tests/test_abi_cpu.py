@@ -94,8 +94,10 @@ def test_chunked_validation(lib):
     assert _chunked(lib, ws=A + (1 << 36), wsb=need - 1, **kw) == E_WS
     assert _chunked(lib, ws=A + (1 << 36) + 8, wsb=need, **kw) == E_ALIGN
     assert _chunked(lib, ws=A + (1 << 34), wsb=need, **kw) == E_ALIAS    # workspace overlaps o
-    # fp32 path: state must fit in LDS
-    assert _chunked(lib, in_dt=F32, p=32, dv=64, C=128) == E_UNSUP
+    # fp32 inputs are supported on the whole advertised set (p = 32, dv = 64 in two
+    # value-column parts): no shape of it is rejected as unsupported
+    for C in (32, 64, 128):
+        assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, C, ASSOC, F32) > 0
 
 
 def test_chunked_passes_validation(lib):
@@ -315,6 +317,10 @@ def test_workspace_bytes(lib):
     # fp32 layout: n*dv + n floats per summary
     w = lib.kata_chunked_workspace_bytes(1, 1, 256, 16, 16, 32, ASSOC, F32)
     assert w == 7 * (136 * 16 + 136) * 4
+    # fp32 at p = 32, dv = 64, C = 128: the state fits LDS only per half of the value columns,
+    # so each summary is two parts of n*dv/2 + n floats
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 128, ASSOC, F32) == 16 * 15 * 2 * (528 * 32 + 528) * 4
+    assert lib.kata_chunked_workspace_bytes(1, 16, 131072, 32, 64, 32, ASSOC, F32) == 16 * 15 * (528 * 64 + 528) * 4
 
 
 def test_quadratic_and_lift_and_decode_validation(lib):
