@@ -32,13 +32,14 @@
 // itself (XOR r = tile): tile 0 is the diagonal, tiles 1-3 hold each within-block pair
 // twice. Tiles 4-15 pair block a with a + d (d = 1..3, XOR r), tiles 16-17 block a with
 // a + 4. Every unordered pair of different blocks appears exactly once per XOR, so each
-// off-diagonal coordinate appears once, with c^2 = 2 folded into the build (partner copies
-// are staged at 2 k_hat), and the within-block pairs twice at weight 1 (tiles 1-3 are built
-// at 2x and halved when the state is handed to the readout).
+// off-diagonal coordinate appears once, with c^2 = 2 folded into the build (the segment pass
+// doubles the own operand of tiles 1-17; the summary pass doubles its result), and the
+// within-block pairs twice at weight 1 (tiles 1-3 are built at 2x and halved when the state
+// is handed to the readout).
 //   * Build (psi(K)^T V on 16x16x32 MFMA, 16-row tiles u = 2 t + half): lane = (row,
-//     8 tokens). Keys and values are staged transposed (component-major k_hat^T, a x2
-//     partner copy, sigma V^T), so each operand of a 32-token step is one 16-byte LDS read:
-//     own component, partner component, value column. The row and piece placement (the
+//     8 tokens). Keys and values are staged transposed (component-major k_hat^T and
+//     sigma V^T), so each operand of a 32-token step is one 16-byte LDS read: own component,
+//     partner component, value column. The row and piece placement (the
 //     tpos comment) keeps those reads free of bank conflicts for ds_read_b128's lane groups.
 //   * Readout (O^T = S^T psi(Q)^T): lane = (token, lane half). A lane holds its token's 32
 //     components as 16 packed fp16 pairs, rotated by one block in the upper lane half, so
@@ -49,15 +50,17 @@
 //     reads quads h and h + 2 of the tile as one 16-byte piece.
 //   * Denominator psi(q)^T Z = q^T M q (Gram matrix, fp32-accurate as hi + lo); the
 //     intra-chunk block computes (q_hat . k_hat)^2 from the components (weight identity of
-//     the lift display) and sums the same fp16 weights that multiply V.
+//     the lift display); the denominator sums the fp32 weights, whose fp16 copies multiply V
+//     (each within 2^-11 of it).
 //
-// Segment pass waves: 0-3 read out (token group of 32, or a share of the tiles of one), 4-11
-// build (nine 16-row tiles per SIMD, waves w and w + 4 share one) and stage the keys and
-// values. Per chunk: phase 1 = readout of chunk c from the state before it and build of
-// chunk c | barrier | phase 2 = output, staging of chunk c + 1, state after chunk c to LDS |
-// barrier. ASSOCIATIVE runs a summary pass (8 build waves and 4 staging waves over a double
-// buffer, one barrier per chunk), the segment scan and the segments; SEQUENTIAL runs one
-// segment per sequence.
+// Segment pass waves: 0-3 read out (token group of 32, or a share of the tiles of one) and
+// stage the queries, 4-11 build (nine 16-row tiles per SIMD, waves w and w + 4 share one) and
+// stage the keys and values. The chunk operands are double-buffered. Per chunk: phase 1 =
+// staging of chunk c + 1 into the other buffers (its loads were issued during chunk c - 1),
+// readout of chunk c from the state before it, build of chunk c, loads of chunk c + 2 |
+// barrier | phase 2 = output, state after chunk c to LDS | barrier. ASSOCIATIVE runs a
+// summary pass (8 build waves and 4 staging waves over a double buffer, one barrier per
+// chunk), the segment scan and the segments; SEQUENTIAL runs one segment per sequence.
 #pragma once
 #include <utility>
 
@@ -135,6 +138,15 @@ __device__ __forceinline__ h4_t ld4(const char* p) { return *reinterpret_cast<co
 __device__ __forceinline__ h8_t ld8(const char* p) { return *reinterpret_cast<const h8_t*>(p); }
 __device__ __forceinline__ void st4(char* p, h4_t x) { *reinterpret_cast<h4_t*>(p) = x; }
 __device__ __forceinline__ void st8(char* p, h8_t x) { *reinterpret_cast<h8_t*>(p) = x; }
+// LDS byte address of a pointer into the kernel's dynamic LDS, and a 16-byte read at such an
+// address. These kernels declare no static LDS, so the dynamic block starts at address 0 and
+// a base folded into an address keeps bits 0-7 of the offset (step reads XOR bits 6-7).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ h8_t ld8a(uint32_t a) {
+  return *(const __attribute__((address_space(3))) h8_t*)(uintptr_t)a;
+}
 
 // ---- LDS layout and work split
 // 12 waves: 0-3 read out, 4-11 build; wave w runs on SIMD w % 4, so every SIMD hosts one
@@ -153,26 +165,33 @@ struct Lay {
   static constexpr int RPB = 256;              // transposed rows (one component or value column), bytes
   static constexpr int MPB = 80;               // Gram row pitch, bytes
   static constexpr int ST = NU * NDV * 64 * 8;  // state fragments: [u][value tile][lane half][column] x 8 fp16
-  static constexpr int OFF_Q = ST;
-  static constexpr int OFF_KR = OFF_Q + C * QPB;     // k_hat rows (intra-chunk scores)
-  static constexpr int OFF_KT = OFF_KR + C * KPB;    // k_hat^T (own operands, Gram)
-  static constexpr int OFF_KT2 = OFF_KT + 32 * RPB;  // 2 k_hat^T (partner operands)
-  static constexpr int OFF_VT = OFF_KT2 + 32 * RPB;  // sigma V^T
-  static constexpr int OFF_M = OFF_VT + DV * RPB;    // Gram hi, lo
+  // chunk operands, two buffers each (chunk c + 1 is staged while chunk c is used)
+  static constexpr int QB = C * QPB, KRB = C * KPB, KTB = 32 * RPB, VTB = DV * RPB;
+  static constexpr int OFF_Q = ST;                   // lambda q_hat rows
+  static constexpr int OFF_KR = OFF_Q + 2 * QB;      // k_hat rows (intra-chunk scores)
+  static constexpr int OFF_KT = OFF_KR + 2 * KRB;    // k_hat^T (build operands, Gram)
+  static constexpr int OFF_VT = OFF_KT + 2 * KTB;    // sigma V^T
+  static constexpr int OFF_M = OFF_VT + 2 * VTB;     // Gram hi, lo
   static constexpr int OFF_PART = OFF_M + 2 * 32 * MPB;
   static constexpr int PART = FS > 1 ? NG * (FS - 1) * NDT * 64 * 64 : 0;
-  static constexpr int OFF_RED = OFF_PART + PART;  // [8 prefix maxima][8 value maxima] (uint32)
-  static constexpr int LDS = OFF_RED + 64;
+  // [8 prefix maxima][2 chunk parities][8 value maxima] (uint32)
+  static constexpr int OFF_RED = OFF_PART + PART;
+  static constexpr int LDS = OFF_RED + 128;
+  __device__ static __forceinline__ int offq(int b) { return OFF_Q + b * QB; }
+  __device__ static __forceinline__ int offkr(int b) { return OFF_KR + b * KRB; }
+  __device__ static __forceinline__ int offkt(int b) { return OFF_KT + b * KTB; }
+  __device__ static __forceinline__ int offvt(int b) { return OFF_VT + b * VTB; }
   // first-chunk split operands alias the state area (there is no readout at chunk 0)
   static constexpr int OFF_QLO = 0;
   static constexpr int OFF_KLO = C * QPB;
   static_assert(OFF_KLO + C * KPB <= ST, "split operands fit the state area");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(C <= 128, "four 64-byte blocks per transposed row");
-  static_assert(OFF_KT % 256 == 0 && OFF_KT2 % 256 == 0 && OFF_VT % 256 == 0, "step reads XOR the address");
-    // summary pass: [k_hat^T | 2 k_hat^T | sigma V^T], double-buffered; value maxima
-  // [2 parities][4 staging waves]
-  static constexpr int SUM_BUF = (64 + DV) * RPB;
+  static_assert(OFF_KT % 256 == 0 && KTB % 256 == 0 && OFF_VT % 256 == 0 && VTB % 256 == 0, "step reads XOR the address");
+    // summary pass: [k_hat^T | sigma V^T], double-buffered (partners read k_hat^T and the
+  // factor 2 of tiles 1-17 is applied to the summary); value maxima [2 parities][4 staging
+  // waves]
+  static constexpr int SUM_BUF = (32 + DV) * RPB;
   static constexpr int SUM_RED = 2 * SUM_BUF;
   static constexpr int SUM_LDS = SUM_RED + 128;
   static_assert(SUM_LDS <= 160 * 1024, "LDS budget (summaries)");
@@ -244,17 +263,28 @@ __device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1
 __device__ __forceinline__ int gram_exp(int tokens) { return tokens <= 1 ? 0 : 32 - __builtin_clz((unsigned)tokens - 1u); }
 
 // max over a wave of nonnegative floats (as ordered bit patterns)
+// (DPP inside 16-lane rows, permlane swaps across rows: no LDS round trips, unlike
+// __shfl_xor, whose ds_bpermute waits would sit on the path to the barrier)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)x, d);
-    x = x > y ? x : y;
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = mx(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xf, 0xf, true));   // lane ^ 1
+  x = mx(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, true));   // lane ^ 2
+  x = mx(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, true));  // other quad of 8
+  x = mx(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xf, 0xf, true));  // other half row
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = mx(r[0], r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = mx(r[0], r[1]);
   }
   return x;
 }
 
 // ---- staging of a chunk (global bf16 -> registers -> scaled fp16 LDS layouts)
-// LDS targets of the key/value staging (byte offsets; kr < 0: no row-major key copy)
+// LDS targets of the key/value staging (byte offsets; kr < 0: no row-major key copy, kt2 < 0:
+// no doubled copy)
 struct KVTarget {
   int kr, kt, kt2, vt, klo;
 };
@@ -370,7 +400,7 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
         const h2_t y = sw ? cvt2(x[0][i ^ 2], x[1][i ^ 2]) : cvt2(x[0][i], x[1][i]);
         const int off = L::tpos(4 * cq + c, pos);
         *reinterpret_cast<h2_t*>(lds + tg.kt + off) = y;
-        *reinterpret_cast<h2_t*>(lds + tg.kt2 + off) = y * h2_t{(_Float16)2.f, (_Float16)2.f};
+        if (tg.kt2 >= 0) *reinterpret_cast<h2_t*>(lds + tg.kt2 + off) = y * h2_t{(_Float16)2.f, (_Float16)2.f};
       }
     }
 #pragma unroll
@@ -417,7 +447,7 @@ struct QStage {
     }
   }
   template <bool LO>
-  __device__ __forceinline__ void store(char* lds, int r0, int tid) const {
+  __device__ __forceinline__ void store(char* lds, int off_q, int r0, int tid) const {
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
       const int pc = tid + NTHR * i;
@@ -436,7 +466,7 @@ struct QStage {
       h2_t hv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) hv[e] = cvt2(x[2 * e] * inv, x[2 * e + 1] * inv);
-      char* dst = lds + L::OFF_Q + row * L::QPB + 16 * e4;
+      char* dst = lds + off_q + row * L::QPB + 16 * e4;
       st4(dst, cat2(hv[0], hv[1]));
       st4(dst + 8, cat2(hv[2], hv[3]));
       if constexpr (LO) {
@@ -453,26 +483,29 @@ struct QStage {
 
 // ---- build (16x16x32 MFMA, 32-token steps): S[u][dv] += psi(K_u)^T (sigma V) for the
 // wave's tiles u = UB, UB + 2, .. (quads 4 HALF .. 4 HALF + 3). A operand lane = (tile row m,
-// 8 token positions of group g): own component 16 HALF + m from k_hat^T times the row's
-// partner component from 2 k_hat^T (k_hat^T for tile 0), one 16-byte read each; B operand
-// lane = (value column, the same 8 positions) from sigma V^T. Accumulator lane (column n,
-// group g) holds quad g of the tile.
-template <int DV, int C, int NU_W, int UB>
-__device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const char* lds, int off_kt, int off_kt2,
-                                            int off_vt) {
+// 8 token positions of group g): own component 16 HALF + m times the row's partner component,
+// both from k_hat^T, one 16-byte read each; B operand lane = (value column, the same 8
+// positions) from sigma V^T. Accumulator lane (column n, group g) holds quad g of the tile.
+// DBL: tiles 1-17 take the own operand doubled (one packed add per step, shared by the
+// wave's tiles), which folds c^2 = 2 of the off-diagonal coordinates into the build; without
+// it the caller applies the factor to the result.
+template <int DV, int C, int NU_W, int UB, bool DBL>
+__device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const char* lds, int off_kt, int off_vt) {
   using L = Lay<DV, C>;
   constexpr int NDV = L::NDV, HALF = UB % 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-  const uint32_t own = (uint32_t)(off_kt + L::tpos(16 * HALF + m, 8 * g));
+  const uint32_t base = lds_addr(lds);
+  const uint32_t own = base + (uint32_t)(off_kt + L::tpos(16 * HALF + m, 8 * g));
   uint32_t vl[NDV];
 #pragma unroll
-  for (int dv = 0; dv < NDV; ++dv) vl[dv] = (uint32_t)(off_vt + L::tpos(16 * dv + m, 8 * g));
+  for (int dv = 0; dv < NDV; ++dv) vl[dv] = base + (uint32_t)(off_vt + L::tpos(16 * dv + m, 8 * g));
   uint32_t part[NU_W];
   [&]<int... UI>(std::integer_sequence<int, UI...>) {
-    ((part[UI] = (uint32_t)((UB + 2 * UI) / 2 == 0 ? off_kt + L::tpos(16 * HALF + m, 8 * g)
-                                                   : off_kt2 + L::tpos(4 * tile_partner((UB + 2 * UI) / 2, 4 * HALF + (m >> 2)) +
+    ((part[UI] = base + (uint32_t)(off_kt + ((UB + 2 * UI) / 2 == 0
+                                                 ? L::tpos(16 * HALF + m, 8 * g)
+                                                 : L::tpos(4 * tile_partner((UB + 2 * UI) / 2, 4 * HALF + (m >> 2)) +
                                                                            ((m & 3) ^ tile_xor((UB + 2 * UI) / 2, 4 * HALF + (m >> 2))),
-                                                                       8 * g))),
+                                                                       8 * g)))),
      ...);
   }(std::make_integer_sequence<int, NU_W>{});
   // steps stay a loop: unrolled, the scheduler hoists every step's operand reads and the
@@ -480,13 +513,14 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
 #pragma unroll 1
   for (int st = 0; st < L::NS; ++st) {
     const uint32_t so = 64 * st;
-    const h8_t ko = ld8(lds + (own ^ so));
+    const h8_t ko = ld8a(own ^ so);
+    const h8_t ko2 = DBL ? ko + ko : ko;
     h8_t vf[NDV];
 #pragma unroll
-    for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8(lds + (vl[dv] ^ so));
+    for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
 #pragma unroll
     for (int u = 0; u < NU_W; ++u) {
-      const h8_t psi = ko * ld8(lds + (part[u] ^ so));
+      const h8_t psi = ((UB + 2 * u) / 2 == 0 ? ko : ko2) * ld8a(part[u] ^ so);
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
     }
@@ -498,10 +532,13 @@ template <int DV, int C>
 __device__ __forceinline__ void gram_chunk(acc4_t (&Mg)[4], const char* lds, int off_kt) {
   using L = Lay<DV, C>;
   const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-  const uint32_t o0 = (uint32_t)(off_kt + L::tpos(m, 8 * g)), o1 = (uint32_t)(off_kt + L::tpos(16 + m, 8 * g));
+  const uint32_t base = lds_addr(lds);
+  const uint32_t o0 = base + (uint32_t)(off_kt + L::tpos(m, 8 * g));
+  const uint32_t o1 = base + (uint32_t)(off_kt + L::tpos(16 + m, 8 * g));
 #pragma unroll 1
   for (int st = 0; st < L::NS; ++st) {
-    const h8_t olo = ld8(lds + (o0 ^ (64 * st))), ohi = ld8(lds + (o1 ^ (64 * st)));
+    const uint32_t so = 64 * st;
+    const h8_t olo = ld8a(o0 ^ so), ohi = ld8a(o1 ^ so);
     Mg[0] = mfma16(olo, olo, Mg[0]);
     Mg[1] = mfma16(olo, ohi, Mg[1]);
     Mg[2] = mfma16(ohi, olo, Mg[2]);
@@ -650,26 +687,28 @@ struct Reader {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         pm = max(pm, red[w]);
-        vb = max(vb, red[8 + w]);
+        vb = max(vb, red[8 + 8 * (c0 & 1) + w]);
       }
       beta = __uint_as_float(pm) + (float)C * __uint_as_float(vb << 16);
       e_sig = scale_exp(beta, 100);
     }
     if (c0 < c1) {
-      if (c0 == 0) qs.template store<true>(lds, 32 * G, qtid);
-      else qs.template store<false>(lds, 32 * G, qtid);
+      if (c0 == 0) qs.template store<true>(lds, L::offq(0), 32 * G, qtid);
+      else qs.template store<false>(lds, L::offq(0), 32 * G, qtid);
+      if (c0 + 1 < c1) qs.load((c0 + 1) * C, 32 * G, qtid);
       if constexpr (GRAM)
         if (c0 > 0) write_gram<DV, C>(Mg, lds, gram_exp(c0 * C));
     }
     __syncthreads();  // prologue 2: chunk c0 staged, state before it in LDS
 
     for (int c = c0; c < c1; ++c) {
-      const int t0 = c * C;
-      if (c + 1 < c1) qs.load(t0 + C, 32 * G, qtid);
-      // ---- phase 1: readout of chunk c
+      const int t0 = c * C, buf = (c - c0) & 1;
+      // ---- phase 1: queries of chunk c + 1 into the other buffer (loaded during the previous
+      // chunk), readout of chunk c, loads of chunk c + 2
+      if (c + 1 < c1) qs.template store<false>(lds, L::offq(buf ^ 1), 32 * G, qtid);
       h2_t R[16];
       {
-        const char* qrow = lds + L::OFF_Q + (32 * G + t) * L::QPB;
+        const char* qrow = lds + L::offq(buf) + (32 * G + t) * L::QPB;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           const h4_t x = ld4(qrow + 8 * ((b + h) & 7));
@@ -709,7 +748,7 @@ struct Reader {
            ...);
         }(std::make_integer_sequence<int, NP>{});
       }
-      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, L::OFF_KT);
+      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, L::offkt(buf));
       float den = 0.f;
       if constexpr (OWNER) {
         // query operand of the component contractions: k-slots 16s + 8(e/4) + 4h + e%4
@@ -740,7 +779,7 @@ struct Reader {
 #pragma unroll
           for (int kg = 0; kg <= G; ++kg) {
             acc_t Sc = zero_acc();
-            const char* krow = lds + L::OFF_KR + (32 * kg + t) * L::KPB;
+            const char* krow = lds + L::offkr(buf) + (32 * kg + t) * L::KPB;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const h8_t kop = cat44(ld4(krow + 8 * (4 * s + h)), ld4(krow + 8 * (4 * s + 2 + h)));
@@ -763,10 +802,8 @@ struct Reader {
                   if (8 * ii + 4 * h + j > t) w0 = 0.f;
                   if (8 * ii + 4 * h + j + 1 > t) w1 = 0.f;
                 }
-                const h2_t wp = cvt2(w0, w1);
-                wv[2 * ii + j / 2] = wp;
-                den += (float)wp[0];
-                den += (float)wp[1];
+                wv[2 * ii + j / 2] = cvt2(w0, w1);
+                den += w0 + w1;
               }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -774,7 +811,7 @@ struct Reader {
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt) {
                 // keys 16s + 4h + j, 16s + 8 + 4h + j sit at positions 16s + 8h .. + 7
-                const h8_t vfr = ld8(lds + L::OFF_VT + L::tpos(32 * dt + t, 32 * kg + 16 * s + 8 * h));
+                const h8_t vfr = ld8(lds + L::offvt(buf) + L::tpos(32 * dt + t, 32 * kg + 16 * s + 8 * h));
                 O[dt] = mfma(vfr, wop, O[dt]);
               }
             }
@@ -784,6 +821,7 @@ struct Reader {
         else intra.template operator()<false>();
         den = xor32_sum(den);
       }
+      if (c + 2 < c1) qs.load(t0 + 2 * C, 32 * G, qtid);
       if constexpr (!OWNER) {  // hand the partial readout to the owner of this group
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -832,10 +870,9 @@ struct Reader {
         // the bound grows by at most C max|v| per chunk (|psi_f| <= 1 with c^2 folded in)
         uint32_t vb = 0;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + w]);
+        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + 8 * ((c + 1) & 1) + w]);
         beta += (float)C * __uint_as_float(vb << 16);
         e_sig = scale_exp(beta, e_sig);
-        qs.template store<false>(lds, 32 * G, qtid);
         if constexpr (GRAM) write_gram<DV, C>(Mg, lds, gram_exp(t0 + C));
       }
       __syncthreads();
@@ -886,12 +923,17 @@ struct Builder {
     KVStage<DV, C, 512> kv;
     kv.init(a.k, a.v, row0, rstep, Tb);
     if (c0 < c1) kv.load(c0 * C, btid);
+    auto publish = [&](int chunk) {  // max |v| of the loaded chunk, slot set chunk & 1
+      const uint32_t vm = wave_max_u32(kv.vmax_bits(btid));
+      if (lane == 0) red[8 + 8 * (chunk & 1) + J] = vm;
+    };
+    auto target = [&](int b, int klo) { return KVTarget{L::offkr(b), L::offkt(b), -1, L::offvt(b), klo}; };
     {
       const uint32_t pm = wave_max_u32(__float_as_uint(pmax));
       const uint32_t vm = wave_max_u32(c0 < c1 ? kv.vmax_bits(btid) : 0u);
       if (lane == 0) {
         red[J] = pm;
-        red[8 + J] = vm;
+        red[8 + 8 * (c0 & 1) + J] = vm;
       }
     }
     __syncthreads();  // prologue 1
@@ -902,7 +944,7 @@ struct Builder {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         pm = max(pm, red[w]);
-        vb = max(vb, red[8 + w]);
+        vb = max(vb, red[8 + 8 * (c0 & 1) + w]);
       }
       beta = __uint_as_float(pm) + (float)C * __uint_as_float(vb << 16);
       e_sig = scale_exp(beta, 100);
@@ -916,40 +958,46 @@ struct Builder {
     }
     if (c0 < c1) {
       if (c0 == 0) {
-        kv.template store<true>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, L::OFF_KLO}, pow2f(e_sig), btid);
+        kv.template store<true>(lds, target(0, L::OFF_KLO), pow2f(e_sig), btid);
       } else {
-        kv.template store<false>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, 0}, pow2f(e_sig), btid);
+        kv.template store<false>(lds, target(0, 0), pow2f(e_sig), btid);
         write_state<DV, C, NU_W, UB>(S, lds);
+      }
+      if (c0 + 1 < c1) {
+        kv.load((c0 + 1) * C, btid);
+        publish(c0 + 1);
       }
     }
     __syncthreads();  // prologue 2
 
     for (int c = c0; c < c1; ++c) {
-      const int t0 = c * C;
-      if (c + 1 < c1) kv.load(t0 + C, btid);
-      // ---- phase 1: build of chunk c
-      build_chunk<DV, C, NU_W, UB>(S, lds, L::OFF_KT, L::OFF_KT2, L::OFF_VT);
-      if (c + 1 < c1) {
-        const uint32_t vm = wave_max_u32(kv.vmax_bits(btid));
-        if (lane == 0) red[8 + J] = vm;
-      }
-      __syncthreads();
-      // ---- phase 2: state after chunk c (scaled for chunk c + 1), staging of chunk c + 1
+      const int buf = (c - c0) & 1;
+      // ---- phase 1: keys and values of chunk c + 1 into the other buffers (scaled for chunk
+      // c + 1; loaded during the previous chunk), build of chunk c, loads of chunk c + 2
+      int e_next = e_sig;
       if (c + 1 < c1) {
         uint32_t vb = 0;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + w]);
+        for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + 8 * ((c + 1) & 1) + w]);
         beta += (float)C * __uint_as_float(vb << 16);
-        const int e_new = scale_exp(beta, e_sig);
-        if (e_new != e_sig) {
-          const float f = pow2f(e_new - e_sig);
+        e_next = scale_exp(beta, e_sig);
+        kv.template store<false>(lds, target(buf ^ 1, 0), pow2f(e_next), btid);
+      }
+      build_chunk<DV, C, NU_W, UB, true>(S, lds, L::offkt(buf), L::offvt(buf));
+      if (c + 2 < c1) kv.load((c + 2) * C, btid);
+      __syncthreads();
+      // ---- phase 2: state after chunk c, scaled for chunk c + 1, to LDS; value maximum of
+      // chunk c + 2 (read by every wave after the next barrier)
+      if (c + 2 < c1) publish(c + 2);
+      if (c + 1 < c1) {
+        if (e_next != e_sig) {
+          const float f = pow2f(e_next - e_sig);
 #pragma unroll
           for (int u = 0; u < NU_W; ++u)
 #pragma unroll
             for (int dv = 0; dv < NDV; ++dv) S[u][dv] *= f;
-          e_sig = e_new;
+          e_sig = e_next;
         }
-        kv.template store<false>(lds, KVTarget{L::OFF_KR, L::OFF_KT, L::OFF_KT2, L::OFF_VT, 0}, pow2f(e_sig), btid);
         write_state<DV, C, NU_W, UB>(S, lds);
       }
       __syncthreads();
@@ -994,7 +1042,7 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   };
   auto target = [&](int buf) {
     const int b = buf * L::SUM_BUF;
-    return KVTarget{-1, b, b + 32 * L::RPB, b + 64 * L::RPB, 0};
+    return KVTarget{-1, b, -1, b + 32 * L::RPB, 0};
   };
   if constexpr (STAGER) {
     kv.init(a.k, a.v, row0, rstep, Tb);
@@ -1040,7 +1088,7 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
     acc4_t Mg[4] = {zero4a(), zero4a(), zero4a(), zero4a()};
     for (int c = c0; c < c1; ++c) {
       const KVTarget tg = target((c - c0) & 1);
-      build_chunk<DV, C, NU_W, UB>(S, lds, tg.kt, tg.kt2, tg.vt);
+      build_chunk<DV, C, NU_W, UB, false>(S, lds, tg.kt, tg.vt);
       if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, tg.kt);
       if (c + 1 < c1) {
         beta += (float)C * vmax_of(c + 1);
@@ -1057,13 +1105,17 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
       __syncthreads();
     }
     float* dst = a.ws + (bh * (a.nseg - 1) + seg) * L::STATE_FLOATS;
+    // summaries are in the forward's accumulator units: tiles 1-17 carry the factor 2 that
+    // the forward's doubled partner copy supplies
     const float inv = pow2f(-e_sig);
 #pragma unroll
-    for (int u = 0; u < NU_W; ++u)
+    for (int u = 0; u < NU_W; ++u) {
+      const float f = (UB + 2 * u) / 2 == 0 ? inv : 2.f * inv;
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv)
         *reinterpret_cast<f32x4_t*>(dst + (((UB + 2 * u) * NDV + dv) * 64 + lane) * 4) =
-            f32x4_t{S[u][dv][0] * inv, S[u][dv][1] * inv, S[u][dv][2] * inv, S[u][dv][3] * inv};
+            f32x4_t{S[u][dv][0] * f, S[u][dv][1] * f, S[u][dv][2] * f, S[u][dv][3] * f};
+    }
     if constexpr (GRAM) {
       float* p = dst + (int64_t)NU * NDV * 256 + lane * 4;
 #pragma unroll
