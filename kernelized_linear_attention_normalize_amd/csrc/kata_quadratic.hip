@@ -6,16 +6,18 @@
 // Eq. (8)); the normalized readout with explicit denominator (normalized-readout
 // paragraph); inclusive causality of the state S_t (feature-value state display).
 //
-// Per workgroup: 512 queries of one (b,h), 8 waves x 64 queries; key blocks of 64,
+// Per workgroup: 512 queries of one (b,h), 8 waves x 64 queries; key blocks of 128 (64 for the
+// reduced families),
 // double-buffered in LDS with one barrier per block (the next block's global loads are in
 // flight during the current block's MFMAs).
-//   * Scores from the raw bf16 inputs: a bf16 x bf16 product is exact in fp32, so the MFMA
-//     dot product q . k is exact up to fp32 accumulation; s = (q . k) / ||k|| is formed in
-//     fp32 with a per-key reciprocal norm staged next to the raw K rows. The query's 1/||q||^2
-//     scales the numerator and the denominator of every output row alike, so it is left
-//     out. Hence no normalised or split copies of q or k are needed.
-//   * S^T = K Q^T (16x16x32 bf16 MFMA, keys as M: the accumulator rows are the k-slots of
-//     the next product), W = (S^T / ||k||)^2 masked on the diagonal blocks, rounded to bf16.
+//   * Scores s = q_hat . k_hat on fp16 MFMA operands: every query is normalised once in
+//     registers and every key when its block is staged; unit-norm components lie in [-1, 1],
+//     where fp16 resolves 2^-11 (8x finer than bf16), and the weight is one square s^2 per
+//     pair with no norm left to apply. The backward's statistics variant keeps the raw query
+//     (its D_t is in raw-query units): scores from the raw bf16 inputs (exact products), with
+//     a per-key reciprocal norm staged next to the raw K rows, s = (q . k) / ||k||.
+//   * S^T = K Q^T (16x16x32 MFMA, keys as M: the accumulator rows are the k-slots of the next
+//     product), W = s^2 masked on the diagonal blocks, rounded to bf16.
 //   * O^T += V^T W^T and den += 1^T W^T (operands swapped, so a lane ends with 4 consecutive
 //     output columns of one query, stored with one 8-byte write, and its own denominator).
 // Weights lie in [0, ||q||^2] and the denominator is a plain sum, so unlike softmax there is
@@ -39,13 +41,31 @@ namespace kata {
 #define KATA_QBM 512
 #endif
 namespace quad {
-constexpr int BM = KATA_QBM, BN = 64, QW = KATA_QW, NQT = QW / 16, NKT = BN / 16, NKP = BN / 32;
+constexpr int BM = KATA_QBM, QW = KATA_QW, NQT = QW / 16;
 constexpr int NTHR = 64 * (BM / QW);  // threads per workgroup
-constexpr int VTP = 80;  // bf16 pitch of V^T rows (160 bytes: conflict-free 16-byte reads)
+// keys per block: 128 for the full map (half the barriers and block bookkeeping of 64), 64 for
+// the reduced families, whose block products need more registers
+constexpr int bn(int fam) { return fam == 0 ? 128 : 64; }
 }
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+typedef _Float16 qh8_t __attribute__((ext_vector_type(8)));
+typedef float qf2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 qh2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4_t mfma16(qh8_t a, qh8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 8 bf16 values (16 bytes) times s, as fp16
+__device__ __forceinline__ u32x4_t bf16x8_scaled_f16(const u32x4_t x, float s) {
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const qh2_t h = __builtin_convertvector(qf2_t{bf16_bits_to_f32(x[e] & 0xffffu) * s, __uint_as_float(x[e] & 0xffff0000u) * s}, qh2_t);
+    r[e] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
 }
 
 // FAM: 0 the full map; 1 KATA-Sigma G, 2 KATA-M G (reduced PSD families paragraph) with
@@ -65,7 +85,14 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
                                                                 float* __restrict__ stats,
                                                                 SeqLayout lay = SeqLayout{}, int H = 0) {
   using namespace quad;
+  constexpr int BN = bn(FAM), NKP = BN / 32;
+  // bf16 pitch of V^T rows: BN + 16 (a float pitch of 8 mod 32: the transposed writes and the
+  // 16-byte reads are conflict-free)
+  constexpr int VTP = BN + 16;
+  static_assert((VTP / 2) % 32 == 8, "V^T pitch");
   static_assert(!(PK && STATS), "statistics take the padded layout");
+  constexpr bool NRM = !STATS;  // normalised fp16 scores (else raw bf16 scores with 1/||k||)
+  using qop_t = std::conditional_t<NRM, qh8_t, bf16x8_t>;
   constexpr int KS = (P + 31) / 32;                        // 32-wide k-steps over components
   constexpr int KP = P == 64 ? 80 : (P == 32 ? 48 : 16);   // bf16 pitch of K rows (8 * odd floats)
   constexpr int NT = DV / 16;                              // 16-wide output column tiles
@@ -102,17 +129,35 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + row0 * P, (uint32_t)len * RQ * 2);
   const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + row0 * DV, (uint32_t)len * RV * 2);
 
-  // ---- raw query fragments (B operand of S^T): query qw0 + 16 qt + ln, comps 32 ks + 8 lg..
-  bf16x8_t qf[NQT][KS];
+  // ---- query fragments (B operand of S^T): query qw0 + 16 qt + ln, comps 32 ks + 8 lg..;
+  //      normalised to fp16 (NRM) over the query's four lane groups, else the raw bf16
+  qop_t qf[NQT][KS];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt)
+  for (int qt = 0; qt < NQT; ++qt) {
+    u32x4_t raw[KS];
+    float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
+      raw[ks] = u32x4_t{0u, 0u, 0u, 0u};
       if (P >= 32 || lg < 2)  // rows past T read as zero
-        raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)((qw0 + 16 * qt + ln) * RQ + 32 * ks + 8 * lg) * 2, 0, 0);
-      qf[qt][ks] = __builtin_bit_cast(bf16x8_t, raw);
+        raw[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)((qw0 + 16 * qt + ln) * RQ + 32 * ks + 8 * lg) * 2, 0, 0);
+      if constexpr (NRM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = bf16_bits_to_f32(raw[ks][e] & 0xffffu), hi = __uint_as_float(raw[ks][e] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
     }
+    if constexpr (NRM) {
+      const float inv = inv_norm_fast(xor32_sum(xor16_sum(ss)));  // lanes ln + 16 lg hold the query
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(qh8_t, bf16x8_scaled_f16(raw[ks], inv));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(bf16x8_t, raw[ks]);
+    }
+  }
 
   // ---- key-block staging: raw K rows (16-byte pieces) + 1/||k|| per key; V^T with the
   //      shared permuted / swizzled layout, one (key pair, 8 columns) piece per thread
@@ -139,7 +184,6 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
       const int pc = tid + NTHR * i;
       if (pc < KPIECES) {  // whole waves
         const int row = pc / KPC, col = pc % KPC;
-        *reinterpret_cast<u32x4_t*>(&sK[buf][row * KP + 8 * col]) = kreg[i];
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -147,7 +191,12 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
           ss += lo * lo + hi * hi;
         }
         ss = group_sum<KPC>(ss);  // the row's pieces are adjacent lanes
-        if (col == 0) sInvK[buf][row] = inv_norm_fast(ss);
+        if constexpr (NRM) {  // k_hat in fp16
+          *reinterpret_cast<u32x4_t*>(&sK[buf][row * KP + 8 * col]) = bf16x8_scaled_f16(kreg[i], inv_norm_fast(ss));
+        } else {
+          *reinterpret_cast<u32x4_t*>(&sK[buf][row * KP + 8 * col]) = kreg[i];
+          if (col == 0) sInvK[buf][row] = inv_norm_fast(ss);
+        }
       }
     }
     if (tid < VPIECES) {
@@ -195,9 +244,13 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
               a[h][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][(16 * (2 * kp + h) + ln) * KP + 32 * ks + 8 * lg]);
-          const f32x4_t ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
-          const f32x4_t ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
-          const f32x4_t ik2[2] = {ik0 * ik0, ik1 * ik1};
+          f32x4_t ik2[2] = {f32x4_t{1.f, 1.f, 1.f, 1.f}, f32x4_t{1.f, 1.f, 1.f, 1.f}};
+          if constexpr (!NRM) {
+            const f32x4_t ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
+            const f32x4_t ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
+            ik2[0] = ik0 * ik0;
+            ik2[1] = ik1 * ik1;
+          }
           bf16x8_t vb[NT];
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
@@ -217,12 +270,12 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
                   f32x4_t St = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                   for (int i = 0; i < KM; ++i)
-                    St = mfma16(__builtin_bit_cast(bf16x8_t, a[h][kb * KM + i]), qf[qt][qa * KM + i], St);
+                    St = mfma16(__builtin_bit_cast(qop_t, a[h][kb * KM + i]), qf[qt][qa * KM + i], St);
                   sq += St * St;
                 }
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                w[4 * h + r] = sq[r] * ik2[h][r];
+                w[4 * h + r] = NRM ? sq[r] : sq[r] * ik2[h][r];
                 if (DIAG && kb0 + 32 * kp + 16 * h + 4 * lg + r > query) w[4 * h + r] = 0.f;
               }
             }
@@ -248,11 +301,14 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
             u32x4_t a = {0u, 0u, 0u, 0u};
             if (P >= 32 || lg < 2) a = *reinterpret_cast<const u32x4_t*>(&sK[buf][(16 * kt + ln) * KP + 32 * ks + 8 * lg]);
 #pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) St[h][qt] = mfma16(__builtin_bit_cast(bf16x8_t, a), qf[qt][ks], St[h][qt]);
+            for (int qt = 0; qt < NQT; ++qt) St[h][qt] = mfma16(__builtin_bit_cast(qop_t, a), qf[qt][ks], St[h][qt]);
           }
         }
-        const f32x4_t ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
-        const f32x4_t ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
+        f32x4_t ik0 = f32x4_t{1.f, 1.f, 1.f, 1.f}, ik1 = ik0;
+        if constexpr (!NRM) {
+          ik0 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 4 * lg]);
+          ik1 = *reinterpret_cast<const f32x4_t*>(&sInvK[buf][32 * kp + 16 + 4 * lg]);
+        }
         // V^T operand: keys 32kp + 4lg + j and 32kp + 16 + 4lg + j, one 16-byte read
         bf16x8_t vb[NT];
 #pragma unroll
@@ -265,7 +321,7 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int h = j >> 2, r = j & 3;
-            const float s = St[h][qt][r] * (h ? ik1[r] : ik0[r]);
+            const float s = NRM ? St[h][qt][r] : St[h][qt][r] * (h ? ik1[r] : ik0[r]);
             const float s2 = s * s;
             float ww = s2;
 #pragma unroll
