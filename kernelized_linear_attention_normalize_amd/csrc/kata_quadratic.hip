@@ -98,9 +98,18 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   constexpr int NT = DV / 16;                              // 16-wide output column tiles
   constexpr int KPC = P / 8;                               // 16-byte pieces per key row
   constexpr int KPIECES = BN * KPC;
-  constexpr int KI = (KPIECES + NTHR - 1) / NTHR;
+  // Staging runs on the first half of the waves only. Of the two waves sharing a SIMD, the
+  // older one gets the matrix core first and finishes its block's MFMAs well ahead of the
+  // other (oldest-first arbitration), so it loads and stages the next block while the
+  // younger one is still computing, instead of both staging after their MFMAs. The loads are
+  // issued after the block's MFMAs, so no staging registers are live across them.
+  // (the statistics variant, which needs more registers for its raw-query scores, stages on
+  // every wave)
+  constexpr int SW = STATS ? NTHR : NTHR / 2;  // staging threads
+  constexpr int KI = (KPIECES + SW - 1) / SW;
   constexpr int VPIECES = (BN / 2) * (DV / 8);
-  static_assert(VPIECES <= NTHR && KPIECES % 64 == 0, "staging layout");
+  constexpr int VI = (VPIECES + SW - 1) / SW;
+  static_assert(KPIECES % 64 == 0 && SW % 64 == 0, "staging layout");
   constexpr int KM = KS / G;  // k-steps per feature block
   static_assert(FAM == 0 ? G == 1 : (P % (32 * G) == 0), "feature blocks are whole k-steps");
   __shared__ __align__(16) uint16_t sK[2][BN * KP];
@@ -161,27 +170,37 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
 
   // ---- key-block staging: raw K rows (16-byte pieces) + 1/||k|| per key; V^T with the
   //      shared permuted / swizzled layout, one (key pair, 8 columns) piece per thread
+  const bool stager = tid < SW;  // whole waves
   u32x4_t kreg[KI];
-  u32x4_t vreg[2];
+  u32x4_t vreg[VI][2];
+  // V piece tid + SW i is piece tid shifted by SW / 8 key pairs (vt_piece: 8 pieces per key
+  // pair; the shift keeps the column group), and vt_pos moves whole 32-key blocks, so piece i
+  // writes at the same addresses plus a constant
+  static_assert(VI == 1 || (SW % 256 == 0 && (SW / 4) % 32 == 0), "V piece shift");
   int vp = 0, vd = 0;
-  if (tid < VPIECES) vt_piece<DV>(tid, vp, vd);
+  if (stager) vt_piece<DV>(tid, vp, vd);
   auto prefetch = [&](int kb0) {
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int pc = tid + NTHR * i;
+      const int pc = tid + SW * i;
       if (pc < KPIECES)
         kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((kb0 + pc / KPC) * RQ + 8 * (pc % KPC)) * 2, 0, 0);
     }
-    if (tid < VPIECES) {
-      const uint32_t off = (uint32_t)((kb0 + 2 * vp) * RV + 8 * vd) * 2;
-      vreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-      vreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + RV * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      if (tid + SW * i < VPIECES) {
+        const uint32_t off = (uint32_t)((kb0 + 2 * vp + (SW / 4) * i) * RV + 8 * vd) * 2;
+        vreg[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        vreg[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + RV * 2, 0, 0);
+      }
     }
   };
   auto stage = [&](int buf) {
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int pc = tid + NTHR * i;
+      const int pc = tid + SW * i;
       if (pc < KPIECES) {  // whole waves
         const int row = pc / KPC, col = pc % KPC;
         float ss = 0.f;
@@ -199,13 +218,16 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
         }
       }
     }
-    if (tid < VPIECES) {
-      char* base = reinterpret_cast<char*>(&sVt[buf][0]) + ((8 * vd) * VTP + vt_pos(2 * vp)) * 2;
+    char* vbase = reinterpret_cast<char*>(&sVt[buf][0]) + ((8 * vd) * VTP + vt_pos(2 * vp)) * 2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (vreg[0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t b = (vreg[1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(base + ((e & 4) + ((e & 3) ^ (vd & 3))) * VTP * 2) = a | (b << 16);
+    for (int i = 0; i < VI; ++i) {
+      if (tid + SW * i < VPIECES) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = (vreg[i][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t b = (vreg[i][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          *reinterpret_cast<uint32_t*>(vbase + (((e & 4) + ((e & 3) ^ (vd & 3))) * VTP + (SW / 4) * i) * 2) = a | (b << 16);
+        }
       }
     }
   };
@@ -231,7 +253,6 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     const int kb0 = kb * BN;
-    if (kb + 1 < nkb) prefetch(kb0 + BN);
     // one key block against this wave's queries; DIAG: some (key > query) pairs to mask
     auto block = [&](auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
@@ -340,7 +361,10 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
       if (kb0 + BN - 1 > qw0) block(std::true_type{});
       else block(std::false_type{});
     }
-    if (kb + 1 < nkb) stage(buf ^ 1);  // buffer of block kb - 1: every wave is past it
+    if (kb + 1 < nkb) {  // into the buffer of block kb - 1: every wave is past it
+      prefetch(kb0 + BN);
+      stage(buf ^ 1);
+    }
     __syncthreads();
   }
 
