@@ -1007,20 +1007,21 @@ struct Builder {
 };
 
 // ---- summary pass: [S | M] of one segment after its chunks, written in true units. Waves
-// 0-7 build (tiles of Fwd8, one build pair per SIMD) and wave 0 also forms the Gram matrix;
-// waves 8-11, one per SIMD, load and stage the keys and values of the next chunk into the
-// other half of a double buffer, so their conversion work runs beside the build MFMAs. One
-// barrier per chunk.
+// 0-3, one per SIMD, load and stage the keys and values of the next chunk into the other half
+// of a double buffer, so their conversion work runs beside the build MFMAs; they are the
+// oldest waves of their SIMDs, whose instructions win the issue arbitration, so the staging
+// is not left waiting behind the builds. Waves 4-11 build (tiles of Fwd8, one build pair per
+// SIMD) and wave 4 also forms the Gram matrix. One barrier per chunk.
 template <int DV, int C, int J>
 __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   using L = Lay<DV, C>;
   constexpr int NDV = L::NDV;
-  constexpr bool STAGER = J >= 8;
-  constexpr int JB = STAGER ? 0 : J;
+  constexpr bool STAGER = J < 4;
+  constexpr int JB = STAGER ? 0 : J - 4;
   constexpr int UB = Fwd8::first(JB), NU_W = STAGER ? 1 : Fwd8::cnt(JB);
-  constexpr bool GRAM = J == 0;
+  constexpr bool GRAM = J == 4;
   const int lane = threadIdx.x & 63;
-  const int stid = (J - 8) * 64 + lane;  // 0..255 over the staging waves
+  const int stid = J * 64 + lane;  // 0..255 over the staging waves
   const int64_t bh = blockIdx.x / a.nblk_per_bh;
   const int seg = blockIdx.x % a.nblk_per_bh;
   int64_t row0;
@@ -1033,7 +1034,7 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   KVStage<DV, C, 256> kv;
   auto publish = [&](int chunk) {  // max |v| of the loaded chunk into slot set chunk & 1
     const uint32_t vm = wave_max_u32(kv.vmax_bits(stid));
-    if (lane == 0) red[4 * (chunk & 1) + (J - 8)] = vm;
+    if (lane == 0) red[4 * (chunk & 1) + J] = vm;
   };
   auto vmax_of = [&](int chunk) {
     const uint32_t* r = red + 4 * (chunk & 1);
