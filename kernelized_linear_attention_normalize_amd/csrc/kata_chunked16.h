@@ -513,16 +513,39 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
 #pragma unroll 1
   for (int st = 0; st < L::NS; ++st) {
     const uint32_t so = 64 * st;
-    const h8_t ko = ld8a(own ^ so);
-    const h8_t ko2 = DBL ? ko + ko : ko;
-    h8_t vf[NDV];
+    // Left to itself, the scheduler issues each partner read after the previous tile's
+    // MFMAs and waits for it at once. The summary pass (more registers free) issues all of a
+    // step's reads before its first product; the segment pass keeps one partner read ahead.
+    if constexpr (!DBL) {
+      const h8_t ko = ld8a(own ^ so);
+      h8_t pt[NU_W], vf[NDV];
 #pragma unroll
-    for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
+      for (int u = 0; u < NU_W; ++u) pt[u] = ld8a(part[u] ^ so);
 #pragma unroll
-    for (int u = 0; u < NU_W; ++u) {
-      const h8_t psi = ((UB + 2 * u) / 2 == 0 ? ko : ko2) * ld8a(part[u] ^ so);
+      for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
+      for (int u = 0; u < NU_W; ++u) {
+        const h8_t psi = ko * pt[u];
+#pragma unroll
+        for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
+      }
+    } else {
+      const h8_t ko = ld8a(own ^ so);
+      h8_t vf[NDV];
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
+      h8_t pn = ld8a(part[0] ^ so);
+      __builtin_amdgcn_sched_barrier(0);
+      const h8_t ko2 = ko + ko;
+#pragma unroll
+      for (int u = 0; u < NU_W; ++u) {
+        const h8_t psi = ((UB + 2 * u) / 2 == 0 ? ko : ko2) * pn;
+        if (u + 1 < NU_W) pn = ld8a(part[u + 1] ^ so);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
+      }
     }
   }
 }
