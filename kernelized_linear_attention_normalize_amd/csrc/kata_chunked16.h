@@ -162,6 +162,11 @@ struct Lay {
   static constexpr int NS = C / 32;            // 32-token build steps
   static constexpr int QPB = 72;               // q_hat row pitch, bytes (8-byte block reads conflict-free)
   static constexpr int KPB = 64;               // row-major key rows (unscaled k_hat), bytes
+  // Byte offset of 4-component block b (8 bytes) of key row r. A read of 8 bytes serves 32
+  // lanes per cycle; the intra-chunk product's lanes read rows 32 kg + t (t = lane % 32) at
+  // a common block, and at a 64-byte pitch rows t and t + 4 would share banks. Block b of
+  // row r therefore sits at block b ^ (r / 4) % 8: the 32 lanes cover all 64 banks.
+  __device__ static __forceinline__ int krpos(int r, int b) { return r * KPB + 8 * (b ^ ((r >> 2) & 7)); }
   static constexpr int RPB = 256;              // transposed rows (one component or value column), bytes
   static constexpr int MPB = 80;               // Gram row pitch, bytes
   static constexpr int ST = NU * NDV * 64 * 8;  // state fragments: [u][value tile][lane half][column] x 8 fp16
@@ -384,9 +389,9 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const h2_t a = cvt2(x[u][0], x[u][1]), b = cvt2(x[u][2], x[u][3]);
-          st4(lds + tg.kr + (2 * p + u) * L::KPB + 8 * cq, cat2(a, b));
+          st4(lds + tg.kr + L::krpos(2 * p + u, cq), cat2(a, b));
           if constexpr (LO)
-            st4(lds + tg.klo + (2 * p + u) * L::KPB + 8 * cq,
+            st4(lds + tg.klo + L::krpos(2 * p + u, cq),
                 cat2(cvt2(x[u][0] - (float)a[0], x[u][1] - (float)a[1]), cvt2(x[u][2] - (float)b[0], x[u][3] - (float)b[1])));
         }
       }
@@ -802,14 +807,15 @@ struct Reader {
 #pragma unroll
           for (int kg = 0; kg <= G; ++kg) {
             acc_t Sc = zero_acc();
-            const char* krow = lds + L::offkr(buf) + (32 * kg + t) * L::KPB;
+            const char* krow = lds + L::offkr(buf);
+            const int kr = 32 * kg + t;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-              const h8_t kop = cat44(ld4(krow + 8 * (4 * s + h)), ld4(krow + 8 * (4 * s + 2 + h)));
+              const h8_t kop = cat44(ld4(krow + L::krpos(kr, 4 * s + h)), ld4(krow + L::krpos(kr, 4 * s + 2 + h)));
               Sc = mfma(kop, qop[s], Sc);
               if constexpr (SPLIT) {
-                const char* lrow = lds + L::OFF_KLO + (32 * kg + t) * L::KPB;
-                Sc = mfma(cat44(ld4(lrow + 8 * (4 * s + h)), ld4(lrow + 8 * (4 * s + 2 + h))), qop[s], Sc);
+                const char* lrow = lds + L::OFF_KLO;
+                Sc = mfma(cat44(ld4(lrow + L::krpos(kr, 4 * s + h)), ld4(lrow + L::krpos(kr, 4 * s + 2 + h))), qop[s], Sc);
                 Sc = mfma(kop, qlo[s], Sc);
               }
             }
