@@ -381,6 +381,26 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                  void* workspace, size_t workspace_bytes, kata_stream_t stream);
 
 /*
+ * kata_quadratic_bwd_varlen - kata_quadratic_bwd for the full map over B sequences packed
+ * without padding in the token-major layout of kata_quadratic_fwd_varlen: q, k, dq, dk are
+ * [total, H, p] and v, grad_o, dv_out are [total, H, dv] (token cu_seqlens[b] + t of sequence
+ * b, head h, is row (cu_seqlens[b] + t) * H + h). cu_seqlens: device int32 [B + 1], 4-byte
+ * aligned, read on the device (offsets clamped to [0, total]); max_len bounds every length
+ * (longer sequences are cut). Each sequence's gradients equal kata_quadratic_bwd's on that
+ * sequence alone; rows outside every sequence are not written. bf16 inputs, p and dv in
+ * {32, 64} (the bf16 MFMA kernels; else KATA_ERR_UNSUPPORTED). workspace: at least
+ * kata_quadratic_bwd_varlen_workspace_bytes(B, H, total) bytes (D_t and delta_t per packed
+ * row); 0 means unsupported arguments. Errors as kata_quadratic_bwd; KATA_ERR_NULL for
+ * cu_seqlens NULL when B H > 0; KATA_ERR_SHAPE for negative sizes or
+ * (max_len + 512) * H * max(p, dv) * 4 >= 2^31.
+ */
+size_t kata_quadratic_bwd_varlen_workspace_bytes(int B, int H, int total);
+kata_status_t kata_quadratic_bwd_varlen(const void* q, const void* k, const void* v, const void* grad_o,
+                                        kata_dtype_t in_dt, int B, int H, int total, int max_len, int p, int dv,
+                                        const int32_t* cu_seqlens, float* dq, float* dk, float* dv_out,
+                                        void* workspace, size_t workspace_bytes, kata_stream_t stream);
+
+/*
  * kata_chunked_bwd - the same gradients as kata_quadratic_bwd for the full map, in O(T):
  * the state form of the forward (feature-value state display, normalized readout, chunked
  * forward paragraph of the HTML page) differentiated. A forward-time pass over the chunks

@@ -21,7 +21,8 @@ __all__ = ["KataError", "library_path", "load", "packed_dim", "feature_dim", "li
            "chunked_workspace_bytes", "chunked_workspace_bytes_family", "chunked_fwd", "quadratic_fwd", "decode_step",
            "SCAN_SEQUENTIAL", "SCAN_ASSOCIATIVE", "PASS_SUMMARIES", "PASS_SCAN", "PASS_SEGMENTS",
            "PASS_ALL", "FEATURES", "quadratic_bwd", "kata_attention", "order_dim", "chunked_fwd_varlen",
-           "quadratic_fwd_varlen", "chunked_bwd", "chunked_bwd_varlen", "kata_attention_varlen", "STATE_BWD_MIN_T",
+           "quadratic_fwd_varlen", "chunked_bwd", "chunked_bwd_varlen", "quadratic_bwd_varlen", "kata_attention_varlen",
+           "STATE_BWD_MIN_T",
            "chunked_fwd_noalloc", "NOALLOC_SCRATCH_BYTES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +104,10 @@ def load():
     lib.kata_quadratic_bwd_workspace_bytes.restype = SZ
     lib.kata_quadratic_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]
     lib.kata_quadratic_bwd.restype = I
+    lib.kata_quadratic_bwd_varlen_workspace_bytes.argtypes = [I, I, I]
+    lib.kata_quadratic_bwd_varlen_workspace_bytes.restype = SZ
+    lib.kata_quadratic_bwd_varlen.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, SZ, P]
+    lib.kata_quadratic_bwd_varlen.restype = I
     lib.kata_quadratic_fwd_family.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, I, P]
     lib.kata_quadratic_fwd_family.restype = I
     lib.kata_decode_step_family.argtypes = [P, P, P, I, I, I, P, P, P, I, I, I, I, I, P]
@@ -472,6 +477,36 @@ def quadratic_bwd(q, k, v, grad_o, family: str = "full", g: int = 1):
     return dq, dk, dvv
 
 
+def quadratic_bwd_varlen(q, k, v, grad_o, cu_seqlens, max_len: int):
+    """Flash-style gradients (dq, dk, dv), float32, of the full-map forward over B sequences
+    packed without padding (the layout of quadratic_fwd_varlen): q, k [total, H, p]; v,
+    grad_o [total, H, dv], bf16, p and dv in {32, 64}. Rows outside every sequence come back
+    as zeros."""
+    lib = load()
+    dev = _dev(q, k, v, grad_o)
+    total, H, p = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or grad_o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v and grad_o")
+    if not (q.dtype == k.dtype == v.dtype == grad_o.dtype):
+        raise TypeError("q, k, v and grad_o must share one dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
+    _dev(cu_seqlens, q)
+    B = cu_seqlens.numel() - 1
+    dq = torch.zeros((total, H, p), dtype=torch.float32, device=dev)
+    dk = torch.zeros_like(dq)
+    dvv = torch.zeros((total, H, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kata_quadratic_bwd_varlen_workspace_bytes(B, H, total))
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.kata_quadratic_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), grad_o.data_ptr(), _dt(q), B,
+                                             H, total, max_len, p, dv, cu_seqlens.data_ptr(), dq.data_ptr(),
+                                             dk.data_ptr(), dvv.data_ptr(), ws.data_ptr(), need, _stream(dev)),
+               "kata_quadratic_bwd_varlen")
+    return dq, dk, dvv
+
+
 def chunked_bwd(q, k, v, grad_o, C: int = 32, scan="associative", workspace=None):
     """O(T) gradients (dq, dk, dv) of the causal full-map forward, float32, from the state form:
     bf16 MFMA kernels for bf16 inputs with p in {16, 32} and dv in {32, 64}, fp32 VALU kernels
@@ -571,15 +606,20 @@ class _KataAttentionVarlen(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_o):
         q, k, v, cu = ctx.saved_tensors
-        dq, dk, dvv = chunked_bwd_varlen(q, k, v, grad_o.contiguous().to(q.dtype), cu, ctx.max_len)
+        go = grad_o.contiguous().to(q.dtype)
+        if ctx.max_len < STATE_BWD_MIN_T and q.shape[-1] == 32:  # short sequences: flash style
+            dq, dk, dvv = quadratic_bwd_varlen(q, k, v, go, cu, ctx.max_len)
+        else:
+            dq, dk, dvv = chunked_bwd_varlen(q, k, v, go, cu, ctx.max_len)
         return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
 
 
 def kata_attention_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64):
     """Differentiable causal KATA attention over B sequences packed without padding (the
     layout of chunked_fwd_varlen: q, k [total, H, p]; v [total, H, dv]; cu_seqlens int32
-    [B + 1]): the packed chunked forward and the packed O(T) backward (bf16 inputs, full map,
-    p in {16, 32}, dv in {32, 64}). Rows outside every sequence get zero gradients."""
+    [B + 1]): the packed chunked forward and a packed backward (bf16 inputs, full map, p in
+    {16, 32}, dv in {32, 64}): the O(T) state form, or the flash-style form for p = 32 when
+    max_len < STATE_BWD_MIN_T. Rows outside every sequence get zero gradients."""
     if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
         raise TypeError("kata_attention_varlen takes bf16 q, k, v")
     if q.shape[-1] not in (16, 32) or v.shape[-1] not in (32, 64):

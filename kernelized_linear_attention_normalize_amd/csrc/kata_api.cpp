@@ -566,6 +566,52 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
                                                (hipStream_t)stream));
 }
 
+size_t kata_quadratic_bwd_varlen_workspace_bytes(int B, int H, int total) {
+  if (B <= 0 || H <= 0 || total <= 0) return 0;
+  return (size_t)total * H * 2 * sizeof(float);
+}
+
+kata_status_t kata_quadratic_bwd_varlen(const void* q, const void* k, const void* v, const void* grad_o,
+                                        kata_dtype_t in_dt, int B, int H, int total, int max_len, int p, int dv,
+                                        const int32_t* cu_seqlens, float* dq, float* dk, float* dv_out,
+                                        void* workspace, size_t workspace_bytes, kata_stream_t stream) {
+  if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
+  if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
+  if (in_dt != KATA_DTYPE_BF16 || !kata::quadratic_bwd_mfma_supported(p, dv)) return KATA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
+  if (cu_seqlens == nullptr) return KATA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
+  // one sequence's rows (H apart) are addressed with 32-bit byte offsets, up to a block of
+  // 512 rows past its end
+  const int w = p > dv ? p : dv;
+  if (mul4(total, H, w, 1) < 0 || ((int64_t)max_len + 512) * H * w * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
+  if ((int64_t)B * H * ((max_len + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
+  if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
+  for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
+    if (!aligned16(ptr)) return KATA_ERR_ALIGN;
+  const size_t need = kata_quadratic_bwd_varlen_workspace_bytes(B, H, total);
+  if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KATA_ERR_ALIGN;
+  const size_t rows = (size_t)total * H;
+  const size_t qb = rows * p * 2, vb = rows * dv * 2;
+  const void* outs[4] = {dq, dk, dv_out, workspace};
+  const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], q, qb) || overlap(outs[i], outb[i], k, qb) || overlap(outs[i], outb[i], v, vb) ||
+        overlap(outs[i], outb[i], grad_o, vb))
+      return KATA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return KATA_ERR_ALIAS;
+  }
+  kata::SeqLayout lay;
+  lay.cu = cu_seqlens;
+  lay.total = total;
+  return hip_status(kata::launch_quadratic_bwd_mfma_varlen(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(grad_o), B, H, max_len, p, dv, lay, static_cast<float*>(workspace), dq, dk,
+      dv_out, (hipStream_t)stream));
+}
+
 // fp32 VALU state-form kernels: the chunk's rows and the fp32 state within LDS
 static bool chunked_bwd_valu_supported(int p, int dv, int C) {
   return p >= 1 && p <= 64 && dv >= 1 && dv <= 64 && in_set(C, {16, 32, 64}) &&

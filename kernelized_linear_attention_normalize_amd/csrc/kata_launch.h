@@ -113,6 +113,11 @@ bool quadratic_bwd_mfma_supported(int p, int dv);
 hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,
                                      int B, int H, int T, int p, int dv, float* stats, float* dq, float* dk,
                                      float* dvo, hipStream_t st);
+// the same over packed sequences (lay.cu, lay.total; T = max_len; stats per packed row)
+hipError_t launch_quadratic_bwd_mfma_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                            const uint16_t* gout, int B, int H, int max_len, int p, int dv,
+                                            SeqLayout lay, float* stats, float* dq, float* dk, float* dvo,
+                                            hipStream_t st);
 hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
                                 int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
                                 float* dvo, hipStream_t st);

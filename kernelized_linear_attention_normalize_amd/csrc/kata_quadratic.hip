@@ -75,7 +75,8 @@ __device__ __forceinline__ u32x4_t bf16x8_scaled_f16(const u32x4_t x, float s) {
 // R (full map only): weights (q_hat . k_hat)^(2R), the inner product of the higher even-order
 // lift psi_2R (psi_2r display of the HTML page); R = 1 is the rank-one map.
 // STATS (backward, full map): no output; instead row t's denominator D_t = sum_s w_ts (with
-// the raw query, as everywhere here) and delta_t = gout_t . o_t go to stats[2 t], [2 t + 1].
+// the raw query, as everywhere here) and delta_t = gout_t . o_t go to stats[2 r], [2 r + 1],
+// r the tensor row of query t (bh T + t padded, its packed row under PK).
 template <int P, int DV, bool OUT_BF16, int FAM = 0, int G = 1, int R = 1, bool STATS = false, bool PK = false>
 __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k,
@@ -90,7 +91,6 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
   // 16-byte reads are conflict-free)
   constexpr int VTP = BN + 16;
   static_assert((VTP / 2) % 32 == 8, "V^T pitch");
-  static_assert(!(PK && STATS), "statistics take the padded layout");
   constexpr bool NRM = !STATS;  // normalised fp16 scores (else raw bf16 scores with 1/||k||)
   using qop_t = std::conditional_t<NRM, qh8_t, bf16x8_t>;
   constexpr int KS = (P + 31) / 32;                        // 32-wide k-steps over components
@@ -376,18 +376,19 @@ __global__ __launch_bounds__(quad::NTHR, KATA_QOCC) void quadratic_bf16_kernel(c
       const float den = D[qt][0];
       const float inv = den > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
       float part = 0.f;  // this lane's columns of gout . o
-      if (query < T) {
+      const int64_t row = row0 + (int64_t)query * stp;
+      if (query < len) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gout + (bh * T + query) * (int64_t)DV + 16 * nt + 4 * lg);
+          const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gout + row * DV + 16 * nt + 4 * lg);
           const f32x4_t x = O[qt][nt] * inv;
           part += x[0] * bf16_bits_to_f32(gw[0] & 0xffffu) + x[1] * __uint_as_float(gw[0] & 0xffff0000u) +
                   x[2] * bf16_bits_to_f32(gw[1] & 0xffffu) + x[3] * __uint_as_float(gw[1] & 0xffff0000u);
         }
       }
       part = xor32_sum(xor16_sum(part));  // over the four lane groups (all lanes take part)
-      if (query < T && lg == 0)
-        *reinterpret_cast<u32x2_t*>(stats + (bh * T + query) * 2) = u32x2_t{__float_as_uint(den), __float_as_uint(part)};
+      if (query < len && lg == 0)
+        *reinterpret_cast<u32x2_t*>(stats + row * 2) = u32x2_t{__float_as_uint(den), __float_as_uint(part)};
     }
     return;
   }
@@ -520,6 +521,25 @@ hipError_t launch_quadratic_bf16_family(const uint16_t* q, const uint16_t* k, co
   if (dv == 16) return launch_quad_fam<16, 2>(q, k, v, o, o_bf16, BH, T, st);
   if (dv == 32) return launch_quad_fam<32, 2>(q, k, v, o, o_bf16, BH, T, st);
   return launch_quad_fam<64, 2>(q, k, v, o, o_bf16, BH, T, st);
+}
+
+// backward statistics of the full map over packed sequences (T = max_len; stats per row of
+// the packed layout)
+hipError_t launch_quadratic_bf16_stats_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                              const uint16_t* gout, float* stats, int B, int H, int max_len, int p,
+                                              int dv, SeqLayout lay, hipStream_t st) {
+  const int BH = B * H;
+  const int nqb = (max_len + quad::BM - 1) / quad::BM;
+  dim3 grid((unsigned)((int64_t)nqb * BH)), block(quad::NTHR);
+#define KATA_SCASE(PP, DD)                                                                                   \
+  if (p == PP && dv == DD) {                                                                                 \
+    quadratic_bf16_kernel<PP, DD, false, 0, 1, 1, true, true>                                                \
+        <<<grid, block, 0, st>>>(q, k, v, nullptr, max_len, nqb, gout, stats, lay, H);                       \
+    return hipGetLastError();                                                                                \
+  }
+  KATA_SCASE(32, 32) KATA_SCASE(32, 64) KATA_SCASE(64, 32) KATA_SCASE(64, 64)
+#undef KATA_SCASE
+  return hipErrorInvalidValue;
 }
 
 // backward statistics of the full map (STATS above) for bf16 q, k, v, gout

@@ -24,6 +24,8 @@
 //   forward's layout); key blocks of 64 (k rows, v rows, k transposed, ik^2) staged in LDS
 //   from the start to the wave's last query. S^T = K Q^T and dP^T = V G^T (keys as rows),
 //   dQ^T += K^T C^T.
+// PK: packed token-major sequences (row0 + t * stp for t < len from cu_seqlens, T = max_len);
+//   workgroups past a sequence's length return at once, rows past it read as zero.
 #include <type_traits>
 
 #include "kata_device.h"
@@ -48,9 +50,10 @@ __device__ __forceinline__ bf16x8_t pack8f(const float (&x)[8]) {
   return __builtin_bit_cast(bf16x8_t, u32x4_t{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])});
 }
 
-// Staging of one 64-row block of a [T, W] bf16 tensor (rows r0..): raw rows at pitch
-// row_pitch<W>() and, when TR, the transposed rows in the permuted key layout of the forward
-// (column c at vt_row(c), row r of the block at vt_pos(r)). Rows past T read as zero.
+// Staging of one 64-row block of a sequence's rows of a bf16 tensor of width W (rows r0..): raw
+// rows at pitch row_pitch<W>() and, when TR, the transposed rows in the permuted key layout of
+// the forward (column c at vt_row(c), row r of the block at vt_pos(r)). Rows past the
+// sequence's length lie outside the buffer resource and read as zero.
 template <int W, bool TR>
 struct BlockStager {
   static constexpr int RP = qbwd::row_pitch<W>();
@@ -60,22 +63,23 @@ struct BlockStager {
   u32x4_t rr[RI];
   u32x4_t tr[2];
   int vp = 0, vd = 0;
-  // tfirst: the first thread of this tensor's transposed pieces (two tensors share the threads)
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int r0, int tfirst) {
+  // tfirst: the first thread of this tensor's transposed pieces (two tensors share the threads);
+  // rs: elements from one row to the next (W padded, H W packed)
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int r0, int tfirst, int rs) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const int pc = tid + qbwd::NTHR * i;
       if (pc < RPIECES)
-        rr[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)((r0 + pc / (W / 8)) * W + 8 * (pc % (W / 8))) * 2, 0, 0);
+        rr[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)((r0 + pc / (W / 8)) * rs + 8 * (pc % (W / 8))) * 2, 0, 0);
     }
     if constexpr (TR) {
       const int pc = tid - tfirst;
       if (pc >= 0 && pc < TPIECES) {
         vt_piece<W>(pc, vp, vd);
-        const uint32_t off = (uint32_t)((r0 + 2 * vp) * W + 8 * vd) * 2;
+        const uint32_t off = (uint32_t)((r0 + 2 * vp) * rs + 8 * vd) * 2;
         tr[0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-        tr[1] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + W * 2, 0, 0);
+        tr[1] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + (uint32_t)rs * 2, 0, 0);
       }
     }
   }
@@ -119,14 +123,14 @@ __device__ __forceinline__ float frag_inv_norm(const bf16x8_t (&f)[KS]) {
 }
 
 // ---------------------------------------------------------------- dK, dV (keys own the wave)
-template <int P, int DV>
+template <int P, int DV, bool PK>
 __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k,
                                                                  const uint16_t* __restrict__ v,
                                                                  const uint16_t* __restrict__ gout,
                                                                  const float* __restrict__ stats,
                                                                  float* __restrict__ dk, float* __restrict__ dvo,
-                                                                 int T, int nkb) {
+                                                                 int T, int nkb, SeqLayout lay, int H) {
   using namespace qbwd;
   constexpr int KS = P / 32, DS = DV / 32, NKT = KW / 16;
   constexpr int QP = row_pitch<P>(), GP = row_pitch<DV>();
@@ -146,10 +150,19 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
   const int64_t bh = blockIdx.x % nbh;
   const int K0 = (int)(blockIdx.x / nbh) * KB;
   const int kw0 = K0 + wave * KW;
-  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
-  const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gout + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
+  // Rows of this sequence: row0 + t * stp for t < len (padded: bh T + t; packed token-major
+  // (PK): H rows apart, the length from cu_seqlens, T = max_len)
+  int64_t row0 = bh * (int64_t)T;
+  int stp = 1, len = T;
+  if constexpr (PK) {
+    seq_rows_of(lay, bh, H, T, row0, stp, len);
+    if (K0 >= len) return;  // uniform over the workgroup: no key of this block exists
+  }
+  const int RQ = PK ? stp * P : P, RV = PK ? stp * DV : DV;  // elements from one row to the next
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + row0 * DV, (uint32_t)len * RV * 2);
+  const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gout + row0 * DV, (uint32_t)len * RV * 2);
 
   // this wave's keys as B operands: key kw0 + 16 kt + ln, components / columns 32 ks + 8 lg ..
   bf16x8_t kf[NKT][KS], vf[NKT][DS];
@@ -159,10 +172,10 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
     const int key = kw0 + 16 * kt + ln;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[kt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)(key * P + 32 * ks + 8 * lg) * 2, 0, 0));
+      kf[kt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)(key * RQ + 32 * ks + 8 * lg) * 2, 0, 0));
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-      vf[kt][ds] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)(key * DV + 32 * ds + 8 * lg) * 2, 0, 0));
+      vf[kt][ds] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (uint32_t)(key * RV + 32 * ds + 8 * lg) * 2, 0, 0));
     const float ik = frag_inv_norm<KS>(kf[kt]);
     ik1[kt] = ik;
     ik2[kt] = ik * ik;
@@ -175,13 +188,13 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
   constexpr int QT_FIRST = 0, GT_FIRST = (BQ / 2) * (P / 8);  // transposed pieces: q first, then g
   static_assert(GT_FIRST + (BQ / 2) * (DV / 8) <= NTHR, "staging layout");
   auto prefetch = [&](int qb0) {
-    stq.load(rq, qb0, QT_FIRST);
-    stg.load(rg, qb0, GT_FIRST);
+    stq.load(rq, qb0, QT_FIRST, RQ);
+    stg.load(rg, qb0, GT_FIRST, RV);
     if (tid < BQ) {
       const int t = qb0 + tid;
       dstat[0] = dstat[1] = 0.f;
-      if (t < T) {
-        const u32x2_t s2 = *reinterpret_cast<const u32x2_t*>(stats + (bh * T + t) * 2);
+      if (t < len) {
+        const u32x2_t s2 = *reinterpret_cast<const u32x2_t*>(stats + (row0 + (int64_t)t * stp) * 2);
         dstat[0] = __uint_as_float(s2[0]);
         dstat[1] = __uint_as_float(s2[1]);
       }
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
     for (int pt = 0; pt < P / 16; ++pt) dKa[kt][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int qb_first = K0 / BQ, nqb = (T + BQ - 1) / BQ;
+  const int qb_first = K0 / BQ, nqb = (len + BQ - 1) / BQ;
   if (qb_first < nqb) {
     prefetch(qb_first * BQ);
     stage(0);
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
         }
       }
     };
-    if (qb0 + BQ - 1 >= kw0 && kw0 < T) {
+    if (qb0 + BQ - 1 >= kw0 && kw0 < len) {
       if (qb0 < kw0 + KW - 1) block(std::true_type{});
       else block(std::false_type{});
     }
@@ -308,8 +321,8 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = kw0 + 16 * kt + 4 * lg + r;
-      if (key >= T) continue;
-      const int64_t row = bh * T + key;
+      if (key >= len) continue;
+      const int64_t row = row0 + (int64_t)key * stp;
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt) dvo[row * DV + 16 * dt + ln] = dVa[kt][dt][r];
 #pragma unroll
@@ -322,13 +335,14 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_keys_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------- dQ (queries own the wave)
-template <int P, int DV>
+template <int P, int DV, bool PK>
 __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ k,
                                                                     const uint16_t* __restrict__ v,
                                                                     const uint16_t* __restrict__ gout,
                                                                     const float* __restrict__ stats,
-                                                                    float* __restrict__ dq, int T, int nqb) {
+                                                                    float* __restrict__ dq, int T, int nqb,
+                                                                    SeqLayout lay, int H) {
   using namespace qbwd;
   constexpr int KS = P / 32, DS = DV / 32, NQT = QW / 16;
   constexpr int KP = row_pitch<P>(), VP = row_pitch<DV>();
@@ -344,10 +358,17 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
   const int64_t bh = blockIdx.x % nbh;
   const int qb0 = (nqb - 1 - (int)(blockIdx.x / nbh)) * QB;
   const int qw0 = qb0 + wave * QW;
-  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + bh * (int64_t)T * P, (uint32_t)T * P * 2);
-  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
-  const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gout + bh * (int64_t)T * DV, (uint32_t)T * DV * 2);
+  int64_t row0 = bh * (int64_t)T;  // rows of this sequence, as in bwd_keys_kernel
+  int stp = 1, len = T;
+  if constexpr (PK) {
+    seq_rows_of(lay, bh, H, T, row0, stp, len);
+    if (qb0 >= len) return;  // uniform over the workgroup: no query of this block exists
+  }
+  const int RQ = PK ? stp * P : P, RV = PK ? stp * DV : DV;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + row0 * P, (uint32_t)len * RQ * 2);
+  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + row0 * DV, (uint32_t)len * RV * 2);
+  const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gout + row0 * DV, (uint32_t)len * RV * 2);
 
   // this wave's queries as B operands: query qw0 + 16 qt + ln, components / columns 32 ks + 8 lg ..
   bf16x8_t qf[NQT][KS], gf[NQT][DS];
@@ -357,13 +378,13 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
     const int query = qw0 + 16 * qt + ln;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[qt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(query * P + 32 * ks + 8 * lg) * 2, 0, 0));
+      qf[qt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(query * RQ + 32 * ks + 8 * lg) * 2, 0, 0));
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-      gf[qt][ds] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(query * DV + 32 * ds + 8 * lg) * 2, 0, 0));
+      gf[qt][ds] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(query * RV + 32 * ds + 8 * lg) * 2, 0, 0));
     dinv[qt] = nd[qt] = 0.f;
-    if (query < T) {
-      const u32x2_t s2 = *reinterpret_cast<const u32x2_t*>(stats + (bh * T + query) * 2);
+    if (query < len) {
+      const u32x2_t s2 = *reinterpret_cast<const u32x2_t*>(stats + (row0 + (int64_t)query * stp) * 2);
       const float D = __uint_as_float(s2[0]);
       dinv[qt] = D > 0.f ? __builtin_amdgcn_rcpf(D) : 0.f;
       nd[qt] = -__uint_as_float(s2[1]) * dinv[qt];
@@ -374,8 +395,8 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
   BlockStager<DV, false> stv;
   static_assert(BlockStager<P, true>::RI == 1, "one key-row piece per thread");
   auto prefetch = [&](int kb0) {
-    stk.load(rk, kb0, 0);
-    stv.load(rv, kb0, 0);
+    stk.load(rk, kb0, 0, RQ);
+    stv.load(rv, kb0, 0, RV);
   };
   // rows to LDS, and ik^2 per key from the row pieces: the P / 8 pieces of a row sit on
   // adjacent lanes (whole waves take part or none)
@@ -402,7 +423,7 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt) dQa[qt][pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int kend = min(T, qb0 + QB);
+  const int kend = min(len, qb0 + QB);
   const int nkb = (kend + BQ - 1) / BQ;
   prefetch(0);
   stage(0);
@@ -459,7 +480,7 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
         }
       }
     };
-    if (kb0 <= qw0 + QW - 1 && qw0 < T) {
+    if (kb0 <= qw0 + QW - 1 && qw0 < len) {
       if (kb0 + BQ - 1 > qw0) block(std::true_type{});
       else block(std::false_type{});
     }
@@ -471,29 +492,33 @@ __global__ __launch_bounds__(qbwd::NTHR, 1) void bwd_queries_kernel(const uint16
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int query = qw0 + 16 * qt + ln;
-    if (query >= T) continue;
+    if (query >= len) continue;
 #pragma unroll
     for (int pt = 0; pt < P / 16; ++pt)
-      *reinterpret_cast<f32x4_t*>(dq + (bh * T + query) * (int64_t)P + 16 * pt + 4 * lg) = dQa[qt][pt] * 2.f;
+      *reinterpret_cast<f32x4_t*>(dq + (row0 + (int64_t)query * stp) * P + 16 * pt + 4 * lg) = dQa[qt][pt] * 2.f;
   }
 }
 
 hipError_t launch_quadratic_bf16_stats(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,
                                        float* stats, int B, int H, int T, int p, int dv, hipStream_t st);
+hipError_t launch_quadratic_bf16_stats_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                              const uint16_t* gout, float* stats, int B, int H, int max_len, int p,
+                                              int dv, SeqLayout lay, hipStream_t st);
 
 bool quadratic_bwd_mfma_supported(int p, int dv) { return (p == 32 || p == 64) && (dv == 32 || dv == 64); }
 
-template <int P, int DV>
+template <int P, int DV, bool PK>
 static hipError_t launch_bwd_pd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* gout,
-                                float* stats, float* dq, float* dk, float* dvo, int BH, int T, hipStream_t st) {
+                                float* stats, float* dq, float* dk, float* dvo, int BH, int H, int T, SeqLayout lay,
+                                hipStream_t st) {
   const int nkb = (T + qbwd::KB - 1) / qbwd::KB;
-  bwd_keys_kernel<P, DV><<<dim3((unsigned)((int64_t)nkb * BH)), dim3(qbwd::NTHR), 0, st>>>(q, k, v, gout, stats, dk,
-                                                                                           dvo, T, nkb);
+  bwd_keys_kernel<P, DV, PK><<<dim3((unsigned)((int64_t)nkb * BH)), dim3(qbwd::NTHR), 0, st>>>(
+      q, k, v, gout, stats, dk, dvo, T, nkb, lay, H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (T + qbwd::QB - 1) / qbwd::QB;
-  bwd_queries_kernel<P, DV><<<dim3((unsigned)((int64_t)nqb * BH)), dim3(qbwd::NTHR), 0, st>>>(q, k, v, gout, stats,
-                                                                                              dq, T, nqb);
+  bwd_queries_kernel<P, DV, PK><<<dim3((unsigned)((int64_t)nqb * BH)), dim3(qbwd::NTHR), 0, st>>>(
+      q, k, v, gout, stats, dq, T, nqb, lay, H);
   return hipGetLastError();
 }
 
@@ -504,7 +529,21 @@ hipError_t launch_quadratic_bwd_mfma(const uint16_t* q, const uint16_t* k, const
   if (e != hipSuccess) return e;
   const int BH = B * H;
 #define KATA_BCASE(PP, DD) \
-  if (p == PP && dv == DD) return launch_bwd_pd<PP, DD>(q, k, v, gout, stats, dq, dk, dvo, BH, T, st);
+  if (p == PP && dv == DD) return launch_bwd_pd<PP, DD, false>(q, k, v, gout, stats, dq, dk, dvo, BH, H, T, SeqLayout{}, st);
+  KATA_BCASE(32, 32) KATA_BCASE(32, 64) KATA_BCASE(64, 32) KATA_BCASE(64, 64)
+#undef KATA_BCASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quadratic_bwd_mfma_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                            const uint16_t* gout, int B, int H, int max_len, int p, int dv,
+                                            SeqLayout lay, float* stats, float* dq, float* dk, float* dvo,
+                                            hipStream_t st) {
+  hipError_t e = launch_quadratic_bf16_stats_varlen(q, k, v, gout, stats, B, H, max_len, p, dv, lay, st);
+  if (e != hipSuccess) return e;
+  const int BH = B * H;
+#define KATA_BCASE(PP, DD) \
+  if (p == PP && dv == DD) return launch_bwd_pd<PP, DD, true>(q, k, v, gout, stats, dq, dk, dvo, BH, H, max_len, lay, st);
   KATA_BCASE(32, 32) KATA_BCASE(32, 64) KATA_BCASE(64, 32) KATA_BCASE(64, 64)
 #undef KATA_BCASE
   return hipErrorInvalidValue;

@@ -269,6 +269,32 @@ def test_chunked_bwd_varlen_validation(lib):
     assert vb(total=0) == OK and vb(max_len=0) == OK and vb(B=0) == OK
 
 
+def test_quadratic_bwd_varlen_validation(lib):
+    """kata_quadratic_bwd_varlen: argument errors come back before any device access."""
+    need = lib.kata_quadratic_bwd_varlen_workspace_bytes(2, 2, 300)
+    assert need == 300 * 2 * 2 * 4                                 # D_t, delta_t per packed row
+    assert lib.kata_quadratic_bwd_varlen_workspace_bytes(2, 2, 0) == 0
+    assert lib.kata_quadratic_bwd_varlen_workspace_bytes(0, 2, 300) == 0
+
+    def qb(cu=A + (1 << 36), **kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, dt=BF16, B=2, H=2, total=300, max_len=200, p=32, dv=64,
+                 dq=A + (1 << 30), dk=A + (2 << 30), dvo=A + (3 << 30), ws=A + (4 << 30), wsb=need)
+        a.update(kw)
+        return lib.kata_quadratic_bwd_varlen(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["total"],
+                                             a["max_len"], a["p"], a["dv"], cu, a["dq"], a["dk"], a["dvo"], a["ws"],
+                                             a["wsb"], None)
+    assert qb(dt=F32) == E_UNSUP and qb(p=16) == E_UNSUP and qb(dv=48) == E_UNSUP   # the MFMA shapes only
+    assert qb(dt=5) == E_DTYPE
+    assert qb(cu=None) == E_NULL and qb(cu=A + (1 << 36) + 2) == E_ALIGN
+    assert qb(total=-1) == E_SHAPE and qb(max_len=-3) == E_SHAPE and qb(H=-1) == E_SHAPE
+    assert qb(wsb=need - 1) == E_WS and qb(ws=None) == E_WS and qb(dq=None) == E_NULL and qb(v=A + 8) == E_ALIGN
+    assert qb(dk=A + (1 << 30)) == E_ALIAS                        # dk on top of dq
+    assert qb(dvo=A + 4096) == E_ALIAS                            # dv_out on top of k
+    assert qb(H=1024, max_len=1 << 14, total=1 << 14) == E_SHAPE  # 32-bit offsets of one sequence
+    assert qb(H=16, max_len=(1 << 19) - 256, total=100) == E_SHAPE  # a block past the end counts
+    assert qb(total=0) == OK and qb(max_len=0) == OK and qb(B=0) == OK and qb(H=0) == OK
+
+
 def test_quadratic_varlen_validation(lib):
     """kata_quadratic_fwd_varlen: argument errors come back before any device access."""
     def qv(cu=A + (1 << 36), **kw):

@@ -256,9 +256,52 @@ def test_chunked_bwd_varlen(p, dv, scan):
         start += L
 
 
+@pytest.mark.parametrize("p,dv,lens,max_len", [(32, 64, [1300, 0, 45, 700], 1400), (64, 32, [700, 129, 0, 513], 700),
+                                              (64, 64, [1300, 64, 1], 1200), (32, 32, [200, 1], 200)])
+def test_quadratic_bwd_varlen(p, dv, lens, max_len):
+    """Packed sequences on the flash-style MFMA backward (kata_quadratic_bwd_varlen): each
+    sequence's gradients bit for bit equal to kata_quadratic_bwd on that sequence alone, and
+    against the oracle at the bf16 MFMA bars. An empty sequence, one-token and short ones, a
+    sequence longer than max_len (cut: its rows past max_len are not written) and rows after
+    the last sequence (left at zero)."""
+    B, H, extra = len(lens), 2, 3
+    Tmax = max(lens)
+    print(f"[case] quadratic bwd varlen p={p} dv={dv} lens={lens} max_len={max_len}", flush=True)
+    q, k, v = draw_qkv(93, B, H, Tmax, p, dv, "bf16")
+    go = draw_qkv(94, B, H, Tmax, dv, dv, "bf16")[0]
+
+    def pack(x):
+        rows = [np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)]
+        return np.concatenate(rows + [np.transpose(x[0, :, :extra], (1, 0, 2))], axis=0)
+
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    got = kata.quadratic_bwd_varlen(*(to_dev(pack(x), "bf16") for x in (q, k, v, go)), cu, max_len)
+    got = [to_np(x) for x in got]
+    n = sum(lens)
+    assert all(np.all(x[n:] == 0.0) for x in got), "rows outside every sequence were written"
+    start = 0
+    for b, L in enumerate(lens):
+        Lc = min(L, max_len)
+        if Lc:
+            seq = lambda x: np.transpose(x[start:start + Lc], (1, 0, 2))[None]
+            alone = kata.quadratic_bwd(*(to_dev(x[b:b + 1, :, :Lc], "bf16") for x in (q, k, v, go)))
+            for name, x, a in zip(("dq", "dk", "dv"), got, alone):
+                assert np.array_equal(seq(x), to_np(a)), (b, name, "differs from the padded call")
+            ref = kb.backward(q[b:b + 1, :, :Lc], k[b:b + 1, :, :Lc], v[b:b + 1, :, :Lc], go[b:b + 1, :, :Lc])
+            for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+                e = _rel(seq(x), r, 1e-2 * float(np.linalg.norm(go[b, :, :Lc])))
+                print(f"  seq {b} L={Lc} {name} rel={e:.2e}", flush=True)
+                assert e <= MFMA_BWD_BAR, (b, name)
+                _rows(f"seq {b} {name}", seq(x), r, ROW_BAR_MFMA)
+        if L > Lc:
+            assert all(np.all(x[start + Lc:start + L] == 0.0) for x in got), "rows past max_len were written"
+        start += L
+
+
 def test_autograd_varlen():
-    """kata_attention_varlen: the packed forward and the packed O(T) backward through autograd,
-    each sequence against the oracle at the bf16 MFMA bar (gradients rounded to bf16 add 2^-9)."""
+    """kata_attention_varlen: the packed forward and a packed backward through autograd (at
+    this max_len the flash-style one), each sequence against the oracle at the bf16 MFMA bar
+    (gradients rounded to bf16 add 2^-9)."""
     B, H, max_len, p, dv = 3, 2, 900, 32, 64
     lens = [900, 0, 333]
     q, k, v = draw_qkv(95, B, H, max_len, p, dv, "bf16")
