@@ -133,6 +133,37 @@ def test_chunked_many_segments(H, dt, p, dv):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("case", ["v*1e4", "v*1e-4", "v jumps 1e4 at T/2", "q*1e-3 k*1e3", "v*1e30"])
+@pytest.mark.parametrize("C,scan", [(128, "associative"), (64, "sequential")])
+def test_chunked_value_and_row_scales(case, C, scan):
+    """The fp16-operand kernels carry values as sigma v with a power-of-two sigma chosen from
+    a running bound, and queries as lambda q_hat: the output must not depend on the scale of
+    v beyond its rounding, nor on the norms of q and k. Uniformly scaled values, a jump of the
+    value scale inside the sequence (sigma falls mid-sequence and the state is rescaled),
+    values near the top of the fp32 range, and scaled query and key rows, at the bf16 bar."""
+    B, H, T, p, dv = 1, 4, 2048, 32, 64
+    q, k, v = draw_qkv(61, B, H, T, p, dv, "f32")
+    if case == "v*1e4":
+        v = v * 1e4
+    elif case == "v*1e-4":
+        v = v * 1e-4
+    elif case == "v jumps 1e4 at T/2":
+        v[:, :, T // 2:] *= 1e4
+    elif case == "q*1e-3 k*1e3":
+        q, k = q * 1e-3, k * 1e3
+    else:
+        v = v * 1e30
+    q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    print(f"[case] chunked scales {case} C={C} {scan}", flush=True)
+    ref = ko.naive(q, k, v)
+    got = to_np(kata.chunked_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), C=C, scan=scan,
+                                 out_dtype=torch.float32))
+    assert np.all(np.isfinite(got))
+    e = row_rel_err(got, ref)
+    print(f"  row-rel err {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T", [1, 5, 31, 64])
 def test_chunked_short_sequences(T):
     q, k, v = _case("chunked-short", 12, 1, 2, T, 32, 64, "bf16")
