@@ -156,10 +156,13 @@ def main():
         step = [lambda: kata.chunked_fwd(qd, kd, vd, C=C, scan=args.scan, out=out, workspace=ws, family=fam, g=g)]
         dominant = 0
         s2 = fam == "sigma" and g == 2
-        kernel_name = f"chunked_bf16_kernel<32, {dv}, {C}, true>" if s2 else "family_chunked_kernel"
+        s2f = s2 and dv == 64 and C in (64, 128)  # the fp16 kernels with the two-block lift
+        kernel_name = (f"chunked_f16_kernel<{dv}, {C}, true> (whole call)" if s2f
+                       else f"chunked_bf16_kernel<32, {dv}, {C}, true>" if s2 else "family_chunked_kernel")
         m = p // g
         n = m * (m + 1) // 2 * (1 if fam == "sigma" else g)
-        Cr = C // 2 if s2 else C  # tokens per chunk (C counts 32-component rows under Sigma 2)
+        # tokens per chunk (the virtual-row kernels count 32-component rows, two per token)
+        Cr = C // 2 if (s2 and not s2f) else C
         pair = 2 * p * g if fam == "sigma" else 2 * p
         flops = (4 * n * (dv + 1) + (Cr + 1) * (pair // 2 + dv + 1)) * B * H * T
         units = B * T

@@ -184,10 +184,14 @@ size_t kata_chunked_workspace_bytes(int B, int H, int T, int p, int dv, int C, k
 }
 
 // kata_chunked_fwd_passes, plus the final state when S and Z are given (want_state)
-// KATA-Sigma 2 at p = 64 with bf16 inputs runs the MFMA kernels over 2T virtual rows
+// KATA-Sigma 2 at p = 64 with bf16 inputs runs on MFMA kernels: the fp16-operand kernels with
+// the two-block lift at dv = 64 (sigma2_f16), else the bf16 kernels over 2T virtual rows
 static bool sigma2_mfma(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
   return fam == KATA_FEAT_SIGMA && g == 2 && p == 64 && in_dt == KATA_DTYPE_BF16 && in_set(dv, {32, 64}) &&
          in_set(C, {64, 128});
+}
+static bool sigma2_f16(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g) {
+  return sigma2_mfma(p, dv, C, in_dt, fam, g) && kata::chunked_f16_s2_supported(dv, C);
 }
 
 // the chunked forward's supported (p, dv, C) for a family and input dtype
@@ -251,7 +255,8 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   // the kernels address one sequence's rows (H rows apart when packed) with 32-bit byte offsets
   if (packed && (int64_t)T * H * (p > dv ? p : dv) * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
   if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, rows, p, dv)) != KATA_OK) return s;
-  const bool s2 = cu == nullptr && sigma2_mfma(p, dv, C, in_dt, fam, g);
+  const bool s2f = cu == nullptr && sigma2_f16(p, dv, C, in_dt, fam, g);
+  const bool s2 = cu == nullptr && !s2f && sigma2_mfma(p, dv, C, in_dt, fam, g);  // virtual rows
   if (s2 && (int64_t)T * 2 > INT32_MAX) return KATA_ERR_SHAPE;
   const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
@@ -279,6 +284,10 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   float* zo = want_state ? Z : nullptr;
   const bool ob16 = o_dt == KATA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
+  if (s2f)
+    return hip_status(kata::launch_chunked_f16_s2(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                                  static_cast<const uint16_t*>(v), o, ob16, B, H, T, dv, C, plan, ws,
+                                                  so, zo, kata::SeqLayout{lens, nullptr, 0}, st));
   if (s2)
     return hip_status(kata::launch_chunked_bf16_sigma2(static_cast<const uint16_t*>(q),
                                                        static_cast<const uint16_t*>(k),
@@ -311,11 +320,14 @@ size_t kata_chunked_workspace_bytes_family(int B, int H, int T, int p, int dv, i
   if (!valid_dt(in_dt) || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)) return 0;
   if (B <= 0 || H <= 0 || T <= 0 || dv < 1 || C < 1) return 0;
   if (!chunked_supported(p, dv, C, in_dt, fam, g)) return 0;
-  const bool s2 = sigma2_mfma(p, dv, C, in_dt, fam, g);
+  const bool s2f = sigma2_f16(p, dv, C, in_dt, fam, g);
+  const bool s2 = !s2f && sigma2_mfma(p, dv, C, in_dt, fam, g);  // virtual rows
   if (s2 && (int64_t)T * 2 > INT32_MAX) return 0;
   const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
   if (plan.nseg <= 1) return 0;
-  const int64_t sf = s2 ? kata::mfma_state_floats(32, dv) : kata::family_state_floats(p, dv, (int)fam, g);
+  const int64_t sf = s2f  ? kata::f16_state_floats(dv)
+                     : s2 ? kata::mfma_state_floats(32, dv)
+                          : kata::family_state_floats(p, dv, (int)fam, g);
   return (size_t)B * H * (plan.nseg - 1) * sf * sizeof(float);
 }
 

@@ -153,50 +153,59 @@ __device__ __forceinline__ h8_t ld8a(uint32_t a) {
 // readout wave and two build waves.
 constexpr int NU = 2 * NTL;  // 16-row build tiles: u = 2 t + half holds quads 4 half .. 4 half + 3 of tile t
 
-template <int DV, int C>
+template <int DV, int C, bool S2 = false>
 struct Lay {
+  // S2: KATA-Sigma 2 on 64-component rows (two 32-component blocks whose lifts are summed);
+  // its operands take twice the rows, so the chunk operands are single-buffered to fit LDS
+  static constexpr int PC = S2 ? 64 : 32;      // components per query and key row
+  static constexpr int NBUF = S2 ? 1 : 2;      // chunk operand buffers
   static constexpr int NDT = DV / 32;          // 32-column value tiles of the readout
   static constexpr int NDV = DV / 16;          // 16-column value tiles of the build
   static constexpr int NG = C / 32;            // 32-token groups per chunk
   static constexpr int FS = 4 / NG;            // readout waves per token group
   static constexpr int NS = C / 32;            // 32-token build steps
-  static constexpr int QPB = 72;               // q_hat row pitch, bytes (8-byte block reads conflict-free)
-  static constexpr int KPB = 64;               // row-major key rows (unscaled k_hat), bytes
+  static constexpr int QPB = 2 * PC + 8;       // q_hat row pitch, bytes (8-byte block reads conflict-free)
+  static constexpr int KPB = 64;               // row-major key rows (unscaled k_hat) of one 32-component block, bytes
   // Byte offset of 4-component block b (8 bytes) of key row r. A read of 8 bytes serves 32
   // lanes per cycle; the intra-chunk product's lanes read rows 32 kg + t (t = lane % 32) at
   // a common block, and at a 64-byte pitch rows t and t + 4 would share banks. Block b of
-  // row r therefore sits at block b ^ (r / 4) % 8: the 32 lanes cover all 64 banks.
-  __device__ static __forceinline__ int krpos(int r, int b) { return r * KPB + 8 * (b ^ ((r >> 2) & 7)); }
+  // row r therefore sits at block b ^ (r / 4) % 8: the 32 lanes cover all 64 banks. S2 keeps
+  // each 32-component block of the keys in a region of its own (block b / 8 of the row), so
+  // the second block's reads are the first block's at a constant offset.
+  __device__ static __forceinline__ int krpos(int r, int b) {
+    return S2 ? (b >> 3) * (C * KPB) + r * KPB + 8 * ((b & 7) ^ ((r >> 2) & 7)) : r * KPB + 8 * (b ^ ((r >> 2) & 7));
+  }
   static constexpr int RPB = 256;              // transposed rows (one component or value column), bytes
   static constexpr int MPB = 80;               // Gram row pitch, bytes
   static constexpr int ST = NU * NDV * 64 * 8;  // state fragments: [u][value tile][lane half][column] x 8 fp16
   // chunk operands, two buffers each (chunk c + 1 is staged while chunk c is used)
-  static constexpr int QB = C * QPB, KRB = C * KPB, KTB = 32 * RPB, VTB = DV * RPB;
-  static constexpr int OFF_Q = ST;                   // lambda q_hat rows
-  static constexpr int OFF_KR = OFF_Q + 2 * QB;      // k_hat rows (intra-chunk scores)
-  static constexpr int OFF_KT = OFF_KR + 2 * KRB;    // k_hat^T (build operands, Gram)
-  static constexpr int OFF_VT = OFF_KT + 2 * KTB;    // sigma V^T
-  static constexpr int OFF_M = OFF_VT + 2 * VTB;     // Gram hi, lo
+  static constexpr int QB = C * QPB, KRB = C * KPB * (PC / 32), KTB = PC * RPB, VTB = DV * RPB;
+  static constexpr int OFF_Q = ST;                      // lambda q_hat rows
+  static constexpr int OFF_KR = OFF_Q + NBUF * QB;      // k_hat rows (intra-chunk scores)
+  static constexpr int OFF_KT = OFF_KR + NBUF * KRB;    // k_hat^T (build operands, Gram)
+  static constexpr int OFF_VT = OFF_KT + NBUF * KTB;    // sigma V^T
+  static constexpr int OFF_M = OFF_VT + NBUF * VTB;     // Gram hi, lo
+  static constexpr int KOFF = 32 * RPB;                 // k_hat^T rows of the second block (S2)
   static constexpr int OFF_PART = OFF_M + 2 * 32 * MPB;
   static constexpr int PART = FS > 1 ? NG * (FS - 1) * NDT * 64 * 64 : 0;
   // [8 prefix maxima][2 chunk parities][8 value maxima] (uint32)
   static constexpr int OFF_RED = OFF_PART + PART;
   static constexpr int LDS = OFF_RED + 128;
-  __device__ static __forceinline__ int offq(int b) { return OFF_Q + b * QB; }
-  __device__ static __forceinline__ int offkr(int b) { return OFF_KR + b * KRB; }
-  __device__ static __forceinline__ int offkt(int b) { return OFF_KT + b * KTB; }
-  __device__ static __forceinline__ int offvt(int b) { return OFF_VT + b * VTB; }
+  __device__ static __forceinline__ int offq(int b) { return OFF_Q + (NBUF == 2 ? b : 0) * QB; }
+  __device__ static __forceinline__ int offkr(int b) { return OFF_KR + (NBUF == 2 ? b : 0) * KRB; }
+  __device__ static __forceinline__ int offkt(int b) { return OFF_KT + (NBUF == 2 ? b : 0) * KTB; }
+  __device__ static __forceinline__ int offvt(int b) { return OFF_VT + (NBUF == 2 ? b : 0) * VTB; }
   // first-chunk split operands alias the state area (there is no readout at chunk 0)
   static constexpr int OFF_QLO = 0;
   static constexpr int OFF_KLO = C * QPB;
-  static_assert(OFF_KLO + C * KPB <= ST, "split operands fit the state area");
+  static_assert(OFF_KLO + KRB <= ST, "split operands fit the state area");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(C <= 128, "four 64-byte blocks per transposed row");
   static_assert(OFF_KT % 256 == 0 && KTB % 256 == 0 && OFF_VT % 256 == 0 && VTB % 256 == 0, "step reads XOR the address");
     // summary pass: [k_hat^T | sigma V^T], double-buffered (partners read k_hat^T and the
   // factor 2 of tiles 1-17 is applied to the summary); value maxima [2 parities][4 staging
   // waves]
-  static constexpr int SUM_BUF = (32 + DV) * RPB;
+  static constexpr int SUM_BUF = (PC + DV) * RPB;
   static constexpr int SUM_RED = 2 * SUM_BUF;
   static constexpr int SUM_LDS = SUM_RED + 128;
   static_assert(SUM_LDS <= 160 * 1024, "LDS budget (summaries)");
@@ -294,11 +303,12 @@ struct KVTarget {
   int kr, kt, kt2, vt, klo;
 };
 
-template <int DV, int C, int NTHR>
+template <int DV, int C, int NTHR, bool S2 = false>
 struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..NTHR-1)
-  using L = Lay<DV, C>;
-  // key item = (token pair p, component quarter cq): the 8 items of a pair are adjacent lanes
-  static constexpr int KI = 4 * C;
+  using L = Lay<DV, C, S2>;
+  static constexpr int PC = L::PC, KQ = PC / 4;
+  // key item = (token pair p, component quarter cq): the KQ items of a pair are adjacent lanes
+  static constexpr int KI = KQ * (C / 2);
   static constexpr int KP = (KI + NTHR - 1) / NTHR;
   // value item = (8-column group dg, token pair p), pairs fastest (row writes of whole lanes)
   static constexpr int VI = (C / 2) * (DV / 8);
@@ -309,15 +319,15 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
   int len;
   uint32_t rsp, rsv;
   __device__ __forceinline__ void init(const uint16_t* k, const uint16_t* v, int64_t row0, int step, int n) {
-    kb = k + row0 * P;
+    kb = k + row0 * PC;
     vb = v + row0 * DV;
     len = n;
-    rsp = (uint32_t)step * P;
+    rsp = (uint32_t)step * PC;
     rsv = (uint32_t)step * DV;
   }
   __device__ __forceinline__ void load(int t0, int tid) {
     const uint32_t left = (uint32_t)(t0 < len ? len - t0 : 0);
-    const uint32_t kbytes = left ? ((left - 1) * rsp + P) * 2 : 0;
+    const uint32_t kbytes = left ? ((left - 1) * rsp + PC) * 2 : 0;
     const uint32_t vbytes = left ? ((left - 1) * rsv + DV) * 2 : 0;
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)t0 * rsp, kbytes);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vb + (int64_t)t0 * rsv, vbytes);
@@ -325,7 +335,7 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + NTHR * i;
       if (pc < KI) {
-        const int p = pc >> 3, cq = pc & 7;
+        const int p = pc >> (S2 ? 4 : 3), cq = pc & (KQ - 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
           kr[i][u] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, ((2 * p + u) * rsp + 4 * cq) * 2, 0, 0));
@@ -370,7 +380,7 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
     for (int i = 0; i < KP; ++i) {
       const int pc = tid + NTHR * i;
       if (pc >= KI) continue;
-      const int p = pc >> 3, cq = pc & 7;
+      const int p = pc >> (S2 ? 4 : 3), cq = pc & (KQ - 1);
       float x[2][4], inv[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -381,7 +391,7 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
           x[u][2 * e + 1] = __uint_as_float(kr[i][u][e] & 0xffff0000u);
           ss += x[u][2 * e] * x[u][2 * e] + x[u][2 * e + 1] * x[u][2 * e + 1];
         }
-        inv[u] = inv_norm_fast(group_sum<8>(ss));
+        inv[u] = inv_norm_fast(group_sum<KQ>(ss));
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[u][e] *= inv[u];
       }
@@ -397,8 +407,8 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
       }
       const int pos = L::pi(2 * p);  // tokens 2p, 2p + 1 share a 4-byte word
       // lanes cq >= 4 write their components in the order 2, 3, 0, 1: rows 4 cq + c and
-      // 4 (cq + 4) + c share bank slots
-      const bool sw = cq >= 4;
+      // 4 (cq + 4) + c share bank slots (S2: quarters cq and cq + 8 still meet, 2-way)
+      const bool sw = S2 ? (cq & 4) != 0 : cq >= 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = i ^ (sw ? 2 : 0);
@@ -426,29 +436,31 @@ struct KVStage {  // keys and values of a chunk, staged by NTHR threads (tid 0..
 };
 
 // queries of one token group: NTHR threads stage rows [r0, r0 + 32) as lambda q_hat
-template <int DV, int C, int NTHR>
+template <int DV, int C, int NTHR, bool S2 = false>
 struct QStage {
-  using L = Lay<DV, C>;
-  static constexpr int QP = (128 + NTHR - 1) / NTHR;
+  using L = Lay<DV, C, S2>;
+  static constexpr int PC = L::PC, QE = PC / 8;  // 8-component pieces per row
+  static constexpr int QI = 32 * QE;             // pieces of a 32-row token group
+  static constexpr int QP = (QI + NTHR - 1) / NTHR;
   u32x4_t qr[QP];
   const uint16_t* qb;
   int len;
   uint32_t rsp;
   __device__ __forceinline__ void init(const uint16_t* q, int64_t row0, int step, int n) {
-    qb = q + row0 * P;
+    qb = q + row0 * PC;
     len = n;
-    rsp = (uint32_t)step * P;
+    rsp = (uint32_t)step * PC;
   }
   __device__ __forceinline__ void load(int t0, int r0, int tid) {
     const int first = t0 + r0;
     const uint32_t left = (uint32_t)(first < len ? len - first : 0);
-    const uint32_t bytes = left ? ((left - 1) * rsp + P) * 2 : 0;
+    const uint32_t bytes = left ? ((left - 1) * rsp + PC) * 2 : 0;
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb + (int64_t)first * rsp, bytes);
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
       const int pc = tid + NTHR * i;
-      if (pc < 128)
-        qr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ((pc >> 2) * rsp + 8 * (pc & 3)) * 2, 0, 0));
+      if (pc < QI)
+        qr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ((pc >> (S2 ? 3 : 2)) * rsp + 8 * (pc & (QE - 1))) * 2, 0, 0));
     }
   }
   template <bool LO>
@@ -456,8 +468,8 @@ struct QStage {
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
       const int pc = tid + NTHR * i;
-      if (pc >= 128) continue;
-      const int row = r0 + (pc >> 2), e4 = pc & 3;
+      if (pc >= QI) continue;
+      const int row = r0 + (pc >> (S2 ? 3 : 2)), e4 = pc & (QE - 1);
       float x[8];
       float ss = 0.f;
 #pragma unroll
@@ -466,7 +478,7 @@ struct QStage {
         x[2 * e + 1] = __uint_as_float(qr[i][e] & 0xffff0000u);
         ss += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
       }
-      ss = group_sum<4>(ss);
+      ss = group_sum<QE>(ss);
       const float inv = inv_norm_fast(ss) * LAMBDA;
       h2_t hv[4];
 #pragma unroll
@@ -494,9 +506,12 @@ struct QStage {
 // DBL: tiles 1-17 take the own operand doubled (one packed add per step, shared by the
 // wave's tiles), which folds c^2 = 2 of the off-diagonal coordinates into the build; without
 // it the caller applies the factor to the result.
-template <int DV, int C, int NU_W, int UB, bool DBL>
+// S2: the lift is summed over the two 32-component blocks of a key: psi = own_1 partner_1 +
+// own_2 partner_2, the second block's rows 32 rows (a constant offset) further on.
+template <int DV, int C, int NU_W, int UB, bool DBL, bool S2 = false>
 __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const char* lds, int off_kt, int off_vt) {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
+  constexpr uint32_t KO = L::KOFF;
   constexpr int NDV = L::NDV, HALF = UB % 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
   const uint32_t base = lds_addr(lds);
@@ -521,7 +536,7 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
     // Left to itself, the scheduler issues each partner read after the previous tile's
     // MFMAs and waits for it at once. The summary pass (more registers free) issues all of a
     // step's reads before its first product; the segment pass keeps one partner read ahead.
-    if constexpr (!DBL) {
+    if constexpr (!DBL && !S2) {
       const h8_t ko = ld8a(own ^ so);
       h8_t pt[NU_W], vf[NDV];
 #pragma unroll
@@ -535,7 +550,7 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
 #pragma unroll
         for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
       }
-    } else {
+    } else if constexpr (!S2) {
       const h8_t ko = ld8a(own ^ so);
       h8_t vf[NDV];
 #pragma unroll
@@ -551,14 +566,35 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
 #pragma unroll
         for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
       }
+    } else {  // S2, one partner pair read ahead in both passes
+      const h8_t ka = ld8a(own ^ so), kb = ld8a((own ^ so) + KO);
+      h8_t vf[NDV];
+#pragma unroll
+      for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
+      h8_t pa = ld8a(part[0] ^ so), pb = ld8a((part[0] ^ so) + KO);
+      __builtin_amdgcn_sched_barrier(0);
+      const h8_t ka2 = DBL ? ka + ka : ka, kb2 = DBL ? kb + kb : kb;
+#pragma unroll
+      for (int u = 0; u < NU_W; ++u) {
+        const bool diag = (UB + 2 * u) / 2 == 0;
+        const h8_t psi = (diag ? ka : ka2) * pa + (diag ? kb : kb2) * pb;
+        if (u + 1 < NU_W) {
+          pa = ld8a(part[u + 1] ^ so);
+          pb = ld8a((part[u + 1] ^ so) + KO);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
+      }
     }
   }
 }
 
 // Gram blocks M_ab = K_a^T K_b (components 16a.., 16b..) of one chunk, a, b in {0, 1}
-template <int DV, int C>
+// (S2: summed over the two 32-component blocks of the keys)
+template <int DV, int C, bool S2 = false>
 __device__ __forceinline__ void gram_chunk(acc4_t (&Mg)[4], const char* lds, int off_kt) {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
   const uint32_t base = lds_addr(lds);
   const uint32_t o0 = base + (uint32_t)(off_kt + L::tpos(m, 8 * g));
@@ -566,11 +602,14 @@ __device__ __forceinline__ void gram_chunk(acc4_t (&Mg)[4], const char* lds, int
 #pragma unroll 1
   for (int st = 0; st < L::NS; ++st) {
     const uint32_t so = 64 * st;
-    const h8_t olo = ld8a(o0 ^ so), ohi = ld8a(o1 ^ so);
-    Mg[0] = mfma16(olo, olo, Mg[0]);
-    Mg[1] = mfma16(olo, ohi, Mg[1]);
-    Mg[2] = mfma16(ohi, olo, Mg[2]);
-    Mg[3] = mfma16(ohi, ohi, Mg[3]);
+#pragma unroll
+    for (int blk = 0; blk < (S2 ? 2 : 1); ++blk) {
+      const h8_t olo = ld8a((o0 ^ so) + blk * L::KOFF), ohi = ld8a((o1 ^ so) + blk * L::KOFF);
+      Mg[0] = mfma16(olo, olo, Mg[0]);
+      Mg[1] = mfma16(olo, ohi, Mg[1]);
+      Mg[2] = mfma16(ohi, olo, Mg[2]);
+      Mg[3] = mfma16(ohi, ohi, Mg[3]);
+    }
   }
 }
 
@@ -598,9 +637,9 @@ __device__ __forceinline__ void write_state(const acc4_t (&S)[NU_W][DV / 16], ch
 // Gram matrix to LDS as fp16 hi + lo of M 2^-ge. Row r holds the denominator operand's
 // k-slots (components 16s + 8(e/4) + 4h + e%4 at position 16s + 8h + e: bits 2 and 3 of
 // the column swapped); by symmetry block (a, b) writes rows 16b + n, columns 16a + 4g + j.
-template <int DV, int C>
+template <int DV, int C, bool S2 = false>
 __device__ __forceinline__ void write_gram(const acc4_t (&Mg)[4], char* lds, int ge) {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int gs = ((g & 1) << 1) | (g >> 1);
   const float sc = pow2f(-ge);
@@ -656,26 +695,32 @@ __device__ __forceinline__ void write_final_z(const Args& a, int64_t bh, const a
 
 // ---- readout wave: token group G, tiles [TB, TE); OWNER also runs the intra block, the
 // denominator and the output; wave 0 also accumulates the Gram blocks of the denominator
-template <int DV, int C, int W>
+template <int DV, int C, int W, bool S2 = false>
 struct Reader {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   static constexpr int NDT = L::NDT;
   static constexpr int G = W / L::FS, F = W % L::FS;
   static constexpr int TB = L::rb(F), TE = L::rb(F + 1);
   static constexpr bool OWNER = F == L::FS - 1;
   static constexpr bool GRAM = W == 0;
 
-  // psi'(q) slots of quad a (lower-half view) for tile T: (c0, c1) and (c2, c3)
+  // psi'(q) slots of quad a (lower-half view) for tile T: (c0, c1) and (c2, c3); S2: the
+  // sum of both blocks' products (second block in R[16..31])
   template <int T, int A>
-  __device__ static __forceinline__ void quad_slots(const h2_t (&R)[16], h2_t& p01, h2_t& p23) {
+  __device__ static __forceinline__ void quad_slots(const h2_t (&R)[S2 ? 32 : 16], h2_t& p01, h2_t& p23) {
     constexpr int B = tile_partner(T, A), r = tile_xor(T, A);
     const h2_t x01 = R[2 * B + (r >> 1)], x23 = R[2 * B + 1 - (r >> 1)];
     p01 = R[2 * A] * ((r & 1) ? swp(x01) : x01);
     p23 = R[2 * A + 1] * ((r & 1) ? swp(x23) : x23);
+    if constexpr (S2) {
+      const h2_t y01 = R[16 + 2 * B + (r >> 1)], y23 = R[16 + 2 * B + 1 - (r >> 1)];
+      p01 = R[16 + 2 * A] * ((r & 1) ? swp(y01) : y01) + p01;
+      p23 = R[16 + 2 * A + 1] * ((r & 1) ? swp(y23) : y23) + p23;
+    }
   }
 
   __device__ static __forceinline__ void run(const Args& a, char* lds) {
-    const int lane = threadIdx.x & 63, t = lane & 31, h = lane >> 5;
+    const int lane = threadIdx.x & 63, t_lane = lane & 31, h_lane = lane >> 5;
     const int64_t bh = blockIdx.x / a.nblk_per_bh;
     const int seg = blockIdx.x % a.nblk_per_bh;
     int64_t row0;
@@ -687,9 +732,6 @@ struct Reader {
     char* obase = static_cast<char*>(a.o) + row0 * DV * osz;
     const uint32_t orsv = (uint32_t)rstep * DV;
     const uint32_t* red = reinterpret_cast<const uint32_t*>(lds + L::OFF_RED);
-    // this lane's state fragment: readout lane (value row t, half h) reads quads h and h + 2
-    // of build tile u, value tile 2 dt + t / 16, as one 16-byte piece
-    const uint32_t fbase = (uint32_t)((t >> 4) * 512 + h * 256 + (t & 15) * 16);
 
     acc4_t Mg[4] = {zero4a(), zero4a(), zero4a(), zero4a()};
     if constexpr (GRAM) {
@@ -702,7 +744,7 @@ struct Reader {
         }
       }
     }
-    QStage<DV, C, 64 * L::FS> qs;
+    QStage<DV, C, 64 * L::FS, S2> qs;
     qs.init(a.q, row0, rstep, Tb);
     const int qtid = F * 64 + lane;
     if (c0 < c1) qs.load(c0 * C, 32 * G, qtid);
@@ -723,26 +765,37 @@ struct Reader {
     if (c0 < c1) {
       if (c0 == 0) qs.template store<true>(lds, L::offq(0), 32 * G, qtid);
       else qs.template store<false>(lds, L::offq(0), 32 * G, qtid);
-      if (c0 + 1 < c1) qs.load((c0 + 1) * C, 32 * G, qtid);
+      if constexpr (L::NBUF == 2)
+        if (c0 + 1 < c1) qs.load((c0 + 1) * C, 32 * G, qtid);
       if constexpr (GRAM)
-        if (c0 > 0) write_gram<DV, C>(Mg, lds, gram_exp(c0 * C));
+        if (c0 > 0) write_gram<DV, C, S2>(Mg, lds, gram_exp(c0 * C));
     }
     __syncthreads();  // prologue 2: chunk c0 staged, state before it in LDS
 
     for (int c = c0; c < c1; ++c) {
       const int t0 = c * C, buf = (c - c0) & 1;
+      // token row t of the group and lane half h (S2: opaque per chunk, so that the many
+      // operand addresses derived from them are formed in the chunk, not held across it)
+      int t = t_lane, h = h_lane;
+      if constexpr (S2) asm volatile("" : "+v"(t), "+v"(h));
+      // this lane's state fragment: readout lane (value row t, half h) reads quads h and h + 2
+      // of build tile u, value tile 2 dt + t / 16, as one 16-byte piece
+      const uint32_t fbase = (uint32_t)((t >> 4) * 512 + h * 256 + (t & 15) * 16);
       // ---- phase 1: queries of chunk c + 1 into the other buffer (loaded during the previous
-      // chunk), readout of chunk c, loads of chunk c + 2
-      if (c + 1 < c1) qs.template store<false>(lds, L::offq(buf ^ 1), 32 * G, qtid);
-      h2_t R[16];
+      // chunk), readout of chunk c, loads of chunk c + 2 (single buffer: both in phase 2)
+      if constexpr (L::NBUF == 2)
+        if (c + 1 < c1) qs.template store<false>(lds, L::offq(buf ^ 1), 32 * G, qtid);
+      h2_t R[S2 ? 32 : 16];
       {
         const char* qrow = lds + L::offq(buf) + (32 * G + t) * L::QPB;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const h4_t x = ld4(qrow + 8 * ((b + h) & 7));
-          R[2 * b] = lo2(x);
-          R[2 * b + 1] = hi2(x);
-        }
+        for (int blk = 0; blk < (S2 ? 2 : 1); ++blk)
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const h4_t x = ld4(qrow + 64 * blk + 8 * ((b + h) & 7));
+            R[16 * blk + 2 * b] = lo2(x);
+            R[16 * blk + 2 * b + 1] = hi2(x);
+          }
       }
       acc_t O[NDT];
 #pragma unroll
@@ -776,47 +829,88 @@ struct Reader {
            ...);
         }(std::make_integer_sequence<int, NP>{});
       }
-      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, L::offkt(buf));
+      if constexpr (GRAM) gram_chunk<DV, C, S2>(Mg, lds, L::offkt(buf));
       float den = 0.f;
       if constexpr (OWNER) {
-        // query operand of the component contractions: k-slots 16s + 8(e/4) + 4h + e%4
-        const h8_t qop[2] = {cat4(R[0], R[1], R[4], R[5]), cat4(R[8], R[9], R[12], R[13])};
-        if (c > 0) {  // denominator, inter-chunk part: X = (M 2^-ge) Q^T, then q . X
-          acc_t X = zero_acc();
+        // query operand of the component contractions: k-slots 16s + 8(e/4) + 4h + e%4 of
+        // block blk (S2: two blocks)
+        constexpr int NB = S2 ? 2 : 1;
+        h8_t qop[NB][2];
+        if constexpr (S2) {  // read again from the query rows: R is not kept past the readout
+          const char* qrow = lds + L::offq(buf) + (32 * G + t) * L::QPB;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const char* mrow = lds + L::OFF_M + t * L::MPB + 2 * (16 * s + 8 * h);
-            X = mfma(ld8(mrow), qop[s], X);
-            X = mfma(ld8(mrow + 32 * L::MPB), qop[s], X);
-          }
+          for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              qop[blk][s] = cat44(ld4(qrow + 64 * blk + 8 * (4 * s + h)), ld4(qrow + 64 * blk + 8 * (4 * s + 2 + h)));
+        } else {
+          qop[0][0] = cat4(R[0], R[1], R[4], R[5]);
+          qop[0][1] = cat4(R[8], R[9], R[12], R[13]);
+        }
+        if (c > 0) {  // denominator, inter-chunk part: X = (M 2^-ge) Q^T, then q . X (per block)
           float dx = 0.f;
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
+          for (int blk = 0; blk < NB; ++blk) {
+            acc_t X = zero_acc();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dx += X[4 * ii + j] * (float)R[4 * ii + j / 2][j & 1];
+            for (int s = 0; s < 2; ++s) {
+              const char* mrow = lds + L::OFF_M + t * L::MPB + 2 * (16 * s + 8 * h);
+              X = mfma(ld8(mrow), qop[blk][s], X);
+              X = mfma(ld8(mrow + 32 * L::MPB), qop[blk][s], X);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                dx += X[4 * ii + j] * (S2 ? (float)qop[blk][ii >> 1][4 * (ii & 1) + j] : (float)R[16 * blk + 4 * ii + j / 2][j & 1]);
+          }
           den = dx * pow2f(gram_exp(t0));
         }
         // intra-chunk block over key groups 0..G
         auto intra = [&]<bool SPLIT>() {
-          h8_t qlo[2];
+          h8_t qlo[NB][2];
           if constexpr (SPLIT) {
             const char* lrow = lds + L::OFF_QLO + (32 * G + t) * L::QPB;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) qlo[s] = cat44(ld4(lrow + 8 * (4 * s + h)), ld4(lrow + 8 * (4 * s + 2 + h)));
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+              for (int s = 0; s < 2; ++s)
+                qlo[blk][s] = cat44(ld4(lrow + 64 * blk + 8 * (4 * s + h)), ld4(lrow + 64 * blk + 8 * (4 * s + 2 + h)));
           }
 #pragma unroll
           for (int kg = 0; kg <= G; ++kg) {
-            acc_t Sc = zero_acc();
             const char* krow = lds + L::offkr(buf);
             const int kr = 32 * kg + t;
+            // scores of the block pairs (query block qa, key block kb); S2: the weight sums
+            // the squares of all four (sq)
+            auto score = [&](int qa, int kb) {
+              // S2: one block pair's operand reads at a time (hoisted over all pairs and key
+              // groups they would not fit the registers)
+              if constexpr (S2) __builtin_amdgcn_sched_barrier(0);
+              acc_t Sc = zero_acc();
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const h8_t kop = cat44(ld4(krow + L::krpos(kr, 4 * s + h)), ld4(krow + L::krpos(kr, 4 * s + 2 + h)));
-              Sc = mfma(kop, qop[s], Sc);
-              if constexpr (SPLIT) {
-                const char* lrow = lds + L::OFF_KLO;
-                Sc = mfma(cat44(ld4(lrow + L::krpos(kr, 4 * s + h)), ld4(lrow + L::krpos(kr, 4 * s + 2 + h))), qop[s], Sc);
-                Sc = mfma(kop, qlo[s], Sc);
+              for (int s = 0; s < 2; ++s) {
+                const h8_t kop = cat44(ld4(krow + L::krpos(kr, 8 * kb + 4 * s + h)), ld4(krow + L::krpos(kr, 8 * kb + 4 * s + 2 + h)));
+                Sc = mfma(kop, qop[qa][s], Sc);
+                if constexpr (SPLIT) {
+                  const char* lrow = lds + L::OFF_KLO;
+                  Sc = mfma(cat44(ld4(lrow + L::krpos(kr, 8 * kb + 4 * s + h)), ld4(lrow + L::krpos(kr, 8 * kb + 4 * s + 2 + h))),
+                            qop[qa][s], Sc);
+                  Sc = mfma(kop, qlo[qa][s], Sc);
+                }
+              }
+              return Sc;
+            };
+            const acc_t Sc = score(0, 0);
+            float sq[S2 ? 16 : 1];
+            if constexpr (S2) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) sq[e] = Sc[e] * Sc[e];
+#pragma unroll
+              for (int pr = 1; pr < 4; ++pr) {
+                const acc_t Sp = score(pr >> 1, pr & 1);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sq[e] += Sp[e] * Sp[e];
               }
             }
             // weights: keys 8ii + 4h + j of group kg for query t; causal on the diagonal group
@@ -825,8 +919,8 @@ struct Reader {
             for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
               for (int j = 0; j < 4; j += 2) {
-                float w0 = Sc[4 * ii + j] * Sc[4 * ii + j];
-                float w1 = Sc[4 * ii + j + 1] * Sc[4 * ii + j + 1];
+                float w0 = S2 ? sq[(4 * ii + j) % (S2 ? 16 : 1)] : Sc[4 * ii + j] * Sc[4 * ii + j];
+                float w1 = S2 ? sq[(4 * ii + j + 1) % (S2 ? 16 : 1)] : Sc[4 * ii + j + 1] * Sc[4 * ii + j + 1];
                 if (kg == G) {
                   if (8 * ii + 4 * h + j > t) w0 = 0.f;
                   if (8 * ii + 4 * h + j + 1 > t) w1 = 0.f;
@@ -850,7 +944,11 @@ struct Reader {
         else intra.template operator()<false>();
         den = xor32_sum(den);
       }
-      if (c + 2 < c1) qs.load(t0 + 2 * C, 32 * G, qtid);
+      if constexpr (L::NBUF == 2) {
+        if (c + 2 < c1) qs.load(t0 + 2 * C, 32 * G, qtid);
+      } else {  // single buffer: chunk c + 1's queries, staged after the barrier
+        if (c + 1 < c1) qs.load(t0 + C, 32 * G, qtid);
+      }
       if constexpr (!OWNER) {  // hand the partial readout to the owner of this group
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -902,8 +1000,10 @@ struct Reader {
         for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + 8 * ((c + 1) & 1) + w]);
         beta += (float)C * __uint_as_float(vb << 16);
         e_sig = scale_exp(beta, e_sig);
-        if constexpr (GRAM) write_gram<DV, C>(Mg, lds, gram_exp(t0 + C));
+        if constexpr (GRAM) write_gram<DV, C, S2>(Mg, lds, gram_exp(t0 + C));
       }
+      if constexpr (L::NBUF == 1)  // queries of chunk c + 1 (every wave is past chunk c's)
+        if (c + 1 < c1) qs.template store<false>(lds, L::offq(0), 32 * G, qtid);
       __syncthreads();
     }
     if constexpr (GRAM)
@@ -913,9 +1013,9 @@ struct Reader {
 
 // ---- build wave j of the forward (tiles Fwd8::ub(j) .. ub(j + 1)), which also stages the
 // keys and values of the next chunk
-template <int DV, int C, int J>
+template <int DV, int C, int J, bool S2 = false>
 struct Builder {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   static constexpr int NDV = L::NDV;
   static constexpr int UB = Fwd8::first(J), NU_W = Fwd8::cnt(J);
 
@@ -949,7 +1049,7 @@ struct Builder {
           for (int e = 0; e < 4; ++e) pmax = fmaxf(pmax, fabsf(x[e]));
         }
     }
-    KVStage<DV, C, 512> kv;
+    KVStage<DV, C, 512, S2> kv;
     kv.init(a.k, a.v, row0, rstep, Tb);
     if (c0 < c1) kv.load(c0 * C, btid);
     auto publish = [&](int chunk) {  // max |v| of the loaded chunk, slot set chunk & 1
@@ -999,6 +1099,36 @@ struct Builder {
     }
     __syncthreads();  // prologue 2
 
+    if constexpr (L::NBUF == 1) {
+      // single buffer: phase 1 = value maximum of chunk c + 1 (in registers since phase 2 of
+      // chunk c - 1; chunk c0 + 1's went out in the prologue), build of chunk c | barrier |
+      // phase 2 = state after chunk c (scaled for c + 1), keys and values of c + 1, loads of
+      // c + 2 | barrier
+      for (int c = c0; c < c1; ++c) {
+        if (c > c0 && c + 1 < c1) publish(c + 1);
+        build_chunk<DV, C, NU_W, UB, true, S2>(S, lds, L::offkt(0), L::offvt(0));
+        __syncthreads();
+        if (c + 1 < c1) {
+          uint32_t vb = 0;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) vb = max(vb, red[8 + 8 * ((c + 1) & 1) + w]);
+          beta += (float)C * __uint_as_float(vb << 16);
+          const int e_next = scale_exp(beta, e_sig);
+          if (e_next != e_sig) {
+            const float f = pow2f(e_next - e_sig);
+#pragma unroll
+            for (int u = 0; u < NU_W; ++u)
+#pragma unroll
+              for (int dv = 0; dv < NDV; ++dv) S[u][dv] *= f;
+            e_sig = e_next;
+          }
+          write_state<DV, C, NU_W, UB>(S, lds);
+          kv.template store<false>(lds, target(0, 0), pow2f(e_sig), btid);
+          if (c + 2 < c1) kv.load((c + 2) * C, btid);
+        }
+        __syncthreads();
+      }
+    } else
     for (int c = c0; c < c1; ++c) {
       const int buf = (c - c0) & 1;
       // ---- phase 1: keys and values of chunk c + 1 into the other buffers (scaled for chunk
@@ -1041,9 +1171,9 @@ struct Builder {
 // oldest waves of their SIMDs, whose instructions win the issue arbitration, so the staging
 // is not left waiting behind the builds. Waves 4-11 build (tiles of Fwd8, one build pair per
 // SIMD) and wave 4 also forms the Gram matrix. One barrier per chunk.
-template <int DV, int C, int J>
+template <int DV, int C, int J, bool S2 = false>
 __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   constexpr int NDV = L::NDV;
   constexpr bool STAGER = J < 4;
   constexpr int JB = STAGER ? 0 : J - 4;
@@ -1060,7 +1190,7 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   const int c0 = seg * a.cps, c1 = min(nchunks, c0 + a.cps);
   uint32_t* red = reinterpret_cast<uint32_t*>(lds + L::SUM_RED);  // [2 parities][4 staging waves]
 
-  KVStage<DV, C, 256> kv;
+  KVStage<DV, C, 256, S2> kv;
   auto publish = [&](int chunk) {  // max |v| of the loaded chunk into slot set chunk & 1
     const uint32_t vm = wave_max_u32(kv.vmax_bits(stid));
     if (lane == 0) red[4 * (chunk & 1) + J] = vm;
@@ -1072,7 +1202,7 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   };
   auto target = [&](int buf) {
     const int b = buf * L::SUM_BUF;
-    return KVTarget{-1, b, -1, b + 32 * L::RPB, 0};
+    return KVTarget{-1, b, -1, b + L::PC * L::RPB, 0};
   };
   if constexpr (STAGER) {
     kv.init(a.k, a.v, row0, rstep, Tb);
@@ -1118,8 +1248,8 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
     acc4_t Mg[4] = {zero4a(), zero4a(), zero4a(), zero4a()};
     for (int c = c0; c < c1; ++c) {
       const KVTarget tg = target((c - c0) & 1);
-      build_chunk<DV, C, NU_W, UB, false>(S, lds, tg.kt, tg.vt);
-      if constexpr (GRAM) gram_chunk<DV, C>(Mg, lds, tg.kt);
+      build_chunk<DV, C, NU_W, UB, false, S2>(S, lds, tg.kt, tg.vt);
+      if constexpr (GRAM) gram_chunk<DV, C, S2>(Mg, lds, tg.kt);
       if (c + 1 < c1) {
         beta += (float)C * vmax_of(c + 1);
         const int e_new = scale_exp(beta, e_sig);
@@ -1155,41 +1285,41 @@ __device__ __forceinline__ void run_summary(const Args& a, char* lds) {
   }
 }
 
-template <int DV, int C>
+template <int DV, int C, bool S2 = false>
 __global__ __launch_bounds__(768, 1) void summary_f16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
-    case 0: run_summary<DV, C, 0>(a, lds); break;
-    case 1: run_summary<DV, C, 1>(a, lds); break;
-    case 2: run_summary<DV, C, 2>(a, lds); break;
-    case 3: run_summary<DV, C, 3>(a, lds); break;
-    case 4: run_summary<DV, C, 4>(a, lds); break;
-    case 5: run_summary<DV, C, 5>(a, lds); break;
-    case 6: run_summary<DV, C, 6>(a, lds); break;
-    case 7: run_summary<DV, C, 7>(a, lds); break;
-    case 8: run_summary<DV, C, 8>(a, lds); break;
-    case 9: run_summary<DV, C, 9>(a, lds); break;
-    case 10: run_summary<DV, C, 10>(a, lds); break;
-    default: run_summary<DV, C, 11>(a, lds); break;
+    case 0: run_summary<DV, C, 0, S2>(a, lds); break;
+    case 1: run_summary<DV, C, 1, S2>(a, lds); break;
+    case 2: run_summary<DV, C, 2, S2>(a, lds); break;
+    case 3: run_summary<DV, C, 3, S2>(a, lds); break;
+    case 4: run_summary<DV, C, 4, S2>(a, lds); break;
+    case 5: run_summary<DV, C, 5, S2>(a, lds); break;
+    case 6: run_summary<DV, C, 6, S2>(a, lds); break;
+    case 7: run_summary<DV, C, 7, S2>(a, lds); break;
+    case 8: run_summary<DV, C, 8, S2>(a, lds); break;
+    case 9: run_summary<DV, C, 9, S2>(a, lds); break;
+    case 10: run_summary<DV, C, 10, S2>(a, lds); break;
+    default: run_summary<DV, C, 11, S2>(a, lds); break;
   }
 }
 
-template <int DV, int C>
+template <int DV, int C, bool S2 = false>
 __global__ __launch_bounds__(768, 1) void chunked_f16_kernel(Args a) {
   extern __shared__ __align__(16) char lds[];
   switch (threadIdx.x >> 6) {
-    case 0: Reader<DV, C, 0>::run(a, lds); break;
-    case 1: Reader<DV, C, 1>::run(a, lds); break;
-    case 2: Reader<DV, C, 2>::run(a, lds); break;
-    case 3: Reader<DV, C, 3>::run(a, lds); break;
-    case 4: Builder<DV, C, 0>::run(a, lds); break;
-    case 5: Builder<DV, C, 1>::run(a, lds); break;
-    case 6: Builder<DV, C, 2>::run(a, lds); break;
-    case 7: Builder<DV, C, 3>::run(a, lds); break;
-    case 8: Builder<DV, C, 4>::run(a, lds); break;
-    case 9: Builder<DV, C, 5>::run(a, lds); break;
-    case 10: Builder<DV, C, 6>::run(a, lds); break;
-    default: Builder<DV, C, 7>::run(a, lds); break;
+    case 0: Reader<DV, C, 0, S2>::run(a, lds); break;
+    case 1: Reader<DV, C, 1, S2>::run(a, lds); break;
+    case 2: Reader<DV, C, 2, S2>::run(a, lds); break;
+    case 3: Reader<DV, C, 3, S2>::run(a, lds); break;
+    case 4: Builder<DV, C, 0, S2>::run(a, lds); break;
+    case 5: Builder<DV, C, 1, S2>::run(a, lds); break;
+    case 6: Builder<DV, C, 2, S2>::run(a, lds); break;
+    case 7: Builder<DV, C, 3, S2>::run(a, lds); break;
+    case 8: Builder<DV, C, 4, S2>::run(a, lds); break;
+    case 9: Builder<DV, C, 5, S2>::run(a, lds); break;
+    case 10: Builder<DV, C, 6, S2>::run(a, lds); break;
+    default: Builder<DV, C, 7, S2>::run(a, lds); break;
   }
 }
 
@@ -1197,17 +1327,17 @@ __global__ __launch_bounds__(768, 1) void chunked_f16_kernel(Args a) {
 
 namespace c16 {
 
-template <int DV, int C>
+template <int DV, int C, bool S2 = false>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16, int B, int H, int T,
                   const SegPlan& plan, float* ws, float* s_out, float* z_out, SeqLayout lay, int passes,
                   hipStream_t st) {
-  using L = Lay<DV, C>;
+  using L = Lay<DV, C, S2>;
   const int BH = B * H;
   Args a{q, k, v, o, ws, T, plan.nseg, plan.cps, 0, o_bf16 ? 0 : 1, s_out, z_out, lay, H};
   hipError_t e;
   if (plan.nseg > 1 && (passes & PASS_SUMMARIES)) {
     a.nblk_per_bh = plan.nseg - 1;
-    auto ks = summary_f16_kernel<DV, C>;
+    auto ks = summary_f16_kernel<DV, C, S2>;
     if ((e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, L::SUM_LDS)) != hipSuccess)
       return e;
     ks<<<dim3((unsigned)(BH * (plan.nseg - 1))), dim3(768), L::SUM_LDS, st>>>(a);
@@ -1216,7 +1346,7 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, void*
   if (plan.nseg > 1 && (passes & PASS_SCAN))
     if ((e = launch_scan(ws, BH, plan.nseg - 1, L::STATE_FLOATS, st)) != hipSuccess) return e;
   if (!(passes & PASS_SEGMENTS)) return hipSuccess;
-  auto kf = chunked_f16_kernel<DV, C>;
+  auto kf = chunked_f16_kernel<DV, C, S2>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS)) != hipSuccess) return e;
   a.nblk_per_bh = plan.nseg;
   kf<<<dim3((unsigned)(BH * plan.nseg)), dim3(768), L::LDS, st>>>(a);

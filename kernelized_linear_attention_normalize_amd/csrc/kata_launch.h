@@ -64,6 +64,12 @@ int64_t f16_state_floats(int dv);
 hipError_t launch_chunked_f16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16, int B,
                               int H, int T, int p, int dv, int C, const SegPlan& plan, float* ws, float* s_out,
                               float* z_out, SeqLayout lay, int passes, hipStream_t st);
+// the same kernels for KATA-Sigma 2 at p = 64 (dv = 64, C in {64, 128}); segment summaries of
+// f16_state_floats(dv) floats, plan over T
+bool chunked_f16_s2_supported(int dv, int C);
+hipError_t launch_chunked_f16_s2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, bool o_bf16, int B,
+                                 int H, int T, int dv, int C, const SegPlan& plan, float* ws, float* s_out,
+                                 float* z_out, SeqLayout lay, hipStream_t st);
 hipError_t launch_chunked_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                bool o_bf16, int B, int H, int T, int p, int dv, int C,
                                const SegPlan& plan, float* ws, float* s_out, float* z_out,
