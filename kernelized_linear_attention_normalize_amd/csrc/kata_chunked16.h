@@ -61,6 +61,13 @@
 // barrier | phase 2 = output, state after chunk c to LDS | barrier. ASSOCIATIVE runs a
 // summary pass (8 build waves and 4 staging waves over a double buffer, one barrier per
 // chunk), the segment scan and the segments; SEQUENTIAL runs one segment per sequence.
+//
+// S2 (KATA-Sigma 2, reduced PSD families paragraph of the HTML page: psi(u) = u_1 u_1^T +
+// u_2 u_2^T over two 32-component blocks of a 64-component row, normalised as a whole): the
+// same tiles, state and scales, with every lifted coordinate the sum of both blocks'
+// products, intra-chunk weights sum_{a,b} (q_a . k_b)^2 and the Gram matrix summed over the
+// blocks. Its operands take twice the rows, so the chunk operands are single-buffered and
+// the next chunk is staged in phase 2.
 #pragma once
 #include <utility>
 

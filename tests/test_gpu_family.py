@@ -75,9 +75,9 @@ def test_family_chunked_many_segments_and_state():
 
 @pytest.mark.parametrize("dv,C,T", [(64, 128, 700), (32, 64, 1000), (64, 64, 333), (32, 128, 129)])
 def test_sigma2_p64_mfma_chunked(dv, C, T):
-    """KATA-Sigma 2 at p = 64 with bf16 inputs: the MFMA kernels over 2T virtual rows (two
-    32-component blocks per token, the key norm over both, token-level causality, the two
-    virtual query rows of a token summed before the division); both scans, ragged T."""
+    """KATA-Sigma 2 at p = 64 with bf16 inputs on the MFMA kernels: dv = 64 on the fp16
+    kernels with the two-block lift, dv = 32 over 2T virtual rows (two 32-component blocks
+    per token, the key norm over both, token-level causality); both scans, ragged T."""
     q, k, v = _case("sigma2-mfma", 46, 2, 3, T, 64, dv, "bf16")
     q[0, 2, 4] = 0.0
     k[1, 1, :2] = 0.0
