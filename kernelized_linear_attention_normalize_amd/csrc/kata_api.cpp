@@ -199,6 +199,7 @@ static bool sigma2_f16(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t 
 static bool chunked_supported(int p, int dv, int C, kata_dtype_t in_dt, kata_feature_t fam, int g,
                               bool packed = false) {
   if (!in_set(C, {32, 64, 128})) return false;
+  if (sigma2_f16(p, dv, C, in_dt, fam, g)) return true;  // padded, ragged or packed
   if (!packed && sigma2_mfma(p, dv, C, in_dt, fam, g)) return true;
   if (fam == KATA_FEAT_FULL) {
     if (!in_set(p, {16, 32}) || !in_set(dv, {16, 32, 64})) return false;
@@ -255,7 +256,7 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   // the kernels address one sequence's rows (H rows apart when packed) with 32-bit byte offsets
   if (packed && (int64_t)T * H * (p > dv ? p : dv) * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
   if ((s = check_fwd_alias(q, k, v, in_dt, o, o_dt, rows, p, dv)) != KATA_OK) return s;
-  const bool s2f = cu == nullptr && sigma2_f16(p, dv, C, in_dt, fam, g);
+  const bool s2f = sigma2_f16(p, dv, C, in_dt, fam, g);
   const bool s2 = cu == nullptr && !s2f && sigma2_mfma(p, dv, C, in_dt, fam, g);  // virtual rows
   if (s2 && (int64_t)T * 2 > INT32_MAX) return KATA_ERR_SHAPE;
   const kata::SegPlan plan = kata::seg_plan(B, H, s2 ? 2 * T : T, C, scan);
@@ -287,7 +288,7 @@ static kata_status_t chunked_impl(const void* q, const void* k, const void* v, k
   if (s2f)
     return hip_status(kata::launch_chunked_f16_s2(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                   static_cast<const uint16_t*>(v), o, ob16, B, H, T, dv, C, plan, ws,
-                                                  so, zo, kata::SeqLayout{lens, nullptr, 0}, st));
+                                                  so, zo, kata::SeqLayout{lens, cu, total}, st));
   if (s2)
     return hip_status(kata::launch_chunked_bf16_sigma2(static_cast<const uint16_t*>(q),
                                                        static_cast<const uint16_t*>(k),

@@ -207,9 +207,10 @@ def test_varlen_validation(lib):
     assert vl(g=3, fam=SIGMA) == E_FEAT
     assert vl(total=0) == OK and vl(max_len=0) == OK and vl(B=0) == OK   # nothing to do
     assert vl(dv=48) == E_UNSUP
-    # the Sigma 2 MFMA path takes the padded layout only; the VALU family kernel's LDS does
-    # not fit this shape
-    assert vl(fam=SIGMA, g=2, p=64, dv=64, C=128) == E_UNSUP
+    # Sigma 2 at p = 64, dv = 64 takes the packed layout on the two-block fp16 kernels: the
+    # call gets as far as its (missing) segment-summary workspace
+    assert vl(fam=SIGMA, g=2, p=64, dv=64, C=128, scan=ASSOC, max_len=200 * 64) == E_WS
+    assert vl(fam=SIGMA, g=2, p=64, dv=48, C=128) == E_UNSUP
     # 32-bit offsets of one packed sequence: max_len * H * max(p, dv) * 4 must stay below 2^31
     assert vl(H=1024, max_len=1 << 14, total=1 << 14) == E_SHAPE
     # the associative scan's workspace is that of the padded call with T = max_len

@@ -61,7 +61,8 @@ def _pack(x, lens):
 @pytest.mark.parametrize("dt,family,p,g,dv,C,scan", [
     ("bf16", "full", 32, 1, 64, 128, "associative"), ("bf16", "full", 32, 1, 64, 64, "sequential"),
     ("bf16", "full", 16, 1, 32, 32, "associative"), ("f32", "full", 16, 1, 32, 64, "associative"),
-    ("bf16", "sigma", 32, 2, 32, 64, "associative"), ("f32", "block", 16, 2, 16, 32, "sequential")])
+    ("bf16", "sigma", 32, 2, 32, 64, "associative"), ("f32", "block", 16, 2, 16, 32, "sequential"),
+    ("bf16", "sigma", 64, 2, 64, 128, "associative")])
 def test_varlen_packed(dt, family, p, g, dv, C, scan):
     """Token-major packed sequences (kata_chunked_fwd_varlen): each sequence against the oracle
     run on it alone, the state after its last token, rows outside every sequence untouched, and
