@@ -291,9 +291,11 @@ kata_status_t kata_chunked_fwd_ragged(const void* q, const void* k, const void* 
  * T = max_len (kata_chunked_workspace_bytes_family(B, H, max_len, ...)). With S, Z (both or
  * neither) the state after each sequence's last token is written, [B, H, n, dv] and
  * [B, H, n] as for kata_chunked_fwd_state (zero for an empty sequence). Rows outside every
- * sequence are not written. The KATA-Sigma 2 MFMA path takes the padded layout only, so
- * Sigma 2 at p = 64 runs here on the VALU family kernel where its LDS fits (else
- * KATA_ERR_UNSUPPORTED). Each sequence's result equals the padded call on that sequence
+ * sequence are not written. bf16 KATA-Sigma 2 at p = 64, dv = 64, C in {64, 128} runs the
+ * fp16 two-block kernels here as in the padded call; the virtual-row MFMA path of the other
+ * bf16 Sigma 2 shapes takes the padded layout only, so those run here on the VALU family
+ * kernel where its LDS fits (else KATA_ERR_UNSUPPORTED). Each sequence's result equals the
+ * padded call on that sequence
  * alone (up to the fp32 summation order of the segments: the plan is that of max_len).
  * Errors as kata_chunked_fwd_family; KATA_ERR_NULL for cu_seqlens NULL when B * H > 0;
  * KATA_ERR_SHAPE for negative total / max_len or max_len * H * max(p, dv) * 4 >= 2^31.
@@ -317,10 +319,13 @@ kata_status_t kata_chunked_fwd_varlen(const void* q, const void* k, const void* 
  * [0, max_len], so invalid contents give unspecified results but no access outside the
  * tensors. No workspace, no state. Rows outside every sequence are not written. Each
  * sequence's rows equal, bit for bit, kata_quadratic_fwd_family on that sequence alone.
- *   Supported: bf16 inputs (else KATA_ERR_UNSUPPORTED); dv in {16, 32, 64}; the full map with
- *   p in {16, 32, 64}, or KATA-Sigma g / KATA-M g with p = 64, g = 2 (reduced PSD families
- *   paragraph); fam, g as for kata_quadratic_fwd_family (KATA_ERR_FEATURE when g does not
- *   fit the family); o in o_dt, must not overlap q, k, v (KATA_ERR_ALIAS).
+ *   Supported: the shapes of kata_quadratic_fwd_family (else KATA_ERR_UNSUPPORTED): the full
+ *   map with p, dv in {16, 32, 64}, or KATA-Sigma g / KATA-M g (reduced PSD families
+ *   paragraph) with p, dv <= 64; bf16 or fp32 inputs. bf16 runs the MFMA kernels (full map;
+ *   KATA-Sigma 2 / KATA-M 2 at p = 64 with dv in {16, 32, 64}), every other case the VALU
+ *   kernels (fp32 full map; the other families and fp32 families); fam, g as for
+ *   kata_quadratic_fwd_family (KATA_ERR_FEATURE when g does not fit the family); o in o_dt,
+ *   must not overlap q, k, v (KATA_ERR_ALIAS).
  *   Errors: KATA_ERR_NULL for a NULL tensor or cu_seqlens when B * H, total and max_len are
  *   all positive (otherwise nothing is done); KATA_ERR_ALIGN for a tensor not 16-byte or
  *   cu_seqlens not 4-byte aligned; KATA_ERR_SHAPE for negative sizes or
@@ -387,8 +392,9 @@ kata_status_t kata_quadratic_bwd(const void* q, const void* k, const void* v, co
  * b, head h, is row (cu_seqlens[b] + t) * H + h). cu_seqlens: device int32 [B + 1], 4-byte
  * aligned, read on the device (offsets clamped to [0, total]); max_len bounds every length
  * (longer sequences are cut). Each sequence's gradients equal kata_quadratic_bwd's on that
- * sequence alone; rows outside every sequence are not written. bf16 inputs, p and dv in
- * {32, 64} (the bf16 MFMA kernels; else KATA_ERR_UNSUPPORTED). workspace: at least
+ * sequence alone; rows outside every sequence are not written. bf16 inputs with p and dv in
+ * {32, 64} run the bf16 MFMA kernels; bf16 or fp32 inputs with other p, dv <= 64 the VALU
+ * kernels (else KATA_ERR_UNSUPPORTED). workspace: at least
  * kata_quadratic_bwd_varlen_workspace_bytes(B, H, total) bytes (D_t and delta_t per packed
  * row); 0 means unsupported arguments. Errors as kata_quadratic_bwd; KATA_ERR_NULL for
  * cu_seqlens NULL when B H > 0; KATA_ERR_SHAPE for negative sizes or
@@ -434,10 +440,13 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
  * (cu_seqlens[b] + t) * H + h). cu_seqlens: device int32 [B + 1], 4-byte aligned, as for the
  * forward; max_len bounds every length (longer sequences are cut). Each sequence's gradients
  * equal the padded call's on that sequence alone; rows outside every sequence are not
- * written. bf16 inputs with p in {16, 32} and dv in {32, 64} (the bf16 MFMA state form; else
- * KATA_ERR_UNSUPPORTED). workspace: kata_chunked_bwd_varlen_workspace_bytes (D_t and delta_t
- * of the total H rows and the segment summaries of the plan of max_len); 0 means unsupported
- * arguments. Errors as kata_chunked_bwd; KATA_ERR_NULL for cu_seqlens NULL when B H > 0;
+ * written. bf16 inputs with p in {16, 32} and dv in {32, 64} run the bf16 MFMA state form;
+ * fp32 inputs and the other shapes the fp32 VALU state form, at the largest chunk of 64, 32
+ * and 16 whose state and rows fit LDS (p, dv <= 64; else KATA_ERR_UNSUPPORTED). workspace:
+ * kata_chunked_bwd_varlen_workspace_bytes (D_t and delta_t of the total H rows and the
+ * segment summaries of the plan of max_len; the larger of the two paths' needs, whatever the
+ * input dtype); 0 means unsupported arguments. Errors as kata_chunked_bwd; KATA_ERR_NULL for
+ * cu_seqlens NULL when B H > 0;
  * KATA_ERR_SHAPE for negative sizes or max_len * H * max(p, dv) * 4 >= 2^31.
  */
 size_t kata_chunked_bwd_varlen_workspace_bytes(int B, int H, int total, int max_len, int p, int dv, kata_scan_t scan);

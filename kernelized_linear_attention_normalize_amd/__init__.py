@@ -247,11 +247,12 @@ def chunked_fwd_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64, scan="ass
 
 def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=None, family: str = "full",
                          g: int = 1):
-    """Flash-style quadratic forward (bf16 inputs) over B sequences packed without padding:
-    q, k [total, H, p]; v [total, H, dv] -> o [total, H, dv], each sequence causal over its own
+    """Flash-style quadratic forward over B sequences packed without padding: q, k
+    [total, H, p]; v [total, H, dv] -> o [total, H, dv], each sequence causal over its own
     tokens. cu_seqlens: int32 device tensor [B + 1] of sequence offsets (0 first,
-    non-decreasing); max_len >= every length. family, g: the full map, or KATA-Sigma 2 /
-    KATA-M 2 at p = 64. Rows outside every sequence are not written."""
+    non-decreasing); max_len >= every length. The shapes of quadratic_fwd (bf16 or fp32;
+    family, g as there): bf16 MFMA kernels where they exist, else the VALU kernels. Rows
+    outside every sequence are not written."""
     lib = load()
     dev = _dev(q, k, v)
     total, H, p = q.shape
@@ -480,8 +481,9 @@ def quadratic_bwd(q, k, v, grad_o, family: str = "full", g: int = 1):
 def quadratic_bwd_varlen(q, k, v, grad_o, cu_seqlens, max_len: int):
     """Flash-style gradients (dq, dk, dv), float32, of the full-map forward over B sequences
     packed without padding (the layout of quadratic_fwd_varlen): q, k [total, H, p]; v,
-    grad_o [total, H, dv], bf16, p and dv in {32, 64}. Rows outside every sequence come back
-    as zeros."""
+    grad_o [total, H, dv], one dtype (bf16 or fp32), p and dv <= 64: bf16 MFMA kernels for
+    p, dv in {32, 64}, else the VALU kernels. Rows outside every sequence come back as
+    zeros."""
     lib = load()
     dev = _dev(q, k, v, grad_o)
     total, H, p = q.shape
@@ -543,7 +545,9 @@ STATE_BWD_MIN_T = 3072
 def chunked_bwd_varlen(q, k, v, grad_o, cu_seqlens, max_len: int, scan="associative", workspace=None):
     """O(T) gradients (dq, dk, dv), float32, of the forward over B sequences packed without
     padding (the layout of chunked_fwd_varlen): q, k [total, H, p]; v, grad_o [total, H, dv],
-    bf16, p in {16, 32}, dv in {32, 64}. Rows outside every sequence come back as zeros."""
+    one dtype: the bf16 MFMA state form for bf16 with p in {16, 32}, dv in {32, 64}, else the
+    fp32 VALU kernels (p, dv <= 64, the largest chunk of 64, 32, 16 that fits LDS). Rows
+    outside every sequence come back as zeros."""
     lib = load()
     dev = _dev(q, k, v, grad_o)
     total, H, p = q.shape
@@ -601,29 +605,37 @@ class _KataAttentionVarlen(torch.autograd.Function):
     def forward(ctx, q, k, v, cu_seqlens, max_len, C):
         ctx.save_for_backward(q, k, v, cu_seqlens)
         ctx.max_len = max_len
-        return chunked_fwd_varlen(q, k, v, cu_seqlens, max_len, C=C)
+        try:  # the O(T) chunked form where its kernels cover the shape, else the quadratic form
+            return chunked_fwd_varlen(q, k, v, cu_seqlens, max_len, C=C)
+        except KataError as e:
+            if e.status != 4:  # KATA_ERR_UNSUPPORTED
+                raise
+        return quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len)
 
     @staticmethod
     def backward(ctx, grad_o):
         q, k, v, cu = ctx.saved_tensors
         go = grad_o.contiguous().to(q.dtype)
-        if ctx.max_len < STATE_BWD_MIN_T and q.shape[-1] == 32:  # short sequences: flash style
+        p, dv = q.shape[-1], v.shape[-1]
+        state_form = q.dtype == torch.bfloat16 and p in (16, 32) and dv in (32, 64)
+        if state_form and not (ctx.max_len < STATE_BWD_MIN_T and p == 32):
+            dq, dk, dvv = chunked_bwd_varlen(q, k, v, go, cu, ctx.max_len)  # O(T): bf16 MFMA
+        else:  # flash style: bf16 MFMA for p, dv in {32, 64}, else the VALU kernels
             dq, dk, dvv = quadratic_bwd_varlen(q, k, v, go, cu, ctx.max_len)
-        else:
-            dq, dk, dvv = chunked_bwd_varlen(q, k, v, go, cu, ctx.max_len)
         return dq.to(q.dtype), dk.to(k.dtype), dvv.to(v.dtype), None, None, None
 
 
 def kata_attention_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64):
-    """Differentiable causal KATA attention over B sequences packed without padding (the
-    layout of chunked_fwd_varlen: q, k [total, H, p]; v [total, H, dv]; cu_seqlens int32
-    [B + 1]): the packed chunked forward and a packed backward (bf16 inputs, full map, p in
-    {16, 32}, dv in {32, 64}): the O(T) state form, or the flash-style form for p = 32 when
-    max_len < STATE_BWD_MIN_T. Rows outside every sequence get zero gradients."""
-    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
-        raise TypeError("kata_attention_varlen takes bf16 q, k, v")
-    if q.shape[-1] not in (16, 32) or v.shape[-1] not in (32, 64):
-        raise ValueError("kata_attention_varlen: p must be 16 or 32 and dv 32 or 64")
+    """Differentiable causal KATA attention (full map) over B sequences packed without
+    padding (the layout of chunked_fwd_varlen: q, k [total, H, p]; v [total, H, dv];
+    cu_seqlens int32 [B + 1]), bf16 or fp32 inputs. Forward: the packed chunked form, or the
+    packed quadratic form where the chunked kernels do not cover the shape. Backward: the O(T)
+    bf16 MFMA state form for bf16 with p in {16, 32} and dv in {32, 64} (except p = 32 with
+    max_len < STATE_BWD_MIN_T), else the packed flash-style form (bf16 MFMA for p, dv in
+    {32, 64}, else the VALU kernels, p, dv <= 64). Rows outside every sequence get zero
+    gradients."""
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("kata_attention_varlen takes q, k, v of one dtype, bf16 or float32")
     return _KataAttentionVarlen.apply(q, k, v, cu_seqlens, max_len, C)
 
 

@@ -456,8 +456,12 @@ kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void
   if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
   kata_status_t s = check_feature(p, fam, g);
   if (s != KATA_OK) return s;
-  if (in_dt != KATA_DTYPE_BF16 || !in_set(dv, {16, 32, 64})) return KATA_ERR_UNSUPPORTED;
-  if (fam == KATA_FEAT_FULL ? !in_set(p, {16, 32, 64}) : !kata::quadratic_bf16_family_supported(p, dv, (int)fam, g))
+  // the shapes of kata_quadratic_fwd_family: bf16 MFMA kernels where they exist, else the
+  // fp32 VALU kernel (full map) or the VALU family kernel, all with the packed layout
+  const bool full = fam == KATA_FEAT_FULL, bf16 = in_dt == KATA_DTYPE_BF16;
+  const bool mfma = bf16 && in_set(dv, {16, 32, 64}) &&
+                    (full ? in_set(p, {16, 32, 64}) : kata::quadratic_bf16_family_supported(p, dv, (int)fam, g));
+  if (full ? (!in_set(p, {16, 32, 64}) || !in_set(dv, {16, 32, 64})) : (p > 64 || dv > 64))
     return KATA_ERR_UNSUPPORTED;
   if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
   if (cu_seqlens == nullptr) return KATA_ERR_NULL;
@@ -473,6 +477,14 @@ kata_status_t kata_quadratic_fwd_varlen(const void* q, const void* k, const void
   kata::SeqLayout lay;
   lay.cu = cu_seqlens;
   lay.total = total;
+  const hipStream_t st = (hipStream_t)stream;
+  if (!mfma && full)
+    return hip_status(kata::launch_quadratic_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                                 static_cast<const float*>(v), o, o_dt == KATA_DTYPE_BF16, B, H,
+                                                 max_len, p, dv, st, lay));
+  if (!mfma)
+    return hip_status(kata::launch_family_quadratic(q, k, v, bf16, o, o_dt == KATA_DTYPE_BF16, B, H, max_len, p, dv,
+                                                    (int)fam, g, st, lay));
   return hip_status(kata::launch_quadratic_bf16_varlen(static_cast<const uint16_t*>(q),
                                                        static_cast<const uint16_t*>(k),
                                                        static_cast<const uint16_t*>(v), o,
@@ -590,12 +602,14 @@ kata_status_t kata_quadratic_bwd_varlen(const void* q, const void* k, const void
                                         void* workspace, size_t workspace_bytes, kata_stream_t stream) {
   if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
   if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
-  if (in_dt != KATA_DTYPE_BF16 || !kata::quadratic_bwd_mfma_supported(p, dv)) return KATA_ERR_UNSUPPORTED;
+  // bf16 MFMA kernels for their shapes, else the VALU kernels (p, dv <= 64), packed layout
+  const bool mfma = in_dt == KATA_DTYPE_BF16 && kata::quadratic_bwd_mfma_supported(p, dv);
+  if (p > 64 || dv > 64) return KATA_ERR_UNSUPPORTED;
   if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
   if (cu_seqlens == nullptr) return KATA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
   // one sequence's rows (H apart) are addressed with 32-bit byte offsets, up to a block of
-  // 512 rows past its end
+  // 512 rows past its end (MFMA kernels; the same bound for both paths)
   const int w = p > dv ? p : dv;
   if (mul4(total, H, w, 1) < 0 || ((int64_t)max_len + 512) * H * w * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
   if ((int64_t)B * H * ((max_len + 31) / 32) > kMaxGrid) return KATA_ERR_SHAPE;
@@ -606,7 +620,7 @@ kata_status_t kata_quadratic_bwd_varlen(const void* q, const void* k, const void
   if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KATA_ERR_ALIGN;
   const size_t rows = (size_t)total * H;
-  const size_t qb = rows * p * 2, vb = rows * dv * 2;
+  const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
   const void* outs[4] = {dq, dk, dv_out, workspace};
   const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
   for (int i = 0; i < 4; ++i) {
@@ -619,6 +633,10 @@ kata_status_t kata_quadratic_bwd_varlen(const void* q, const void* k, const void
   kata::SeqLayout lay;
   lay.cu = cu_seqlens;
   lay.total = total;
+  if (!mfma)
+    return hip_status(kata::launch_quadratic_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, max_len, p, dv,
+                                                 (int)KATA_FEAT_FULL, 1, static_cast<float*>(workspace), dq, dk,
+                                                 dv_out, (hipStream_t)stream, lay));
   return hip_status(kata::launch_quadratic_bwd_mfma_varlen(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(grad_o), B, H, max_len, p, dv, lay, static_cast<float*>(workspace), dq, dk,
@@ -633,6 +651,13 @@ static bool chunked_bwd_valu_supported(int p, int dv, int C) {
 // a shape one of the two paths runs (the bf16 MFMA kernels choose their own chunking)
 static bool chunked_bwd_supported(int p, int dv, int C) {
   return in_set(C, {16, 32, 64}) && (chunked_bwd_valu_supported(p, dv, C) || kata::chunked_bwd_mfma_supported(p, dv));
+}
+
+// chunk of the VALU kernels when the caller gives none (packed sequences): the largest that fits
+static int chunked_bwd_valu_chunk(int p, int dv) {
+  for (int C : {64, 32, 16})
+    if (chunked_bwd_valu_supported(p, dv, C)) return C;
+  return 0;
 }
 
 size_t kata_chunked_bwd_workspace_bytes(int B, int H, int T, int p, int dv, int C, kata_scan_t scan) {
@@ -699,8 +724,20 @@ kata_status_t kata_chunked_bwd(const void* q, const void* k, const void* v, cons
 size_t kata_chunked_bwd_varlen_workspace_bytes(int B, int H, int total, int max_len, int p, int dv, kata_scan_t scan) {
   if (B <= 0 || H <= 0 || total < 0 || max_len <= 0 || (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE))
     return 0;
-  if (!kata::chunked_bwd_mfma_supported(p, dv)) return 0;
-  return kata::chunked_bwd_mfma_workspace_floats(B, H, max_len, p, dv, scan, (int64_t)total * H) * sizeof(float);
+  // the larger of the two paths' needs (the size does not depend on the input dtype)
+  size_t need = 0;
+  if (const int C = chunked_bwd_valu_chunk(p, dv)) {
+    const kata::SegPlan plan = kata::seg_plan(B, H, max_len, C, scan);
+    const size_t rows = (size_t)total * H;
+    const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
+    need = (rows * 2 + 2 * sums) * sizeof(float);
+  }
+  if (kata::chunked_bwd_mfma_supported(p, dv)) {
+    const size_t m =
+        kata::chunked_bwd_mfma_workspace_floats(B, H, max_len, p, dv, scan, (int64_t)total * H) * sizeof(float);
+    need = m > need ? m : need;
+  }
+  return need;
 }
 
 kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* v, const void* grad_o,
@@ -710,13 +747,16 @@ kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* 
   if (!valid_dt(in_dt)) return KATA_ERR_DTYPE;
   if (scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return KATA_ERR_SCAN;
   if (B < 0 || H < 0 || total < 0 || max_len < 0 || p < 1 || dv < 1) return KATA_ERR_SHAPE;
-  if (in_dt != KATA_DTYPE_BF16 || !kata::chunked_bwd_mfma_supported(p, dv)) return KATA_ERR_UNSUPPORTED;
+  // bf16 MFMA kernels for their shapes, else the fp32 VALU kernels at the largest chunk that fits
+  const bool mfma = in_dt == KATA_DTYPE_BF16 && kata::chunked_bwd_mfma_supported(p, dv);
+  const int Cv = mfma ? 0 : chunked_bwd_valu_chunk(p, dv);
+  if (!mfma && Cv == 0) return KATA_ERR_UNSUPPORTED;
   if ((int64_t)B * H == 0 || total == 0 || max_len == 0) return KATA_OK;
   if (cu_seqlens == nullptr) return KATA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0) return KATA_ERR_ALIGN;
   const int w = p > dv ? p : dv;
   if (mul4(total, H, w, 1) < 0 || (int64_t)max_len * H * w * 4 >= INT32_MAX) return KATA_ERR_SHAPE;
-  const kata::SegPlan plan = kata::seg_plan(B, H, max_len, kata::CHUNKED_BWD_FWD_C, scan);
+  const kata::SegPlan plan = kata::seg_plan(B, H, max_len, mfma ? kata::CHUNKED_BWD_FWD_C : Cv, scan);
   if ((int64_t)B * H * plan.nseg > kMaxGrid) return KATA_ERR_SHAPE;
   if (!q || !k || !v || !grad_o || !dq || !dk || !dv_out) return KATA_ERR_NULL;
   for (const void* ptr : {q, k, v, grad_o, (const void*)dq, (const void*)dk, (const void*)dv_out})
@@ -725,7 +765,7 @@ kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* 
   if (!workspace || workspace_bytes < need) return KATA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KATA_ERR_ALIGN;
   const size_t rows = (size_t)total * H;
-  const size_t qb = rows * p * 2, vb = rows * dv * 2;
+  const size_t qb = rows * p * dt_size(in_dt), vb = rows * dv * dt_size(in_dt);
   const void* outs[4] = {dq, dk, dv_out, workspace};
   const size_t outb[4] = {rows * p * 4, rows * p * 4, rows * dv * 4, need};
   for (int i = 0; i < 4; ++i) {
@@ -738,6 +778,14 @@ kata_status_t kata_chunked_bwd_varlen(const void* q, const void* k, const void* 
   kata::SeqLayout lay;
   lay.cu = cu_seqlens;
   lay.total = total;
+  if (!mfma) {
+    float* stats = static_cast<float*>(workspace);
+    const size_t sums = plan.nseg > 1 ? (size_t)B * H * (plan.nseg - 1) * kata::chunked_bwd_state_floats(p, dv) : 0;
+    float* fsum = stats + rows * 2;
+    float* rsum = fsum + sums;
+    return hip_status(kata::launch_chunked_bwd(q, k, v, grad_o, in_dt == KATA_DTYPE_BF16, B, H, max_len, p, dv, Cv,
+                                               plan, stats, fsum, rsum, dq, dk, dv_out, (hipStream_t)stream, lay));
+  }
   return hip_status(kata::launch_chunked_bwd_mfma(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(grad_o), B, H, max_len, p, dv, (int)scan, lay, (int64_t)rows,

@@ -85,7 +85,7 @@ template <bool IN_BF16>
 __global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                         const void* __restrict__ v, const void* __restrict__ go,
                                                         int T, int p, int dv, BwFeat F, float* __restrict__ ws,
-                                                        float* __restrict__ dq) {
+                                                        float* __restrict__ dq, SeqLayout lay, int H) {
   extern __shared__ float sm[];
   float* qh = sm;
   float* gq = qh + BW_B * p;
@@ -100,20 +100,26 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__
   const int nqb = (T + BW_B - 1) / BW_B;
   const int64_t bh = blockIdx.x / nqb;
   const int tq0 = (blockIdx.x % nqb) * BW_B;
+  // rows of this sequence: row0 + t * stp for t < len (padded: bh T + t, len = T)
+  int64_t row0;
+  int stp, len;
+  seq_rows_of(lay, bh, H, T, row0, stp, len);
+  if (tq0 >= len) return;  // the whole workgroup: no query of this block exists
+  auto row = [&](int t) { return row0 + (int64_t)t * stp; };
   const int qi = tid >> 3, sub = tid & 7;  // thread: query qi, columns / components sub + 8u
-  if (tid < BW_B) qn[tid] = bw_load_row<IN_BF16>(q, bh * T + tq0 + tid, tq0 + tid < T, p, qh + tid * p);
+  if (tid < BW_B) qn[tid] = bw_load_row<IN_BF16>(q, row(tq0 + tid), tq0 + tid < len, p, qh + tid * p);
   for (int e = tid; e < BW_B * dv; e += 256)
-    gq[e] = tq0 + e / dv < T ? load_as_f32<IN_BF16>(go, (bh * T + tq0) * dv + e) : 0.f;
+    gq[e] = tq0 + e / dv < len ? load_as_f32<IN_BF16>(go, row(tq0 + e / dv) * dv + e % dv) : 0.f;
   // ---- forward recompute: N_t, D_t
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int tk0 = 0; tk0 <= tq0; tk0 += BW_B) {
     __syncthreads();
-    if (tid < BW_B) bw_load_row<IN_BF16>(k, bh * T + tk0 + tid, tk0 + tid < T, p, kh + tid * p);
+    if (tid < BW_B) bw_load_row<IN_BF16>(k, row(tk0 + tid), tk0 + tid < len, p, kh + tid * p);
     for (int e = tid; e < BW_B * dv; e += 256)
-      vv[e] = tk0 + e / dv < T ? load_as_f32<IN_BF16>(v, (bh * T + tk0) * dv + e) : 0.f;
+      vv[e] = tk0 + e / dv < len ? load_as_f32<IN_BF16>(v, row(tk0 + e / dv) * dv + e % dv) : 0.f;
     __syncthreads();
-    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, T);
+    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, len);
     __syncthreads();
     for (int j = 0; j < BW_B; ++j) {
       const float wij = w[qi * (BW_B + 1) + j];
@@ -132,20 +138,20 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__
   if (sub == 0) {
     Ds[qi] = den;
     dl[qi] = part;
-    if (tq0 + qi < T) {
-      ws[(bh * T + tq0 + qi) * 2] = den;
-      ws[(bh * T + tq0 + qi) * 2 + 1] = part;
+    if (tq0 + qi < len) {
+      ws[row(tq0 + qi) * 2] = den;
+      ws[row(tq0 + qi) * 2 + 1] = part;
     }
   }
   // ---- gradient pass: dq_hat
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // components sub + 8u
   for (int tk0 = 0; tk0 <= tq0; tk0 += BW_B) {
     __syncthreads();
-    if (tid < BW_B) bw_load_row<IN_BF16>(k, bh * T + tk0 + tid, tk0 + tid < T, p, kh + tid * p);
+    if (tid < BW_B) bw_load_row<IN_BF16>(k, row(tk0 + tid), tk0 + tid < len, p, kh + tid * p);
     for (int e = tid; e < BW_B * dv; e += 256)
-      vv[e] = tk0 + e / dv < T ? load_as_f32<IN_BF16>(v, (bh * T + tk0) * dv + e) : 0.f;
+      vv[e] = tk0 + e / dv < len ? load_as_f32<IN_BF16>(v, row(tk0 + e / dv) * dv + e % dv) : 0.f;
     __syncthreads();
-    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, T);
+    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, len);
     __syncthreads();
     for (int e = tid; e < BW_B * BW_B; e += 256) {  // w <- dw
       const int i = e / BW_B, j = e % BW_B;
@@ -176,10 +182,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(const void* __restrict__
     if (sub + 8 * u < p) pr += acc[u] * qh[qi * p + sub + 8 * u];
   pr = group_sum<8>(pr);
   const float nq = qn[qi];
-  if (tq0 + qi < T)
+  if (tq0 + qi < len)
     for (int u = 0; u < 8; ++u) {
       const int c = sub + 8 * u;
-      if (c < p) dq[(bh * T + tq0 + qi) * (int64_t)p + c] = nq > 0.f ? (acc[u] - qh[qi * p + c] * pr) / nq : 0.f;
+      if (c < p) dq[row(tq0 + qi) * p + c] = nq > 0.f ? (acc[u] - qh[qi * p + c] * pr) / nq : 0.f;
     }
 }
 
@@ -189,7 +195,8 @@ template <bool IN_BF16>
 __global__ __launch_bounds__(256) void bwd_key_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                       const void* __restrict__ v, const void* __restrict__ go, int T,
                                                       int p, int dv, BwFeat F, const float* __restrict__ ws,
-                                                      float* __restrict__ dk, float* __restrict__ dvo) {
+                                                      float* __restrict__ dk, float* __restrict__ dvo, SeqLayout lay,
+                                                      int H) {
   extern __shared__ float sm[];
   float* kh = sm;
   float* vv = kh + BW_B * p;
@@ -205,24 +212,29 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(const void* __restrict__ q
   const int nkb = (T + BW_B - 1) / BW_B;
   const int64_t bh = blockIdx.x / nkb;
   const int tk0 = (blockIdx.x % nkb) * BW_B;
+  int64_t row0;
+  int stp, len;
+  seq_rows_of(lay, bh, H, T, row0, stp, len);
+  if (tk0 >= len) return;  // the whole workgroup: no key of this block exists
+  auto row = [&](int t) { return row0 + (int64_t)t * stp; };
   const int sj = tid >> 3, sub = tid & 7;  // thread: key sj, columns / components sub + 8u
-  if (tid < BW_B) kn[tid] = bw_load_row<IN_BF16>(k, bh * T + tk0 + tid, tk0 + tid < T, p, kh + tid * p);
+  if (tid < BW_B) kn[tid] = bw_load_row<IN_BF16>(k, row(tk0 + tid), tk0 + tid < len, p, kh + tid * p);
   for (int e = tid; e < BW_B * dv; e += 256)
-    vv[e] = tk0 + e / dv < T ? load_as_f32<IN_BF16>(v, (bh * T + tk0) * dv + e) : 0.f;
+    vv[e] = tk0 + e / dv < len ? load_as_f32<IN_BF16>(v, row(tk0 + e / dv) * dv + e % dv) : 0.f;
   float gvs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // dv_s, columns sub + 8u
   float gks[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // dk_hat_s, components sub + 8u
-  for (int tq0 = tk0; tq0 < T; tq0 += BW_B) {
+  for (int tq0 = tk0; tq0 < len; tq0 += BW_B) {
     __syncthreads();
     if (tid < BW_B) {
-      bw_load_row<IN_BF16>(q, bh * T + tq0 + tid, tq0 + tid < T, p, qh + tid * p);
-      const bool ok = tq0 + tid < T;
-      Ds[tid] = ok ? ws[(bh * T + tq0 + tid) * 2] : 0.f;
-      dl[tid] = ok ? ws[(bh * T + tq0 + tid) * 2 + 1] : 0.f;
+      const bool ok = tq0 + tid < len;
+      bw_load_row<IN_BF16>(q, row(tq0 + tid), ok, p, qh + tid * p);
+      Ds[tid] = ok ? ws[row(tq0 + tid) * 2] : 0.f;
+      dl[tid] = ok ? ws[row(tq0 + tid) * 2 + 1] : 0.f;
     }
     for (int e = tid; e < BW_B * dv; e += 256)
-      gq[e] = tq0 + e / dv < T ? load_as_f32<IN_BF16>(go, (bh * T + tq0) * dv + e) : 0.f;
+      gq[e] = tq0 + e / dv < len ? load_as_f32<IN_BF16>(go, row(tq0 + e / dv) * dv + e % dv) : 0.f;
     __syncthreads();
-    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, T);  // dots[r][t][s], w[t][s]
+    bw_dots(F, qh, kh, p, dots, w, tq0, tk0, len);  // dots[r][t][s], w[t][s]
     __syncthreads();
     for (int e = tid; e < BW_B * BW_B; e += 256) {
       const int i = e / BW_B, j = e % BW_B;  // query i, key j
@@ -258,12 +270,12 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(const void* __restrict__ q
     if (sub + 8 * u < p) pr += gks[u] * kh[sj * p + sub + 8 * u];
   pr = group_sum<8>(pr);
   const float nk = kn[sj];
-  if (tk0 + sj < T) {
+  if (tk0 + sj < len) {
     for (int u = 0; u < 8; ++u) {
       const int c = sub + 8 * u;
-      if (c < p) dk[(bh * T + tk0 + sj) * (int64_t)p + c] = nk > 0.f ? (gks[u] - kh[sj * p + c] * pr) / nk : 0.f;
+      if (c < p) dk[row(tk0 + sj) * p + c] = nk > 0.f ? (gks[u] - kh[sj * p + c] * pr) / nk : 0.f;
       const int d = sub + 8 * u;
-      if (d < dv) dvo[(bh * T + tk0 + sj) * (int64_t)dv + d] = gvs[u];
+      if (d < dv) dvo[row(tk0 + sj) * dv + d] = gvs[u];
     }
   }
 }
@@ -272,7 +284,7 @@ int bwd_pairs(int p, int fam, int g) { return make_bw(p, fam, g).npr; }
 
 hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
                                 int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
-                                float* dvo, hipStream_t st) {
+                                float* dvo, hipStream_t st, SeqLayout lay) {
   const BwFeat F = make_bw(p, fam, g);
   const int64_t BH = (int64_t)B * H;
   const int nb = (T + BW_B - 1) / BW_B;
@@ -287,9 +299,9 @@ hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, con
     return e;
   if ((e = hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsk)) != hipSuccess)
     return e;
-  k1<<<dim3((unsigned)(BH * nb)), dim3(256), ldsq, st>>>(q, k, v, go, T, p, dv, F, ws, dq);
+  k1<<<dim3((unsigned)(BH * nb)), dim3(256), ldsq, st>>>(q, k, v, go, T, p, dv, F, ws, dq, lay, H);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k2<<<dim3((unsigned)(BH * nb)), dim3(256), ldsk, st>>>(q, k, v, go, T, p, dv, F, ws, dk, dvo);
+  k2<<<dim3((unsigned)(BH * nb)), dim3(256), ldsk, st>>>(q, k, v, go, T, p, dv, F, ws, dk, dvo, lay, H);
   return hipGetLastError();
 }
 

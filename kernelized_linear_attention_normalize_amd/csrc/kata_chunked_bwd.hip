@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
                                                           int nblk_per_bh, float* __restrict__ fsum,
                                                           float* __restrict__ rsum, int64_t sf,
                                                           float* __restrict__ stats, float* __restrict__ dq,
-                                                          float* __restrict__ dk, float* __restrict__ dvo) {
+                                                          float* __restrict__ dk, float* __restrict__ dvo,
+                                                          SeqLayout lay, int H) {
   extern __shared__ float sm[];
   const int n = p * (p + 1) / 2;
   float* St = sm;                 // [n][dv] then [n]: S | Z or R | r
@@ -67,7 +68,13 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / nblk_per_bh;
   const int seg = (int)(blockIdx.x % nblk_per_bh) + (MODE == CB_RSUM ? 1 : 0);
-  const int nchunks = (T + C - 1) / C;
+  // rows of this sequence: row0 + t * stp for t < Tb (padded: bh T + t, Tb = T); the plan is
+  // that of T, so the segments past a shorter sequence's end are empty (zero summaries)
+  int64_t row0;
+  int stp, Tb;
+  seq_rows_of(lay, bh, H, T, row0, stp, Tb);
+  auto row = [&](int t) { return row0 + (int64_t)t * stp; };
+  const int nchunks = (Tb + C - 1) / C;
   const int c0 = seg * cps, c1 = min(nchunks, c0 + cps);
   const float r2 = 1.41421356237309515f;
 
@@ -81,12 +88,11 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
   if (MODE == CB_RDK && seg < nseg - 1) init = rsum + (bh * (nseg - 1) + (nseg - 2 - seg)) * sf;
   for (int e = tid; e < n * dv + n; e += 256) St[e] = init ? init[e] : 0.f;
 
-  const int64_t rbase = bh * (int64_t)T;
   const bool fwd_order = MODE == CB_FSUM || MODE == CB_FDQ;
   for (int ci = 0; ci < c1 - c0; ++ci) {
     const int c = fwd_order ? c0 + ci : c1 - 1 - ci;
     const int t0 = c * C;
-    const int L = min(C, T - t0);
+    const int L = min(C, Tb - t0);
     __syncthreads();
     // rows of the chunk: normalised q and k with their norms, v, g; rows >= L are zero
     const bool need_q = MODE != CB_FSUM, need_k = MODE != CB_RSUM, need_v = MODE != CB_RSUM;
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
       float* dst = (isq ? qh : kh) + t * p;
       float ss = 0.f;
       for (int i = 0; i < p; ++i) {
-        const float x = t < L ? load_as_f32<IN_BF16>(isq ? q : k, (rbase + t0 + t) * p + i) : 0.f;
+        const float x = t < L ? load_as_f32<IN_BF16>(isq ? q : k, row(t0 + t) * p + i) : 0.f;
         dst[i] = x;
         ss += x * x;
       }
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
     }
     for (int e = tid; e < C * dv; e += 256) {
       const int t = e / dv;
-      const int64_t gi = (rbase + t0 + t) * dv + e % dv;
+      const int64_t gi = row(t0 + t) * dv + e % dv;
       if (need_v) vv[e] = t < L ? load_as_f32<IN_BF16>(v, gi) : 0.f;
       if (MODE != CB_FSUM) gg[e] = t < L ? load_as_f32<IN_BF16>(go, gi) : 0.f;
     }
@@ -115,8 +121,8 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
       for (int t = tid; t < C; t += 256) {
         float D = 0.f, dl = 0.f;
         if (t < L) {
-          D = stats[(rbase + t0 + t) * 2];
-          dl = stats[(rbase + t0 + t) * 2 + 1];
+          D = stats[row(t0 + t) * 2];
+          dl = stats[row(t0 + t) * 2 + 1];
         }
         const float inv = D > 0.f ? 1.f / D : 0.f;
         dd[t] = inv;  // here: 1 / D_t
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
         float dl = 0.f;
         for (int d = 0; d < dv; ++d) dl += aa[t * dv + d];
         const float D = dd[t], inv = D > 0.f ? 1.f / D : 0.f;
-        if (t < L) *reinterpret_cast<float2*>(stats + (rbase + t0 + t) * 2) = make_float2(D, dl);
+        if (t < L) *reinterpret_cast<float2*>(stats + row(t0 + t) * 2) = make_float2(D, dl);
         bb[t] = -dl * inv;
         dd[t] = inv;
       }
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
         if (t >= L) continue;
         float pr = 0.f;
         for (int i = 0; i < p; ++i) pr += qh[t * p + i] * dh[t * p + i];
-        dq[(rbase + t0 + t) * p + e % p] = qn[t] > 0.f ? (dh[e] - qh[e] * pr) / qn[t] : 0.f;
+        dq[row(t0 + t) * p + e % p] = qn[t] > 0.f ? (dh[e] - qh[e] * pr) / qn[t] : 0.f;
       }
     }
 
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
           acc += (i == j ? 1.f : r2) * ks[i] * ks[j] * St[f * dv + d];
         }
         for (int t = s; t < L; ++t) acc += W[t * C + s] * aa[t * dv + d];
-        dvo[(rbase + t0 + s) * dv + d] = acc;
+        dvo[row(t0 + s) * dv + d] = acc;
       }
       __syncthreads();
       for (int e = tid; e < C * p; e += 256) {
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(256) void chunked_bwd_kernel(const void* __restrict
         if (s >= L) continue;
         float pr = 0.f;
         for (int i = 0; i < p; ++i) pr += kh[s * p + i] * dh[s * p + i];
-        dk[(rbase + t0 + s) * p + e % p] = kn[s] > 0.f ? (dh[e] - kh[e] * pr) / kn[s] : 0.f;
+        dk[row(t0 + s) * p + e % p] = kn[s] > 0.f ? (dh[e] - kh[e] * pr) / kn[s] : 0.f;
       }
     }
     __syncthreads();
@@ -302,7 +308,7 @@ hipError_t launch_scan(float* ws, int BH, int nslots, int64_t E, hipStream_t st)
 template <bool IN_BF16>
 static hipError_t launch_cb(const void* q, const void* k, const void* v, const void* go, int B, int H, int T, int p,
                             int dv, int C, const SegPlan& plan, float* stats, float* fsum, float* rsum, float* dq,
-                            float* dk, float* dvo, hipStream_t st) {
+                            float* dk, float* dvo, hipStream_t st, SeqLayout lay) {
   const int BH = B * H;
   const size_t lds = chunked_bwd_lds_bytes(p, dv, C);
   const int64_t sf = chunked_bwd_state_floats(p, dv);
@@ -312,7 +318,7 @@ static hipError_t launch_cb(const void* q, const void* k, const void* v, const v
     if (r != hipSuccess) return r;
     kern<<<dim3(nblk_per_bh * (unsigned)BH), dim3(256), lds, st>>>(q, k, v, go, T, p, dv, C, plan.nseg, plan.cps,
                                                                   (int)nblk_per_bh, fsum, rsum, sf, stats, dq, dk,
-                                                                  dvo);
+                                                                  dvo, lay, H);
     return hipGetLastError();
   };
   const bool segs = plan.nseg > 1;
@@ -330,10 +336,10 @@ static hipError_t launch_cb(const void* q, const void* k, const void* v, const v
 
 hipError_t launch_chunked_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B, int H,
                               int T, int p, int dv, int C, const SegPlan& plan, float* stats, float* fsum,
-                              float* rsum, float* dq, float* dk, float* dvo, hipStream_t st) {
+                              float* rsum, float* dq, float* dk, float* dvo, hipStream_t st, SeqLayout lay) {
   if (in_bf16)
-    return launch_cb<true>(q, k, v, go, B, H, T, p, dv, C, plan, stats, fsum, rsum, dq, dk, dvo, st);
-  return launch_cb<false>(q, k, v, go, B, H, T, p, dv, C, plan, stats, fsum, rsum, dq, dk, dvo, st);
+    return launch_cb<true>(q, k, v, go, B, H, T, p, dv, C, plan, stats, fsum, rsum, dq, dk, dvo, st, lay);
+  return launch_cb<false>(q, k, v, go, B, H, T, p, dv, C, plan, stats, fsum, rsum, dq, dk, dvo, st, lay);
 }
 
 }  // namespace kata

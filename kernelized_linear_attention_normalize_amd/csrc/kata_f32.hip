@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void quadratic_f32_kernel(const float* __restr
                                                             const float* __restrict__ k,
                                                             const float* __restrict__ v,
                                                             void* __restrict__ o, int T, int p,
-                                                            int dv) {
+                                                            int dv, SeqLayout lay, int H) {
   extern __shared__ float sm[];
   float* qh = sm;                   // [BQ][p]
   float* kh = qh + QF_BQ * p;       // [BK][p]
@@ -232,13 +232,16 @@ __global__ __launch_bounds__(256) void quadratic_f32_kernel(const float* __restr
   const int64_t bh = blockIdx.x / nqb;
   const int qblk = nqb - 1 - (int)(blockIdx.x % nqb);  // longest rows first
   const int tq0 = qblk * QF_BQ;
-  const float* qb = q + bh * (int64_t)T * p;
-  const float* kb = k + bh * (int64_t)T * p;
-  const float* vb = v + bh * (int64_t)T * dv;
+  // rows of this sequence: row0 + t * stp for t < len (padded: bh T + t, len = T)
+  int64_t row0;
+  int stp, len;
+  seq_rows_of(lay, bh, H, T, row0, stp, len);
+  if (tq0 >= len) return;  // the whole workgroup: no query of this block exists
+  auto row = [&](int t) { return row0 + (int64_t)t * stp; };
   for (int r = tid; r < QF_BQ; r += 256) {
     float ss = 0.f;
     for (int i = 0; i < p; ++i) {
-      const float x = tq0 + r < T ? qb[(int64_t)(tq0 + r) * p + i] : 0.f;
+      const float x = tq0 + r < len ? q[row(tq0 + r) * p + i] : 0.f;
       qh[r * p + i] = x;
       ss += x * x;
     }
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void quadratic_f32_kernel(const float* __restr
     for (int r = tid; r < QF_BK; r += 256) {
       float ss = 0.f;
       for (int i = 0; i < p; ++i) {
-        const float x = kb0 + r < T ? kb[(int64_t)(kb0 + r) * p + i] : 0.f;
+        const float x = kb0 + r < len ? k[row(kb0 + r) * p + i] : 0.f;
         kh[r * p + i] = x;
         ss += x * x;
       }
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void quadratic_f32_kernel(const float* __restr
       for (int i = 0; i < p; ++i) kh[r * p + i] *= inv;
     }
     for (int e = tid; e < QF_BK * dv; e += 256)
-      vv[e] = kb0 + e / dv < T ? vb[(int64_t)kb0 * dv + e] : 0.f;
+      vv[e] = kb0 + e / dv < len ? v[row(kb0 + e / dv) * dv + e % dv] : 0.f;
     __syncthreads();
     for (int e = tid; e < QF_BQ * QF_BK; e += 256) {
       const int i = e / QF_BK, j = e % QF_BK;
@@ -280,20 +283,20 @@ __global__ __launch_bounds__(256) void quadratic_f32_kernel(const float* __restr
     }
   }
   const int t = tq0 + qi;
-  if (t < T) {
+  if (t < len) {
     for (int u = 0; u < 8; ++u) {
       const int dd = dsub + 8 * u;
-      if (dd < dv) store_from_f32<OUT_BF16>(o, (bh * T + t) * (int64_t)dv + dd, dacc > 0.f ? acc[u] / dacc : 0.f);
+      if (dd < dv) store_from_f32<OUT_BF16>(o, row(t) * dv + dd, dacc > 0.f ? acc[u] / dacc : 0.f);
     }
   }
 }
 
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
-                                bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st) {
+                                bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st, SeqLayout lay) {
   const size_t lds = 4 * ((size_t)QF_BQ * p + (size_t)QF_BK * p + (size_t)QF_BK * dv + QF_BQ * (QF_BK + 1));
   dim3 grid((unsigned)((int64_t)((T + QF_BQ - 1) / QF_BQ) * B * H)), block(256);
-  if (o_bf16) quadratic_f32_kernel<true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv);
-  else quadratic_f32_kernel<false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv);
+  if (o_bf16) quadratic_f32_kernel<true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, lay, H);
+  else quadratic_f32_kernel<false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, lay, H);
   return hipGetLastError();
 }
 

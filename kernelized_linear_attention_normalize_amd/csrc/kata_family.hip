@@ -414,7 +414,7 @@ constexpr int FQ_BQ = 32, FQ_BK = 32;
 template <bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(256) void family_quadratic_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                                const void* __restrict__ v, void* __restrict__ o,
-                                                               int T, int p, int dv, Feat F) {
+                                                               int T, int p, int dv, Feat F, SeqLayout lay, int H) {
   extern __shared__ float sm[];
   float* qh = sm;                  // [BQ][p]
   float* kh = qh + FQ_BQ * p;      // [BK][p]
@@ -425,15 +425,21 @@ __global__ __launch_bounds__(256) void family_quadratic_kernel(const void* __res
   const int nbh = (int)(gridDim.x / nqb);
   const int64_t bh = blockIdx.x % nbh;
   const int tq0 = (nqb - 1 - (int)(blockIdx.x / nbh)) * FQ_BQ;
-  for (int r = tid; r < FQ_BQ; r += 256) load_norm_row<IN_BF16>(q, bh * T + tq0 + r, tq0 + r < T, p, qh + r * p);
+  // rows of this sequence: row0 + t * stp for t < len (padded: bh T + t, len = T)
+  int64_t row0;
+  int stp, len;
+  seq_rows_of(lay, bh, H, T, row0, stp, len);
+  if (tq0 >= len) return;  // the whole workgroup: no query of this block exists
+  auto row = [&](int t) { return row0 + (int64_t)t * stp; };
+  for (int r = tid; r < FQ_BQ; r += 256) load_norm_row<IN_BF16>(q, row(tq0 + r), tq0 + r < len, p, qh + r * p);
   const int qi = tid >> 3, dsub = tid & 7;  // thread owns query qi, columns dsub + 8u
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float dacc = 0.f;
   for (int kb0 = 0; kb0 <= tq0; kb0 += FQ_BK) {
     __syncthreads();
-    for (int r = tid; r < FQ_BK; r += 256) load_norm_row<IN_BF16>(k, bh * T + kb0 + r, kb0 + r < T, p, kh + r * p);
+    for (int r = tid; r < FQ_BK; r += 256) load_norm_row<IN_BF16>(k, row(kb0 + r), kb0 + r < len, p, kh + r * p);
     for (int e = tid; e < FQ_BK * dv; e += 256)
-      vv[e] = kb0 + e / dv < T ? load_as_f32<IN_BF16>(v, (bh * T + kb0) * dv + e) : 0.f;
+      vv[e] = kb0 + e / dv < len ? load_as_f32<IN_BF16>(v, row(kb0 + e / dv) * dv + e % dv) : 0.f;
     __syncthreads();
     for (int e = tid; e < FQ_BQ * FQ_BK; e += 256) {
       const int i = e / FQ_BK, j = e % FQ_BK;
@@ -450,23 +456,24 @@ __global__ __launch_bounds__(256) void family_quadratic_kernel(const void* __res
     }
   }
   const int t = tq0 + qi;
-  if (t < T)
+  if (t < len)
     for (int u = 0; u < 8; ++u) {
       const int dd = dsub + 8 * u;
-      if (dd < dv) store_from_f32<OUT_BF16>(o, (bh * T + t) * (int64_t)dv + dd, dacc > 0.f ? acc[u] / dacc : 0.f);
+      if (dd < dv) store_from_f32<OUT_BF16>(o, row(t) * dv + dd, dacc > 0.f ? acc[u] / dacc : 0.f);
     }
 }
 
 hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, bool in_bf16, void* o, bool o_bf16,
-                                   int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st) {
+                                   int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st,
+                                   SeqLayout lay) {
   // fam 3: the full map with weights (q_hat . k_hat)^(2g) (order r = g)
   const Feat F = fam == 3 ? make_order(p, g) : make_feat(p, fam, g);
   const size_t lds = 4 * ((size_t)FQ_BQ * p + (size_t)FQ_BK * p + (size_t)FQ_BK * dv + FQ_BQ * (FQ_BK + 1));
   dim3 grid((unsigned)((int64_t)((T + FQ_BQ - 1) / FQ_BQ) * B * H)), block(256);
-  if (in_bf16 && o_bf16) family_quadratic_kernel<true, true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F);
-  else if (in_bf16) family_quadratic_kernel<true, false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F);
-  else if (o_bf16) family_quadratic_kernel<false, true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F);
-  else family_quadratic_kernel<false, false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F);
+  if (in_bf16 && o_bf16) family_quadratic_kernel<true, true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F, lay, H);
+  else if (in_bf16) family_quadratic_kernel<true, false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F, lay, H);
+  else if (o_bf16) family_quadratic_kernel<false, true><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F, lay, H);
+  else family_quadratic_kernel<false, false><<<grid, block, lds, st>>>(q, k, v, o, T, p, dv, F, lay, H);
   return hipGetLastError();
 }
 

@@ -57,7 +57,8 @@ hipError_t launch_chunked_f32(const float* q, const float* k, const float* v, vo
                               float* ws, float* s_out, float* z_out, SeqLayout lay, int passes,
                               hipStream_t st);
 hipError_t launch_quadratic_f32(const float* q, const float* k, const float* v, void* o,
-                                bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
+                                bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st,
+                                SeqLayout lay = SeqLayout{});
 // fp16-operand chunked forward (kata_chunked16.h): p = 32, dv = 64, C in {64, 128}
 bool chunked_f16_supported(int p, int dv, int C);
 int64_t f16_state_floats(int dv);
@@ -103,7 +104,8 @@ size_t chunked_bwd_lds_bytes(int p, int dv, int C);
 int64_t chunked_bwd_state_floats(int p, int dv);
 hipError_t launch_chunked_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B, int H,
                               int T, int p, int dv, int C, const SegPlan& plan, float* stats, float* fsum,
-                              float* rsum, float* dq, float* dk, float* dvo, hipStream_t st);
+                              float* rsum, float* dq, float* dk, float* dvo, hipStream_t st,
+                              SeqLayout lay = SeqLayout{});
 // O(T) chunked backward of the full map on bf16 MFMA (p in {16, 32}, dv in {32, 64}); the
 // forward it runs first (for o and the segment prefixes) uses chunks of CHUNKED_BWD_FWD_C
 constexpr int CHUNKED_BWD_FWD_C = 128;
@@ -126,7 +128,7 @@ hipError_t launch_quadratic_bwd_mfma_varlen(const uint16_t* q, const uint16_t* k
                                             hipStream_t st);
 hipError_t launch_quadratic_bwd(const void* q, const void* k, const void* v, const void* go, bool in_bf16, int B,
                                 int H, int T, int p, int dv, int fam, int g, float* ws, float* dq, float* dk,
-                                float* dvo, hipStream_t st);
+                                float* dvo, hipStream_t st, SeqLayout lay = SeqLayout{});
 // bf16 MFMA quadratic form with weights (q_hat . k_hat)^4 (psi_4), full map's (p, dv) set
 hipError_t launch_quadratic_bf16_order2(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                         bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
@@ -140,7 +142,8 @@ hipError_t launch_order_lift(const void* u, bool u_bf16, int64_t rows, int p, in
                              bool psi_bf16, hipStream_t st);
 // fam 3 selects the full map with weights (q_hat . k_hat)^(2g)
 hipError_t launch_family_quadratic(const void* q, const void* k, const void* v, bool in_bf16, void* o, bool o_bf16,
-                                   int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st);
+                                   int B, int H, int T, int p, int dv, int fam, int g, hipStream_t st,
+                                   SeqLayout lay = SeqLayout{});
 hipError_t launch_quadratic_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                                  bool o_bf16, int B, int H, int T, int p, int dv, hipStream_t st);
 // the same over packed token-major sequences (lay.cu set; T = max_len): the full map (fam 0)

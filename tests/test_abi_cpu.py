@@ -248,8 +248,11 @@ def test_chunked_bwd_varlen_validation(lib):
     """kata_chunked_bwd_varlen: argument errors come back before any device access."""
     need = lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 64, ASSOC)
     assert need >= 300 * 2 * 2 * 4                                  # at least D_t, delta_t per row
-    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 64, 64, ASSOC) == 0   # p = 64: no MFMA form
-    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 16, ASSOC) == 0
+    # p = dv = 64: no MFMA form, and the fp32 state does not fit LDS at any chunk
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 64, 64, ASSOC) == 0
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 96, ASSOC) == 0
+    # dv = 16: the fp32 VALU form (chunk 64), D_t and delta_t per row plus its summaries
+    assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 300, 200, 32, 16, ASSOC) >= 300 * 2 * 2 * 4
     # D_t, delta_t are kept for every row of the packed tensor, including rows past the last sequence
     assert lib.kata_chunked_bwd_varlen_workspace_bytes(2, 2, 3000, 200, 32, 64, ASSOC) > need
 
@@ -260,7 +263,10 @@ def test_chunked_bwd_varlen_validation(lib):
         return lib.kata_chunked_bwd_varlen(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["total"],
                                            a["max_len"], a["p"], a["dv"], a["scan"], cu, a["dq"], a["dk"], a["dvo"],
                                            a["ws"], a["wsb"], None)
-    assert vb(dt=F32) == E_UNSUP and vb(p=64) == E_UNSUP and vb(dv=48) == E_UNSUP
+    assert vb(p=64) == E_UNSUP and vb(dv=96) == E_UNSUP and vb(p=80, dv=16) == E_UNSUP
+    # fp32 inputs and other shapes take the VALU form: accepted up to the later checks
+    assert vb(dt=F32, wsb=need - 1) == E_WS and vb(dt=F32, dq=None) == E_NULL
+    assert vb(dv=48, dq=None) == E_NULL and vb(p=16, dv=16, ws=None) == E_WS
     assert vb(scan=7) == E_SCAN and vb(dt=5) == E_DTYPE
     assert vb(cu=None) == E_NULL and vb(cu=A + (1 << 36) + 2) == E_ALIGN
     assert vb(total=-1) == E_SHAPE and vb(max_len=-3) == E_SHAPE
@@ -284,7 +290,9 @@ def test_quadratic_bwd_varlen_validation(lib):
         return lib.kata_quadratic_bwd_varlen(a["q"], a["k"], a["v"], a["g"], a["dt"], a["B"], a["H"], a["total"],
                                              a["max_len"], a["p"], a["dv"], cu, a["dq"], a["dk"], a["dvo"], a["ws"],
                                              a["wsb"], None)
-    assert qb(dt=F32) == E_UNSUP and qb(p=16) == E_UNSUP and qb(dv=48) == E_UNSUP   # the MFMA shapes only
+    assert qb(p=65) == E_UNSUP and qb(dv=80) == E_UNSUP              # p, dv <= 64
+    # fp32 and the non-MFMA shapes run the VALU kernels: accepted up to the later checks
+    assert qb(dt=F32, wsb=need - 1) == E_WS and qb(p=16, dq=None) == E_NULL and qb(dv=48, ws=None) == E_WS
     assert qb(dt=5) == E_DTYPE
     assert qb(cu=None) == E_NULL and qb(cu=A + (1 << 36) + 2) == E_ALIGN
     assert qb(total=-1) == E_SHAPE and qb(max_len=-3) == E_SHAPE and qb(H=-1) == E_SHAPE
@@ -304,8 +312,11 @@ def test_quadratic_varlen_validation(lib):
         a.update(kw)
         return lib.kata_quadratic_fwd_varlen(a["q"], a["k"], a["v"], a["dt"], a["o"], a["odt"], a["B"], a["H"],
                                              a["total"], a["max_len"], a["p"], a["dv"], a["fam"], a["g"], cu, None)
-    assert qv(dt=F32) == E_UNSUP and qv(p=48) == E_UNSUP and qv(dv=8) == E_UNSUP
-    assert qv(fam=1, g=2) == E_UNSUP and qv(fam=2, g=4, p=64) == E_UNSUP   # families: p = 64, g = 2 only
+    assert qv(p=48) == E_UNSUP and qv(dv=8) == E_UNSUP                  # full map: p, dv in {16, 32, 64}
+    assert qv(fam=1, g=2, p=128) == E_UNSUP and qv(fam=2, g=4, p=64, dv=80) == E_UNSUP   # families: p, dv <= 64
+    # fp32 inputs and the families without MFMA kernels run the VALU kernels: accepted up to
+    # the later checks
+    assert qv(dt=F32, q=None) == E_NULL and qv(fam=1, g=2, o=None) == E_NULL and qv(fam=2, g=4, p=64, v=A + 8) == E_ALIGN
     assert qv(fam=1, g=3) == E_FEAT and qv(fam=0, g=2) == E_FEAT and qv(fam=9) == E_FEAT
     assert qv(dt=5) == E_DTYPE and qv(odt=2) == E_DTYPE
     assert qv(cu=None) == E_NULL and qv(cu=A + (1 << 36) + 2) == E_ALIGN

@@ -323,6 +323,114 @@ def test_autograd_varlen():
         start += L
 
 
+def _pack_rows(x, lens, extra):
+    """[B, H, T, w] -> token-major packed [sum(lens) + extra, H, w]: the sequences' rows, then
+    `extra` rows of sequence 0 that belong to no sequence"""
+    rows = [np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)]
+    return np.concatenate(rows + [np.transpose(x[0, :, :extra], (1, 0, 2))], axis=0)
+
+
+@pytest.mark.parametrize("dt,p,dv,lens,max_len", [
+    ("f32", 32, 64, [300, 0, 45, 170], 320), ("bf16", 16, 16, [200, 1, 0, 97], 200),
+    ("f32", 64, 32, [260, 33], 240), ("bf16", 32, 48, [129, 64], 130)])
+def test_quadratic_bwd_varlen_valu(dt, p, dv, lens, max_len):
+    """Packed sequences on the VALU flash-style backward (kata_quadratic_bwd_varlen with fp32
+    inputs or a shape without MFMA kernels): each sequence's gradients bit for bit equal to
+    kata_quadratic_bwd on that sequence alone, and within the fp32 bars of the oracle. An
+    empty and a one-token sequence, a sequence longer than max_len (its rows past max_len are
+    not written) and rows after the last sequence (left at zero)."""
+    B, H, extra = len(lens), 2, 3
+    print(f"[case] quadratic bwd varlen valu {dt} p={p} dv={dv} lens={lens} max_len={max_len}", flush=True)
+    q, k, v = draw_qkv(97, B, H, max(lens), p, dv, dt)
+    go = draw_qkv(98, B, H, max(lens), dv, dv, dt)[0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    got = kata.quadratic_bwd_varlen(*(to_dev(_pack_rows(x, lens, extra), dt) for x in (q, k, v, go)), cu, max_len)
+    got = [to_np(x) for x in got]
+    n = sum(lens)
+    assert all(np.all(x[n:] == 0.0) for x in got), "rows outside every sequence were written"
+    start = 0
+    for b, L in enumerate(lens):
+        Lc = min(L, max_len)
+        if Lc:
+            seq = lambda x: np.transpose(x[start:start + Lc], (1, 0, 2))[None]
+            alone = kata.quadratic_bwd(*(to_dev(np.ascontiguousarray(x[b:b + 1, :, :Lc]), dt) for x in (q, k, v, go)))
+            for name, x, a in zip(("dq", "dk", "dv"), got, alone):
+                assert np.array_equal(seq(x), to_np(a)), (b, name, "differs from the padded call")
+            ref = kb.backward(q[b:b + 1, :, :Lc], k[b:b + 1, :, :Lc], v[b:b + 1, :, :Lc], go[b:b + 1, :, :Lc])
+            # one token: the exact dq, dk vanish (o = v whatever q and k are) and fp32 returns
+            # rounding noise scaled by 1 / (q_hat . k_hat), so only dv = g is checked
+            for name, x, r in list(zip(("dq", "dk", "dv"), got, ref))[0 if Lc > 1 else 2:]:
+                e = _rel(seq(x), r, 1e-2 * float(np.linalg.norm(go[b, :, :Lc])))
+                print(f"  seq {b} L={Lc} {name} rel={e:.2e}", flush=True)
+                assert e <= 2e-4, (b, name)
+                _rows(f"seq {b} {name}", seq(x), r, ROW_BAR_F32)
+        if L > Lc:
+            assert all(np.all(x[start + Lc:start + L] == 0.0) for x in got), "rows past max_len were written"
+        start += L
+
+
+@pytest.mark.parametrize("dt,p,dv,scan", [("f32", 32, 64, "associative"), ("bf16", 32, 16, "sequential"),
+                                           ("f32", 16, 32, "associative")])
+def test_chunked_bwd_varlen_valu(dt, p, dv, scan):
+    """Packed sequences on the fp32 VALU state form (kata_chunked_bwd_varlen with fp32 inputs or
+    a shape without MFMA kernels; the chunk is the largest of 64, 32, 16 that fits LDS): each
+    sequence's gradients against the oracle on it alone at the fp32 bars. Several segments per
+    sequence-head, an empty sequence, a short one (its later segments are empty) and rows
+    after the last sequence (left at zero)."""
+    B, H, max_len, extra = 4, 2, 700, 3
+    lens = [650, 0, 45, 300]
+    print(f"[case] chunked bwd varlen valu {dt} p={p} dv={dv} {scan} lens={lens}", flush=True)
+    q, k, v = draw_qkv(99, B, H, max_len, p, dv, dt)
+    go = draw_qkv(100, B, H, max_len, dv, dv, dt)[0]
+    q[3, 1, 7] = 0.0  # a zero query row: zero dq
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    got = kata.chunked_bwd_varlen(*(to_dev(_pack_rows(x, lens, extra), dt) for x in (q, k, v, go)), cu, max_len,
+                                  scan=scan)
+    got = [to_np(x) for x in got]
+    n = sum(lens)
+    assert all(np.all(x[n:] == 0.0) for x in got), "rows outside every sequence were written"
+    assert np.all(got[0][lens[0] + lens[1] + lens[2] + 7, 1] == 0.0), "zero query row"
+    start = 0
+    for b, L in enumerate(lens):
+        if L:
+            seq = lambda x: np.transpose(x[start:start + L], (1, 0, 2))[None]
+            ref = kb.backward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], go[b:b + 1, :, :L])
+            for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+                e = _rel(seq(x), r, 1e-2 * float(np.linalg.norm(go[b, :, :L])))
+                print(f"  seq {b} L={L} {name} rel={e:.2e}", flush=True)
+                assert e <= 2e-4, (b, name)
+                _rows(f"seq {b} {name}", seq(x), r, ROW_BAR_F32)
+        start += L
+
+
+@pytest.mark.parametrize("dt,p,dv,bar", [("f32", 32, 64, 2e-4), ("bf16", 64, 32, 1.2e-2)])
+def test_autograd_varlen_other_inputs(dt, p, dv, bar):
+    """kata_attention_varlen beyond the bf16 state-form shapes: fp32 inputs (the packed fp32
+    chunked forward and the VALU flash-style backward) and p = 64 (no chunked kernels: the
+    packed quadratic forward, and the MFMA flash-style backward), each sequence against the
+    oracle (fp32 bar, or the bf16 MFMA bar with gradients rounded to bf16)."""
+    B, H, max_len = 3, 2, 400
+    lens = [400, 0, 133]
+    print(f"[case] autograd varlen {dt} p={p} dv={dv}", flush=True)
+    q, k, v = draw_qkv(101, B, H, max_len, p, dv, dt)
+    go = draw_qkv(102, B, H, max_len, dv, dv, dt)[0]
+    pack = lambda x: np.concatenate([np.transpose(x[b, :, :L], (1, 0, 2)) for b, L in enumerate(lens)], axis=0)
+    qd, kd, vd = (to_dev(pack(x), dt).requires_grad_(True) for x in (q, k, v))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    o = kata.kata_attention_varlen(qd, kd, vd, cu, max_len)
+    (o.float() * to_dev(pack(go), "f32")).sum().backward()
+    start = 0
+    for b, L in enumerate(lens):
+        if L:
+            ref = kb.backward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], go[b:b + 1, :, :L])
+            for name, t, r in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
+                got = np.transpose(to_np(t.float())[start:start + L], (1, 0, 2))[None]
+                e = _rel(got, r, 1e-2 * float(np.linalg.norm(go[b, :, :L])))
+                print(f"  seq {b} {name} rel={e:.2e}", flush=True)
+                assert e <= bar, (b, name)
+        start += L
+
+
 @pytest.mark.parametrize("B,H,T,p,dv,scan", [(4, 16, 128, 32, 64, "associative"), (3, 8, 33, 16, 32, "associative"),
                                              (2, 16, 256, 32, 32, "sequential")])
 def test_chunked_bwd_mfma_many_heads(B, H, T, p, dv, scan):

@@ -142,3 +142,42 @@ def test_quadratic_varlen_packed(family, g, p, dv, odt, cut):
         alone = kata.quadratic_fwd(*(to_dev(np.ascontiguousarray(x[b:b + 1, :, :Lc]), "bf16") for x in (q, k, v)),
                                    out_dtype=odt, family=family, g=g)
         assert np.array_equal(got, to_np(alone)[0]), f"seq {b} differs from the padded call"
+
+
+@pytest.mark.parametrize("dt,family,g,p,dv,odt,cut", [
+    ("f32", "full", 1, 32, 64, torch.float32, False), ("f32", "full", 1, 16, 16, torch.bfloat16, True),
+    ("bf16", "sigma", 2, 32, 32, torch.float32, False), ("f32", "block", 2, 64, 48, torch.float32, True),
+    ("bf16", "sigma", 4, 64, 16, torch.bfloat16, False)])
+def test_quadratic_varlen_valu(dt, family, g, p, dv, odt, cut):
+    """Packed sequences on the VALU quadratic kernels (kata_quadratic_fwd_varlen with fp32
+    inputs, or a family shape without MFMA kernels): each sequence against the oracle on it
+    alone, bit for bit equal to kata_quadratic_fwd on it alone, rows outside every sequence
+    untouched; cut: max_len below the longest length (its rows past max_len not written)."""
+    B, H = 6, 2
+    lens = [300, 0, 1, 37, 170, 65]
+    max_len = 256 if cut else 320
+    print(f"[case] quadratic varlen valu {dt} {family}{g} p={p} dv={dv} out={odt} max_len={max_len}", flush=True)
+    q, k, v = draw_qkv(57, B, H, max(lens), p, dv, dt)
+    extra = 5
+    pk = [np.concatenate([_pack(x, lens), x[0, :, :extra].transpose(1, 0, 2)], axis=0) for x in (q, k, v)]
+    total = pk[0].shape[0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda:0")
+    out = torch.full((total, H, dv), 7.0, dtype=odt, device="cuda:0")
+    o = to_np(kata.quadratic_fwd_varlen(*(to_dev(x, dt) for x in pk), cu, max_len, out=out, family=family, g=g))
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    assert np.all(o[starts[-1]:] == 7.0), "rows outside every sequence were written"
+    bar = 1e-4 if odt == torch.float32 else TOL["bf16"]
+    for b, L in enumerate(lens):
+        Lc = min(L, max_len)
+        if L > Lc:
+            assert np.all(o[starts[b] + Lc:starts[b] + L] == 7.0), "rows past max_len were written"
+        if Lc == 0:
+            continue
+        got = np.transpose(o[starts[b]:starts[b] + Lc], (1, 0, 2))
+        ref = kf.naive_family(q[b, :, :Lc], k[b, :, :Lc], v[b, :, :Lc], family, g)
+        err = row_rel_err(got, ref)
+        print(f"  seq {b} L={Lc} rel_err={err:.3e}", flush=True)
+        assert err <= bar
+        alone = kata.quadratic_fwd(*(to_dev(np.ascontiguousarray(x[b:b + 1, :, :Lc]), dt) for x in (q, k, v)),
+                                   out_dtype=odt, family=family, g=g)
+        assert np.array_equal(got, to_np(alone)[0]), f"seq {b} differs from the padded call"
