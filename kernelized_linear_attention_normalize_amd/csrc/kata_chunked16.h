@@ -551,11 +551,16 @@ __device__ __forceinline__ void build_chunk(acc4_t (&S)[NU_W][DV / 16], const ch
 #pragma unroll
       for (int dv = 0; dv < NDV; ++dv) vf[dv] = ld8a(vl[dv] ^ so);
       __builtin_amdgcn_sched_barrier(0);
+      // every tile's lifted operand first, each in its partner's registers, then the products
+      // back to back (a lift into the registers of the previous tile's operand, in flight in
+      // its MFMAs, measured 1.3% slower)
+#pragma unroll
+      for (int u = 0; u < NU_W; ++u) pt[u] = ko * pt[u];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < NU_W; ++u) {
-        const h8_t psi = ko * pt[u];
 #pragma unroll
-        for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(psi, vf[dv], S[u][dv]);
+        for (int dv = 0; dv < NDV; ++dv) S[u][dv] = mfma16(pt[u], vf[dv], S[u][dv]);
       }
     } else if constexpr (!S2) {
       const h8_t ko = ld8a(own ^ so);
