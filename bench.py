@@ -11,6 +11,7 @@ on its own. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--chunk 64|128] [--scan associative|sequential]
                     [--workload long|quadratic|decode|copy] [--no-cpu-baseline]
+                    [--decode-states K]  (decode: K state copies in turn; K >= 4 reads the state from DRAM)
 
 --workload copy times a plain device-to-device copy of 1 GiB (torch's copy kernel); it is
 the reference for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels.
@@ -115,6 +116,8 @@ def main():
     ap.add_argument("--workload", default="long",
                     choices=["long", "quadratic", "decode", "copy", "backward", "varlen"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-states", type=int, default=1,
+                    help="decode workload: state copies used in turn (4 or more: the state comes from DRAM)")
     ap.add_argument("--family", default="full", choices=["full", "sigma", "block"],
                     help="PSD feature family of the quadratic workload (sigma = KATA-Sigma g, "
                          "block = KATA-M g)")
@@ -347,21 +350,28 @@ def main():
         out = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
         nsteps = DECODE["steps"]
         ctr = {"i": 0}
+        # --decode-states K > 1: K copies of the state, used in turn, so that a step's state was
+        # last touched K steps earlier; at K >= 4 (1.1 GB) it cannot stay in the Infinity Cache
+        states = [(S, Z)] + [(S.clone(), Z.clone()) for _ in range(args.decode_states - 1)]
 
         def decode():
             i = ctr["i"] % nsteps
+            Sc, Zc = states[ctr["i"] % len(states)]
             ctr["i"] += 1
-            return kata.decode_step(qd[i], kd[i], vd[i], S, Z, out=out)
+            return kata.decode_step(qd[i], kd[i], vd[i], Sc, Zc, out=out)
         step = [decode]
         dominant = 0
         kernel_name = "decode_kernel"
         flops = None
         units = N
         bytes_alg = N * H * (2 * n * dv * 4 + 2 * n * 4 + (2 * p + 2 * dv) * 2)
+        cached = args.decode_states == 1
         metric = ("recurrent decode step tokens/s (128 seqs x 16 heads) + algorithmic bytes / time vs HBM "
-                  "bandwidth (the state largely stays in the 256 MB Infinity Cache between steps)")
+                  "bandwidth" + (" (the state largely stays in the 256 MB Infinity Cache between steps)" if cached
+                                 else f" ({args.decode_states} state copies used in turn: the state comes from DRAM)"))
         config = {"workload": f"decode: {N} sequences x H={H}, p={p} (n={n}) dv={dv}, fp32 state "
-                              f"from a {DECODE['hist']}-token history, bf16 tokens",
+                              f"from a {DECODE['hist']}-token history, bf16 tokens"
+                              + ("" if cached else f", {args.decode_states} state copies in turn"),
                   "global_batch": N, "heads": H, "p": p, "dv": dv, "parallelism": "single-gpu"}
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         traffic_file = "decode_traffic.txt"
@@ -405,10 +415,14 @@ def main():
             "kernel": kernel_name, "kernel_ms": round(ms_dom, 5),
             "algorithmic_per_launch": alg_per_launch, "step_frac": round(step_frac, 4),
             "launch_ms": [round(x, 5) for x in launch_ms]}
-    if args.workload == "decode":
+    if args.workload == "decode" and args.decode_states == 1:
         roof["note"] = ("achieved = algorithmic bytes (state read + write, tokens) / time; between steps most "
                         "of the 277 MB state stays in the 256 MB Infinity Cache, so this is not a DRAM rate "
-                        "(FETCH_SIZE / WRITE_SIZE count L2-fabric bytes)")
+                        "(FETCH_SIZE / WRITE_SIZE count L2-fabric bytes); --decode-states 4 gives the DRAM rate")
+    elif args.workload == "decode":
+        roof["note"] = (f"achieved = algorithmic bytes (state read + write, tokens) / time, with "
+                        f"{args.decode_states} state copies used in turn ({args.decode_states * 277} MB), "
+                        "so each step reads its state from DRAM")
 
     cpu = None
     if args.workload == "long" and args.family == "full" and not args.no_cpu_baseline:

@@ -74,8 +74,13 @@ hipError_t launch_lift(const void* u, bool u_bf16, int64_t rows, int p, void* ps
 // from HBM: read, add psi_f(k) v, write back, and accumulate psi_f(q) * S_new[f, :].
 // Bytes per head-step: 2 n dv 4 (S) + 2 n 4 (Z) + q, k, v, o. Threads are laid out so
 // that consecutive threads touch consecutive 16-byte pieces of consecutive rows.
+// The state loads do not depend on the lifts, so each thread issues its first DEC_PF
+// pieces before normalising and lifting q and k (every workgroup of the grid starts at
+// once, and HBM would otherwise idle through that prologue), and then keeps DEC_PF loads
+// in flight: the pieces of pass it + DEC_PF are requested before pass it is updated.
 constexpr int DEC_MAXP = 64;
 constexpr int DEC_MAXN = DEC_MAXP * (DEC_MAXP + 1) / 2;
+constexpr int DEC_PF = 8;  // state pieces in flight per thread (12 and 16 measured: no better)
 
 template <bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
@@ -90,6 +95,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = blockIdx.x;
   const int n = p * (p + 1) / 2;
+
+  const int D4 = dv >> 2;                 // float4 pieces per state row
+  const int RPP = 256 / D4;               // rows per pass
+  const bool active = tid < RPP * D4;
+  const int d4 = tid % D4, rr = tid / D4;
+  const int npass = (n + RPP - 1) / RPP;  // passes over the rows (row rr + RPP it)
+  // this head's state through a buffer resource: pieces past row n - 1 load as zero and
+  // their stores are dropped, so the loads need no bounds test
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(S + bh * (int64_t)n * dv, (uint32_t)(n * dv * 4));
+  const uint32_t off0 = (uint32_t)(rr * dv * 4 + d4 * 16), stp = (uint32_t)(RPP * dv * 4);
+  u32x4_t pre[DEC_PF];
+#pragma unroll
+  for (int u = 0; u < DEC_PF; ++u)
+    pre[u] = active ? __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + u * stp, 0, 0) : u32x4_t{0u, 0u, 0u, 0u};
 
   if (wave < 2) {  // wave 0 normalises q, wave 1 normalises k (p <= 64)
     const void* src = wave == 0 ? q : k;
@@ -109,20 +128,26 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   }
   __syncthreads();
 
-  const int D4 = dv >> 2;                 // float4 pieces per state row
-  const int RPP = 256 / D4;               // rows per pass
-  const bool active = tid < RPP * D4;
-  const int d4 = tid % D4, rr = tid / D4;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     const f32x4_t v4 = {vv[4 * d4], vv[4 * d4 + 1], vv[4 * d4 + 2], vv[4 * d4 + 3]};
-    f32x4_t* Sb = reinterpret_cast<f32x4_t*>(S + bh * (int64_t)n * dv);
-#pragma unroll 4
-    for (int f = rr; f < n; f += RPP) {
-      f32x4_t s = Sb[(int64_t)f * D4 + d4];
-      s += psk[f] * v4;
-      Sb[(int64_t)f * D4 + d4] = s;
-      acc += psq[f] * s;
+    for (int it = 0; it < npass; it += DEC_PF) {
+      u32x4_t cur[DEC_PF];
+      const uint32_t offc = off0 + (uint32_t)it * stp;
+#pragma unroll
+      for (int u = 0; u < DEC_PF; ++u) {
+        cur[u] = pre[u];
+        pre[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, offc + (DEC_PF + u) * stp, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < DEC_PF; ++u) {
+        const int f = rr + (it + u) * RPP;
+        if (f < n) {
+          const f32x4_t s = __builtin_bit_cast(f32x4_t, cur[u]) + psk[f] * v4;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, s), rs, offc + u * stp, 0, 0);
+          acc += psq[f] * s;
+        }
+      }
     }
   }
   red[tid] = acc;
