@@ -7,11 +7,15 @@ associative inter-segment scan; seeded N(0,1) synthetic inputs (seed 2).
 One step = the whole forward: its three passes (segment summaries, scan, segments),
 issued as kata_chunked_fwd_passes calls on one stream with HIP events between them, so
 the dominant kernel (the segment pass, which performs all of the method's flops) is timed
-on its own. Prints ONE JSON line.
+on its own. Before the W warmup steps, untimed steps run for --settle-s seconds (default 0.3),
+so that the GPU is at its steady clock when the K timed steps start (from idle it takes some
+tens of milliseconds of work to get there); the JSON's "settle" field records them.
+Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--chunk 64|128] [--scan associative|sequential]
                     [--workload long|quadratic|decode|copy] [--no-cpu-baseline]
                     [--decode-states K]  (decode: K state copies in turn; K >= 4 reads the state from DRAM)
+                    [--settle-s S]  (seconds of untimed steps before the warmup steps; default 0.3)
 
 --workload copy times a plain device-to-device copy of 1 GiB (torch's copy kernel); it is
 the reference for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels.
@@ -116,6 +120,8 @@ def main():
     ap.add_argument("--workload", default="long",
                     choices=["long", "quadratic", "decode", "copy", "backward", "varlen"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warmup steps, so the GPU reaches its steady clock")
     ap.add_argument("--decode-states", type=int, default=1,
                     help="decode workload: state copies used in turn (4 or more: the state comes from DRAM)")
     ap.add_argument("--family", default="full", choices=["full", "sigma", "block"],
@@ -376,8 +382,20 @@ def main():
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         traffic_file = "decode_traffic.txt"
 
-    # every launch of a step is bracketed by HIP events on the stream it runs on
+    # Clock settle: from idle, the GPU takes some tens of milliseconds of work to reach its
+    # steady clock (measured: the first ~100 steps of the long workload run up to 17% slower),
+    # far more than a few warmup steps. So untimed steps run for args.settle_s seconds first;
+    # then the args.warmup warmup steps, then exactly args.steps timed steps.
     torch.cuda.synchronize(dev)
+    settle_steps, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(8):
+            for call in step:
+                call()
+        settle_steps += 8
+        torch.cuda.synchronize(dev)
+    settle_s = time.perf_counter() - t_settle
+    # every launch of a step is bracketed by HIP events on the stream it runs on
     for _ in range(args.warmup):
         for call in step:
             call()
@@ -431,6 +449,7 @@ def main():
     rec = {"metric": metric, "value": round(value, 1),
            "unit": "bytes/s" if args.workload == "copy" else "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "settle": {"steps": settle_steps, "s": round(settle_s, 3)},
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1))", "config": config, "roofline": roof,
            "cpu_baseline": cpu, "source_hash": source_hash()}

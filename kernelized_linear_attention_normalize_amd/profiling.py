@@ -8,6 +8,9 @@
     python -m kernelized_linear_attention_normalize_amd.profiling traffic \\
         --kernel <substring> --fetch <csv> --write <csv> --copy-fetch <csv> --copy-write <csv> \\
         --copy-bytes <bytes> --cmd "<commands>" --out profiles/<name>_traffic.txt
+    python -m kernelized_linear_attention_normalize_amd.profiling counters \\
+        --pmc <csv of pass A> --pmc <csv of pass B> --kernel "<label>=<substring>" ... \\
+        --title "<workload>" --cmd "<commands>" --out profiles/<name>_counters.txt
 
 The traffic summary scales the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) by
 what they read for a plain device copy of known size, averages over the dispatches of the
@@ -85,7 +88,7 @@ def cmd_traffic(a):
     sf = a.copy_bytes / (cf * 1024.0)   # true bytes per counted byte, reads
     sw = a.copy_bytes / (cw * 1024.0)   # writes
     fetch_b, write_b = fk * 1024.0 * sf, wk * 1024.0 * sw
-    lines = [f"# HBM traffic per dispatch of '{a.kernel}' from rocprofv3 PMC counters",
+    lines = [f"# HBM traffic per dispatch of '{a.kernel}' from rocprofv3 PMC counters" + (f" ({a.title})" if a.title else ""),
              f"# commands: {a.cmd}",
              f"# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the ratio of the",
              f"# known bytes of a plain {a.copy_bytes}-byte device copy ('{a.copy_kernel}') to what the",
@@ -114,7 +117,7 @@ def cmd_mfma(a):
     gui, _ = counter_per_dispatch(a.pmc, "GRBM_GUI_ACTIVE", a.kernel)
     cycles = gui / XCDS
     frac = busy / (cycles * SIMDS)
-    lines = [f"# MFMA pipe occupancy of '{a.kernel}' from rocprofv3 PMC counters",
+    lines = [f"# MFMA pipe occupancy of '{a.kernel}' from rocprofv3 PMC counters" + (f" ({a.title})" if a.title else ""),
              f"# command: {a.cmd}",
              f"# busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs);",
              f"# it counts every executed MFMA (padding and recompute included), unlike the",
@@ -124,6 +127,40 @@ def cmd_mfma(a):
              f"gpu_active_cycles_per_xcd: {cycles:.0f}",
              f"mfma_busy_fraction: {frac:.4f}",
              f"source_hash: {source_hash()}"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _per_dispatch_any(paths, counter, kernel):
+    for path in paths:
+        try:
+            return counter_per_dispatch(path, counter, kernel)[0]
+        except SystemExit:
+            continue
+    return float("nan")
+
+
+def cmd_counters(a):
+    """Wait, VALU and LDS shares of the named kernels from two counter passes: fractions of
+    wave cycles (SQ_WAIT_ANY, SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_VALU over SQ_WAVE_CYCLES, all in
+    the same quad-cycle units), LDS activity and bank conflicts over SQ_BUSY_CU_CYCLES, and
+    instruction counts per dispatch (SQ_INSTS_VALU includes the MFMAs)."""
+    lines = [f"# rocprofv3 counter summary: {a.title}", f"# commands (one run per pass): {a.cmd}",
+             "# wait_any, wait_lds, valu_act: fractions of SQ_WAVE_CYCLES; lds_busy = SQ_LDS_IDX_ACTIVE /",
+             "# SQ_BUSY_CU_CYCLES, bank_cf = SQ_LDS_BANK_CONFLICT / SQ_BUSY_CU_CYCLES; instruction counts",
+             "# per dispatch (SQ_INSTS_VALU includes the MFMAs)", "#",
+             f"{'kernel':28s} {'wait_any':>8s} {'wait_lds':>8s} {'valu_act':>8s} {'lds_busy':>8s} {'bank_cf':>8s} "
+             f"{'valu_insts':>11s} {'mfma_insts':>11s} {'salu_insts':>11s}"]
+    for spec in a.kernel:
+        label, sub = spec.split("=", 1)
+        g = lambda c: _per_dispatch_any(a.pmc, c, sub)
+        wave = g("SQ_WAVE_CYCLES")
+        busy = g("SQ_BUSY_CU_CYCLES")
+        lines.append(f"{label[:28]:28s} {g('SQ_WAIT_ANY') / wave:8.2f} {g('SQ_WAIT_INST_LDS') / wave:8.2f} "
+                     f"{g('SQ_ACTIVE_INST_VALU') / wave:8.2f} {g('SQ_LDS_IDX_ACTIVE') / busy:8.2f} "
+                     f"{g('SQ_LDS_BANK_CONFLICT') / busy:8.3f} {g('SQ_INSTS_VALU'):11.4g} "
+                     f"{g('SQ_INSTS_MFMA'):11.4g} {g('SQ_INSTS_SALU'):11.4g}")
+    lines.append(f"source_hash: {source_hash()}")
     open(a.out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -143,6 +180,7 @@ def main():
     m.add_argument("--kernel", required=True)
     m.add_argument("--cmd", required=True)
     m.add_argument("--out", required=True)
+    m.add_argument("--title", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--fetch", required=True)
@@ -153,8 +191,15 @@ def main():
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--title", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", action="append", required=True)
+    c.add_argument("--kernel", action="append", required=True, help="label=kernel-name substring")
+    c.add_argument("--title", default="")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"kernels": cmd_kernels, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "mfma": cmd_mfma, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
