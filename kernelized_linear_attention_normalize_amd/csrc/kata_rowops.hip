@@ -77,17 +77,22 @@ hipError_t launch_lift(const void* u, bool u_bf16, int64_t rows, int p, void* ps
 // The state loads do not depend on the lifts, so each thread issues its first DEC_PF
 // pieces before normalising and lifting q and k (every workgroup of the grid starts at
 // once, and HBM would otherwise idle through that prologue), and then keeps DEC_PF loads
-// in flight: the pieces of pass it + DEC_PF are requested before pass it is updated.
+// in flight: once pass it is updated and stored, its registers are refilled with pass
+// it + DEC_PF. The shape (p = 32, dv = 64) is compiled with fixed sizes, so its 33 passes
+// unroll and the compiler waits for exactly the load a pass needs.
 constexpr int DEC_MAXP = 64;
 constexpr int DEC_MAXN = DEC_MAXP * (DEC_MAXP + 1) / 2;
-constexpr int DEC_PF = 8;  // state pieces in flight per thread (12 and 16 measured: no better)
+constexpr int DEC_PF = 8;  // state pieces in flight per thread
 
-template <bool IN_BF16, bool OUT_BF16>
+// PT, DVT > 0 fix p and dv at compile time (the pass loop then unrolls into straight-line
+// code whose load waits the compiler counts exactly); 0 takes them from the arguments
+template <bool IN_BF16, bool OUT_BF16, int PT = 0, int DVT = 0>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
                                                      const void* __restrict__ k,
                                                      const void* __restrict__ v,
                                                      float* __restrict__ S, float* __restrict__ Z,
-                                                     void* __restrict__ o, int p, int dv) {
+                                                     void* __restrict__ o, int p_arg, int dv_arg) {
+  const int p = PT > 0 ? PT : p_arg, dv = DVT > 0 ? DVT : dv_arg;
   __shared__ float qh[DEC_MAXP], kh[DEC_MAXP], vv[DEC_MAXP];
   __shared__ float psq[DEC_MAXN], psk[DEC_MAXN];
   __shared__ f32x4_t red[256];
@@ -131,22 +136,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     const f32x4_t v4 = {vv[4 * d4], vv[4 * d4 + 1], vv[4 * d4 + 2], vv[4 * d4 + 3]};
+#pragma unroll
     for (int it = 0; it < npass; it += DEC_PF) {
-      u32x4_t cur[DEC_PF];
       const uint32_t offc = off0 + (uint32_t)it * stp;
 #pragma unroll
       for (int u = 0; u < DEC_PF; ++u) {
-        cur[u] = pre[u];
-        pre[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, offc + (DEC_PF + u) * stp, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < DEC_PF; ++u) {
+        // slot u: update pass it + u, then refill the slot's registers with pass it + u + DEC_PF
+        // (in that order, so the refill lands in the registers the loop carries and needs no
+        // copy, which would wait for the load)
         const int f = rr + (it + u) * RPP;
         if (f < n) {
-          const f32x4_t s = __builtin_bit_cast(f32x4_t, cur[u]) + psk[f] * v4;
+          const f32x4_t s = __builtin_bit_cast(f32x4_t, pre[u]) + psk[f] * v4;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, s), rs, offc + u * stp, 0, 0);
           acc += psq[f] * s;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        pre[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, offc + (DEC_PF + u) * stp, 0, 0);
       }
     }
   }
@@ -174,7 +179,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool in_bf
                          float* Z, void* o, bool o_bf16, int N, int H, int p, int dv,
                          hipStream_t st) {
   dim3 grid((unsigned)((int64_t)N * H)), block(256);
-  if (in_bf16 && o_bf16) decode_kernel<true, true><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
+  if (in_bf16 && o_bf16 && p == 32 && dv == 64) decode_kernel<true, true, 32, 64><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
+  else if (in_bf16 && o_bf16) decode_kernel<true, true><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
   else if (in_bf16) decode_kernel<true, false><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
   else if (o_bf16) decode_kernel<false, true><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
   else decode_kernel<false, false><<<grid, block, 0, st>>>(q, k, v, S, Z, o, p, dv);
