@@ -136,6 +136,29 @@ def _dev(*ts: torch.Tensor) -> torch.device:
     return dev
 
 
+def _same_dtype(*ts: torch.Tensor) -> None:
+    """The C calls take one input dtype for q, k and v (and grad_o): a mismatch would make a
+    kernel read a tensor with the wrong element size."""
+    for t in ts:
+        if t.dtype != ts[0].dtype:
+            raise TypeError("q, k and v must share one dtype (float32 or bfloat16)")
+    _dt(ts[0])
+
+
+def _out(out, shape, dtype, dev: torch.device) -> torch.Tensor:
+    """A new output tensor, or the caller's after checking its shape and dtype (the C calls
+    write shape's elements through the pointer)."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    _dt(out)
+    _dev(out)
+    if out.device != dev:
+        raise ValueError("out must be on the inputs' device")
+    return out
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -216,14 +239,13 @@ def chunked_fwd_varlen(q, k, v, cu_seqlens, max_len: int, C: int = 64, scan="ass
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:2] != q.shape[:2]:
         raise ValueError("shape mismatch between q, k and v")
+    _same_dtype(q, k, v)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
     _dev(cu_seqlens, q)
     B = cu_seqlens.numel() - 1
     sc = _scan_code(scan)
-    if out is None:
-        out = torch.empty((total, H, dv), dtype=out_dtype or v.dtype, device=dev)
-    _dev(out, q)
+    out = _out(out, (total, H, dv), out_dtype or v.dtype, dev)
     fam = _fam(family, g)
     need = int(lib.kata_chunked_workspace_bytes_family(B, H, max_len, p, dv, C, sc, _dt(q), fam, g))
     if workspace is None and need > 0:
@@ -259,13 +281,12 @@ def quadratic_fwd_varlen(q, k, v, cu_seqlens, max_len: int, out_dtype=None, out=
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:2] != q.shape[:2]:
         raise ValueError("shape mismatch between q, k and v")
+    _same_dtype(q, k, v)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-d int32 tensor [B + 1]")
     _dev(cu_seqlens, q)
     B = cu_seqlens.numel() - 1
-    if out is None:
-        out = torch.empty((total, H, dv), dtype=out_dtype or v.dtype, device=dev)
-    _dev(out, q)
+    out = _out(out, (total, H, dv), out_dtype or v.dtype, dev)
     with torch.cuda.device(dev):
         _check(lib.kata_quadratic_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q), out.data_ptr(),
                                              _dt(out), B, H, total, max_len, p, dv, _fam(family, g), g,
@@ -299,6 +320,8 @@ def chunked_fwd_noalloc(q, k, v, out, C: int = 64, scan="associative"):
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != q.shape[:3] or tuple(out.shape) != (B, H, T, dv):
         raise ValueError("shape mismatch between q, k, v and out")
+    _same_dtype(q, k, v)
+    _dt(out)
     with torch.cuda.device(dev):
         _check(lib.kata_chunked_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
                                             out.data_ptr(), _dt(out), B, H, T, p, dv, C, _scan_code(scan),
@@ -325,10 +348,9 @@ def chunked_fwd(q, k, v, C: int = 64, scan="associative", out_dtype=None, out=No
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
         raise ValueError("shape mismatch between q, k and v")
+    _same_dtype(q, k, v)
     sc = _scan_code(scan)
-    if out is None:
-        out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
-    _dev(out, q)
+    out = _out(out, (B, H, T, dv), out_dtype or v.dtype, dev)
     fam = _fam(family, g)
     need = int(lib.kata_chunked_workspace_bytes_family(B, H, T, p, dv, C, sc, _dt(q), fam, g))
     if workspace is None and need > 0:
@@ -404,9 +426,8 @@ def quadratic_fwd(q, k, v, out_dtype=None, out=None, family: str = "full", g: in
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
         raise ValueError("shape mismatch between q, k and v")
-    if out is None:
-        out = torch.empty((B, H, T, dv), dtype=out_dtype or v.dtype, device=dev)
-    _dev(out, q)
+    _same_dtype(q, k, v)
+    out = _out(out, (B, H, T, dv), out_dtype or v.dtype, dev)
     with torch.cuda.device(dev):
         if order != 1:
             if family != "full":
@@ -434,14 +455,15 @@ def decode_step(q, k, v, S, Z, out_dtype=None, out=None, family: str = "full", g
     dev = _dev(q, k, v, S, Z)
     N, H, p = q.shape
     dv = v.shape[-1]
+    if k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("shape mismatch between q, k and v")
+    _same_dtype(q, k, v)
     n = feature_dim(p, family, g)
     if S.dtype != torch.float32 or Z.dtype != torch.float32:
         raise TypeError("S and Z must be float32")
     if tuple(S.shape) != (N, H, n, dv) or tuple(Z.shape) != (N, H, n):
         raise ValueError("state shape mismatch")
-    if out is None:
-        out = torch.empty((N, H, dv), dtype=out_dtype or v.dtype, device=dev)
-    _dev(out, q)
+    out = _out(out, (N, H, dv), out_dtype or v.dtype, dev)
     with torch.cuda.device(dev):
         if family == "full":
             _check(lib.kata_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q),
