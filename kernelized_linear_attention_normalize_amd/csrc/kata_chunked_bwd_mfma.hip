@@ -56,7 +56,10 @@ template <int P, int DV>
 struct Lay {
   static constexpr int NT = DV / 16, NH = P / 16, KQ = P / 4, NKS = DV / 32, NV8 = DV / 8;
   static constexpr int NTL = ntiles<P>(), NPAIR = (NTL + 1) / 2;
-  static constexpr int QP = P + 8;   // fp32 row pitch
+  // fp32 row pitch: 16 lanes reading 16 rows at one column with 16-byte reads then start at
+  // 16 distinct 4-bank groups (at P + 8 = 40 floats only 8, a 2-way conflict; P + 4 measured
+  // 3.6% faster over the whole backward, bitwise equal)
+  static constexpr int QP = P + 4;
   static constexpr int TP = 80;      // transposed fp32 rows: token t of component c at c TP + 8 (c / KQ) + t
   static constexpr int VTP = 80;     // transposed bf16 rows, token t at vt_pos(t)
   static constexpr int RP = DV + 8;  // bf16 row pitch
@@ -689,7 +692,7 @@ __device__ __forceinline__ void write_pairs(uint16_t* sb, const f32x4_t (&R)[wav
 // hi + lo, the raw key exact), masked to t >= s: lane (s, lg) holds queries 16 q2 + 4 lg + r
 template <int P>
 __device__ __forceinline__ f32x4_t rev_scores(const float* qhr, bf16x8_t kb, float invk, int q2, int kt, int ln, int lg) {
-  constexpr int QP = P + 8;
+  constexpr int QP = P + 4;  // Lay::QP
   f32x4_t Sc = zero4();
   if (q2 >= kt) {
     float qs[8];
